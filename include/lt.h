@@ -1,0 +1,175 @@
+/*
+ * lt.h -- C ABI of liblt, just-in-time decompression of compressed tensors in
+ * MI355X (gfx950) device memory.
+ *
+ * The method: tensors stay resident in device memory in compressed form and
+ * are expanded into a working buffer right before use (page "Openai/692db884
+ * ..." (section 28), the five-step decode description: a compact blob plus a
+ * small metadata record per tensor, decoded into a temporary buffer whose
+ * pointer is handed to the consumer).  For weights the compressed form is
+ * INT4 or INT8 codes with fp16 scales and int8 zero points, LZ4-compressed in
+ * independent blocks, expanded on the GPU straight to fp16 ("GPU Compression
+ * Pipeline - TDD Roadmap", Phase 1.1, Phase 1.2, Phase 2.1, Phase 3.1; the
+ * 64 KiB block size from Phase 6.1).  For zero-heavy ReLU activations it is
+ * plain LZ4, decoded to bytes (page "Openai/691a41cd ..." (section 38), the
+ * list of what wastes GPU memory: zeros after ReLU).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked DEVICE point to device memory; HOST to host memory.
+ *   - Every device entry point is asynchronous on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream).  It checks its arguments
+ *     synchronously, launches, and returns; it never synchronizes, allocates,
+ *     or keeps state.  The caller owns every buffer; device buffers must stay
+ *     alive until the stream work completes.  Calls are reentrant.
+ *   - Tensors are row-major [rows, cols]; element e = r*cols + c.
+ *   - INT4 codes are unsigned 0..15, two per byte, element 2k in the low
+ *     nibble of byte k and element 2k+1 in the high nibble.  INT8 codes are
+ *     signed bytes.
+ *   - Groups are `group` consecutive elements in element order: element e
+ *     uses scale and zero point number e / group.  Per-row (per-channel)
+ *     scaling is group = cols, per-tensor is group = rows*cols.  Either
+ *     cols % group == 0 or group % cols == 0, and (rows*cols) % group == 0.
+ *   - Scales are fp16 bit patterns (uint16).  Zero points are int8; zp = NULL
+ *     means every zero point is 0.
+ *   - Dequantization: out[e] = fp16_rne( (q[e] - zp[g]) * scale[g] ).  The
+ *     product is exact before the single rounding, so results are bit-exact.
+ *   - The return value reports argument and launch errors only.  Decode errors
+ *     are reported per chunk on the device in `chunk_status` (may be NULL).
+ *     A failed chunk's own output range holds unspecified bytes afterwards;
+ *     nothing outside the chunk's range is ever written.
+ */
+#ifndef LT_H
+#define LT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LT_ABI_VERSION 1
+
+typedef enum lt_status {
+  LT_OK = 0,
+  LT_ERR_INVALID_ARG = 1, /* a pointer, size, shape or alignment is invalid */
+  LT_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve */
+  LT_ERR_LAUNCH = 3,      /* the HIP runtime refused the launch */
+  LT_ERR_DEVICE = 4       /* no usable gfx950 device for the current context */
+} lt_status;
+
+/* Per-chunk codes written to chunk_status[i] (DEVICE, int32). */
+enum {
+  LT_CHUNK_OK = 0,
+  LT_CHUNK_TRUNCATED = 1,     /* block ended inside a sequence, or is empty */
+  LT_CHUNK_BAD_OFFSET = 2,    /* match distance 0, or before the chunk start */
+  LT_CHUNK_OVERRUN = 3,       /* a sequence would write past the chunk end */
+  LT_CHUNK_SIZE_MISMATCH = 4, /* block decoded to fewer bytes than the chunk */
+  LT_CHUNK_BAD_TABLE = 5      /* the chunk's table entries are inconsistent */
+};
+
+/* Largest decoded chunk the device decoder accepts (bytes). */
+#define LT_MAX_CHUNK_BYTES (1u << 30)
+
+/*
+ * Chunk table (HOST struct; its members point to DEVICE memory).
+ * A tensor's byte stream (packed INT4 codes, INT8 codes or raw bytes) of
+ * total_bytes bytes is cut into n_chunks consecutive chunks; chunk i holds
+ * decoded bytes [dst_off[i], dst_off[i+1]) and is stored as one raw LZ4 block
+ * (no frame, no size prefix, no dictionary) at comp[comp_off[i] ..
+ * comp_off[i+1]).  The blocks are independent: a match never reaches before
+ * its own chunk's start.
+ *   comp       DEVICE uint8[comp_bytes]
+ *   comp_off   DEVICE uint64[n_chunks + 1], non-decreasing, comp_off[n] <= comp_bytes
+ *   dst_off    DEVICE uint64[n_chunks + 1], dst_off[0] = 0, non-decreasing,
+ *              dst_off[n] = total_bytes, dst_off[i] % 16 == 0 for i < n
+ *   max_chunk_bytes  host-known max(dst_off[i+1] - dst_off[i]),
+ *              1 <= max_chunk_bytes <= LT_MAX_CHUNK_BYTES (ignored if n_chunks == 0)
+ * Entries that break these rules make that chunk fail with LT_CHUNK_BAD_TABLE
+ * (checked on the device); the struct itself is read only during the call.
+ */
+typedef struct lt_chunk_table {
+  const uint8_t *comp;
+  const uint64_t *comp_off;
+  const uint64_t *dst_off;
+  uint32_t n_chunks;
+  uint32_t max_chunk_bytes;
+  uint64_t total_bytes;
+  uint64_t comp_bytes;
+} lt_chunk_table;
+
+/*
+ * lt_decode_lz4 -- decode-only mode (zero-heavy activations, or any bytes).
+ * dst: DEVICE uint8[t->total_bytes], 16-byte aligned.
+ * chunk_status: DEVICE int32[t->n_chunks] or NULL.
+ * Decodes every chunk of the table into dst.  One workgroup per chunk.
+ */
+lt_status lt_decode_lz4(const lt_chunk_table *t, uint8_t *dst, int32_t *chunk_status,
+                        void *stream);
+
+/*
+ * lt_dequant_int4 -- packed INT4 -> fp16 (roadmap Phase 1.1).
+ * packed: DEVICE uint8[rows*cols/2]; scales: DEVICE uint16[rows*cols/group];
+ * zp: DEVICE int8[rows*cols/group] or NULL; out: DEVICE uint16 (fp16)
+ * [rows*cols], 16-byte aligned.  rows*cols must be even and > 0.
+ */
+lt_status lt_dequant_int4(const uint8_t *packed, const uint16_t *scales, const int8_t *zp,
+                          uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                          void *stream);
+
+/*
+ * lt_dequant_int8 -- INT8 -> fp16, per-tensor or per-channel (roadmap Phase
+ * 1.2).  q: DEVICE int8[rows*cols]; other arguments as lt_dequant_int4.
+ */
+lt_status lt_dequant_int8(const int8_t *q, const uint16_t *scales, const int8_t *zp,
+                          uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                          void *stream);
+
+/*
+ * lt_fused_lz4_int4 -- LZ4 decode fused with INT4 unpack and dequantization
+ * (roadmap Phase 2.1: decompress and dequantize in one kernel, no
+ * intermediate buffer).  The table's decoded stream is the packed INT4 codes:
+ * t->total_bytes must equal rows*cols/2.  out: DEVICE uint16 (fp16)
+ * [rows*cols], 16-byte aligned; other arguments as lt_dequant_int4.
+ * Result equals lt_dequant_int4 applied to lt_decode_lz4's output.
+ */
+lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                            uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                            int32_t *chunk_status, void *stream);
+
+/*
+ * lt_fused_lz4_int8 -- LZ4 decode fused with INT8 dequantization; the
+ * table's decoded stream is the int8 codes: t->total_bytes == rows*cols.
+ */
+lt_status lt_fused_lz4_int8(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                            uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                            int32_t *chunk_status, void *stream);
+
+/* ---- host-side packer: builds the inputs above (no device work) ---- */
+
+/* Worst-case size of one LZ4 block holding n bytes. */
+uint64_t lt_lz4_bound(uint64_t n);
+
+/*
+ * lt_pack_int4 -- HOST.  codes: uint8[n_codes] (values 0..15, higher bits
+ * ignored), n_codes even; packed: uint8[n_codes/2].  Low nibble first.
+ */
+lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed);
+
+/*
+ * lt_compress_chunks -- HOST.  Compresses src[dst_off[i] .. dst_off[i+1]) for
+ * each of n_chunks chunks as an independent LZ4 block and concatenates them
+ * into comp (capacity comp_cap); comp_off (uint64[n_chunks+1]) receives the
+ * prefix sums.  threads <= 0 means one per host core.  Returns
+ * LT_ERR_INVALID_ARG for a non-monotone table or too small a buffer
+ * (sum of lt_lz4_bound over the chunks always suffices).
+ */
+lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
+                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads);
+
+const char *lt_status_str(lt_status s);
+int lt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LT_H */

@@ -498,9 +498,9 @@ static uint64_t pick_len(uint64_t *s, uint64_t lo, uint64_t hi, const uint64_t *
 /* Build a random valid LZ4 block and the bytes it must decode to, side by
  * side, without using the compressor: literal lengths biased to the nibble /
  * extra-byte boundaries, match lengths likewise, distances biased to small and
- * extreme values (1, 2, 3, 4, 7, 8, 63, 64, 65, 65535).  Stops once `target`
- * output bytes would be exceeded; the block always ends with a literal-only
- * sequence.  Returns the stream length (0 if a capacity is too small);
+ * extreme values (1, 2, 3, 4, 7, 8, 63, 64, 65, 65535).  Once the next match
+ * would pass `target` output bytes, a literal-only last sequence fills the
+ * output to exactly `target` bytes.  Returns the stream length (0 if a capacity is too small);
  * *out_len gets the output length.  Needs stream_cap >= 2*target + 64 and
  * out_cap >= target. */
 uint64_t ltref_seqgen(uint64_t seed, uint64_t target, uint8_t *stream, uint64_t stream_cap,
@@ -525,7 +525,13 @@ uint64_t ltref_seqgen(uint64_t seed, uint64_t target, uint8_t *stream, uint64_t 
     uint64_t after = op + nl;
     uint64_t ml = pick_len(&s, 4, 300, MSP, 11);
     if (after == 0 || ml > target - after) {
-      o = put_sequence(stream, o, lit, nl, 0, 0, 0);   /* last: literals only */
+      /* last sequence: literals only, filling the output to exactly target */
+      nl = target - op;
+      for (uint64_t k = 0; k < nl; k++) {
+        uint64_t r = sm64(&s);
+        lit[k] = (r & 3) ? (uint8_t)((r >> 8) & 7) : (uint8_t)(r >> 16);
+      }
+      o = put_sequence(stream, o, lit, nl, 0, 0, 0);
       memcpy(expected + op, lit, nl);
       op += nl;
       break;

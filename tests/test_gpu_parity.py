@@ -1,0 +1,338 @@
+"""GPU parity: every liblt entry point against the CPU oracle, element by element.
+
+Bar: bit-exact for decoded bytes and for fp16 outputs (the dequantized value
+is the exact product rounded once, so 0 ULP is well defined).  Inputs are the
+seeded synthetic workloads (synth) at full size and at small sizes that span
+several 1 KiB tiles, several chunks and a ragged tail; LZ4 streams come from
+both the library's host packer (the configuration the benchmark times) and
+the oracle's own compressor and sequence generator.  Expected values come from
+the oracle applied to the generator's codes, never from the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_dequantization_amd as lt
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def t_u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def t_i8(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int8)).to(DEV)
+
+
+def t_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(DEV)
+
+
+def host_u16(t):
+    torch.cuda.synchronize()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+
+
+def assert_same(got, ref, what):
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "%s: %d of %d differ, first at %d: got %#x want %#x" % (
+        what, bad.size, ref.size, bad[0], got[bad[0]], ref[bad[0]])
+
+
+def status_tensor(n):
+    return torch.full((max(n, 1),), -1, dtype=torch.int32, device=DEV)
+
+
+def statuses(st, n):
+    torch.cuda.synchronize()
+    return st[:n].cpu().numpy()
+
+
+def table_from_oracle(ot: O.Table):
+    return lt.ChunkTable.from_host(ot.comp, ot.comp_off, ot.dst_off, DEV)
+
+
+# ------------------------------------------------------------ raw dequant
+
+def _raw_int4(codes, scales, zp, rows, cols, group):
+    packed = lt.pack_int4(codes)
+    out = lt.dequant_int4(t_u8(packed), t_u16(scales), t_i8(zp), (rows, cols), group)
+    ref = O.dequant_int4(O.pack_int4(codes), scales, zp, group)
+    assert_same(host_u16(out), ref, "dequant_int4 %dx%d g%d" % (rows, cols, group))
+
+
+def test_raw_int4_config1():
+    w = synth.config1()
+    _raw_int4(w.codes, w.scales, w.zp, w.rows, w.cols, w.group)
+
+
+def test_raw_int4_config3_full():
+    w = synth.config3()
+    _raw_int4(w.codes, w.scales, w.zp, w.rows, w.cols, w.group)
+
+
+def test_raw_int4_whole_domain():
+    """every code x every zero point x every finite fp16 scale, group 16"""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    scales = h[(h & 0x7C00) != 0x7C00]
+    n_groups = scales.size * 256
+    sc = np.repeat(scales[None, :], 256, axis=0).ravel()
+    zp = np.repeat(np.arange(-128, 128, dtype=np.int64).astype(np.int8), scales.size)
+    codes = np.tile(np.arange(16, dtype=np.uint8), n_groups)
+    _raw_int4(codes, sc, zp, n_groups, 16, 16)
+
+
+@pytest.mark.parametrize("rows,cols,group", [
+    (10, 36, 6), (10, 36, 12), (10, 36, 36), (10, 36, 360), (3, 2, 2), (1, 6, 6), (7, 10, 70),
+    (33, 128, 128), (64, 4096, 4096 * 64), (17, 24, 8), (5, 1000, 1000),
+])
+def test_raw_int4_groups_and_tails(rows, cols, group):
+    rng = np.random.default_rng(rows * 1000 + cols + group)
+    n = rows * cols
+    codes = rng.integers(0, 16, n, dtype=np.uint8)
+    scales = synth.fp16_bits(rng.uniform(-2, 2, n // group))
+    zp = rng.integers(-128, 128, n // group).astype(np.int8)
+    _raw_int4(codes, scales, zp, rows, cols, group)
+    _raw_int4(codes, scales, None, rows, cols, group)
+
+
+def _raw_int8(q, scales, zp, rows, cols, group):
+    out = lt.dequant_int8(t_i8(q), t_u16(scales), t_i8(zp), (rows, cols), group)
+    ref = O.dequant_int8(q, scales, zp, group)
+    assert_same(host_u16(out), ref, "dequant_int8 %dx%d g%d" % (rows, cols, group))
+
+
+def test_raw_int8_config2():
+    w = synth.config2()
+    _raw_int8(w.q, w.scales, w.zp, w.rows, w.cols, w.group)
+
+
+def test_raw_int8_domain_and_groups():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    scales = h[(h & 0x7C00) != 0x7C00]
+    q = np.tile(np.arange(-128, 128, dtype=np.int64).astype(np.int8), scales.size)
+    _raw_int8(q, scales, None, scales.size, 256, 256)
+    rng = np.random.default_rng(3)
+    zp = rng.integers(-128, 128, scales.size).astype(np.int8)
+    _raw_int8(q, scales, zp, scales.size, 256, 256)
+    for rows, cols, g in [(10, 36, 6), (3, 5, 5), (1, 13, 13), (9, 9, 81), (4, 24, 12)]:
+        n = rows * cols
+        qq = rng.integers(-128, 128, n).astype(np.int8)
+        s = synth.fp16_bits(rng.uniform(-1, 1, n // g))
+        z = rng.integers(-128, 128, n // g).astype(np.int8)
+        _raw_int8(qq, s, z, rows, cols, g)
+
+
+# ------------------------------------------------------------- decode-only
+
+def _decode_check(table, expected, what):
+    st = status_tensor(table.n_chunks)
+    out = lt.decode_lz4(table, status=st)
+    s = statuses(st, table.n_chunks)
+    assert np.all(s == 0), "%s: chunk statuses %s" % (what, np.unique(s))
+    got = out.cpu().numpy()
+    bad = np.nonzero(got != expected)[0]
+    assert bad.size == 0, "%s: %d bytes differ, first at %d" % (what, bad.size, bad[0])
+
+
+def _seq_table(seeds, sizes):
+    streams, expect = [], []
+    for sd, n in zip(seeds, sizes):
+        s, e = O.seqgen(int(sd), int(n))
+        streams.append(s)
+        expect.append(e)
+    comp_off = np.cumsum([0] + [s.size for s in streams]).astype(np.uint64)
+    dst_off = np.cumsum([0] + list(sizes)).astype(np.uint64)
+    return O.Table(np.concatenate(streams), comp_off, dst_off), np.concatenate(expect)
+
+
+def test_decode_generated_streams():
+    """Generator-built streams (boundary lengths, distances 1..65535,
+    overlapping matches), many per table; chunk sizes multiples of 16 except
+    the last."""
+    rng = np.random.default_rng(11)
+    for trial in range(6):
+        n = int(rng.integers(1, 300))
+        sizes = list(16 * rng.integers(0, 70000 // 16, n))
+        sizes[-1] = int(rng.integers(0, 70000))
+        t, e = _seq_table(rng.integers(0, 2**62, n), sizes)
+        _decode_check(table_from_oracle(t), e, "seqgen table %d" % trial)
+
+
+@pytest.mark.parametrize("size", [65536 + 16, 200000, 262144, 1 << 20, 3_000_017])
+def test_decode_chunks_larger_than_history(size):
+    """Chunks over 64 KiB wrap the history ring; distances up to 65535."""
+    t, e = _seq_table([size], [size])
+    _decode_check(table_from_oracle(t), e, "big chunk %d" % size)
+
+
+def test_decode_config4_full():
+    a = synth.config4()
+    _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV), a.data, "config4 packer")
+    _decode_check(table_from_oracle(O.compress_table(a.data, a.dst_off)), a.data, "config4 oracle")
+
+
+def test_decode_stress_blocks():
+    x = np.full(65536, 0xAB, np.uint8)
+    for blk in (O.lz4_compress(x), O.lz4_store(x)):
+        t = O.Table(blk, np.array([0, blk.size], np.uint64), np.array([0, 65536], np.uint64))
+        _decode_check(table_from_oracle(t), x, "0xAB block %d" % blk.size)
+    r = np.random.default_rng(2).integers(0, 256, 65536, dtype=np.uint8)
+    blk = O.lz4_compress(r)
+    t = O.Table(blk, np.array([0, blk.size], np.uint64), np.array([0, 65536], np.uint64))
+    _decode_check(table_from_oracle(t), r, "all-literal block")
+    # empty chunks and a zero-length block
+    e = np.zeros(0, np.uint8)
+    t = O.Table(np.array([0x00, 0x00], np.uint8), np.array([0, 1, 2], np.uint64), np.array([0, 0, 0], np.uint64))
+    _decode_check(table_from_oracle(t), e, "empty chunks")
+
+
+def _guarded_decode(ot, total, guard=4096):
+    table = table_from_oracle(ot)
+    buf = torch.full((total + 2 * guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    st = status_tensor(table.n_chunks)
+    lt.decode_lz4(table, out=buf[guard:guard + max(total, 1)], status=st)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard] == 0xA5) and np.all(b[guard + total:] == 0xA5), "write outside the output"
+    return statuses(st, table.n_chunks), b[guard:guard + total]
+
+
+def test_decode_corrupt_streams_status_and_bounds():
+    rng = np.random.default_rng(5)
+    s, e = O.seqgen(99, 20000)
+    # truncations of one block, each as its own 20000-byte chunk: all fail
+    cuts = list(range(0, s.size, max(1, s.size // 300)))
+    ot = O.Table(np.concatenate([s[:c] for c in cuts]), np.cumsum([0] + cuts).astype(np.uint64),
+                 np.arange(len(cuts) + 1, dtype=np.uint64) * np.uint64(20000))
+    st, _ = _guarded_decode(ot, ot.total)
+    _, ost = O.decode_table(ot)
+    assert np.all(st != 0) and np.all(ost != 0)
+    # one flipped byte per block: the GPU reports OK exactly when the oracle
+    # does, and chunks decoded OK hold the oracle's bytes
+    blocks = []
+    for k in range(300):
+        c = s.copy()
+        c[rng.integers(0, c.size)] ^= np.uint8(rng.integers(1, 256))
+        blocks.append(c)
+    ot = O.Table(np.concatenate(blocks), np.cumsum([0] + [b.size for b in blocks]).astype(np.uint64),
+                 np.arange(len(blocks) + 1, dtype=np.uint64) * np.uint64(20000))
+    st, got = _guarded_decode(ot, ot.total)
+    oout, ost = O.decode_table(ot)
+    assert np.array_equal(st == 0, ost == 0)
+    for i in np.nonzero(ost == 0)[0]:
+        assert np.array_equal(got[20000 * i:20000 * (i + 1)], oout[20000 * i:20000 * (i + 1)])
+
+
+def test_decode_bad_table_entries():
+    data = np.arange(300000, dtype=np.uint32).astype(np.uint8)
+    ot = O.compress_table(data, synth.uniform_chunks(data.size, 32768))
+    bad = O.Table(ot.comp, ot.comp_off.copy(), ot.dst_off.copy())
+    bad.comp_off[3] = bad.comp_off[2] - np.uint64(1)
+    bad.dst_off[6] += np.uint64(8)                       # misaligned chunk start
+    st, got = _guarded_decode(bad, bad.total)
+    _, ost = O.decode_table(bad)
+    assert st[2] == lt.CHUNK_BAD_TABLE and st[6] == lt.CHUNK_BAD_TABLE
+    assert st[0] == 0 and np.array_equal(got[:32768], data[:32768])
+    assert np.all((st == 0) <= (ost == 0))
+
+
+# ------------------------------------------------------------ fused paths
+
+def _fused4(table, w, what):
+    st = status_tensor(table.n_chunks)
+    out = lt.fused_lz4_int4(table, t_u16(w.scales), t_i8(w.zp), (w.rows, w.cols), w.group, status=st)
+    s = statuses(st, table.n_chunks)
+    assert np.all(s == 0), "%s: statuses %s" % (what, np.unique(s))
+    ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)
+    assert_same(host_u16(out), ref, what)
+
+
+def test_fused_int4_config1_both_compressors():
+    w = synth.config1()
+    packed = lt.pack_int4(w.codes)
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "config1 packer")
+    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "config1 oracle")
+
+
+def test_fused_int4_config3_full():
+    """The benchmark's workload: 8192x28672, group 128, packer streams."""
+    w = synth.config3()
+    packed = lt.pack_int4(w.codes)
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "config3 packer")
+
+
+def test_fused_int4_config3_oracle_stream():
+    w = synth.config3_small(rows=1024)
+    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "config3 oracle")
+
+
+@pytest.mark.parametrize("rows,cols,group,chunk", [
+    (64, 4096, 128, 48 * 1024),       # ragged chunks, several tiles
+    (61, 1000, 8, 1040),               # chunk not a tile multiple, ragged tail
+    (10, 36, 6, 16),                   # group splits lanes' codes (slow path)
+    (7, 30, 10, 48),                   # tiny chunks, odd tail bytes
+    (128, 8192, 8192, 65536),          # per-row groups
+    (16, 4096, 16 * 4096, 65536),      # per-tensor group
+    (512, 8192, 128, "mixed"),         # 16/64/256 KiB chunks (ring wrap)
+    (1, 2, 2, 16),                     # one byte
+])
+def test_fused_int4_shapes(rows, cols, group, chunk):
+    w = synth.int4_weight(rows, cols, group, rows * 7 + cols, chunking="mixed" if chunk == "mixed" else "64k")
+    if chunk != "mixed":
+        w.dst_off = synth.uniform_chunks(w.packed_bytes, chunk)
+    packed = lt.pack_int4(w.codes)
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "fused %dx%d g%d" % (rows, cols, group))
+    w.zp = None
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "fused no-zp %dx%d" % (rows, cols))
+
+
+def test_fused_int4_generated_streams():
+    """Arbitrary LZ4 structure (overlaps, far distances) through the fused path."""
+    rng = np.random.default_rng(21)
+    sizes = [int(v) for v in 16 * rng.integers(1, 5000, 40)] + [1000]
+    t, e = _seq_table(rng.integers(0, 2**62, len(sizes)), sizes)
+    n_codes = 2 * e.size
+    rows, cols, group = 1, n_codes, 8
+    scales = synth.fp16_bits(rng.uniform(-1, 1, n_codes // group))
+    zp = rng.integers(-128, 128, n_codes // group).astype(np.int8)
+    st = status_tensor(t.n)
+    out = lt.fused_lz4_int4(table_from_oracle(t), t_u16(scales), t_i8(zp), (rows, cols), group, status=st)
+    assert np.all(statuses(st, t.n) == 0)
+    assert_same(host_u16(out), O.dequant_int4(e, scales, zp, group), "fused seqgen")
+
+
+def test_fused_int8_config2():
+    w = synth.config2()
+    table = lt.ChunkTable.build(w.q.view(np.uint8), w.dst_off, DEV)
+    st = status_tensor(table.n_chunks)
+    out = lt.fused_lz4_int8(table, t_u16(w.scales), None, (w.rows, w.cols), w.group, status=st)
+    assert np.all(statuses(st, table.n_chunks) == 0)
+    assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "config2 fused int8")
+
+
+def test_fused_int8_small_groups_zp():
+    rng = np.random.default_rng(8)
+    rows, cols, group = 300, 1000, 100
+    q = rng.integers(-128, 128, rows * cols).astype(np.int8)
+    q[rng.random(q.size) < 0.5] = 0
+    scales = synth.fp16_bits(rng.uniform(-1, 1, rows * cols // group))
+    zp = rng.integers(-128, 128, rows * cols // group).astype(np.int8)
+    dst_off = synth.uniform_chunks(q.size, 4096 + 16)
+    table = lt.ChunkTable.build(q.view(np.uint8), dst_off, DEV)
+    st = status_tensor(table.n_chunks)
+    out = lt.fused_lz4_int8(table, t_u16(scales), t_i8(zp), (rows, cols), group, status=st)
+    assert np.all(statuses(st, table.n_chunks) == 0)
+    assert_same(host_u16(out), O.dequant_int8(q, scales, zp, group), "fused int8 g100")

@@ -1,0 +1,129 @@
+"""Host-side checks of liblt.so that need no GPU.
+
+* the library loads and exports every function include/lt.h declares;
+* argument validation returns LT_ERR_INVALID_ARG before any device work;
+* the host packer (nibble packing, LZ4 compressor) produces blocks that the
+  CPU oracle decodes back to the input, on every workload.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+import weight_dequantization_amd as lt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"\b(lt_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 10
+    L = C.CDLL(lt.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert lt.lib().lt_abi_version() == 1
+    assert lt.lib().lt_status_str(1) == b"invalid argument"
+
+
+def test_invalid_arguments_rejected_without_gpu():
+    L = lt.lib()
+    V = C.c_void_p
+    fake = V(0x10000)        # never dereferenced: validation fails first
+    unaligned = V(0x10008)
+    # null pointers
+    assert L.lt_dequant_int4(None, fake, None, 4, 4, 4, fake, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int4(fake, None, None, 4, 4, 4, fake, None) == lt.LT_ERR_INVALID_ARG
+    # unaligned output, zero sizes, odd element count, bad groups
+    assert L.lt_dequant_int4(fake, fake, None, 4, 4, 4, unaligned, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int4(fake, fake, None, 0, 4, 4, fake, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int4(fake, fake, None, 1, 3, 3, fake, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int4(fake, fake, None, 4, 6, 4, fake, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int8(fake, fake, None, 4, 4, 0, fake, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int8(fake, fake, None, 3, 4, 8, fake, None) == lt.LT_ERR_INVALID_ARG
+    # chunk tables
+    t = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 9, 100)           # 16 codes need 8 bytes
+    assert L.lt_fused_lz4_int4(C.byref(t), fake, None, 4, 4, 4, fake, None, None) == lt.LT_ERR_INVALID_ARG
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 0, 8, 100)               # max_chunk_bytes 0
+    assert L.lt_fused_lz4_int4(C.byref(t), fake, None, 4, 4, 4, fake, None, None) == lt.LT_ERR_INVALID_ARG
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, (1 << 30) + 1, 8, 100)   # above the limit
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
+    t = lt._Table(None, 0x10000, 0x10000, 1, 8, 8, 100)
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100)
+    assert L.lt_decode_lz4(C.byref(t), unaligned, None, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_decode_lz4(None, fake, None, None) == lt.LT_ERR_INVALID_ARG
+    # int8 table size must equal rows*cols
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 16, 16, 100)
+    assert L.lt_fused_lz4_int8(C.byref(t), fake, None, 4, 8, 8, fake, None, None) == lt.LT_ERR_INVALID_ARG
+    # empty tables are valid no-ops (no device work)
+    t = lt._Table(0, 0, 0, 0, 0, 0, 0)
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_OK
+
+
+def test_pack_int4_matches_oracle():
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 16, 100002, dtype=np.uint8)
+    assert np.array_equal(lt.pack_int4(codes), O.pack_int4(codes))
+    with pytest.raises(lt.LtError):
+        lt.pack_int4(codes[:3])
+
+
+def _oracle_round_trip(data, dst_off):
+    comp, comp_off = lt.compress_chunks(data, dst_off)
+    t = O.Table(comp, comp_off, dst_off)
+    out, st = O.decode_table(t)
+    assert np.all(st == O.OK) and np.array_equal(out, data)
+    return comp.size
+
+
+def test_packer_blocks_decode_with_oracle_small():
+    rng = np.random.default_rng(1)
+    for n in (0, 1, 12, 13, 100, 4095, 70000):
+        for kind in range(3):
+            if kind == 0:
+                x = rng.integers(0, 256, n, dtype=np.uint8)
+            elif kind == 1:
+                x = np.zeros(n, np.uint8)
+            else:
+                x = (rng.random(n) < 0.2).astype(np.uint8) * rng.integers(0, 4, n, dtype=np.uint8)
+            _oracle_round_trip(x, np.array([0, n], np.uint64))
+    x = np.full(65536, 0xAB, np.uint8)
+    assert _oracle_round_trip(x, np.array([0, 65536], np.uint64)) < 300
+
+
+def test_packer_config1_and_config3_small():
+    for w in (synth.config1(), synth.config3_small()):
+        packed = lt.pack_int4(w.codes)
+        size = _oracle_round_trip(packed, w.dst_off)
+        ref = O.compress_table(packed, w.dst_off).comp_bytes
+        # the product packer is within a few percent of the oracle's greedy compressor
+        assert size <= ref * 1.03, (size, ref)
+
+
+@pytest.mark.slow
+def test_packer_full_configs():
+    for k in (2, 3, 4):
+        w = synth.config(k)
+        data = {2: lambda: w.q.view(np.uint8), 3: lambda: lt.pack_int4(w.codes), 4: lambda: w.data}[k]()
+        size = _oracle_round_trip(data, w.dst_off)
+        print("config", k, "compressed", size, "of", data.size)
+
+
+def test_packer_mixed_chunks():
+    w = synth.int4_weight(512, 8192, 128, 77, chunking="mixed")
+    packed = lt.pack_int4(w.codes)
+    _oracle_round_trip(packed, w.dst_off)

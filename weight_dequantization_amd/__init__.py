@@ -1,0 +1,253 @@
+"""weight_dequantization_amd -- just-in-time decompression of compressed tensors
+on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``liblt.so`` (HIP, built in-tree by
+``python -m weight_dequantization_amd.build``).  The names mirror the C ABI in
+``include/lt.h``; this module only marshals arguments: every step of the
+decode and dequantization runs in the library's kernels.  PyTorch provides
+device memory and the current stream.
+
+Device entry points (asynchronous on torch's current stream):
+    decode_lz4(table, out=None, status=None)                 -> uint8 tensor
+    dequant_int4(packed, scales, zp, shape, group, out=None) -> fp16 tensor
+    dequant_int8(q, scales, zp, shape, group, out=None)      -> fp16 tensor
+    fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
+    fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
+Host packer (numpy in, numpy out):
+    pack_int4(codes) -> packed bytes (low nibble first)
+    compress_chunks(src, dst_off, threads=0) -> (comp, comp_off)
+    ChunkTable.build(src_bytes, dst_off, device) -> table resident on the GPU
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblt.so")
+
+LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE = range(5)
+CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE = range(6)
+MAX_CHUNK_BYTES = 1 << 30
+
+
+class LtError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, _lib().lt_status_str(status).decode()))
+
+
+class LtDecodeError(RuntimeError):
+    """Some chunks failed to decode; `chunks` lists (index, code)."""
+
+    def __init__(self, chunks):
+        self.chunks = chunks
+        super().__init__("%d chunk(s) failed to decode, first: %s" % (len(chunks), chunks[:4]))
+
+
+class _Table(C.Structure):
+    _fields_ = [("comp", C.c_void_p), ("comp_off", C.c_void_p), ("dst_off", C.c_void_p),
+                ("n_chunks", C.c_uint32), ("max_chunk_bytes", C.c_uint32),
+                ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64)]
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("liblt.so is not built: run `python -m weight_dequantization_amd.build` "
+                              "(or __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        vp, u64, u32, i32 = C.c_void_p, C.c_uint64, C.c_uint32, C.c_int
+        tp = C.POINTER(_Table)
+        sig = {
+            "lt_decode_lz4": (i32, [tp, vp, vp, vp]),
+            "lt_dequant_int4": (i32, [vp, vp, vp, u64, u64, u64, vp, vp]),
+            "lt_dequant_int8": (i32, [vp, vp, vp, u64, u64, u64, vp, vp]),
+            "lt_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
+            "lt_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
+            "lt_lz4_bound": (u64, [u64]),
+            "lt_pack_int4": (i32, [vp, u64, vp]),
+            "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32]),
+            "lt_status_str": (C.c_char_p, [i32]),
+            "lt_abi_version": (i32, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _L = L
+    return _L
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _lib()
+
+
+# ----------------------------------------------------------------- host side
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.size // 2, np.uint8)
+    st = _lib().lt_pack_int4(_np_ptr(codes), codes.size, _np_ptr(out))
+    if st != LT_OK:
+        raise LtError(st, "lt_pack_int4")
+    return out
+
+
+def lz4_bound(n: int) -> int:
+    return int(_lib().lt_lz4_bound(n))
+
+
+def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0):
+    src = np.ascontiguousarray(src, dtype=np.uint8)
+    dst_off = np.ascontiguousarray(dst_off, dtype=np.uint64)
+    n = dst_off.size - 1
+    sizes = np.diff(dst_off.astype(np.int64)) if n > 0 else np.zeros(0, np.int64)
+    cap = int(np.sum(sizes + sizes // 255 + 16)) + 16
+    comp = np.empty(max(cap, 1), np.uint8)
+    comp_off = np.empty(n + 1, np.uint64)
+    st = _lib().lt_compress_chunks(_np_ptr(src), _np_ptr(dst_off), n, _np_ptr(comp), cap,
+                                   _np_ptr(comp_off), threads)
+    if st != LT_OK:
+        raise LtError(st, "lt_compress_chunks")
+    return comp[:int(comp_off[-1])].copy(), comp_off
+
+
+# --------------------------------------------------------------- device side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+@dataclass
+class ChunkTable:
+    """A chunk table resident on the GPU (see lt_chunk_table in include/lt.h)."""
+    comp: object            # torch.uint8 [comp_bytes]
+    comp_off: object        # torch.int64 [n+1] (read as uint64 by the library)
+    dst_off: object         # torch.int64 [n+1]
+    n_chunks: int
+    max_chunk_bytes: int
+    total_bytes: int
+    comp_bytes: int
+
+    @classmethod
+    def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda"):
+        torch = _torch()
+        comp_off = np.ascontiguousarray(comp_off, np.uint64)
+        dst_off = np.ascontiguousarray(dst_off, np.uint64)
+        n = dst_off.size - 1
+        sizes = np.diff(dst_off.astype(np.int64)) if n > 0 else np.zeros(0, np.int64)
+        comp_t = torch.from_numpy(np.ascontiguousarray(comp, np.uint8).copy()).to(device)
+        if comp_t.numel() == 0:
+            comp_t = torch.zeros(16, dtype=torch.uint8, device=device)
+        return cls(comp_t,
+                   torch.from_numpy(comp_off.view(np.int64).copy()).to(device),
+                   torch.from_numpy(dst_off.view(np.int64).copy()).to(device),
+                   n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
+                   int(comp_off[-1]) if comp_off.size else 0)
+
+    @classmethod
+    def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0):
+        """Compress `src` chunk by chunk on the host and upload the table."""
+        comp, comp_off = compress_chunks(src, dst_off, threads)
+        return cls.from_host(comp, comp_off, dst_off, device)
+
+    def as_c(self) -> _Table:
+        return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
+                      self.n_chunks, self.max_chunk_bytes, self.total_bytes, self.comp_bytes)
+
+
+def _check(st, where):
+    if st != LT_OK:
+        raise LtError(st, where)
+
+
+def check_status(status) -> None:
+    """Raise LtDecodeError if any chunk status is not OK (synchronizes)."""
+    s = status.cpu().numpy()
+    bad = np.nonzero(s != CHUNK_OK)[0]
+    if bad.size:
+        raise LtDecodeError([(int(i), int(s[i])) for i in bad])
+
+
+def decode_lz4(table: ChunkTable, out=None, status=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(max(table.total_bytes, 1), dtype=torch.uint8, device=table.comp.device)
+    t = table.as_c()
+    _check(_lib().lt_decode_lz4(C.byref(t), _dptr(out), _dptr(status), _stream_ptr(stream)),
+           "lt_decode_lz4")
+    return out[:table.total_bytes] if out.numel() > table.total_bytes else out
+
+
+def _out_f16(out, n, device):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float16, device=device)
+    return out
+
+
+def _shape(shape):
+    rows, cols = (int(shape[0]), int(shape[1])) if len(shape) == 2 else (1, int(shape[0]))
+    return rows, cols
+
+
+def dequant_int4(packed, scales, zp, shape, group: int, out=None, stream=None):
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, packed.device)
+    _check(_lib().lt_dequant_int4(_dptr(packed), _dptr(scales), _dptr(zp), rows, cols, group,
+                                  _dptr(out), _stream_ptr(stream)), "lt_dequant_int4")
+    return out.view(rows, cols)
+
+
+def dequant_int8(q, scales, zp, shape, group: int, out=None, stream=None):
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, q.device)
+    _check(_lib().lt_dequant_int8(_dptr(q), _dptr(scales), _dptr(zp), rows, cols, group,
+                                  _dptr(out), _stream_ptr(stream)), "lt_dequant_int8")
+    return out.view(rows, cols)
+
+
+def fused_lz4_int4(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
+                   stream=None):
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, table.comp.device)
+    t = table.as_c()
+    _check(_lib().lt_fused_lz4_int4(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group,
+                                    _dptr(out), _dptr(status), _stream_ptr(stream)),
+           "lt_fused_lz4_int4")
+    return out.view(rows, cols)
+
+
+def fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
+                   stream=None):
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, table.comp.device)
+    t = table.as_c()
+    _check(_lib().lt_fused_lz4_int8(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group,
+                                    _dptr(out), _dptr(status), _stream_ptr(stream)),
+           "lt_fused_lz4_int8")
+    return out.view(rows, cols)

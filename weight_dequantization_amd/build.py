@@ -1,0 +1,54 @@
+"""Build liblt.so in-tree for gfx950.
+
+    python -m weight_dequantization_amd.build
+
+The device code is compiled for gfx950 only, with packed-fp32 instruction
+selection disabled; the host packer is plain C++17.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "liblt.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    pack_o = os.path.join(BUILD, "lt_pack.o")
+    api_o = os.path.join(BUILD, "lt_api.o")
+    cmds = [
+        ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-c",
+         os.path.join(CSRC, "lt_pack.cpp"), "-o", pack_o],
+        [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "lt_api.hip"), "-o", api_o],
+        [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", api_o, pack_o, "-pthread",
+         "-o", LIB + ".tmp"],
+    ]
+    for c in cmds:
+        if verbose:
+            print(" ".join(c), flush=True)
+        r = subprocess.run(c, capture_output=True, text=True)
+        err = "\n".join(l for l in (r.stderr or "").splitlines()
+                        if "packed-fp32-ops" not in l)
+        if r.returncode != 0:
+            raise RuntimeError("build step failed: %s\n%s" % (" ".join(c), err))
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

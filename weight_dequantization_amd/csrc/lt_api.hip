@@ -1,0 +1,266 @@
+// lt_api.hip -- liblt's C ABI: argument checks and kernel launches.
+//
+// Entry points follow the calls the roadmap page sketches ("GPU Compression
+// Pipeline - TDD Roadmap": INT4 dequantization in Phase 1.1, INT8 in Phase
+// 1.2, fused LZ4 + INT4 in Phase 2.1, parallel LZ4 decode in Phase 3.1),
+// reshaped for a chunk table of independent LZ4 blocks and caller-owned
+// device buffers.  Everything runs on the caller's stream; nothing here
+// allocates, synchronizes or keeps state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lt.h"
+#include "lt_device.hpp"
+#include "lt_lz4.hpp"
+
+namespace lt {
+
+// ------------------------------------------------- raw (uncompressed) dequant
+
+struct RawParams {
+  const uint8_t *src;        // packed int4 or int8 codes
+  const uint16_t *scales;
+  const int8_t *zp;
+  uint64_t n_bytes;          // bytes of src
+  uint64_t group;
+  uint32_t group_shift;      // log2(group) if group is a power of two, else 64
+  uint16_t *out;
+};
+
+constexpr int RAW_THREADS = 256;
+constexpr int RAW_UNROLL = 4;   // dwords per thread
+
+__device__ __forceinline__ uint64_t grp(uint64_t e, const RawParams &P) {
+  return P.group_shift < 64 ? (e >> P.group_shift) : e / P.group;
+}
+
+// Each thread takes RAW_UNROLL dwords spaced a workgroup-width apart, so each
+// load instruction reads 1 KiB and each store instruction writes 4 KiB (int4)
+// contiguously across the workgroup.
+__global__ void __launch_bounds__(RAW_THREADS) dequant_int4_kernel(RawParams P) {
+  const uint64_t n_dw = P.n_bytes / 4;
+  const uint64_t base = (uint64_t)blockIdx.x * RAW_THREADS * RAW_UNROLL + threadIdx.x;
+  uint32_t w[RAW_UNROLL];
+#pragma unroll
+  for (int k = 0; k < RAW_UNROLL; k++) {
+    uint64_t d = base + (uint64_t)k * RAW_THREADS;
+    if (d < n_dw) __builtin_memcpy(&w[k], P.src + 4 * d, 4);
+  }
+#pragma unroll
+  for (int k = 0; k < RAW_UNROLL; k++) {
+    uint64_t d = base + (uint64_t)k * RAW_THREADS;
+    if (d < n_dw) {
+      uint64_t e0 = 8 * d;
+      uint64_t g0 = grp(e0, P), g1 = grp(e0 + 7, P);
+      if (g0 == g1) {
+        int z = P.zp ? (int)P.zp[g0] : 0;
+        uint4 r = deq8_int4(w[k], splat_h2((uint16_t)f16_bits_1024_plus(z)), splat_h2(P.scales[g0]));
+        *(uint4 *)(P.out + e0) = r;
+      } else {
+        for (int c = 0; c < 8; c++) {
+          uint64_t g = grp(e0 + c, P);
+          int z = P.zp ? (int)P.zp[g] : 0;
+          P.out[e0 + c] = deq1((w[k] >> (4 * c)) & 15, z, P.scales[g]);
+        }
+      }
+    }
+  }
+  // trailing bytes (n_bytes % 4) go to the first thread of the grid
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (uint64_t b = n_dw * 4; b < P.n_bytes; b++) {
+      uint32_t v = P.src[b];
+      for (int c = 0; c < 2; c++) {
+        uint64_t e = 2 * b + c;
+        uint64_t g = grp(e, P);
+        int z = P.zp ? (int)P.zp[g] : 0;
+        P.out[e] = deq1((v >> (4 * c)) & 15, z, P.scales[g]);
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(RAW_THREADS) dequant_int8_kernel(RawParams P) {
+  // each thread: RAW_UNROLL pairs of dwords (8 codes -> 16 output bytes)
+  const uint64_t n_q = P.n_bytes / 8;
+  const uint64_t base = (uint64_t)blockIdx.x * RAW_THREADS * RAW_UNROLL + threadIdx.x;
+  uint2 w[RAW_UNROLL];
+#pragma unroll
+  for (int k = 0; k < RAW_UNROLL; k++) {
+    uint64_t d = base + (uint64_t)k * RAW_THREADS;
+    if (d < n_q) __builtin_memcpy(&w[k], P.src + 8 * d, 8);
+  }
+#pragma unroll
+  for (int k = 0; k < RAW_UNROLL; k++) {
+    uint64_t d = base + (uint64_t)k * RAW_THREADS;
+    if (d < n_q) {
+      uint64_t e0 = 8 * d;
+      uint64_t g0 = grp(e0, P), g1 = grp(e0 + 7, P);
+      if (g0 == g1) {
+        int z = P.zp ? (int)P.zp[g0] : 0;
+        h2 c2 = splat_h2((uint16_t)f16_bits_1024_plus(128 + z)), s2 = splat_h2(P.scales[g0]);
+        uint2 a = deq4_int8(w[k].x, c2, s2), b = deq4_int8(w[k].y, c2, s2);
+        *(uint4 *)(P.out + e0) = make_uint4(a.x, a.y, b.x, b.y);
+      } else {
+        for (int c = 0; c < 8; c++) {
+          uint64_t g = grp(e0 + c, P);
+          int z = P.zp ? (int)P.zp[g] : 0;
+          uint32_t word = (c < 4) ? w[k].x : w[k].y;
+          P.out[e0 + c] = deq1((int)(int8_t)(word >> ((c & 3) * 8)), z, P.scales[g]);
+        }
+      }
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (uint64_t e = n_q * 8; e < P.n_bytes; e++) {
+      uint64_t g = grp(e, P);
+      int z = P.zp ? (int)P.zp[g] : 0;
+      P.out[e] = deq1((int)(int8_t)P.src[e], z, P.scales[g]);
+    }
+  }
+}
+
+}  // namespace lt
+
+// ---------------------------------------------------------------- C ABI
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// rows*cols elements in groups of `group`; see lt.h for the rule.
+bool shape_ok(uint64_t rows, uint64_t cols, uint64_t group) {
+  if (rows == 0 || cols == 0 || group == 0) return false;
+  if (rows > (~0ull) / cols) return false;
+  uint64_t n = rows * cols;
+  if (n > (1ull << 48)) return false;
+  if (cols % group != 0 && group % cols != 0) return false;
+  if (n % group != 0) return false;
+  return true;
+}
+
+uint32_t shift_of(uint64_t g) {
+  return (g & (g - 1)) == 0 ? (uint32_t)__builtin_ctzll(g) : 64u;
+}
+
+lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *chunk_status,
+                        const uint16_t *scales, const int8_t *zp, uint64_t group, void *stream) {
+  lt::ChunkParams P;
+  P.comp = t->comp;
+  P.comp_off = t->comp_off;
+  P.dst_off = t->dst_off;
+  P.comp_bytes = t->comp_bytes;
+  P.total = t->total_bytes;
+  P.n = t->n_chunks;
+  P.max_chunk = t->max_chunk_bytes;
+  P.out = out;
+  P.status = chunk_status;
+  P.scales = scales;
+  P.zp = zp;
+  P.group = group;
+  hipStream_t s = (hipStream_t)stream;
+  dim3 grid(t->n_chunks), block(lt::NTHREADS);
+  switch (mode) {
+    case lt::MODE_BYTES: hipLaunchKernelGGL(lt::chunk_kernel<lt::MODE_BYTES>, grid, block, 0, s, P); break;
+    case lt::MODE_INT4: hipLaunchKernelGGL(lt::chunk_kernel<lt::MODE_INT4>, grid, block, 0, s, P); break;
+    default: hipLaunchKernelGGL(lt::chunk_kernel<lt::MODE_INT8>, grid, block, 0, s, P); break;
+  }
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+}
+
+bool table_ok(const lt_chunk_table *t) {
+  if (!t) return false;
+  if (t->n_chunks == 0) return t->total_bytes == 0;
+  if (!t->comp || !t->comp_off || !t->dst_off) return false;
+  if (t->max_chunk_bytes == 0 || t->max_chunk_bytes > LT_MAX_CHUNK_BYTES) return false;
+  if (t->n_chunks > 0x7FFFFFFFu) return false;
+  return true;
+}
+
+lt_status fused_common(int mode, const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                       uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                       int32_t *chunk_status, void *stream) {
+  if (!table_ok(t) || !scales || !out || !aligned16(out)) return LT_ERR_INVALID_ARG;
+  if (!shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
+  uint64_t n = rows * cols;
+  if (mode == lt::MODE_INT4) {
+    if (n % 2 != 0 || t->total_bytes != n / 2) return LT_ERR_INVALID_ARG;
+  } else {
+    if (t->total_bytes != n) return LT_ERR_INVALID_ARG;
+  }
+  if (t->n_chunks == 0) return LT_OK;
+  return launch_chunks(mode, t, out, chunk_status, scales, zp, group, stream);
+}
+
+lt_status raw_common(bool int4, const uint8_t *src, const uint16_t *scales, const int8_t *zp,
+                     uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out, void *stream) {
+  if (!src || !scales || !out || !aligned16(out)) return LT_ERR_INVALID_ARG;
+  if (!shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
+  uint64_t n = rows * cols;
+  if (int4 && n % 2 != 0) return LT_ERR_INVALID_ARG;
+  lt::RawParams P;
+  P.src = src;
+  P.scales = scales;
+  P.zp = zp;
+  P.n_bytes = int4 ? n / 2 : n;
+  P.group = group;
+  P.group_shift = shift_of(group);
+  P.out = out;
+  uint64_t units = int4 ? P.n_bytes / 4 : P.n_bytes / 8;
+  uint64_t per_block = (uint64_t)lt::RAW_THREADS * lt::RAW_UNROLL;
+  uint64_t blocks = (units + per_block - 1) / per_block;
+  if (blocks == 0) blocks = 1;
+  if (blocks > 0x7FFFFFFFull) return LT_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (int4)
+    hipLaunchKernelGGL(lt::dequant_int4_kernel, dim3((uint32_t)blocks), dim3(lt::RAW_THREADS), 0, s, P);
+  else
+    hipLaunchKernelGGL(lt::dequant_int8_kernel, dim3((uint32_t)blocks), dim3(lt::RAW_THREADS), 0, s, P);
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+lt_status lt_decode_lz4(const lt_chunk_table *t, uint8_t *dst, int32_t *chunk_status, void *stream) {
+  if (!table_ok(t) || !dst || !aligned16(dst)) return LT_ERR_INVALID_ARG;
+  if (t->n_chunks == 0) return LT_OK;
+  return launch_chunks(lt::MODE_BYTES, t, dst, chunk_status, nullptr, nullptr, 1, stream);
+}
+
+lt_status lt_dequant_int4(const uint8_t *packed, const uint16_t *scales, const int8_t *zp,
+                          uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out, void *stream) {
+  return raw_common(true, packed, scales, zp, rows, cols, group, out, stream);
+}
+
+lt_status lt_dequant_int8(const int8_t *q, const uint16_t *scales, const int8_t *zp, uint64_t rows,
+                          uint64_t cols, uint64_t group, uint16_t *out, void *stream) {
+  return raw_common(false, (const uint8_t *)q, scales, zp, rows, cols, group, out, stream);
+}
+
+lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                            uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                            int32_t *chunk_status, void *stream) {
+  return fused_common(lt::MODE_INT4, t, scales, zp, rows, cols, group, out, chunk_status, stream);
+}
+
+lt_status lt_fused_lz4_int8(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                            uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                            int32_t *chunk_status, void *stream) {
+  return fused_common(lt::MODE_INT8, t, scales, zp, rows, cols, group, out, chunk_status, stream);
+}
+
+const char *lt_status_str(lt_status s) {
+  switch (s) {
+    case LT_OK: return "ok";
+    case LT_ERR_INVALID_ARG: return "invalid argument";
+    case LT_ERR_UNSUPPORTED: return "unsupported";
+    case LT_ERR_LAUNCH: return "kernel launch failed";
+    case LT_ERR_DEVICE: return "no usable device";
+  }
+  return "unknown status";
+}
+
+int lt_abi_version(void) { return LT_ABI_VERSION; }
+
+}  // extern "C"

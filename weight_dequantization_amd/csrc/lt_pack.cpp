@@ -1,0 +1,169 @@
+// lt_pack.cpp -- host-side packer for liblt: nibble packing and an LZ4 block
+// compressor that builds the chunk tables the device entry points consume
+// (the pages' packing tool and compressor, "Openai/691a41cd ..." (section 38),
+// the list of shipped tools; block size 64 KiB from "GPU Compression Pipeline
+// - TDD Roadmap", Phase 6.1).
+//
+// The compressor is greedy.  At each position it tries two candidates and
+// keeps the longer match:
+//   * a run check at distance 1 (runs of one byte: pruned rows, zero groups,
+//     ReLU zeros), accepted from 4 bytes;
+//   * the most recent earlier position with the same 4-byte hash (distance up
+//     to 65535), accepted from 8 bytes, so isolated 4-byte coincidences in
+//     near-random code bytes do not split long literal runs.
+// It keeps the format's end-of-block rules (the last 5 bytes are literals and
+// no match starts within the last 12 bytes), so standard LZ4 block decoders
+// accept its output.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "../../include/lt.h"
+
+namespace {
+
+constexpr uint32_t kMinRun = 4;       // accepted length for distance-1 runs
+constexpr uint32_t kMinMatch = 8;     // accepted length for hashed matches
+constexpr uint32_t kLastLiterals = 5;
+constexpr uint32_t kMatchLimit = 12;  // no match may start in the last 12 bytes
+constexpr uint32_t kMaxDist = 65535;
+constexpr int kHashBits = 15;
+
+inline uint32_t rd32(const uint8_t *p) {
+  uint32_t v;
+  memcpy(&v, p, 4);
+  return v;
+}
+
+inline uint32_t hash32(uint32_t v) { return (v * 2654435761u) >> (32 - kHashBits); }
+
+struct Writer {
+  uint8_t *out;
+  uint64_t pos;
+  void len_bytes(uint64_t v) {  // v = length - 15
+    while (v >= 255) {
+      out[pos++] = 255;
+      v -= 255;
+    }
+    out[pos++] = (uint8_t)v;
+  }
+  void sequence(const uint8_t *lit, uint64_t nlit, uint64_t dist, uint64_t mlen) {
+    uint64_t mc = mlen ? mlen - 4 : 0;
+    out[pos++] = (uint8_t)((std::min<uint64_t>(nlit, 15) << 4) | std::min<uint64_t>(mc, 15));
+    if (nlit >= 15) len_bytes(nlit - 15);
+    memcpy(out + pos, lit, nlit);
+    pos += nlit;
+    if (mlen) {
+      out[pos++] = (uint8_t)(dist & 255);
+      out[pos++] = (uint8_t)(dist >> 8);
+      if (mc >= 15) len_bytes(mc - 15);
+    }
+  }
+};
+
+// Compress src[0, n) into out (capacity >= lt_lz4_bound(n)); returns size.
+uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vector<int32_t> &table) {
+  Writer w{out, 0};
+  if (n < kMatchLimit + 1) {
+    w.sequence(src, n, 0, 0);
+    return w.pos;
+  }
+  std::fill(table.begin(), table.end(), -1);
+  const uint64_t match_end = n - kLastLiterals;  // matches must stop before this
+  uint64_t anchor = 0, i = 0;
+  while (i + kMatchLimit <= n) {
+    uint64_t best_len = 0, best_dist = 0;
+    // distance-1 run
+    if (i > 0 && src[i] == src[i - 1]) {
+      uint64_t len = 0;
+      while (i + len < match_end && src[i + len] == src[i - 1]) len++;
+      if (len >= kMinRun) {
+        best_len = len;
+        best_dist = 1;
+      }
+    }
+    uint32_t h = hash32(rd32(src + i));
+    int64_t c = table[h];
+    table[h] = (int32_t)i;
+    if (c >= 0 && i - (uint64_t)c <= kMaxDist && i - (uint64_t)c > 1 && rd32(src + c) == rd32(src + i)) {
+      uint64_t len = 4;
+      while (i + len < match_end && src[c + len] == src[i + len]) len++;
+      if (len >= kMinMatch && len > best_len) {
+        best_len = len;
+        best_dist = i - (uint64_t)c;
+      }
+    }
+    if (best_len) {
+      w.sequence(src + anchor, i - anchor, best_dist, best_len);
+      uint64_t stop = i + best_len;
+      // index a few positions inside the match so later repeats find it
+      for (uint64_t j = std::max<uint64_t>(i + 1, stop > 2 ? stop - 2 : 0); j < stop && j + kMatchLimit <= n; j++)
+        table[hash32(rd32(src + j))] = (int32_t)j;
+      i = stop;
+      anchor = i;
+    } else {
+      i++;
+    }
+  }
+  w.sequence(src + anchor, n - anchor, 0, 0);
+  return w.pos;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t lt_lz4_bound(uint64_t n) { return n + n / 255 + 16; }
+
+lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed) {
+  if ((!codes || !packed) && n_codes) return LT_ERR_INVALID_ARG;
+  if (n_codes % 2) return LT_ERR_INVALID_ARG;
+  for (uint64_t k = 0; k < n_codes / 2; k++)
+    packed[k] = (uint8_t)((codes[2 * k] & 15) | ((codes[2 * k + 1] & 15) << 4));
+  return LT_OK;
+}
+
+lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
+                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads) {
+  if (!dst_off || !comp_off) return LT_ERR_INVALID_ARG;
+  if (n_chunks == 0) {
+    comp_off[0] = 0;
+    return LT_OK;
+  }
+  if (!src || !comp || dst_off[0] != 0) return LT_ERR_INVALID_ARG;
+  uint64_t need = 0;
+  for (uint32_t i = 0; i < n_chunks; i++) {
+    if (dst_off[i + 1] < dst_off[i]) return LT_ERR_INVALID_ARG;
+    need += lt_lz4_bound(dst_off[i + 1] - dst_off[i]);
+  }
+  if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
+  threads = std::min<int>(threads, (int)n_chunks);
+  threads = std::min(threads, 256);
+  // compress each chunk into its own slot of a scratch buffer, then pack
+  std::vector<uint64_t> slot(n_chunks + 1, 0), size(n_chunks, 0);
+  for (uint32_t i = 0; i < n_chunks; i++) slot[i + 1] = slot[i] + lt_lz4_bound(dst_off[i + 1] - dst_off[i]);
+  std::vector<uint8_t> scratch(need);
+  auto work = [&](int t) {
+    std::vector<int32_t> table(1u << kHashBits);
+    for (uint32_t i = (uint32_t)t; i < n_chunks; i += (uint32_t)threads)
+      size[i] = compress_block(src + dst_off[i], dst_off[i + 1] - dst_off[i], scratch.data() + slot[i], table);
+  };
+  std::vector<std::thread> pool;
+  for (int t = 1; t < threads; t++) pool.emplace_back(work, t);
+  work(0);
+  for (auto &th : pool) th.join();
+  uint64_t pos = 0;
+  comp_off[0] = 0;
+  for (uint32_t i = 0; i < n_chunks; i++) {
+    if (pos + size[i] > comp_cap) return LT_ERR_INVALID_ARG;
+    memcpy(comp + pos, scratch.data() + slot[i], size[i]);
+    pos += size[i];
+    comp_off[i + 1] = pos;
+  }
+  return LT_OK;
+}
+
+}  // extern "C"
