@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark: fused LZ4 + INT4 -> fp16 on one MI355X.
+
+Workload: an INT4 MLP projection 8192 x 28672, group 128, zero points U{0..15},
+codes rounded N(7.5, 3) clipped to 0..15, 20% all-zero groups, packed two per
+byte (low nibble first) and LZ4-compressed in independent 64 KiB chunks by the
+library's host packer (seeded synthetic data; it stands in for real quantized
+weights).  A step is one lt_fused_lz4_int4 call over the whole layer: chunk
+lookup, compressed-byte staging, LZ4 parse, literal/match copies, nibble
+unpack, group-scale dequantization and the fp16 stores, with the compressed
+table, scales and zero points already resident in HBM.
+
+Metric: GB/s (1e9 B/s) of algorithmic bytes per step = compressed bytes read
++ fp16 bytes written (scales, zero points and the offset table are reported
+separately as metadata), and the fraction of the 8.0 TB/s HBM peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+
+Prints one JSON line.  --extra adds measurements of the raw (uncompressed)
+INT4 path and of plain fill/copy ceilings under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_int4_8192x28672_hbm_traffic.md")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources, to tell whether stored counter data is stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_dequantization_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".hpp")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the HIP sources changed since the counters were taken."""
+    try:
+        kv = dict(line.split(": ", 1) for line in open(PROFILE_TRAFFIC).read().splitlines()
+                  if line.startswith(("source_hash: ", "traffic_bytes_per_launch: ")))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(w, out_gpu, chunks: int, threads: int):
+    """The CPU oracle (as it stands) on a bounded sample of the workload: the
+    first `chunks` 64 KiB chunks of the same layer (all 1792 by default), compressed by the oracle's
+    own compressor, decoded and dequantized with `threads` host threads.  The
+    sample's outputs are also compared with the GPU's."""
+    import oracle as O
+    packed = O.pack_int4(w.codes)
+    n = min(chunks, w.dst_off.size - 1)
+    d_end = int(w.dst_off[n])
+    dst_off = w.dst_off[:n + 1].copy()
+    t = O.compress_table(packed[:d_end], dst_off, threads=threads)
+    n_elem = 2 * d_end
+    n_groups = -(-n_elem // w.group)
+    scales, zp = w.scales[:n_groups], w.zp[:n_groups]
+    out = np.zeros(n_elem, np.uint16)
+    O.fused_int4_chunked(t, scales, zp, w.group, out, threads)        # warm caches
+    times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        bad, _ = O.fused_int4_chunked(t, scales, zp, w.group, out, threads)
+        times.append(time.perf_counter() - t0)
+        assert bad == 0
+    sec = sorted(times)[2]
+    alg = t.comp_bytes + 2 * n_elem
+    mismatches = int(np.count_nonzero(out != out_gpu[:n_elem]))
+    return {
+        "value": round(alg / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "first %d of %d chunks (%d elements, %.1f MB algorithmic), oracle-compressed, "
+                  "median of 5 runs, %.2f s each" % (n, w.dst_off.size - 1, n_elem, alg / 1e6, sec),
+        "gpu_mismatches_on_sample": mismatches,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--extra", action="store_true")
+    ap.add_argument("--cpu-chunks", type=int, default=1792)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(chunks shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import weight_dequantization_amd as lt
+
+    dev = torch.device("cuda:0")
+    w = synth.config3()
+    packed = lt.pack_int4(w.codes)
+    table = lt.ChunkTable.build(packed, w.dst_off, dev)
+    scales = torch.from_numpy(w.scales.view(np.int16)).to(dev)
+    zp = torch.from_numpy(w.zp).to(dev)
+    n_elem = w.rows * w.cols
+    out = torch.empty(n_elem, dtype=torch.float16, device=dev)
+    status = torch.full((table.n_chunks,), -1, dtype=torch.int32, device=dev)
+    shape = (w.rows, w.cols)
+    alg_bytes = table.comp_bytes + 2 * n_elem
+    meta_bytes = 2 * w.scales.size + w.zp.size + 16 * (table.n_chunks + 1)
+
+    def step():
+        lt.fused_lz4_int4(table, scales, zp, shape, w.group, out=out, status=status)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lt.check_status(status)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lt.check_status(status)
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    avg_kern_ms = float(np.mean(kern_ms))
+    value = alg_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = alg_bytes / (avg_kern_ms / 1e3) / 1e9
+
+    result = {
+        "metric": "fused LZ4+INT4->fp16 GB/s (compressed in + fp16 out) and % of HBM peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; codes ~ rounded N(7.5,3) clipped 0..15, 20% zero groups)",
+        "config": {
+            "workload": "fused LZ4+INT4 -> fp16, 8192x28672 MLP projection, group 128, "
+                        "asymmetric int8 zero points, 64 KiB LZ4 chunks (host packer)",
+            "rows": w.rows, "cols": w.cols, "group": w.group, "chunks": table.n_chunks,
+            "compressed_bytes": table.comp_bytes, "fp16_bytes": 2 * n_elem,
+            "algorithmic_bytes": alg_bytes, "metadata_bytes": int(meta_bytes),
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
+            "kernel": "lt::chunk_kernel<1>", "avg_launch_ms": round(avg_kern_ms, 5),
+            "min_launch_ms": round(float(np.min(kern_ms)), 5),
+            "bytes_per_launch": alg_bytes,
+        },
+    }
+
+    if args.extra:
+        result["extra"] = extra_measurements(torch, lt, w, packed, scales, zp, dev)
+
+    if not args.no_cpu:
+        out_host = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        threads = max(1, min(threads, 64))
+        result["cpu_baseline"] = cpu_baseline(w, out_host, args.cpu_chunks, threads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
+    """Raw INT4 dequant on the same layer, and plain fill / copy ceilings."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+    n_elem = w.rows * w.cols
+    out = torch.empty(n_elem, dtype=torch.float16, device=dev)
+    pk = torch.from_numpy(packed).to(dev)
+    ms_raw = timed(lambda: lt.dequant_int4(pk, scales, zp, (w.rows, w.cols), w.group, out=out))
+    raw_bytes = packed.size + 2 * n_elem
+    ms_fill = timed(lambda: out.fill_(1.0))
+    src = torch.empty(2 * n_elem, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: dst.copy_(src))
+    return {
+        "raw_int4_GBps": round(raw_bytes / ms_raw / 1e6, 1), "raw_int4_ms": round(ms_raw, 4),
+        "fill_fp16_GBps": round(2 * n_elem / ms_fill / 1e6, 1),
+        "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
+    }
+
+
+if __name__ == "__main__":
+    main()

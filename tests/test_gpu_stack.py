@@ -1,0 +1,113 @@
+"""GPU parity over the 80-layer Llama-70B-shaped INT4 stack (config 5).
+
+Every one of the 80 layers x 7 projections (q, k, v, o, gate, up, down; INT4,
+group 128, LZ4 chunks of 16/64/256 KiB drawn per chunk) is resident on the
+device in compressed form and decoded layer by layer into 7 reused fp16
+buffers, one lt_fused_lz4_int4 launch per tensor (560 launches), as a model
+would expand one layer at a time.
+
+Generating 80 distinct layers (68.5e9 codes) on the host would take far
+longer than a test may run, so two distinct layers are generated (the seeds of
+layers 0 and 79) and their compressed tables are copied into 80 separate
+device allocations (even layers from layer 0, odd layers from layer 79).
+Every launch is checked on sampled elements against the oracle applied to the
+generator's codes; layer 0's 7 tensors are also checked in full once.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_dequantization_amd as lt
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+N_SAMPLE = 8192
+
+
+def _expected_at(w, idx):
+    """Oracle dequant of the generator's codes at element indices idx."""
+    codes = w.codes[idx]
+    g = idx // w.group
+    scales = w.scales[g]
+    zp = w.zp[g]
+    # one element per group: pack each code with a zero partner
+    pairs = np.zeros(2 * idx.size, np.uint8)
+    pairs[0::2] = codes
+    ref = O.dequant_int4(O.pack_int4(pairs), np.repeat(scales, 2), np.repeat(zp, 2), 1)
+    return ref[0::2]
+
+
+def test_llama70b_stack_layer_by_layer():
+    assert torch.cuda.is_available()
+    rng = np.random.default_rng(77)
+    distinct = {}
+    for src_layer in (0, 79):
+        for t in range(len(synth.LLAMA70B_LAYER)):
+            w = synth.config5_tensor(src_layer, t)
+            packed = lt.pack_int4(w.codes)
+            comp, comp_off = lt.compress_chunks(packed, w.dst_off)
+            sizes = np.diff(w.dst_off.astype(np.int64))
+            assert set(np.unique(sizes[:-1])) <= {16384, 65536, 262144}
+            idx = rng.integers(0, w.rows * w.cols, N_SAMPLE)
+            distinct[(src_layer, t)] = dict(w=w, comp=comp, comp_off=comp_off,
+                                            idx=idx, ref=_expected_at(w, idx))
+            del packed
+
+    # 80 device-resident layers (separate allocations, copied on the device)
+    base = {}
+    for key, d in distinct.items():
+        w = d["w"]
+        base[key] = (lt.ChunkTable.from_host(d["comp"], d["comp_off"], w.dst_off, DEV),
+                     torch.from_numpy(w.scales.view(np.int16)).to(DEV),
+                     torch.from_numpy(w.zp).to(DEV))
+    layers = []
+    for layer in range(synth.N_LAYERS_70B):
+        src = 0 if layer % 2 == 0 else 79
+        tensors = []
+        for t in range(len(synth.LLAMA70B_LAYER)):
+            tb, sc, zp = base[(src, t)]
+            copy = lt.ChunkTable(tb.comp.clone(), tb.comp_off.clone(), tb.dst_off.clone(), tb.n_chunks,
+                                 tb.max_chunk_bytes, tb.total_bytes, tb.comp_bytes)
+            tensors.append((copy, sc.clone(), zp.clone(), src))
+        layers.append(tensors)
+    resident = sum(tb.comp_bytes for L in layers for tb, _, _, _ in L)
+    assert resident > 25e9            # ~28 GB of compressed weights on the device
+
+    outs = [torch.empty(r * c, dtype=torch.float16, device=DEV) for _, r, c in synth.LLAMA70B_LAYER]
+    statuses = [torch.empty(max(tb.n_chunks for L in layers for tb, _, _, _ in L), dtype=torch.int32,
+                            device=DEV) for _ in synth.LLAMA70B_LAYER]
+    sample_idx = [torch.from_numpy(distinct[(0, t)]["idx"]).to(DEV) for t in range(7)]
+    sample_idx79 = [torch.from_numpy(distinct[(79, t)]["idx"]).to(DEV) for t in range(7)]
+    for layer, tensors in enumerate(layers):
+        got = []
+        for t, (tb, sc, zp, src) in enumerate(tensors):
+            name, r, c = synth.LLAMA70B_LAYER[t]
+            statuses[t].fill_(-1)
+            lt.fused_lz4_int4(tb, sc, zp, (r, c), 128, out=outs[t], status=statuses[t])
+            idx = sample_idx[t] if src == 0 else sample_idx79[t]
+            got.append(outs[t][idx].clone())
+        torch.cuda.synchronize()
+        for t, (tb, _, _, src) in enumerate(tensors):
+            st = statuses[t][:tb.n_chunks].cpu().numpy()
+            assert np.all(st == 0), (layer, t, np.unique(st))
+            g = got[t].view(torch.int16).cpu().numpy().view(np.uint16)
+            ref = distinct[(src, t)]["ref"]
+            bad = np.count_nonzero(g != ref)
+            assert bad == 0, "layer %d tensor %s: %d of %d sampled outputs differ" % (
+                layer, synth.LLAMA70B_LAYER[t][0], bad, ref.size)
+
+    # full check of layer 0's tensors, once
+    for (src, t), d in distinct.items():
+        if src != 0:
+            continue
+        w = d["w"]
+        tb, sc, zp = base[(src, t)]
+        out = lt.fused_lz4_int4(tb, sc, zp, (w.rows, w.cols), 128)
+        torch.cuda.synchronize()
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+        ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, 128)
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, "layer %d tensor %d: %d differ, first %d" % (src, t, bad.size, bad[0])

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"),
 ]
 
 
@@ -30,7 +30,7 @@ def build(verbose: bool = False) -> str:
     pack_o = os.path.join(BUILD, "lt_pack.o")
     api_o = os.path.join(BUILD, "lt_api.o")
     cmds = [
-        ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-c",
+        ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-I" + os.path.join(ROOT, "include"), "-c",
          os.path.join(CSRC, "lt_pack.cpp"), "-o", pack_o],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "lt_api.hip"), "-o", api_o],
         [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", api_o, pack_o, "-pthread",

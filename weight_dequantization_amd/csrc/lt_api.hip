@@ -9,7 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/lt.h"
+#include "lt.h"
 #include "lt_device.hpp"
 #include "lt_lz4.hpp"
 
@@ -157,6 +157,7 @@ lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *c
   P.scales = scales;
   P.zp = zp;
   P.group = group;
+  P.group_shift = shift_of(group);
   hipStream_t s = (hipStream_t)stream;
   dim3 grid(t->n_chunks), block(lt::NTHREADS);
   switch (mode) {

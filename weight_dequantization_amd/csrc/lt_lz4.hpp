@@ -5,7 +5,9 @@
 //                     decoded bytes into a 64 KiB LDS history ring (literal
 //                     copies from the input ring, match copies from history);
 //   wave 1  feeder  : streams the chunk's compressed bytes from HBM into an
-//                     8 KiB LDS input ring ahead of the decoder;
+//                     8 KiB LDS input ring with LDS-DMA loads
+//                     (global_load_lds_dwordx4), several 1 KiB segments in
+//                     flight;
 //   waves 2+ flushers: take completed 1 KiB tiles of history and write them
 //                     out: as bytes (decode-only), or unpacked and
 //                     dequantized to fp16 (fused INT4 / INT8), with coalesced
@@ -21,8 +23,15 @@
 // is what byte-serial copying gives when d < M; every source byte lies before
 // p, so all lanes may copy a match at once.
 //
-// The roles talk through LDS counters (relaxed atomics after an explicit
-// lgkmcnt(0) wait, so the data they publish is already in LDS):
+// LDS traffic is kept to naturally aligned accesses: every lane owns an
+// aligned 16-byte block of the destination, gathers its source bytes with
+// aligned dword reads and v_alignbyte, and writes the partial blocks at the
+// ends of a copy with aligned byte / half / dword stores (no read-modify-
+// write).  The decoder reads the next parse window together with a
+// sequence's literal bytes, so a typical sequence costs one LDS round trip.
+//
+// The roles talk through LDS counters (relaxed atomics, published only after
+// an lgkmcnt(0) / vmcnt wait, so the data they announce is already in LDS):
 //   in_avail  feeder  -> decoder : input bytes present in the ring
 //   in_used   decoder -> feeder  : input before this position is consumed
 //   out_done  decoder -> flushers: history bytes that are final
@@ -44,11 +53,14 @@ constexpr uint32_t HIST = 1u << 16;   // LZ4 distances reach 65535
 constexpr uint32_t HMASK = HIST - 1;
 constexpr uint32_t INR = 1u << 13;    // compressed-input ring
 constexpr uint32_t IMASK = INR - 1;
+constexpr uint32_t SEG = 1024;        // feeder unit: one 16-byte DMA load per lane
+constexpr uint32_t QMAX = INR / SEG;  // segments in flight at most
 constexpr uint32_t TILE = 1024;       // flush granularity (bytes of decoded stream)
 constexpr int NFLUSH = 2;
 constexpr int NWAVES = 2 + NFLUSH;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr uint32_t LEN_CAP = 1u << 31;
+constexpr uint32_t LIT_ONE_STEP = 960;  // literal runs copied with one gather step
 
 enum : uint32_t { ST_RUN = 0, ST_DONE = 1, ST_FAIL = 2 };
 enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5 };
@@ -67,7 +79,6 @@ struct Ctl {
 struct Smem {
   uint8_t hist[HIST];
   uint8_t inr[INR];
-  Ctl ctl;
 };
 
 struct ChunkParams {
@@ -83,108 +94,192 @@ struct ChunkParams {
   const uint16_t *scales;
   const int8_t *zp;
   uint64_t group;
+  uint32_t group_shift;      // log2(group) when group is a power of two, else 64
 };
 
 // ------------------------------------------------------------ LDS sync
 
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
 
+// vmcnt(k), leaving expcnt and lgkmcnt unconstrained (gfx9 encoding)
+template <int K>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(K >= 0 && K < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_vm_le(uint32_t k) {
+  switch (k) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    default: wait_vm<7>(); break;
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_get(uint32_t *p) {
   uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Publish a counter after this wave's earlier LDS writes have completed.
-__device__ __forceinline__ void lds_put(uint32_t *p, uint32_t v, uint32_t lane) {
-  wait_lds();
+__device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t lane) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// The feeder's counter accesses go through inline asm: its LDS-DMA loads
+// would otherwise make the compiler wait for every load in flight before any
+// LDS access of that wave.  Each read waits for its own result inside the asm
+// block, so its output register is final when the block ends.
+__device__ __forceinline__ uint32_t lds_addr(const uint32_t *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t *)p;
+}
+
+__device__ __forceinline__ uint32_t lds_get_asm(const uint32_t *p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ void lds_set_asm(uint32_t *p, uint32_t v, uint32_t lane) {
+  if (lane == 0) asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// Publish a counter after this wave's earlier LDS operations have completed.
+__device__ __forceinline__ void lds_put(uint32_t *p, uint32_t v, uint32_t lane) {
+  wait_lds();
+  lds_set(p, v, lane);
+}
+
 // ------------------------------------------------------ LDS byte moves
 
-__device__ __forceinline__ uint4 lds_ld16(const uint8_t *p) {
-  uint4 v;
-  __builtin_memcpy(&v, p, 16);
-  return v;
+// 16 bytes starting at ring index si (any alignment), from five aligned
+// dword reads; ring sizes are multiples of 4, so no read straddles the end.
+template <uint32_t MASK>
+__device__ __forceinline__ uint4 gather16(const uint8_t *ring, uint32_t si) {
+  const uint32_t *r = (const uint32_t *)ring;
+  uint32_t a = si & ~3u, sh = si & 3u;
+  uint32_t d0 = r[(a & MASK) >> 2];
+  uint32_t d1 = r[((a + 4) & MASK) >> 2];
+  uint32_t d2 = r[((a + 8) & MASK) >> 2];
+  uint32_t d3 = r[((a + 12) & MASK) >> 2];
+  uint32_t d4 = r[((a + 16) & MASK) >> 2];
+  return make_uint4(__builtin_amdgcn_alignbyte(d1, d0, sh), __builtin_amdgcn_alignbyte(d2, d1, sh),
+                    __builtin_amdgcn_alignbyte(d3, d2, sh), __builtin_amdgcn_alignbyte(d4, d3, sh));
 }
 
-// dword k (0..3) of v, selected without indexing a register array
-__device__ __forceinline__ uint32_t dword_of(uint4 v, uint32_t k) {
-  uint32_t lo = (k & 1) ? v.y : v.x;
-  uint32_t hi = (k & 1) ? v.w : v.z;
-  return (k & 2) ? hi : lo;
-}
-
-__device__ __forceinline__ uint32_t byte_of(uint4 v, uint32_t b) {
-  return (dword_of(v, b >> 2) >> ((b & 3) * 8)) & 0xFFu;
-}
-
-// Write the first n (1..16) bytes of v at p, without touching p[n..16).
-__device__ __forceinline__ void lds_st_part(uint8_t *p, uint4 v, uint32_t n) {
-  if (n == 16) {
-    __builtin_memcpy(p, &v, 16);
+// bytes [lo, hi) of dword d, which sits at p + base (base multiple of 4)
+__device__ __forceinline__ void st_dword_part(uint8_t *p, uint32_t d, uint32_t base, uint32_t lo,
+                                              uint32_t hi) {
+  uint32_t s = lo > base ? lo : base;
+  uint32_t e = hi < base + 4 ? hi : base + 4;
+  if (s >= e) return;
+  if (s == base && e == base + 4) {
+    *(uint32_t *)(p + base) = d;
     return;
   }
-  uint32_t o = 0;
-  if (n & 8) {
-    uint2 a = make_uint2(v.x, v.y);
-    __builtin_memcpy(p, &a, 8);
-    o = 8;
+  uint32_t x = d >> (8 * (s - base));
+  if (s & 1) {
+    p[s] = (uint8_t)x;
+    s++;
+    x >>= 8;
   }
-  if (n & 4) {
-    uint32_t a = dword_of(v, o >> 2);
-    __builtin_memcpy(p + o, &a, 4);
-    o += 4;
+  if (e - s >= 2) {
+    *(uint16_t *)(p + s) = (uint16_t)x;
+    s += 2;
+    x >>= 16;
   }
-  if (n & 2) {
-    uint16_t h = (uint16_t)(dword_of(v, o >> 2) >> ((o & 3) * 8));
-    __builtin_memcpy(p + o, &h, 2);
-    o += 2;
-  }
-  if (n & 1) p[o] = (uint8_t)byte_of(v, o);
+  if (s < e) p[s] = (uint8_t)x;
 }
 
-// 16 bytes from a ring at arbitrary (wrapping) positions
-template <uint32_t MASK>
-__device__ __forceinline__ uint4 ring_ld16(const uint8_t *ring, uint32_t pos) {
-  uint32_t w[4];
-#pragma unroll
-  for (int k = 0; k < 4; k++) {
-    w[k] = 0;
-#pragma unroll
-    for (int b = 0; b < 4; b++) w[k] |= (uint32_t)ring[(pos + 4 * k + b) & MASK] << (8 * b);
+// bytes [lo, hi) (0 <= lo < hi <= 16) of v into the 16-byte aligned block p,
+// with naturally aligned stores only
+__device__ __forceinline__ void st_block(uint8_t *p, uint4 v, uint32_t lo, uint32_t hi) {
+  if (lo == 0 && hi == 16) {
+    *(uint4 *)p = v;
+    return;
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// first n (1..16) bytes of v to a ring at arbitrary (wrapping) positions
-template <uint32_t MASK>
-__device__ __forceinline__ void ring_st_part(uint8_t *ring, uint32_t pos, uint4 v, uint32_t n) {
-  for (uint32_t b = 0; b < n; b++) ring[(pos + b) & MASK] = (uint8_t)byte_of(v, b);
+  st_dword_part(p, v.x, 0, lo, hi);
+  st_dword_part(p, v.y, 4, lo, hi);
+  st_dword_part(p, v.z, 8, lo, hi);
+  st_dword_part(p, v.w, 12, lo, hi);
 }
 
 // ---------------------------------------------------------- the decoder
 
 struct Decoder {
   Smem &sm;
+  Ctl &ctl;
   uint32_t lane;
-  uint32_t rbase;     // ring index of input position y = 0
-  uint32_t y;         // input position (bytes from the 16-aligned block start)
+  uint32_t y;          // input position (bytes from the 16-aligned block start)
   uint32_t y_end;
-  uint32_t op;        // output position within the chunk
-  uint32_t N;         // chunk's decoded size
-  uint32_t avail;     // cached ctl.in_avail
-  uint32_t flushed;   // cached: tiles below this * TILE are written out
-  uint32_t wy;        // window start (multiple of 4); window = [wy, wy + 256)
-  uint32_t win;       // this lane's dword of the window
-  uint32_t used;      // last value published to ctl.in_used
+  uint32_t op;         // output position within the chunk
+  uint32_t N;          // chunk's decoded size
+  uint32_t avail;      // cached ctl.in_avail
+  uint32_t flushed;    // cached: history below this is written out
+  uint32_t wy;         // window start (multiple of 4); window = [wy, wy + 256)
+  uint32_t win;        // this lane's dword of the window
+  uint32_t used;       // last value published to ctl.in_used
+  uint32_t last_byte;  // the decoded byte at op - 1
+  uint4 cur;           // the 16-byte block holding op; bytes below op are final
+
+  // While every position written so far is below HIST (the first pass
+  // through the ring), copies write whole aligned blocks: bytes past a copy's
+  // end are future positions, rewritten before any match or flush reads
+  // them.  Past that point a block may still hold bytes a long match needs,
+  // so copies write exactly their own bytes.
+  __device__ bool whole_blocks(uint32_t end) const { return end + 15 <= HIST; }
+
+  static __device__ __forceinline__ uint4 readlane4(uint4 v, uint32_t l) {
+    return make_uint4(__builtin_amdgcn_readlane(v.x, l), __builtin_amdgcn_readlane(v.y, l),
+                      __builtin_amdgcn_readlane(v.z, l), __builtin_amdgcn_readlane(v.w, l));
+  }
+
+  // bytes [0, keep) from c, the rest from v (keep = 0 leaves v unchanged)
+  static __device__ __forceinline__ uint4 merge_head(uint4 c, uint4 v, uint32_t keep) {
+    uint32_t m[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint32_t k = keep > 4u * j ? keep - 4u * j : 0u;
+      m[j] = k >= 4 ? 0xFFFFFFFFu : ((1u << (8 * k)) - 1u);
+    }
+    return make_uint4((c.x & m[0]) | (v.x & ~m[0]),
+                      (c.y & m[1]) | (v.y & ~m[1]), (c.z & m[2]) | (v.z & ~m[2]),
+                      (c.w & m[3]) | (v.w & ~m[3]));
+  }
+
+  // Whole-block copy of history [od, od + n): block P's bytes come from
+  // src(P); the head block keeps cur's bytes below od.  Each 64-block step
+  // reads all its sources before writing.  Leaves cur / last_byte at the end.
+  template <class Src>
+  __device__ void put_blocks(uint32_t od, uint32_t n, Src src) {
+    const uint32_t A = od & ~15u, end = od + n, keep = od & 15u;
+    const uint32_t nb = (end - A + 15) >> 4;
+    uint4 last = cur;
+    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+      const uint32_t b = b0 + lane;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (b < nb) v = src(A + 16 * b);
+      v = merge_head(cur, v, b == 0 ? keep : 0u);
+      if (b < nb) *(uint4 *)(sm.hist + A + 16 * b) = v;
+      const uint32_t lb = nb - 1 - b0;
+      if (lb < 64) last = readlane4(v, lb);
+    }
+    cur = last;
+    const uint32_t q = (end - 1) & 15u;
+    const uint32_t d = q < 4 ? last.x : q < 8 ? last.y : q < 12 ? last.z : last.w;
+    last_byte = (d >> (8 * (q & 3))) & 0xFFu;
+  }
 
   __device__ void need_input(uint32_t upto) {
     if (upto > y_end) upto = y_end;
     while (avail < upto) {
-      avail = lds_get(&sm.ctl.in_avail);
+      avail = lds_get(&ctl.in_avail);
       if (avail < upto) __builtin_amdgcn_s_sleep(1);
     }
   }
@@ -195,13 +290,24 @@ struct Decoder {
     if (end <= HIST) return;
     uint32_t need = end - HIST;
     while (flushed < need) {
-      uint32_t m = lds_get(&sm.ctl.next_tile[0]);
+      uint32_t m = lds_get(&ctl.next_tile[0]);
       for (int f = 1; f < NFLUSH; f++) {
-        uint32_t t = lds_get(&sm.ctl.next_tile[f]);
+        uint32_t t = lds_get(&ctl.next_tile[f]);
         m = t < m ? t : m;
       }
       flushed = (m >= (0xFFFFFFFFu / TILE)) ? 0xFFFFFFFFu : m * TILE;
       if (flushed < need) __builtin_amdgcn_s_sleep(1);
+    }
+  }
+
+  // Announce progress; cheap right after a wait that already completed this
+  // wave's earlier LDS operations.
+  __device__ void publish(uint32_t new_used) {
+    wait_lds();
+    lds_set(&ctl.out_done, op, lane);
+    if (new_used > used) {
+      used = new_used;
+      lds_set(&ctl.in_used, used, lane);
     }
   }
 
@@ -211,13 +317,16 @@ struct Decoder {
     // distances before p are parsed, and literal runs start at or after p
     if (wy > used) {
       used = wy;
-      lds_put(&sm.ctl.in_used, used, lane);
+      lds_put(&ctl.in_used, used, lane);
     }
     need_input(wy + 256);
-    win = *(const uint32_t *)(sm.inr + ((rbase + wy + 4 * lane) & IMASK));
+    win = *(const uint32_t *)(sm.inr + ((wy + 4 * lane) & IMASK));
+    // wait here, on this path only: otherwise the compiler waits at every
+    // byte_at for all outstanding LDS writes, whether the window reloaded or not
+    wait_lds();
   }
 
-  // byte at input position p; the window must cover p
+  // byte at input position p (reloads the window when p is outside it)
   __device__ uint32_t byte_at(uint32_t p) {
     if (p < wy || p >= wy + 256) load_window(p);
     uint32_t rel = p - wy;
@@ -225,75 +334,61 @@ struct Decoder {
     return (d >> ((rel & 3) * 8)) & 0xFFu;
   }
 
-  __device__ void publish_out() { lds_put(&sm.ctl.out_done, op, lane); }
-
-  // copy n literal bytes from input position ys to history position od
-  __device__ void copy_from_input(uint32_t ys, uint32_t od, uint32_t n) {
-    for (uint32_t base = 0; base < n; base += 64 * 16) {
-      uint32_t j = base + 16 * lane;
-      if (j < n) {
-        uint32_t cnt = n - j < 16 ? n - j : 16;
-        uint32_t s = (rbase + ys + j) & IMASK;
-        uint32_t d = (od + j) & HMASK;
-        uint4 v = (s + 16 <= INR) ? lds_ld16(sm.inr + s) : ring_ld16<IMASK>(sm.inr, s);
-        if (d + 16 <= HIST) lds_st_part(sm.hist + d, v, cnt);
-        else ring_st_part<HMASK>(sm.hist, d, v, cnt);
-      }
-    }
-  }
-
-  // contiguous history copy: dst od.., src od - dist.., n bytes, where every
-  // source byte is final before this call's first write of its 1 KiB step
-  __device__ void copy_hist(uint32_t od, uint32_t dist, uint32_t n) {
-    for (uint32_t base = 0; base < n; base += 64 * 16) {
-      uint32_t j = base + 16 * lane;
-      if (j < n) {
-        uint32_t cnt = n - j < 16 ? n - j : 16;
-        uint32_t s = (od + j - dist) & HMASK;
-        uint32_t d = (od + j) & HMASK;
-        uint4 v = (s + 16 <= HIST) ? lds_ld16(sm.hist + s) : ring_ld16<HMASK>(sm.hist, s);
-        if (d + 16 <= HIST) lds_st_part(sm.hist + d, v, cnt);
-        else ring_st_part<HMASK>(sm.hist, d, v, cnt);
+  // history [od, od + n) from ring R at index src0 + (P - od); every source
+  // byte is final before each 64-block step writes
+  template <uint32_t MASK>
+  __device__ void copy_blocks(const uint8_t *R, uint32_t src0, uint32_t od, uint32_t n) {
+    const uint32_t A = od & ~15u, end = od + n;
+    const uint32_t nb = (end - A + 15) >> 4;
+    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+      uint32_t b = b0 + lane;
+      if (b < nb) {
+        uint32_t P = A + 16 * b;
+        uint32_t lo = od > P ? od - P : 0;
+        uint32_t hi = end - P < 16 ? end - P : 16;
+        uint4 v = gather16<MASK>(R, src0 + (P - od));
+        st_block(sm.hist + (P & HMASK), v, lo, hi);
       }
     }
   }
 
   __device__ void fill(uint32_t od, uint32_t byte, uint32_t n) {
-    uint32_t w = byte * 0x01010101u;
-    uint4 v = make_uint4(w, w, w, w);
-    for (uint32_t base = 0; base < n; base += 64 * 16) {
-      uint32_t j = base + 16 * lane;
-      if (j < n) {
-        uint32_t cnt = n - j < 16 ? n - j : 16;
-        uint32_t d = (od + j) & HMASK;
-        if (d + 16 <= HIST) lds_st_part(sm.hist + d, v, cnt);
-        else ring_st_part<HMASK>(sm.hist, d, v, cnt);
-      }
+    const uint32_t w = byte * 0x01010101u;
+    const uint4 v = make_uint4(w, w, w, w);
+    const uint32_t A = od & ~15u, end = od + n;
+    const uint32_t nb = (end - A + 15) >> 4;
+    for (uint32_t b = lane; b < nb; b += 64) {
+      uint32_t P = A + 16 * b;
+      uint32_t lo = od > P ? od - P : 0;
+      uint32_t hi = end - P < 16 ? end - P : 16;
+      st_block(sm.hist + (P & HMASK), v, lo, hi);
     }
   }
 
-  // first min(M, 1 KiB) bytes of an overlapping match, byte by byte:
-  // out[op + j] = out[op - dist + (j mod dist)]
-  __device__ void copy_periodic_first(uint32_t od, uint32_t dist, uint32_t n) {
-    uint32_t j = 16 * lane;
-    if (j < n) {
-      uint32_t cnt = n - j < 16 ? n - j : 16;
-      uint32_t r = j % dist;
-      uint32_t src0 = od - dist;
-      uint32_t w[4];
+  // the first n (<= 1 KiB) bytes of an overlapping match, byte by byte:
+  // out[od + j] = out[od - dist + (j mod dist)]
+  __device__ void copy_periodic(uint32_t od, uint32_t dist, uint32_t n) {
+    const uint32_t A = od & ~15u, end = od + n;
+    const uint32_t nb = (end - A + 15) >> 4;
+    for (uint32_t b = lane; b < nb; b += 64) {
+      uint32_t P = A + 16 * b;
+      uint32_t lo = od > P ? od - P : 0;
+      uint32_t hi = end - P < 16 ? end - P : 16;
+      uint32_t r = (P + lo - od) % dist;
+      uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        w[k] = 0;
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-          w[k] |= (uint32_t)sm.hist[(src0 + r) & HMASK] << (8 * b);
+      for (uint32_t q = 0; q < 16; q++) {
+        if (q >= lo && q < hi) {
+          uint32_t v = sm.hist[(od - dist + r) & HMASK];
+          uint32_t sv = v << (8 * (q & 3));
+          if (q < 4) w0 |= sv;
+          else if (q < 8) w1 |= sv;
+          else if (q < 12) w2 |= sv;
+          else w3 |= sv;
           r = (r + 1 == dist) ? 0 : r + 1;
         }
       }
-      uint32_t d = (od + j) & HMASK;
-      uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
-      if (d + 16 <= HIST) lds_st_part(sm.hist + d, v, cnt);
-      else ring_st_part<HMASK>(sm.hist, d, v, cnt);
+      st_block(sm.hist + (P & HMASK), make_uint4(w0, w1, w2, w3), lo, hi);
     }
   }
 
@@ -301,26 +396,49 @@ struct Decoder {
     // pieces keep the writes within what the ring can hold ahead of the flushers
     const uint32_t PIECE = 32768;
     if (dist == 1) {
-      uint32_t b = sm.hist[(op - 1) & HMASK];
-      b = __builtin_amdgcn_readfirstlane(b);
+      const uint32_t w = last_byte * 0x01010101u;
       while (M) {
         uint32_t n = M < PIECE ? M : PIECE;
         need_ring(op + n);
-        fill(op, b, n);
+        if (whole_blocks(op + n)) put_blocks(op, n, [&](uint32_t) { return make_uint4(w, w, w, w); });
+        else fill(op, last_byte, n);
         op += n;
         M -= n;
-        publish_out();
+        if (M) publish(used);
       }
       return;
     }
     uint32_t done = 0;
+    bool exact = false;
     if (dist < M && dist < 1024) {
       uint32_t n = M < 1024 ? M : 1024;
       need_ring(op + n);
-      copy_periodic_first(op, dist, n);
+      if (whole_blocks(op + n)) {
+        const uint32_t od = op;
+        put_blocks(od, n, [&](uint32_t P) {
+          uint32_t lo = od > P ? od - P : 0;
+          uint32_t r = (P + lo - od) % dist;
+          uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+          for (uint32_t q = 0; q < 16; q++) {
+            if (q >= lo) {
+              uint32_t sv = (uint32_t)sm.hist[(od - dist + r) & HMASK] << (8 * (q & 3));
+              if (q < 4) w0 |= sv;
+              else if (q < 8) w1 |= sv;
+              else if (q < 12) w2 |= sv;
+              else w3 |= sv;
+              r = (r + 1 == dist) ? 0 : r + 1;
+            }
+          }
+          return make_uint4(w0, w1, w2, w3);
+        });
+      } else {
+        copy_periodic(op, dist, n);
+        exact = true;
+      }
       op += n;
       done = n;
-      publish_out();
+      publish(used);
       // later bytes repeat with any multiple of dist; the smallest multiple
       // >= 1 KiB keeps each 1 KiB step's sources before the step
       dist = dist * ((1024 + dist - 1) / dist);
@@ -328,11 +446,69 @@ struct Decoder {
     while (done < M) {
       uint32_t n = M - done < PIECE ? M - done : PIECE;
       need_ring(op + n);
-      copy_hist(op, dist, n);
+      if (whole_blocks(op + n)) {
+        const uint32_t dd = dist;
+        put_blocks(op, n, [&](uint32_t P) { return gather16<HMASK>(sm.hist, P - dd); });
+      } else {
+        copy_blocks<HMASK>(sm.hist, op - dist, op, n);
+        exact = true;
+      }
       op += n;
       done += n;
-      publish_out();
+      if (done < M) publish(used);
     }
+    if (exact) last_byte = __builtin_amdgcn_readfirstlane(sm.hist[(op - 1) & HMASK]);
+  }
+
+  // literal run of L bytes at input y: copy, advance y / op, and leave the
+  // window covering the bytes that follow
+  __device__ void literals(uint32_t L) {
+    const uint32_t ye = y + L;
+    if (L <= LIT_ONE_STEP && whole_blocks(op + L)) {
+      const uint32_t nw = ye & ~3u;
+      need_input((ye > nw + 256) ? ye : nw + 256);
+      const uint32_t A = op & ~15u, end = op + L, keep = op & 15u;
+      const uint32_t nb = (end - A + 15) >> 4;   // <= 62
+      const uint32_t P = A + 16 * lane;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (lane < nb) v = gather16<IMASK>(sm.inr, y + (P - op));
+      const uint32_t nwin = *(const uint32_t *)(sm.inr + ((nw + 4 * lane) & IMASK));
+      publish(y);   // waits for the reads above (and so for every earlier write)
+      v = merge_head(cur, v, lane == 0 ? keep : 0u);
+      if (lane < nb) *(uint4 *)(sm.hist + P) = v;
+      cur = readlane4(v, nb - 1);
+      const uint32_t q = (end - 1) & 15u;
+      const uint32_t d = q < 4 ? cur.x : q < 8 ? cur.y : q < 12 ? cur.z : cur.w;
+      last_byte = (d >> (8 * (q & 3))) & 0xFFu;
+      win = nwin;
+      wy = nw;
+      y = ye;
+      op += L;
+      return;
+    }
+    uint32_t left = L;
+    bool exact = false;
+    while (left) {
+      // the feeder fills whole segments up to QMAX past the segment holding
+      // `used`, so a piece of INR - 2 * SEG bytes is always deliverable
+      uint32_t piece = left < INR - 2 * SEG ? left : INR - 2 * SEG;
+      used = y;
+      lds_put(&ctl.in_used, used, lane);
+      need_input(y + piece);
+      need_ring(op + piece);
+      if (whole_blocks(op + piece)) {
+        const uint32_t ys = y, od = op;
+        put_blocks(op, piece, [&](uint32_t Pb) { return gather16<IMASK>(sm.inr, ys + (Pb - od)); });
+      } else {
+        copy_blocks<IMASK>(sm.inr, y, op, piece);
+        exact = true;
+      }
+      y += piece;
+      op += piece;
+      left -= piece;
+      publish(used);
+    }
+    if (exact) last_byte = byte_at(ye - 1);
   }
 
   // Returns the chunk status.
@@ -355,18 +531,7 @@ struct Decoder {
       }
       if (L > y_end - y) { st = C_TRUNC; break; }
       if (L > N - op) { st = C_OVERRUN; break; }
-      while (L) {
-        uint32_t piece = L < INR - 64 ? L : INR - 64;
-        used = y;
-        lds_put(&sm.ctl.in_used, used, lane);
-        need_input(y + piece);
-        need_ring(op + piece);
-        copy_from_input(y, op, piece);
-        y += piece;
-        op += piece;
-        L -= piece;
-        publish_out();
-      }
+      if (L) literals(L);
       if (y == y_end) break;
       if (y_end - y < 2) { st = C_TRUNC; break; }
       uint32_t dist = byte_at(y);
@@ -386,8 +551,6 @@ struct Decoder {
       }
       if (M > N - op) { st = C_OVERRUN; break; }
       copy_match(dist, M);
-      used = y;
-      lds_put(&sm.ctl.in_used, used, lane);
     }
   out:
     if (st == C_OK && op != N) st = C_SIZE;
@@ -397,45 +560,76 @@ struct Decoder {
 
 // -------------------------------------------------------------- feeder
 
-__device__ void feeder(Smem &sm, uint32_t lane, const uint8_t *S, uint32_t rbase, uint32_t y_end) {
-  constexpr int FU = 4;   // 16-byte blocks per lane per batch (4 KiB per batch)
-  uint32_t nblk = (y_end + 15) / 16;
-  uint32_t next = 0;
-  while (next < nblk) {
-    uint32_t used = lds_get(&sm.ctl.in_used);
-    uint32_t state = lds_get(&sm.ctl.state);
-    if (state != ST_RUN) break;
-    uint32_t limit = ((used & ~15u) + INR) / 16;
-    if (limit > nblk) limit = nblk;
-    if (limit <= next) {
+// Streams the chunk's 16-byte aligned blocks into the input ring, one 1 KiB
+// segment (one LDS-DMA load per lane) at a time, keeping up to QMAX segments
+// in flight within the ring space the decoder has released.
+__device__ void feeder(Smem &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end) {
+  const uint32_t nblk = (y_end + 15) / 16;
+  const uint32_t nseg = (y_end + SEG - 1) / SEG;
+  uint32_t issued = 0, landed = 0;
+  while (landed < nseg) {
+    if (lds_get_asm(&ctl.state) != ST_RUN) break;
+    uint32_t used = lds_get_asm(&ctl.in_used);
+    uint32_t limit = used / SEG + QMAX;
+    if (limit > nseg) limit = nseg;
+    while (issued < limit && issued - landed < QMAX) {
+      uint32_t blk = issued * (SEG / 16) + lane;
+      if (blk >= nblk) blk = nblk - 1;   // stay within the chunk's blocks
+      __builtin_amdgcn_global_load_lds((const void *)(S + 16ull * blk),
+                                       (__attribute__((address_space(3))) void *)(sm.inr + ((issued * SEG) & IMASK)),
+                                       16, 0, 0);
+      issued++;
+    }
+    if (issued == landed) {
       __builtin_amdgcn_s_sleep(1);
       continue;
     }
-    uint32_t cnt = limit - next;
-    if (cnt > 64u * FU) cnt = 64u * FU;
-    // every lane loads FU blocks (indices clamped into the batch, so all loads
-    // are issued back to back and read only blocks of this chunk), then the
-    // lanes whose blocks are in the batch write them to the ring
-    const uint32_t last = next + cnt - 1;
-    uint32_t b0 = next + lane, b1 = b0 + 64, b2 = b0 + 128, b3 = b0 + 192;
-    uint4 v0 = *(const uint4 *)(S + 16ull * (b0 < last ? b0 : last));
-    uint4 v1 = *(const uint4 *)(S + 16ull * (b1 < last ? b1 : last));
-    uint4 v2 = *(const uint4 *)(S + 16ull * (b2 < last ? b2 : last));
-    uint4 v3 = *(const uint4 *)(S + 16ull * (b3 < last ? b3 : last));
-    if (b0 <= last) *(uint4 *)(sm.inr + ((rbase + 16 * b0) & IMASK)) = v0;
-    if (b1 <= last) *(uint4 *)(sm.inr + ((rbase + 16 * b1) & IMASK)) = v1;
-    if (b2 <= last) *(uint4 *)(sm.inr + ((rbase + 16 * b2) & IMASK)) = v2;
-    if (b3 <= last) *(uint4 *)(sm.inr + ((rbase + 16 * b3) & IMASK)) = v3;
-    next += cnt;
-    lds_put(&sm.ctl.in_avail, next * 16, lane);
+    wait_vm_le(issued - landed - 1);   // the oldest segment in flight has landed
+    landed++;
+    lds_set_asm(&ctl.in_avail, landed * SEG, lane);
   }
+  wait_vm<0>();   // no LDS-DMA write outlives this wave
 }
 
 // ------------------------------------------------------------- flushers
 
+struct Meta4 {
+  uint32_t s[4];
+  uint32_t z[4];
+};
+
+// scales / zero points of one INT4 tile (fast path: group is a power of two
+// >= 8, so each lane's 8 codes share one group).  The loads are issued here
+// and consumed only after the wait for the tile (see meta_ready).
+__device__ __forceinline__ Meta4 int4_meta(const ChunkParams &P, uint64_t dst0, uint32_t t,
+                                           uint32_t lane, uint32_t N) {
+  Meta4 m;
+  // without zero points, read any valid byte and discard it (no branch)
+  const int8_t *zsrc = P.zp ? P.zp : (const int8_t *)P.scales;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    uint32_t p = t * TILE + 256 * k + 4 * lane;
+    if (p >= N) p = 0;   // any valid group; unused
+    uint64_t g = (2 * (dst0 + p)) >> P.group_shift;
+    m.s[k] = P.scales[g];
+    m.z[k] = (uint32_t)(int32_t)zsrc[g];
+  }
+  return m;
+}
+
+// Make the tile's scale registers opaque here, so the compiler consumes (and
+// waits for) them at this point instead of right after issuing the loads.
+__device__ __forceinline__ void meta_ready(Meta4 &m, bool has_zp) {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    asm volatile("" : "+v"(m.s[k]), "+v"(m.z[k]));
+    if (!has_zp) m.z[k] = 0;
+  }
+}
+
 template <int MODE>
 __device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
-                           uint32_t t, uint32_t N) {
+                           uint32_t t, uint32_t N, const Meta4 &m, bool fast) {
   uint32_t base = t * TILE;
   if constexpr (MODE == MODE_BYTES) {
     uint8_t *out = (uint8_t *)P.out + dst0;
@@ -445,33 +639,39 @@ __device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64
       if (p + 16 <= N) {
         *(uint4 *)(out + p) = v;
       } else {
-        for (uint32_t b = 0; b < N - p; b++) out[p + b] = (uint8_t)byte_of(v, b);
+#pragma unroll
+        for (uint32_t b = 0; b < 16; b++) {
+          uint32_t d = b < 4 ? v.x : b < 8 ? v.y : b < 12 ? v.z : v.w;
+          if (p + b < N) out[p + b] = (uint8_t)(d >> ((b & 3) * 8));
+        }
       }
     }
   } else if constexpr (MODE == MODE_INT4) {
     uint16_t *out = (uint16_t *)P.out;
     const uint64_t G = P.group;
+    uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       uint32_t p = base + 256 * k + 4 * lane;
-      if (p < N) {
-        uint32_t w = *(const uint32_t *)(sm.hist + (p & HMASK));
-        uint64_t e0 = 2 * (dst0 + p);
+      w[k] = (p < N) ? *(const uint32_t *)(sm.hist + (p & HMASK)) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      uint32_t p = base + 256 * k + 4 * lane;
+      if (p >= N) continue;
+      uint64_t e0 = 2 * (dst0 + p);
+      if (fast && p + 4 <= N) {
+        uint4 r = deq8_int4(w[k], splat_h2((uint16_t)f16_bits_1024_plus((int)m.z[k])),
+                            splat_h2((uint16_t)m.s[k]));
+        *(uint4 *)(out + e0) = r;
+      } else {
         uint32_t nb = N - p < 4 ? N - p : 4;
-        uint64_t g0 = e0 / G, g1 = (e0 + 2 * nb - 1) / G;
-        if (nb == 4 && g0 == g1) {
-          uint16_t sb = P.scales[g0];
-          int z = P.zp ? (int)P.zp[g0] : 0;
-          uint4 r = deq8_int4(w, splat_h2((uint16_t)f16_bits_1024_plus(z)), splat_h2(sb));
-          *(uint4 *)(out + e0) = r;
-        } else {
-          for (uint32_t c = 0; c < 2 * nb; c++) {
-            uint64_t e = e0 + c;
-            uint64_t g = e / G;
-            int q = (w >> (4 * c)) & 15;
-            int z = P.zp ? (int)P.zp[g] : 0;
-            out[e] = deq1(q, z, P.scales[g]);
-          }
+        for (uint32_t c = 0; c < 2 * nb; c++) {
+          uint64_t e = e0 + c;
+          uint64_t g = e / G;
+          int q = (w[k] >> (4 * c)) & 15;
+          int z = P.zp ? (int)P.zp[g] : 0;
+          out[e] = deq1(q, z, P.scales[g]);
         }
       }
     }
@@ -496,7 +696,8 @@ __device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64
           for (uint32_t c = 0; c < nb; c++) {
             uint64_t e = e0 + c;
             uint64_t g = e / G;
-            int q = (int)(int8_t)byte_of(make_uint4(w.x, w.y, 0, 0), c);
+            uint32_t word = c < 4 ? w.x : w.y;
+            int q = (int)(int8_t)(word >> ((c & 3) * 8));
             int z = P.zp ? (int)P.zp[g] : 0;
             out[e] = deq1(q, z, P.scales[g]);
           }
@@ -507,34 +708,41 @@ __device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64
 }
 
 template <int MODE>
-__device__ void flusher(Smem &sm, uint32_t lane, uint32_t f, const ChunkParams &P, uint64_t dst0,
-                        uint32_t N) {
-  uint32_t ntiles = (N + TILE - 1) / TILE;
+__device__ void flusher(Smem &sm, Ctl &ctl, uint32_t lane, uint32_t f, const ChunkParams &P,
+                        uint64_t dst0, uint32_t N) {
+  const uint32_t ntiles = (N + TILE - 1) / TILE;
+  const bool fast = MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8;
   uint32_t done = 0;
   for (uint32_t t = f; t < ntiles; t += NFLUSH) {
+    // the tile's scales are fetched before waiting for the tile, so their
+    // latency overlaps the wait for the decoder
+    Meta4 cur{};
+    if (fast) cur = int4_meta(P, dst0, t, lane, N);
     uint32_t t_end = (t + 1) * TILE < N ? (t + 1) * TILE : N;
     while (done < t_end) {
-      done = lds_get(&sm.ctl.out_done);
+      done = lds_get(&ctl.out_done);
       if (done >= t_end) break;
-      if (lds_get(&sm.ctl.state) != ST_RUN) {
-        done = lds_get(&sm.ctl.out_done);
+      if (lds_get(&ctl.state) != ST_RUN) {
+        done = lds_get(&ctl.out_done);
         if (done >= t_end) break;
         goto finish;   // the decoder stopped short of this tile (failed chunk)
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    flush_tile<MODE>(sm, lane, P, dst0, t, N);
-    lds_put(&sm.ctl.next_tile[f], t + NFLUSH, lane);
+    if (fast) meta_ready(cur, P.zp != nullptr);
+    flush_tile<MODE>(sm, lane, P, dst0, t, N, cur, fast);
+    lds_put(&ctl.next_tile[f], t + NFLUSH, lane);
   }
 finish:
-  lds_put(&sm.ctl.next_tile[f], 0xFFFFFFFFu, lane);
+  lds_put(&ctl.next_tile[f], 0xFFFFFFFFu, lane);
 }
 
 // -------------------------------------------------------------- kernel
 
 template <int MODE>
 __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
-  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ Ctl ctl;
   const uint32_t i = blockIdx.x;
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -554,32 +762,31 @@ __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
   // (an aligned block never crosses a page, so it is always mapped)
   const uint32_t head = (uint32_t)((uintptr_t)(P.comp + c0) & 15);
   const uint8_t *S = P.comp + (c0 - head);
-  const uint32_t rbase = (uint32_t)((uintptr_t)S & IMASK);
   const uint32_t y_end = head + (uint32_t)(c1 - c0);
 
   if (tid == 0) {
-    sm.ctl.in_avail = 0;
-    sm.ctl.in_used = 0;
-    sm.ctl.out_done = 0;
-    sm.ctl.state = ST_RUN;
-    for (int f = 0; f < NFLUSH; f++) sm.ctl.next_tile[f] = f;
-    sm.ctl.status = 0;
+    ctl.in_avail = 0;
+    ctl.in_used = 0;
+    ctl.out_done = 0;
+    ctl.state = ST_RUN;
+    for (int f = 0; f < NFLUSH; f++) ctl.next_tile[f] = f;
+    ctl.status = 0;
   }
   __syncthreads();
 
   if (wave == 0) {
-    Decoder D{sm, lane, rbase, head, y_end, 0, N, 0, 0, 0xFFFFFF00u, 0, 0};
+    Decoder D{sm, ctl, lane, head, y_end, 0, N, 0, 0, 0xFFFFFF00u, 0, 0, 0, make_uint4(0, 0, 0, 0)};
     int32_t st = (y_end == head) ? C_TRUNC : D.run();
-    D.publish_out();
-    if (lane == 0) sm.ctl.status = st;
-    lds_put(&sm.ctl.state, st == C_OK ? ST_DONE : ST_FAIL, lane);
+    D.publish(D.used);
+    if (lane == 0) ctl.status = st;
+    lds_put(&ctl.state, st == C_OK ? ST_DONE : ST_FAIL, lane);
   } else if (wave == 1) {
-    feeder(sm, lane, S, rbase, y_end);
+    feeder(sm, ctl, lane, S, y_end);
   } else {
-    flusher<MODE>(sm, lane, wave - 2, P, d0, N);
+    flusher<MODE>(sm, ctl, lane, wave - 2, P, d0, N);
   }
   __syncthreads();
-  if (tid == 0 && P.status) P.status[i] = sm.ctl.status;
+  if (tid == 0 && P.status) P.status[i] = ctl.status;
 }
 
 }  // namespace lt

@@ -21,7 +21,7 @@
 #include <thread>
 #include <vector>
 
-#include "../../include/lt.h"
+#include "lt.h"
 
 namespace {
 
