@@ -67,8 +67,10 @@ enum {
   LT_CHUNK_BAD_TABLE = 5      /* the chunk's table entries are inconsistent */
 };
 
-/* Largest decoded chunk the device decoder accepts (bytes). */
-#define LT_MAX_CHUNK_BYTES (1u << 30)
+/* Largest decoded chunk the device decoder accepts (bytes).  It bounds a
+ * sequence's length-extension run (about size / 255 bytes) so that the
+ * decoder's 8 KiB compressed-input ring always holds what is being parsed. */
+#define LT_MAX_CHUNK_BYTES (1u << 20)
 
 /*
  * Chunk table (HOST struct; its members point to DEVICE memory).

@@ -59,7 +59,7 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.lt_fused_lz4_int4(C.byref(t), fake, None, 4, 4, 4, fake, None, None) == lt.LT_ERR_INVALID_ARG
     t = lt._Table(0x10000, 0x10000, 0x10000, 1, 0, 8, 100)               # max_chunk_bytes 0
     assert L.lt_fused_lz4_int4(C.byref(t), fake, None, 4, 4, 4, fake, None, None) == lt.LT_ERR_INVALID_ARG
-    t = lt._Table(0x10000, 0x10000, 0x10000, 1, (1 << 30) + 1, 8, 100)   # above the limit
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, (1 << 20) + 1, 8, 100)   # above the limit
     assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
     t = lt._Table(None, 0x10000, 0x10000, 1, 8, 8, 100)
     assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG

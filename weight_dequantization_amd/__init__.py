@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "liblt.so")
 
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE = range(5)
 CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE = range(6)
-MAX_CHUNK_BYTES = 1 << 30
+MAX_CHUNK_BYTES = 1 << 20
 
 
 class LtError(RuntimeError):

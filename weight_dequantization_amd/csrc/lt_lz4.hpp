@@ -1,17 +1,26 @@
 // lt_lz4.hpp -- chunk-parallel LZ4 block decoding on gfx950, one workgroup
-// per independently compressed chunk, with three wave roles:
+// per independently compressed chunk, with three wave roles that form a
+// pipeline through LDS:
 //
-//   wave 0  decoder : parses the block's sequences and materializes the
-//                     decoded bytes into a 64 KiB LDS history ring (literal
-//                     copies from the input ring, match copies from history);
+//   wave 0  parser  : walks the block's sequences, validates them, and emits
+//                     one small record per sequence (where its literals sit
+//                     in the input and in the decoded stream, the match
+//                     distance) into an LDS record ring;
 //   wave 1  feeder  : streams the chunk's compressed bytes from HBM into an
 //                     8 KiB LDS input ring with LDS-DMA loads
 //                     (global_load_lds_dwordx4), several 1 KiB segments in
 //                     flight;
-//   waves 2+ flushers: take completed 1 KiB tiles of history and write them
-//                     out: as bytes (decode-only), or unpacked and
-//                     dequantized to fp16 (fused INT4 / INT8), with coalesced
-//                     16-byte stores.
+//   waves 2+ builders: builder b owns the aligned 1 KiB tiles t = b, b + NB,
+//                     b + 2 NB, ... of the decoded stream.  From the records
+//                     it builds its tile in a 64 KiB LDS history ring, all 64
+//                     lanes at once (each lane owns 16 bytes of the tile), and
+//                     then writes the tile out: as bytes (decode-only), or
+//                     unpacked and dequantized to fp16 (fused INT4 / INT8),
+//                     with coalesced 16-byte stores.
+//
+// Only the parser is serial, and it does the least work per sequence that
+// finding the next sequence allows; the tiles are built and written by NB
+// waves side by side.
 //
 // The LZ4 block format (the pages name LZ4 for compressed weight blocks but
 // do not define it; "GPU Compression Pipeline - TDD Roadmap", Phase 2.1 and
@@ -20,27 +29,37 @@
 // byte < 255), the literals, a 2-byte little-endian distance, and the match
 // length's extra bytes; the last sequence has literals only.  A match of
 // length M at distance d produces out[p + j] = out[p - d + (j mod d)], which
-// is what byte-serial copying gives when d < M; every source byte lies before
-// p, so all lanes may copy a match at once.
+// is what byte-serial copying gives when d < M.
 //
-// LDS traffic is kept to naturally aligned accesses: every lane owns an
-// aligned 16-byte block of the destination, gathers its source bytes with
-// aligned dword reads and v_alignbyte, and writes the partial blocks at the
-// ends of a copy with aligned byte / half / dword stores (no read-modify-
-// write).  The decoder reads the next parse window together with a
-// sequence's literal bytes, so a typical sequence costs one LDS round trip.
+// Building a tile.  Most tiles hold a few sequences whose matches are runs of
+// one byte (distance 1, the byte known to the parser) or copies from before
+// the part of the match that lies in the tile.  Such a tile is built in one
+// pass: each lane walks the pieces (literal run, match) that meet its 16
+// bytes, gathers each piece's bytes with aligned dword reads and
+// v_alignbyte, and merges them; the whole tile is then written with one
+// 16-byte LDS store per lane.  Where a match reads bytes of the same tile,
+// the pass is repeated once per such match, each pass reading what the
+// previous one wrote (all of a pass's reads precede its stores).  Tiles with
+// many sequences or short-distance overlapping matches are built sequence by
+// sequence instead.
 //
-// The roles talk through LDS counters (relaxed atomics, published only after
-// an lgkmcnt(0) / vmcnt wait, so the data they announce is already in LDS):
-//   in_avail  feeder  -> decoder : input bytes present in the ring
-//   in_used   decoder -> feeder  : input before this position is consumed
-//   out_done  decoder -> flushers: history bytes that are final
-//   next_tile flushers -> decoder: tiles below it are written out (ring reuse
-//                                  for chunks over 64 KiB)
-//   state     decoder -> all     : running / done / failed
-// Every wait is bounded: the decoder consumes at least one input byte per
-// sequence and stops at the chunk's end or at the first error, and it sets
-// `state` before leaving, which releases every other wave.
+// The roles talk through LDS counters (relaxed atomics; one wave's LDS
+// operations complete in program order, so a counter written after data is
+// seen after that data):
+//   in_avail     feeder   -> all     : input bytes present in the ring
+//   need[0]      parser   -> feeder  : first input byte the parser still reads
+//   need[1 + b]  builder  -> feeder  : first input byte builder b still reads
+//   nrec, cov    parser   -> builders: records written; decoded bytes covered
+//   bk[b]        builder  -> parser  : first record builder b still reads
+//   next_tile[b] builder  -> builders: builder b's tiles below it are final
+//   pstate       parser   -> all     : running / done / failed
+// Every wait is bounded.  The parser consumes at least one input byte per
+// sequence and stops at the chunk's end or at the first error; builders stop
+// when the parser stops short of their next tile.  The ring sizes are chosen
+// so that a waiting wave never holds what the wave it waits for needs: the
+// record ring holds more records than one tile can overlap, and decoded
+// chunks are at most 1 MiB, so a length field's extra bytes (about 1/255 of
+// the length) fit in the input ring beside the oldest tile's literals.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,30 +74,40 @@ constexpr uint32_t INR = 1u << 13;    // compressed-input ring
 constexpr uint32_t IMASK = INR - 1;
 constexpr uint32_t SEG = 1024;        // feeder unit: one 16-byte DMA load per lane
 constexpr uint32_t QMAX = INR / SEG;  // segments in flight at most
-constexpr uint32_t TILE = 1024;       // flush granularity (bytes of decoded stream)
-constexpr int NFLUSH = 2;
-constexpr int NWAVES = 2 + NFLUSH;
+constexpr uint32_t TILE = 1024;       // build / write-out unit (bytes of decoded stream)
+constexpr uint32_t HTILES = HIST / TILE;
+// Sequence records in flight (parser -> builders).  A 1 KiB tile overlaps at
+// most 257 records (every non-final sequence decodes to >= 4 bytes), and the
+// parser must be able to hold all of them while the oldest tile's builder
+// waits for the tile's coverage, so the ring holds more than 257.
+constexpr uint32_t RING = 320;
+constexpr int NB = 6;                 // builder waves
+constexpr int NWAVES = 2 + NB;        // parser, feeder, builders
 constexpr int NTHREADS = 64 * NWAVES;
+constexpr uint32_t NSLOT = 8;         // counter array length (>= NB + 1)
+constexpr uint32_t BULK_RECS = 16;    // most sequences in a tile built in one pass
 constexpr uint32_t LEN_CAP = 1u << 31;
-constexpr uint32_t LIT_ONE_STEP = 960;  // literal runs copied with one gather step
 
 enum : uint32_t { ST_RUN = 0, ST_DONE = 1, ST_FAIL = 2 };
 enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5 };
 enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2 };
 
-struct Ctl {
-  uint32_t in_avail;
-  uint32_t in_used;
-  uint32_t out_done;
-  uint32_t state;
-  uint32_t next_tile[NFLUSH];
+struct __attribute__((aligned(16))) Ctl {
+  uint32_t need[NSLOT];       // first input byte still read: [0] parser, [1 + b] builder b
+  uint32_t bk[NSLOT];         // builder b: first record it may still read
+  uint32_t next_tile[NSLOT];  // builder b: its next tile (all ones once it has left)
+  uint32_t in_avail;          // feeder: input bytes present in the ring
+  uint32_t nrec;              // parser: records written
+  uint32_t cov;               // parser: decoded bytes fully described by records
+  uint32_t pstate;            // parser: running / done / failed
+  uint32_t nfinished;         // builders that have left
   int32_t status;
-  uint32_t pad;
 };
 
 struct Smem {
   uint8_t hist[HIST];
   uint8_t inr[INR];
+  uint4 recs[RING];
 };
 
 struct ChunkParams {
@@ -121,8 +150,13 @@ __device__ __forceinline__ void wait_vm_le(uint32_t k) {
   }
 }
 
+// Counter reads stay in program order with this wave's other LDS accesses
+// (the hardware executes one wave's LDS operations in order; the fences keep
+// the compiler from moving loads across the read).
 __device__ __forceinline__ uint32_t lds_get(uint32_t *p) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return __builtin_amdgcn_readfirstlane(v);
 }
 
@@ -132,12 +166,22 @@ __device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t lane) 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// The feeder's counter accesses go through inline asm: its LDS-DMA loads
-// would otherwise make the compiler wait for every load in flight before any
-// LDS access of that wave.  Each read waits for its own result inside the asm
-// block, so its output register is final when the block ends.
-__device__ __forceinline__ uint32_t lds_addr(const uint32_t *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t *)p;
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Minimum of an 8-entry counter array (16-byte aligned), read at once.  Like
+// every counter access of the feeder wave, it goes through inline asm: that
+// wave's LDS-DMA loads would otherwise make the compiler wait for every load
+// in flight before any LDS access.  The read waits for its own result inside
+// the asm block, so its output registers are final when the block ends.
+__device__ __forceinline__ uint32_t min8(const uint32_t *a) {
+  uint4 u, v;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(u), "=v"(v) : "v"(lds_addr(a)) : "memory");
+  uint32_t m0 = min(min(u.x, u.y), min(u.z, u.w));
+  uint32_t m1 = min(min(v.x, v.y), min(v.z, v.w));
+  return __builtin_amdgcn_readfirstlane(min(m0, m1));
 }
 
 __device__ __forceinline__ uint32_t lds_get_asm(const uint32_t *p) {
@@ -148,12 +192,6 @@ __device__ __forceinline__ uint32_t lds_get_asm(const uint32_t *p) {
 
 __device__ __forceinline__ void lds_set_asm(uint32_t *p, uint32_t v, uint32_t lane) {
   if (lane == 0) asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
-}
-
-// Publish a counter after this wave's earlier LDS operations have completed.
-__device__ __forceinline__ void lds_put(uint32_t *p, uint32_t v, uint32_t lane) {
-  wait_lds();
-  lds_set(p, v, lane);
 }
 
 // ------------------------------------------------------ LDS byte moves
@@ -210,71 +248,49 @@ __device__ __forceinline__ void st_block(uint8_t *p, uint4 v, uint32_t lo, uint3
   st_dword_part(p, v.w, 12, lo, hi);
 }
 
-// ---------------------------------------------------------- the decoder
+// keep the first c bytes of dword acc and take the rest from v (c may be
+// negative: take all of v; or 4 and more: keep all of acc)
+__device__ __forceinline__ uint32_t merge_from(uint32_t acc, uint32_t v, int c) {
+  const uint32_t m = c <= 0 ? 0xFFFFFFFFu : (c >= 4 ? 0u : (0xFFFFFFFFu << (8 * c)));
+  return (v & m) | (acc & ~m);
+}
 
-struct Decoder {
+// ----------------------------------------------------------- sequences
+
+// A sequence record, written by the parser into an LDS ring and read by the
+// builders: the decoded-stream position where the sequence's literals start,
+// the input position of the literals, their count, and the match (distance,
+// fill byte for distance 1 when known, flags).  A record's match ends where
+// the next record starts; the last record written ends at ctl.cov.
+constexpr uint32_t F_MATCH = 1u << 24;  // match fields are final
+constexpr uint32_t F_FILL = 2u << 24;   // distance 1 and bits 16..23 hold the byte it repeats
+constexpr uint32_t F_LAST = 4u << 24;   // literal-only last sequence
+
+__device__ __forceinline__ uint32_t ridx(uint32_t j) { return j % RING; }
+__device__ __forceinline__ uint32_t rec_dist(uint32_t info) { return info & 0xFFFFu; }
+__device__ __forceinline__ uint32_t rec_fill(uint32_t info) { return (info >> 16) & 0xFFu; }
+
+// ---------------------------------------------------------- the parser
+
+// Wave 0.  Walks the block's sequences, validates every field and bound, and
+// emits one record per sequence.  Its only LDS round trip per sequence is the
+// parse window at the literal run's end, which also holds the distance, the
+// match length bytes and the next token.
+struct Parser {
   Smem &sm;
   Ctl &ctl;
   uint32_t lane;
-  uint32_t y;          // input position (bytes from the 16-aligned block start)
+  uint32_t y;           // input position of the next byte to parse
   uint32_t y_end;
-  uint32_t op;         // output position within the chunk
-  uint32_t N;          // chunk's decoded size
-  uint32_t avail;      // cached ctl.in_avail
-  uint32_t flushed;    // cached: history below this is written out
-  uint32_t wy;         // window start (multiple of 4); window = [wy, wy + 256)
-  uint32_t win;        // this lane's dword of the window
-  uint32_t used;       // last value published to ctl.in_used
-  uint32_t last_byte;  // the decoded byte at op - 1
-  uint4 cur;           // the 16-byte block holding op; bytes below op are final
-
-  // While every position written so far is below HIST (the first pass
-  // through the ring), copies write whole aligned blocks: bytes past a copy's
-  // end are future positions, rewritten before any match or flush reads
-  // them.  Past that point a block may still hold bytes a long match needs,
-  // so copies write exactly their own bytes.
-  __device__ bool whole_blocks(uint32_t end) const { return end + 15 <= HIST; }
-
-  static __device__ __forceinline__ uint4 readlane4(uint4 v, uint32_t l) {
-    return make_uint4(__builtin_amdgcn_readlane(v.x, l), __builtin_amdgcn_readlane(v.y, l),
-                      __builtin_amdgcn_readlane(v.z, l), __builtin_amdgcn_readlane(v.w, l));
-  }
-
-  // bytes [0, keep) from c, the rest from v (keep = 0 leaves v unchanged)
-  static __device__ __forceinline__ uint4 merge_head(uint4 c, uint4 v, uint32_t keep) {
-    uint32_t m[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t k = keep > 4u * j ? keep - 4u * j : 0u;
-      m[j] = k >= 4 ? 0xFFFFFFFFu : ((1u << (8 * k)) - 1u);
-    }
-    return make_uint4((c.x & m[0]) | (v.x & ~m[0]),
-                      (c.y & m[1]) | (v.y & ~m[1]), (c.z & m[2]) | (v.z & ~m[2]),
-                      (c.w & m[3]) | (v.w & ~m[3]));
-  }
-
-  // Whole-block copy of history [od, od + n): block P's bytes come from
-  // src(P); the head block keeps cur's bytes below od.  Each 64-block step
-  // reads all its sources before writing.  Leaves cur / last_byte at the end.
-  template <class Src>
-  __device__ void put_blocks(uint32_t od, uint32_t n, Src src) {
-    const uint32_t A = od & ~15u, end = od + n, keep = od & 15u;
-    const uint32_t nb = (end - A + 15) >> 4;
-    uint4 last = cur;
-    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
-      const uint32_t b = b0 + lane;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (b < nb) v = src(A + 16 * b);
-      v = merge_head(cur, v, b == 0 ? keep : 0u);
-      if (b < nb) *(uint4 *)(sm.hist + A + 16 * b) = v;
-      const uint32_t lb = nb - 1 - b0;
-      if (lb < 64) last = readlane4(v, lb);
-    }
-    cur = last;
-    const uint32_t q = (end - 1) & 15u;
-    const uint32_t d = q < 4 ? last.x : q < 8 ? last.y : q < 12 ? last.z : last.w;
-    last_byte = (d >> (8 * (q & 3))) & 0xFFu;
-  }
+  uint32_t op;          // decoded bytes described by finished sequences
+  uint32_t N;
+  uint32_t avail;       // cached ctl.in_avail
+  uint32_t wy;          // window start (multiple of 4); window = [wy, wy + 256)
+  uint32_t win;         // this lane's dword of the window
+  uint32_t nrec;        // records written
+  uint32_t rec_free;    // cached: records below this may be overwritten
+  uint32_t fill_ok;     // the byte at op - 1 is known ...
+  uint32_t fill;        // ... and is this
 
   __device__ void need_input(uint32_t upto) {
     if (upto > y_end) upto = y_end;
@@ -284,49 +300,16 @@ struct Decoder {
     }
   }
 
-  // History positions below `end` may be written once the flushers are past
-  // end - HIST (only chunks larger than the ring ever wait here).
-  __device__ void need_ring(uint32_t end) {
-    if (end <= HIST) return;
-    uint32_t need = end - HIST;
-    while (flushed < need) {
-      uint32_t m = lds_get(&ctl.next_tile[0]);
-      for (int f = 1; f < NFLUSH; f++) {
-        uint32_t t = lds_get(&ctl.next_tile[f]);
-        m = t < m ? t : m;
-      }
-      flushed = (m >= (0xFFFFFFFFu / TILE)) ? 0xFFFFFFFFu : m * TILE;
-      if (flushed < need) __builtin_amdgcn_s_sleep(1);
-    }
-  }
-
-  // Announce progress; cheap right after a wait that already completed this
-  // wave's earlier LDS operations.
-  __device__ void publish(uint32_t new_used) {
-    wait_lds();
-    lds_set(&ctl.out_done, op, lane);
-    if (new_used > used) {
-      used = new_used;
-      lds_set(&ctl.in_used, used, lane);
-    }
-  }
-
+  // Nothing before the window start is parsed again (literals are read by
+  // the builders, which announce their own needs).
   __device__ void load_window(uint32_t p) {
     wy = p & ~3u;
-    // nothing before the window is read again: tokens, length bytes and
-    // distances before p are parsed, and literal runs start at or after p
-    if (wy > used) {
-      used = wy;
-      lds_put(&ctl.in_used, used, lane);
-    }
+    lds_set(&ctl.need[0], wy, lane);
     need_input(wy + 256);
     win = *(const uint32_t *)(sm.inr + ((wy + 4 * lane) & IMASK));
-    // wait here, on this path only: otherwise the compiler waits at every
-    // byte_at for all outstanding LDS writes, whether the window reloaded or not
-    wait_lds();
+    wait_lds();   // on this path only, so byte_at never waits on stores
   }
 
-  // byte at input position p (reloads the window when p is outside it)
   __device__ uint32_t byte_at(uint32_t p) {
     if (p < wy || p >= wy + 256) load_window(p);
     uint32_t rel = p - wy;
@@ -334,189 +317,25 @@ struct Decoder {
     return (d >> ((rel & 3) * 8)) & 0xFFu;
   }
 
-  // history [od, od + n) from ring R at index src0 + (P - od); every source
-  // byte is final before each 64-block step writes
-  template <uint32_t MASK>
-  __device__ void copy_blocks(const uint8_t *R, uint32_t src0, uint32_t od, uint32_t n) {
-    const uint32_t A = od & ~15u, end = od + n;
-    const uint32_t nb = (end - A + 15) >> 4;
-    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
-      uint32_t b = b0 + lane;
-      if (b < nb) {
-        uint32_t P = A + 16 * b;
-        uint32_t lo = od > P ? od - P : 0;
-        uint32_t hi = end - P < 16 ? end - P : 16;
-        uint4 v = gather16<MASK>(R, src0 + (P - od));
-        st_block(sm.hist + (P & HMASK), v, lo, hi);
-      }
+  __device__ void wait_ring() {
+    while (nrec - rec_free >= RING) {
+      rec_free = min8(ctl.bk);
+      if (nrec - rec_free >= RING) __builtin_amdgcn_s_sleep(1);
     }
   }
 
-  __device__ void fill(uint32_t od, uint32_t byte, uint32_t n) {
-    const uint32_t w = byte * 0x01010101u;
-    const uint4 v = make_uint4(w, w, w, w);
-    const uint32_t A = od & ~15u, end = od + n;
-    const uint32_t nb = (end - A + 15) >> 4;
-    for (uint32_t b = lane; b < nb; b += 64) {
-      uint32_t P = A + 16 * b;
-      uint32_t lo = od > P ? od - P : 0;
-      uint32_t hi = end - P < 16 ? end - P : 16;
-      st_block(sm.hist + (P & HMASK), v, lo, hi);
-    }
+  // records and coverage for the builders (the record stores were issued
+  // earlier, so they land first)
+  __device__ void publish(uint32_t cov) {
+    lds_set(&ctl.nrec, nrec, lane);
+    lds_set(&ctl.cov, cov, lane);
   }
 
-  // the first n (<= 1 KiB) bytes of an overlapping match, byte by byte:
-  // out[od + j] = out[od - dist + (j mod dist)]
-  __device__ void copy_periodic(uint32_t od, uint32_t dist, uint32_t n) {
-    const uint32_t A = od & ~15u, end = od + n;
-    const uint32_t nb = (end - A + 15) >> 4;
-    for (uint32_t b = lane; b < nb; b += 64) {
-      uint32_t P = A + 16 * b;
-      uint32_t lo = od > P ? od - P : 0;
-      uint32_t hi = end - P < 16 ? end - P : 16;
-      uint32_t r = (P + lo - od) % dist;
-      uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-#pragma unroll
-      for (uint32_t q = 0; q < 16; q++) {
-        if (q >= lo && q < hi) {
-          uint32_t v = sm.hist[(od - dist + r) & HMASK];
-          uint32_t sv = v << (8 * (q & 3));
-          if (q < 4) w0 |= sv;
-          else if (q < 8) w1 |= sv;
-          else if (q < 12) w2 |= sv;
-          else w3 |= sv;
-          r = (r + 1 == dist) ? 0 : r + 1;
-        }
-      }
-      st_block(sm.hist + (P & HMASK), make_uint4(w0, w1, w2, w3), lo, hi);
-    }
-  }
-
-  __device__ void copy_match(uint32_t dist, uint32_t M) {
-    // pieces keep the writes within what the ring can hold ahead of the flushers
-    const uint32_t PIECE = 32768;
-    if (dist == 1) {
-      const uint32_t w = last_byte * 0x01010101u;
-      while (M) {
-        uint32_t n = M < PIECE ? M : PIECE;
-        need_ring(op + n);
-        if (whole_blocks(op + n)) put_blocks(op, n, [&](uint32_t) { return make_uint4(w, w, w, w); });
-        else fill(op, last_byte, n);
-        op += n;
-        M -= n;
-        if (M) publish(used);
-      }
-      return;
-    }
-    uint32_t done = 0;
-    bool exact = false;
-    if (dist < M && dist < 1024) {
-      uint32_t n = M < 1024 ? M : 1024;
-      need_ring(op + n);
-      if (whole_blocks(op + n)) {
-        const uint32_t od = op;
-        put_blocks(od, n, [&](uint32_t P) {
-          uint32_t lo = od > P ? od - P : 0;
-          uint32_t r = (P + lo - od) % dist;
-          uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-#pragma unroll
-          for (uint32_t q = 0; q < 16; q++) {
-            if (q >= lo) {
-              uint32_t sv = (uint32_t)sm.hist[(od - dist + r) & HMASK] << (8 * (q & 3));
-              if (q < 4) w0 |= sv;
-              else if (q < 8) w1 |= sv;
-              else if (q < 12) w2 |= sv;
-              else w3 |= sv;
-              r = (r + 1 == dist) ? 0 : r + 1;
-            }
-          }
-          return make_uint4(w0, w1, w2, w3);
-        });
-      } else {
-        copy_periodic(op, dist, n);
-        exact = true;
-      }
-      op += n;
-      done = n;
-      publish(used);
-      // later bytes repeat with any multiple of dist; the smallest multiple
-      // >= 1 KiB keeps each 1 KiB step's sources before the step
-      dist = dist * ((1024 + dist - 1) / dist);
-    }
-    while (done < M) {
-      uint32_t n = M - done < PIECE ? M - done : PIECE;
-      need_ring(op + n);
-      if (whole_blocks(op + n)) {
-        const uint32_t dd = dist;
-        put_blocks(op, n, [&](uint32_t P) { return gather16<HMASK>(sm.hist, P - dd); });
-      } else {
-        copy_blocks<HMASK>(sm.hist, op - dist, op, n);
-        exact = true;
-      }
-      op += n;
-      done += n;
-      if (done < M) publish(used);
-    }
-    if (exact) last_byte = __builtin_amdgcn_readfirstlane(sm.hist[(op - 1) & HMASK]);
-  }
-
-  // literal run of L bytes at input y: copy, advance y / op, and leave the
-  // window covering the bytes that follow
-  __device__ void literals(uint32_t L) {
-    const uint32_t ye = y + L;
-    if (L <= LIT_ONE_STEP && whole_blocks(op + L)) {
-      const uint32_t nw = ye & ~3u;
-      need_input((ye > nw + 256) ? ye : nw + 256);
-      const uint32_t A = op & ~15u, end = op + L, keep = op & 15u;
-      const uint32_t nb = (end - A + 15) >> 4;   // <= 62
-      const uint32_t P = A + 16 * lane;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (lane < nb) v = gather16<IMASK>(sm.inr, y + (P - op));
-      const uint32_t nwin = *(const uint32_t *)(sm.inr + ((nw + 4 * lane) & IMASK));
-      publish(y);   // waits for the reads above (and so for every earlier write)
-      v = merge_head(cur, v, lane == 0 ? keep : 0u);
-      if (lane < nb) *(uint4 *)(sm.hist + P) = v;
-      cur = readlane4(v, nb - 1);
-      const uint32_t q = (end - 1) & 15u;
-      const uint32_t d = q < 4 ? cur.x : q < 8 ? cur.y : q < 12 ? cur.z : cur.w;
-      last_byte = (d >> (8 * (q & 3))) & 0xFFu;
-      win = nwin;
-      wy = nw;
-      y = ye;
-      op += L;
-      return;
-    }
-    uint32_t left = L;
-    bool exact = false;
-    while (left) {
-      // the feeder fills whole segments up to QMAX past the segment holding
-      // `used`, so a piece of INR - 2 * SEG bytes is always deliverable
-      uint32_t piece = left < INR - 2 * SEG ? left : INR - 2 * SEG;
-      used = y;
-      lds_put(&ctl.in_used, used, lane);
-      need_input(y + piece);
-      need_ring(op + piece);
-      if (whole_blocks(op + piece)) {
-        const uint32_t ys = y, od = op;
-        put_blocks(op, piece, [&](uint32_t Pb) { return gather16<IMASK>(sm.inr, ys + (Pb - od)); });
-      } else {
-        copy_blocks<IMASK>(sm.inr, y, op, piece);
-        exact = true;
-      }
-      y += piece;
-      op += piece;
-      left -= piece;
-      publish(used);
-    }
-    if (exact) last_byte = byte_at(ye - 1);
-  }
-
-  // Returns the chunk status.
   __device__ int32_t run() {
     int32_t st = C_OK;
     for (;;) {
       if (y >= y_end) { st = C_TRUNC; break; }
-      uint32_t token = byte_at(y);
+      const uint32_t token = byte_at(y);
       y++;
       uint32_t L = token >> 4;
       if (L == 15) {
@@ -526,18 +345,39 @@ struct Decoder {
           b = byte_at(y);
           y++;
           L += b;
-          if (L > LEN_CAP) { st = C_OVERRUN; goto out; }
+          // stop as soon as the run cannot fit: this also bounds how far the
+          // parser reads ahead of the builders inside a length field
+          if (L > N - op) { st = C_OVERRUN; goto out; }
         } while (b == 255);
       }
       if (L > y_end - y) { st = C_TRUNC; break; }
       if (L > N - op) { st = C_OVERRUN; break; }
-      if (L) literals(L);
-      if (y == y_end) break;
-      if (y_end - y < 2) { st = C_TRUNC; break; }
+      const uint32_t ye = y + L;
+      // record, phase 1: the literal run
+      if (nrec - rec_free >= RING) wait_ring();
+      const uint32_t k = nrec;
+      if (lane == 0) sm.recs[ridx(k)] = make_uint4(op, y, L, ye == y_end ? F_LAST : 0u);
+      nrec++;
+      if (ye == y_end) {   // literal-only last sequence
+        op += L;
+        y = ye;
+        break;
+      }
+      publish(op + L);
+      if (y_end - ye < 2) { st = C_TRUNC; break; }
+      // the window at the run's end: last literal byte, distance, match
+      // length bytes, next token
+      const uint32_t wpos = L ? ye - 1 : ye;
+      if (wpos < wy || wpos + 16 > wy + 256) load_window(wpos);
+      if (L) {
+        fill = byte_at(ye - 1);
+        fill_ok = 1;
+      }
+      y = ye;
       uint32_t dist = byte_at(y);
       dist |= byte_at(y + 1) << 8;
       y += 2;
-      if (dist == 0 || dist > op) { st = C_BADOFF; break; }
+      if (dist == 0 || dist > op + L) { st = C_BADOFF; break; }
       uint32_t M = (token & 15) + 4;
       if ((token & 15) == 15) {
         uint32_t b;
@@ -546,30 +386,37 @@ struct Decoder {
           b = byte_at(y);
           y++;
           M += b;
-          if (M > LEN_CAP) { st = C_OVERRUN; goto out; }
+          if (M > N - op - L) { st = C_OVERRUN; goto out; }
         } while (b == 255);
       }
-      if (M > N - op) { st = C_OVERRUN; break; }
-      copy_match(dist, M);
+      if (M > N - op - L) { st = C_OVERRUN; break; }
+      // phase 2: the match
+      uint32_t info = F_MATCH | dist;
+      if (dist == 1 && fill_ok) info |= F_FILL | (fill << 16);
+      if (lane == 0) sm.recs[ridx(k)].w = info;
+      if (dist != 1) fill_ok = 0;
+      op += L + M;
     }
   out:
     if (st == C_OK && op != N) st = C_SIZE;
+    if (st == C_OK) publish(op);   // a failed chunk's builders stop at what was announced before
     return st;
   }
 };
 
 // -------------------------------------------------------------- feeder
 
-// Streams the chunk's 16-byte aligned blocks into the input ring, one 1 KiB
-// segment (one LDS-DMA load per lane) at a time, keeping up to QMAX segments
-// in flight within the ring space the decoder has released.
+// Wave 1.  Streams the chunk's 16-byte aligned blocks into the input ring,
+// one 1 KiB segment (one LDS-DMA load per lane) at a time, keeping up to QMAX
+// segments in flight within the ring space that every reader has released.
 __device__ void feeder(Smem &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end) {
   const uint32_t nblk = (y_end + 15) / 16;
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
   uint32_t issued = 0, landed = 0;
   while (landed < nseg) {
-    if (lds_get_asm(&ctl.state) != ST_RUN) break;
-    uint32_t used = lds_get_asm(&ctl.in_used);
+    // nobody reads input once the parser has stopped and every builder has left
+    if (lds_get_asm(&ctl.nfinished) == (uint32_t)NB && lds_get_asm(&ctl.pstate) != ST_RUN) break;
+    const uint32_t used = min8(ctl.need);
     uint32_t limit = used / SEG + QMAX;
     if (limit > nseg) limit = nseg;
     while (issued < limit && issued - landed < QMAX) {
@@ -591,7 +438,7 @@ __device__ void feeder(Smem &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint
   wait_vm<0>();   // no LDS-DMA write outlives this wave
 }
 
-// ------------------------------------------------------------- flushers
+// ------------------------------------------------------------ write-out
 
 struct Meta4 {
   uint32_t s[4];
@@ -600,7 +447,7 @@ struct Meta4 {
 
 // scales / zero points of one INT4 tile (fast path: group is a power of two
 // >= 8, so each lane's 8 codes share one group).  The loads are issued here
-// and consumed only after the wait for the tile (see meta_ready).
+// and consumed only after the tile is built (see meta_ready).
 __device__ __forceinline__ Meta4 int4_meta(const ChunkParams &P, uint64_t dst0, uint32_t t,
                                            uint32_t lane, uint32_t N) {
   Meta4 m;
@@ -707,35 +554,334 @@ __device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64
   }
 }
 
+// ------------------------------------------------------------ builders
+
+// Waves 2 .. 2 + NB - 1.  Builder b builds and writes out tiles b, b + NB, ...
 template <int MODE>
-__device__ void flusher(Smem &sm, Ctl &ctl, uint32_t lane, uint32_t f, const ChunkParams &P,
-                        uint64_t dst0, uint32_t N) {
-  const uint32_t ntiles = (N + TILE - 1) / TILE;
-  const bool fast = MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8;
-  uint32_t done = 0;
-  for (uint32_t t = f; t < ntiles; t += NFLUSH) {
-    // the tile's scales are fetched before waiting for the tile, so their
-    // latency overlaps the wait for the decoder
-    Meta4 cur{};
-    if (fast) cur = int4_meta(P, dst0, t, lane, N);
-    uint32_t t_end = (t + 1) * TILE < N ? (t + 1) * TILE : N;
-    while (done < t_end) {
-      done = lds_get(&ctl.out_done);
-      if (done >= t_end) break;
-      if (lds_get(&ctl.state) != ST_RUN) {
-        done = lds_get(&ctl.out_done);
-        if (done >= t_end) break;
-        goto finish;   // the decoder stopped short of this tile (failed chunk)
+struct Builder {
+  Smem &sm;
+  Ctl &ctl;
+  const ChunkParams &P;
+  uint64_t dst0;
+  uint32_t lane;
+  uint32_t b;
+  uint32_t N;
+  uint32_t k;          // first record that may overlap the current tile (announced in bk[b])
+  uint32_t nrec;       // cached ctl.nrec
+  uint32_t cov;        // cached ctl.cov
+  uint32_t pst;        // cached ctl.pstate
+  uint32_t avail;      // cached ctl.in_avail
+  uint32_t done;       // cached: tiles below this are final
+  uint32_t need_pub;   // announced in need[1 + b]
+
+  __device__ void refresh() {
+    pst = lds_get(&ctl.pstate);   // read first: if done, cov and nrec below are final
+    cov = lds_get(&ctl.cov);      // before nrec: records up to cov are all counted
+    nrec = lds_get(&ctl.nrec);
+  }
+
+  __device__ void need_input(uint32_t upto) {
+    while (avail < upto) {
+      avail = lds_get(&ctl.in_avail);
+      if (avail < upto) __builtin_amdgcn_s_sleep(1);
+    }
+  }
+
+  // wait until tiles [0, tiles) are final; false if the chunk failed first
+  __device__ bool wait_done(uint32_t tiles) {
+    while (done < tiles) {
+      done = min8(ctl.next_tile);
+      if (done >= tiles) break;
+      if (lds_get(&ctl.pstate) == ST_FAIL) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+  }
+
+  // Advance k to the last record starting at or before T, the one that
+  // contains T once the records reach that far (records are sorted by
+  // start), and announce that records below it are no longer read.
+  __device__ void find_k(uint32_t T) {
+    uint32_t kk = k;
+    for (;;) {   // records from k on are protected by bk[b] <= k
+      const uint32_t j = kk + lane;
+      const uint32_t x = (j < nrec) ? sm.recs[ridx(j)].x : 0xFFFFFFFFu;
+      const uint64_t bal = __ballot(x <= T);   // lanes 0 .. h
+      const uint32_t h = 63 - __builtin_clzll(bal | 1ull);
+      kk += h;
+      if (h < 63) break;
+    }
+    if (kk > k) {
+      k = kk;
+      lds_set(&ctl.bk[b], kk, lane);
+    }
+  }
+
+  // Announce the first input byte still read: the literal byte of record k
+  // at position T, or the end of record k's literals when T lies past them
+  // (later records' literals follow in the input).
+  __device__ void announce(uint32_t T) {
+    const uint4 r = rec(k);
+    uint32_t off = T > r.x ? T - r.x : 0u;
+    off = off < r.z ? off : r.z;
+    const uint32_t nd = r.y + off;
+    if (nd > need_pub) {
+      need_pub = nd;
+      lds_set(&ctl.need[1 + b], nd, lane);
+    }
+  }
+
+  // wait until records cover [T, Tend); false if the parser stopped short
+  __device__ bool wait_cov(uint32_t T, uint32_t Tend) {
+    while (cov < Tend) {
+      refresh();
+      if (cov >= Tend) break;
+      if (pst != ST_RUN) return false;
+      // move past the records that end before T (nrec may be newer than
+      // cov, so the search looks at the records' starts, not at cov)
+      if (nrec > 0) {
+        find_k(T);
+        announce(T);
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (fast) meta_ready(cur, P.zp != nullptr);
-    flush_tile<MODE>(sm, lane, P, dst0, t, N, cur, fast);
-    lds_put(&ctl.next_tile[f], t + NFLUSH, lane);
+    return true;
   }
-finish:
-  lds_put(&ctl.next_tile[f], 0xFFFFFFFFu, lane);
-}
+
+  // record j's four words (broadcast read)
+  __device__ uint4 rec(uint32_t j) {
+    uint4 r = sm.recs[ridx(j)];
+    return make_uint4(__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                      __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w));
+  }
+  __device__ uint32_t rec_start(uint32_t j) {
+    return j < nrec ? __builtin_amdgcn_readfirstlane(sm.recs[ridx(j)].x) : cov;
+  }
+
+  // ---- sequence-by-sequence path (exact writes, any match)
+
+  template <uint32_t MASK>
+  __device__ void copy_exact(const uint8_t *R, uint32_t src0, uint32_t a, uint32_t n) {
+    const uint32_t A = a & ~15u, end = a + n;
+    const uint32_t nb = (end - A + 15) >> 4;
+    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+      uint32_t bb = b0 + lane;
+      if (bb < nb) {
+        uint32_t Pp = A + 16 * bb;
+        uint32_t lo = a > Pp ? a - Pp : 0;
+        uint32_t hi = end - Pp < 16 ? end - Pp : 16;
+        st_block(sm.hist + (Pp & HMASK), gather16<MASK>(R, src0 + (Pp - a)), lo, hi);
+      }
+    }
+  }
+
+  __device__ void fill_exact(uint32_t a, uint32_t byte, uint32_t n) {
+    const uint32_t w = byte * 0x01010101u;
+    const uint4 v = make_uint4(w, w, w, w);
+    const uint32_t A = a & ~15u, end = a + n;
+    const uint32_t nb = (end - A + 15) >> 4;
+    for (uint32_t bb = lane; bb < nb; bb += 64) {
+      uint32_t Pp = A + 16 * bb;
+      uint32_t lo = a > Pp ? a - Pp : 0;
+      uint32_t hi = end - Pp < 16 ? end - Pp : 16;
+      st_block(sm.hist + (Pp & HMASK), v, lo, hi);
+    }
+  }
+
+  // bytes [a, a + n) of a match with distance dist < n that started at or
+  // before a: the match repeats with period dist, so out[q] = out[a - dist +
+  // ((q - a) mod dist)], whose sources lie in the dist bytes before a (recent
+  // enough to be in the history ring however long the match is)
+  __device__ void periodic_exact(uint32_t dist, uint32_t a, uint32_t n) {
+    const uint32_t A = a & ~15u, end = a + n;
+    const uint32_t nb = (end - A + 15) >> 4;
+    for (uint32_t bb = lane; bb < nb; bb += 64) {
+      uint32_t Pp = A + 16 * bb;
+      uint32_t lo = a > Pp ? a - Pp : 0;
+      uint32_t hi = end - Pp < 16 ? end - Pp : 16;
+      uint32_t r = (Pp + lo - a) % dist;
+      uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+      for (uint32_t q = 0; q < 16; q++) {
+        if (q >= lo && q < hi) {
+          uint32_t sv = (uint32_t)sm.hist[(a - dist + r) & HMASK] << (8 * (q & 3));
+          if (q < 4) w0 |= sv;
+          else if (q < 8) w1 |= sv;
+          else if (q < 12) w2 |= sv;
+          else w3 |= sv;
+          r = (r + 1 == dist) ? 0 : r + 1;
+        }
+      }
+      st_block(sm.hist + (Pp & HMASK), make_uint4(w0, w1, w2, w3), lo, hi);
+    }
+  }
+
+  // the match bytes [a, a + n) of a record (the match started at or before a)
+  __device__ void match_exact(uint32_t info, uint32_t a, uint32_t n) {
+    const uint32_t dist = rec_dist(info);
+    if (dist == 1) {   // every byte of the run equals the one before a
+      uint32_t bb = (info & F_FILL) ? rec_fill(info)
+                                    : __builtin_amdgcn_readfirstlane(sm.hist[(a - 1) & HMASK]);
+      fill_exact(a, bb, n);
+    } else if (dist >= n) {
+      copy_exact<HMASK>(sm.hist, a - dist, a, n);   // sources q - dist < a are final
+    } else {
+      periodic_exact(dist, a, n);
+    }
+  }
+
+  // Build [T, Tend) record by record, starting at record k.  Every byte
+  // before T must be final.
+  __device__ void tile_exact(uint32_t T, uint32_t Tend) {
+    uint32_t j = k;
+    for (;;) {
+      uint4 r = rec(j);
+      const uint32_t os = r.x, src = r.y, L = r.z, info = r.w;
+      const uint32_t re = rec_start(j + 1);
+      const uint32_t le = os + L;
+      uint32_t a = os > T ? os : T, e = le < Tend ? le : Tend;
+      if (a < e) {
+        need_input(src + (e - os));
+        copy_exact<IMASK>(sm.inr, src + (a - os), a, e - a);
+      }
+      a = le > T ? le : T;
+      e = re < Tend ? re : Tend;
+      if (a < e) match_exact(info, a, e - a);   // LDS ops of one wave stay in order
+      if (re >= Tend || j + 1 >= nrec) return;
+      j++;
+    }
+  }
+
+  // ---- one-pass path
+
+  // Build [T, Tend) from the m records k .. k + m - 1 held in lanes 0 .. m - 1
+  // of rv (lane m holds the end of the last one), in 1 + extra passes.
+  __device__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t m, uint32_t extra) {
+    const uint32_t P = T + 16 * lane;
+    const uint32_t bend = P + 16 < Tend ? P + 16 : Tend;
+    // the record under the block's first byte
+    uint32_t j0 = 0;
+    for (uint32_t i = 1; i < m; i++) {
+      const uint32_t xi = __builtin_amdgcn_readlane(rv.x, i);
+      j0 = (xi <= P) ? i : j0;
+    }
+    const uint32_t inr_at = lds_addr(sm.inr), hist_at = lds_addr(sm.hist);
+    for (uint32_t pass = 0; pass <= extra; pass++) {
+      uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t pos = P, j = j0;
+      bool active = pos < bend;
+      while (__ballot(active)) {
+        const uint32_t os = __builtin_amdgcn_ds_bpermute(4 * j, rv.x);
+        const uint32_t src = __builtin_amdgcn_ds_bpermute(4 * j, rv.y);
+        const uint32_t L = __builtin_amdgcn_ds_bpermute(4 * j, rv.z);
+        const uint32_t info = __builtin_amdgcn_ds_bpermute(4 * j, rv.w);
+        const uint32_t re = __builtin_amdgcn_ds_bpermute(4 * (j + 1), rv.x);
+        if (active) {
+          const uint32_t le = os + L;
+          const bool lit = pos < le;
+          const uint32_t pe0 = lit ? le : re;
+          const uint32_t pe = pe0 < bend ? pe0 : bend;
+          // block byte q comes from ring index q + delta: the input ring for
+          // literals, the history ring (q - dist) for matches
+          const uint32_t base = lit ? inr_at : hist_at;
+          const uint32_t mask = lit ? IMASK : HMASK;
+          const uint32_t si = P + (lit ? src - os : 0u - rec_dist(info));
+          const uint32_t a = si & ~3u, sh = si & 3u;
+          uint32_t d[5];
+#pragma unroll
+          for (int q = 0; q < 5; q++)
+            d[q] = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + ((a + 4 * q) & mask));
+          uint4 v = make_uint4(__builtin_amdgcn_alignbyte(d[1], d[0], sh), __builtin_amdgcn_alignbyte(d[2], d[1], sh),
+                               __builtin_amdgcn_alignbyte(d[3], d[2], sh), __builtin_amdgcn_alignbyte(d[4], d[3], sh));
+          if (!lit && (info & F_FILL)) {
+            const uint32_t fw = rec_fill(info) * 0x01010101u;
+            v = make_uint4(fw, fw, fw, fw);
+          }
+          const int lo = (int)(pos - P);
+          acc.x = merge_from(acc.x, v.x, lo);
+          acc.y = merge_from(acc.y, v.y, lo - 4);
+          acc.z = merge_from(acc.z, v.z, lo - 8);
+          acc.w = merge_from(acc.w, v.w, lo - 12);
+          pos = pe;
+          if (pe >= re) j++;
+          active = pos < bend;
+        }
+      }
+      // the last block of a chunk's last tile is stored only up to the end:
+      // its ring slot beyond holds bytes that a later pass may still read
+      if (P + 16 <= Tend) *(uint4 *)(sm.hist + (P & HMASK)) = acc;
+      else if (P < Tend) st_block(sm.hist + (P & HMASK), acc, 0, Tend - P);
+    }
+  }
+
+  __device__ void run() {
+    const uint32_t ntiles = (N + TILE - 1) / TILE;
+    const bool fast = MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8;
+    for (uint32_t t = b; t < ntiles; t += NB) {
+      const uint32_t T = t * TILE;
+      const uint32_t Tend = T + TILE < N ? T + TILE : N;
+      // the tile's scales are fetched first, so their latency overlaps the build
+      Meta4 cur{};
+      if (fast) cur = int4_meta(P, dst0, t, lane, N);
+      if (!wait_cov(T, Tend)) break;
+      find_k(T);
+      announce(T);
+      // records k .. k + 63 in lanes; missing ones read as {cov, 0, 0, 0}
+      const uint32_t jr = k + lane;
+      uint4 rv = make_uint4(cov, 0u, 0u, 0u);
+      if (jr < nrec) rv = sm.recs[ridx(jr)];
+      const uint32_t m = __builtin_popcountll(__ballot(jr < nrec && rv.x < Tend));
+      // classify: one pass possible?  how many passes?  which input and
+      // which earlier tiles are read?
+      bool hard = m > BULK_RECS;
+      uint32_t extra = 0, src_need = 0, in_end = 0;
+      if (!hard) {
+        for (uint32_t i = 0; i < m; i++) {
+          const uint32_t x = __builtin_amdgcn_readlane(rv.x, i);
+          const uint32_t yy = __builtin_amdgcn_readlane(rv.y, i);
+          const uint32_t L = __builtin_amdgcn_readlane(rv.z, i);
+          const uint32_t info = __builtin_amdgcn_readlane(rv.w, i);
+          const uint32_t re = __builtin_amdgcn_readlane(rv.x, i + 1);
+          const uint32_t le = x + L;
+          if (le > T) in_end = yy + ((le < Tend ? le : Tend) - x);
+          const uint32_t base = le > T ? le : T;
+          const uint32_t pend = re < Tend ? re : Tend;
+          if (base < pend && !(info & F_FILL)) {
+            const uint32_t dist = rec_dist(info);
+            if (dist < 16 || dist < pend - base) hard = true;   // overlapping copy
+            const uint32_t s_hi = pend - dist;                  // sources end here
+            if (s_hi > T) extra++;                              // reads this tile
+            const uint32_t s_fin = s_hi < T ? s_hi : T;
+            src_need = s_fin > src_need ? s_fin : src_need;
+          }
+        }
+      }
+      // Beyond the first 64 KiB, sources up to 65535 bytes back share this
+      // tile's own ring slot: one pass reads them before its stores, but a
+      // second pass would read this tile's bytes instead.  Sequence by
+      // sequence, every such source lies ahead of the bytes written so far.
+      if (t >= HTILES && extra) hard = true;
+      // tiles before this one that are read, and (for chunks over 64 KiB)
+      // every tile that might still read the ring slot this one overwrites
+      uint32_t need_tiles = hard ? t : (src_need + TILE - 1) / TILE;
+      if (t >= HTILES) need_tiles = t;
+      if (!wait_done(need_tiles)) break;
+      if (hard) {
+        tile_exact(T, Tend);
+      } else {
+        need_input(in_end);
+        tile_bulk(T, Tend, rv, m, extra);
+      }
+      if (fast) meta_ready(cur, P.zp != nullptr);
+      flush_tile<MODE>(sm, lane, P, dst0, t, N, cur, fast);
+      lds_set(&ctl.next_tile[b], t + NB, lane);
+    }
+    lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
+    lds_set(&ctl.bk[b], 0xFFFFFFFFu, lane);
+    lds_set(&ctl.next_tile[b], 0xFFFFFFFFu, lane);
+    if (lane == 0) __hip_atomic_fetch_add(&ctl.nfinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+};
 
 // -------------------------------------------------------------- kernel
 
@@ -764,26 +910,32 @@ __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
   const uint8_t *S = P.comp + (c0 - head);
   const uint32_t y_end = head + (uint32_t)(c1 - c0);
 
+  if (tid < NSLOT) {
+    ctl.need[tid] = tid <= (uint32_t)NB ? 0u : 0xFFFFFFFFu;
+    ctl.bk[tid] = tid < (uint32_t)NB ? 0u : 0xFFFFFFFFu;
+    ctl.next_tile[tid] = tid < (uint32_t)NB ? tid : 0xFFFFFFFFu;
+  }
   if (tid == 0) {
     ctl.in_avail = 0;
-    ctl.in_used = 0;
-    ctl.out_done = 0;
-    ctl.state = ST_RUN;
-    for (int f = 0; f < NFLUSH; f++) ctl.next_tile[f] = f;
+    ctl.nrec = 0;
+    ctl.cov = 0;
+    ctl.pstate = ST_RUN;
+    ctl.nfinished = 0;
     ctl.status = 0;
   }
   __syncthreads();
 
   if (wave == 0) {
-    Decoder D{sm, ctl, lane, head, y_end, 0, N, 0, 0, 0xFFFFFF00u, 0, 0, 0, make_uint4(0, 0, 0, 0)};
-    int32_t st = (y_end == head) ? C_TRUNC : D.run();
-    D.publish(D.used);
+    Parser Pa{sm, ctl, lane, head, y_end, 0, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0};
+    int32_t st = (y_end == head) ? C_TRUNC : Pa.run();
     if (lane == 0) ctl.status = st;
-    lds_put(&ctl.state, st == C_OK ? ST_DONE : ST_FAIL, lane);
+    lds_set(&ctl.need[0], 0xFFFFFFFFu, lane);
+    lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
   } else if (wave == 1) {
     feeder(sm, ctl, lane, S, y_end);
   } else {
-    flusher<MODE>(sm, ctl, lane, wave - 2, P, d0, N);
+    Builder<MODE> B{sm, ctl, P, d0, lane, wave - 2, N, 0, 0, 0, ST_RUN, 0, 0, 0};
+    B.run();
   }
   __syncthreads();
   if (tid == 0 && P.status) P.status[i] = ctl.status;

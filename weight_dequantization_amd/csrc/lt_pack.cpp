@@ -11,6 +11,10 @@
 //   * the most recent earlier position with the same 4-byte hash (distance up
 //     to 65535), accepted from 8 bytes, so isolated 4-byte coincidences in
 //     near-random code bytes do not split long literal runs.
+// A hashed match is passed over when a run starting at the next byte covers
+// as much (a zero group after a nonzero byte, say): the run costs one more
+// literal byte, but the device decoder builds it without reading earlier
+// output, so the tiles of the decoded stream stay independent.
 // It keeps the format's end-of-block rules (the last 5 bytes are literals and
 // no match starts within the last 12 bytes), so standard LZ4 block decoders
 // accept its output.
@@ -95,6 +99,14 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
         best_len = len;
         best_dist = i - (uint64_t)c;
       }
+    }
+    if (best_dist > 1 && i + 1 + kMatchLimit <= n && src[i + 1] == src[i]) {
+      // A run of src[i] starting at i + 1 that covers as much as the hashed
+      // match (with src[i] as one more literal) is taken instead: a run
+      // decodes without reading earlier output.
+      uint64_t r = 0;
+      while (i + 1 + r < match_end && src[i + 1 + r] == src[i]) r++;
+      if (r >= kMinRun && r + 1 >= best_len) best_len = 0;
     }
     if (best_len) {
       w.sequence(src + anchor, i - anchor, best_dist, best_len);
