@@ -331,73 +331,163 @@ struct Parser {
     lds_set(&ctl.cov, cov, lane);
   }
 
+  // bytes p .. p + 7 from the window (p >= wy, p + 12 <= wy + 256)
+  __device__ uint64_t peek8(uint32_t p) {
+    const uint32_t r = p - wy, i = r >> 2, sh = (r & 3) * 8;
+    const uint32_t d0 = __builtin_amdgcn_readlane(win, i);
+    const uint32_t d1 = __builtin_amdgcn_readlane(win, i + 1);
+    const uint32_t d2 = __builtin_amdgcn_readlane(win, i + 2);
+    const uint32_t lo = (uint32_t)((((uint64_t)d1 << 32) | d0) >> sh);
+    const uint32_t hi = (uint32_t)((((uint64_t)d2 << 32) | d1) >> sh);
+    return ((uint64_t)hi << 32) | lo;
+  }
+
+  // One sequence of the common shape -- at most two extra length bytes per
+  // length field, well inside the block, window reachable without waiting --
+  // parsed from two 8-byte peeks and written as one finished record.  Returns
+  // false, with the sequence untouched, when any of that does not hold or any
+  // check fails; the general step then parses (and diagnoses) it.
+  __device__ bool fast_step() {
+    if (y < wy || y + 12 > wy + 256 || y + 8 > y_end) return false;
+    const uint64_t q = peek8(y);
+    const uint32_t token = (uint32_t)q & 0xFFu;
+    uint32_t L = token >> 4, hdr = 1;
+    if (L == 15) {
+      const uint32_t e1 = (uint32_t)(q >> 8) & 0xFFu, e2 = (uint32_t)(q >> 16) & 0xFFu;
+      if (e1 < 255) {
+        L = 15 + e1;
+        hdr = 2;
+      } else if (e2 < 255) {
+        L = 270 + e2;
+        hdr = 3;
+      } else {
+        return false;
+      }
+    }
+    const uint32_t ys = y + hdr;
+    if (L > N - op || L > y_end - ys || y_end - (ys + L) < 12) return false;
+    const uint32_t ye = ys + L;
+    if (nrec - rec_free >= RING) return false;
+    // the last literal byte, the distance, the match length bytes
+    const uint32_t p = L ? ye - 1 : ye;
+    if (p < wy || p + 12 > wy + 256) {
+      const uint32_t w2 = p & ~3u;
+      const uint32_t upto = w2 + 256 < y_end ? w2 + 256 : y_end;
+      if (avail < upto) {
+        avail = lds_get(&ctl.in_avail);
+        if (avail < upto) return false;   // the general step announces the literals first
+      }
+      wy = w2;
+      lds_set(&ctl.need[0], wy, lane);
+      win = *(const uint32_t *)(sm.inr + ((wy + 4 * lane) & IMASK));
+      wait_lds();
+    }
+    const uint64_t pq = peek8(p);
+    const uint64_t mq = pq >> (L ? 8 : 0);
+    const uint32_t dist = (uint32_t)mq & 0xFFFFu;
+    const uint32_t m1 = (uint32_t)(mq >> 16) & 0xFFu, m2 = (uint32_t)(mq >> 24) & 0xFFu;
+    uint32_t M = (token & 15) + 4, mext = 0;
+    if ((token & 15) == 15) {
+      if (m1 < 255) {
+        M += m1;
+        mext = 1;
+      } else if (m2 < 255) {
+        M += 255 + m2;
+        mext = 2;
+      } else {
+        return false;
+      }
+    }
+    if (dist == 0 || dist > op + L || M > N - op - L) return false;
+    if (L) {
+      fill = (uint32_t)pq & 0xFFu;
+      fill_ok = 1;
+    }
+    uint32_t info = F_MATCH | dist;
+    if (dist == 1 && fill_ok) info |= F_FILL | (fill << 16);
+    if (dist != 1) fill_ok = 0;
+    if (lane == 0) sm.recs[ridx(nrec)] = make_uint4(op, ys, L, info);
+    nrec++;
+    op += L + M;
+    y = ye + 2 + mext;
+    publish(op);
+    return true;
+  }
+
+  // One sequence, byte by byte, with every check.  Returns false when the
+  // block ends (st: C_OK after the literal-only last sequence) or fails.
+  __device__ bool slow_step(int32_t &st) {
+    if (y >= y_end) { st = C_TRUNC; return false; }
+    const uint32_t token = byte_at(y);
+    y++;
+    uint32_t L = token >> 4;
+    if (L == 15) {
+      uint32_t b;
+      do {
+        if (y >= y_end) { st = C_TRUNC; return false; }
+        b = byte_at(y);
+        y++;
+        L += b;
+        // stop as soon as the run cannot fit: this also bounds how far the
+        // parser reads ahead of the builders inside a length field
+        if (L > N - op) { st = C_OVERRUN; return false; }
+      } while (b == 255);
+    }
+    if (L > y_end - y) { st = C_TRUNC; return false; }
+    if (L > N - op) { st = C_OVERRUN; return false; }
+    const uint32_t ye = y + L;
+    // record, phase 1: the literal run
+    if (nrec - rec_free >= RING) wait_ring();
+    const uint32_t k = nrec;
+    if (lane == 0) sm.recs[ridx(k)] = make_uint4(op, y, L, ye == y_end ? F_LAST : 0u);
+    nrec++;
+    if (ye == y_end) {   // literal-only last sequence
+      op += L;
+      y = ye;
+      return false;
+    }
+    publish(op + L);
+    if (y_end - ye < 2) { st = C_TRUNC; return false; }
+    // the window at the run's end: last literal byte, distance, match
+    // length bytes, next token
+    const uint32_t wpos = L ? ye - 1 : ye;
+    if (wpos < wy || wpos + 16 > wy + 256) load_window(wpos);
+    if (L) {
+      fill = byte_at(ye - 1);
+      fill_ok = 1;
+    }
+    y = ye;
+    uint32_t dist = byte_at(y);
+    dist |= byte_at(y + 1) << 8;
+    y += 2;
+    if (dist == 0 || dist > op + L) { st = C_BADOFF; return false; }
+    uint32_t M = (token & 15) + 4;
+    if ((token & 15) == 15) {
+      uint32_t b;
+      do {
+        if (y >= y_end) { st = C_TRUNC; return false; }
+        b = byte_at(y);
+        y++;
+        M += b;
+        if (M > N - op - L) { st = C_OVERRUN; return false; }
+      } while (b == 255);
+    }
+    if (M > N - op - L) { st = C_OVERRUN; return false; }
+    // phase 2: the match
+    uint32_t info = F_MATCH | dist;
+    if (dist == 1 && fill_ok) info |= F_FILL | (fill << 16);
+    if (lane == 0) sm.recs[ridx(k)].w = info;
+    if (dist != 1) fill_ok = 0;
+    op += L + M;
+    return true;
+  }
+
   __device__ int32_t run() {
     int32_t st = C_OK;
     for (;;) {
-      if (y >= y_end) { st = C_TRUNC; break; }
-      const uint32_t token = byte_at(y);
-      y++;
-      uint32_t L = token >> 4;
-      if (L == 15) {
-        uint32_t b;
-        do {
-          if (y >= y_end) { st = C_TRUNC; goto out; }
-          b = byte_at(y);
-          y++;
-          L += b;
-          // stop as soon as the run cannot fit: this also bounds how far the
-          // parser reads ahead of the builders inside a length field
-          if (L > N - op) { st = C_OVERRUN; goto out; }
-        } while (b == 255);
-      }
-      if (L > y_end - y) { st = C_TRUNC; break; }
-      if (L > N - op) { st = C_OVERRUN; break; }
-      const uint32_t ye = y + L;
-      // record, phase 1: the literal run
-      if (nrec - rec_free >= RING) wait_ring();
-      const uint32_t k = nrec;
-      if (lane == 0) sm.recs[ridx(k)] = make_uint4(op, y, L, ye == y_end ? F_LAST : 0u);
-      nrec++;
-      if (ye == y_end) {   // literal-only last sequence
-        op += L;
-        y = ye;
-        break;
-      }
-      publish(op + L);
-      if (y_end - ye < 2) { st = C_TRUNC; break; }
-      // the window at the run's end: last literal byte, distance, match
-      // length bytes, next token
-      const uint32_t wpos = L ? ye - 1 : ye;
-      if (wpos < wy || wpos + 16 > wy + 256) load_window(wpos);
-      if (L) {
-        fill = byte_at(ye - 1);
-        fill_ok = 1;
-      }
-      y = ye;
-      uint32_t dist = byte_at(y);
-      dist |= byte_at(y + 1) << 8;
-      y += 2;
-      if (dist == 0 || dist > op + L) { st = C_BADOFF; break; }
-      uint32_t M = (token & 15) + 4;
-      if ((token & 15) == 15) {
-        uint32_t b;
-        do {
-          if (y >= y_end) { st = C_TRUNC; goto out; }
-          b = byte_at(y);
-          y++;
-          M += b;
-          if (M > N - op - L) { st = C_OVERRUN; goto out; }
-        } while (b == 255);
-      }
-      if (M > N - op - L) { st = C_OVERRUN; break; }
-      // phase 2: the match
-      uint32_t info = F_MATCH | dist;
-      if (dist == 1 && fill_ok) info |= F_FILL | (fill << 16);
-      if (lane == 0) sm.recs[ridx(k)].w = info;
-      if (dist != 1) fill_ok = 0;
-      op += L + M;
+      if (fast_step()) continue;
+      if (!slow_step(st)) break;
     }
-  out:
     if (st == C_OK && op != N) st = C_SIZE;
     if (st == C_OK) publish(op);   // a failed chunk's builders stop at what was announced before
     return st;
