@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 1
+#define LT_ABI_VERSION 2
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -72,6 +72,11 @@ enum {
  * decoder's 8 KiB compressed-input ring always holds what is being parsed. */
 #define LT_MAX_CHUNK_BYTES (1u << 20)
 
+/* Tables whose max_dist is at most this (bytes) are decoded with a 16 KiB
+ * history per chunk instead of 64 KiB, which lets more chunks share a CU.
+ * lt_compress_chunks produces such tables when asked for this window. */
+#define LT_SMALL_WINDOW 11264u
+
 /*
  * Chunk table (HOST struct; its members point to DEVICE memory).
  * A tensor's byte stream (packed INT4 codes, INT8 codes or raw bytes) of
@@ -86,6 +91,13 @@ enum {
  *              dst_off[n] = total_bytes, dst_off[i] % 16 == 0 for i < n
  *   max_chunk_bytes  host-known max(dst_off[i+1] - dst_off[i]),
  *              1 <= max_chunk_bytes <= LT_MAX_CHUNK_BYTES (ignored if n_chunks == 0)
+ *   max_dist   the largest match distance in any block, 1..65535, or 0 when
+ *              not known (any distance).  It is a promise about the blocks:
+ *              a match farther back makes its chunk fail with
+ *              LT_CHUNK_BAD_OFFSET.  LZ4 blocks may use distances up to
+ *              65535; a compressor that keeps them shorter lets the decoder
+ *              keep less history (see LT_SMALL_WINDOW).
+ *   reserved   0
  * Entries that break these rules make that chunk fail with LT_CHUNK_BAD_TABLE
  * (checked on the device); the struct itself is read only during the call.
  */
@@ -97,6 +109,8 @@ typedef struct lt_chunk_table {
   uint32_t max_chunk_bytes;
   uint64_t total_bytes;
   uint64_t comp_bytes;
+  uint32_t max_dist;
+  uint32_t reserved;
 } lt_chunk_table;
 
 /*
@@ -161,12 +175,15 @@ lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed);
  * lt_compress_chunks -- HOST.  Compresses src[dst_off[i] .. dst_off[i+1]) for
  * each of n_chunks chunks as an independent LZ4 block and concatenates them
  * into comp (capacity comp_cap); comp_off (uint64[n_chunks+1]) receives the
- * prefix sums.  threads <= 0 means one per host core.  Returns
+ * prefix sums.  threads <= 0 means one per host core.  Matches reach at most
+ * max_dist bytes back (0 or anything above 65535 means 65535); the table
+ * built from the result may declare that window.  Returns
  * LT_ERR_INVALID_ARG for a non-monotone table or too small a buffer
  * (sum of lt_lz4_bound over the chunks always suffices).
  */
 lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
-                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads);
+                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
+                             uint32_t max_dist);
 
 const char *lt_status_str(lt_status s);
 int lt_abi_version(void);

@@ -1,0 +1,24 @@
+"""Host-side walk over LZ4 raw blocks, for checks that need the sequence
+structure (not the decoded bytes) of a block the packer wrote."""
+
+
+def max_match_distance(blk):
+    """Largest match distance in a valid LZ4 block (host-side walk)."""
+    b = [int(v) for v in blk]
+    y, best = 0, 0
+    while True:
+        t = b[y]; y += 1
+        L = t >> 4
+        if L == 15:
+            while True:
+                v = b[y]; y += 1; L += v
+                if v != 255: break
+        y += L
+        if y >= len(b):
+            return best
+        best = max(best, b[y] | (b[y + 1] << 8))
+        y += 2
+        if (t & 15) == 15:
+            while True:
+                v = b[y]; y += 1
+                if v != 255: break

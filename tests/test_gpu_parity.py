@@ -15,6 +15,7 @@ import torch
 import oracle as O
 import synth
 import weight_dequantization_amd as lt
+from lz4_blocks import max_match_distance
 
 pytestmark = pytest.mark.gpu
 
@@ -178,6 +179,56 @@ def test_decode_chunks_larger_than_history(size):
     _decode_check(table_from_oracle(t), e, "big chunk %d" % size)
 
 
+def _repeats(n, seed, reach):
+    """Bytes with copies from up to `reach` bytes back, runs and noise."""
+    rng = np.random.default_rng(seed)
+    x = (rng.integers(0, 16, n, dtype=np.uint8) * 17).astype(np.uint8)
+    x[::97] = 0
+    for r in range(0, n - 700, 1500):
+        d = int(rng.integers(1, reach))
+        if r >= d:
+            x[r:r + 700] = x[r - d:r - d + 700]
+    return x
+
+
+@pytest.mark.parametrize("size", [16384 + 16, 65536, 200000, 1 << 20])
+def test_decode_short_window_chunks(size):
+    """Tables that declare a window within SMALL_WINDOW decode with a 16 KiB
+    history ring, which chunks over 16 KiB wrap many times."""
+    x = _repeats(3 * size + 5, size, lt.SMALL_WINDOW)
+    dst = np.array([0, size, 2 * size, 3 * size, 3 * size + 5], np.uint64)
+    table = lt.ChunkTable.build(x, dst, DEV)
+    assert table.max_dist == lt.SMALL_WINDOW
+    _decode_check(table, x, "short window, chunk %d" % size)
+    # the same blocks declared with any window (64 KiB history) decode alike
+    t2 = lt.ChunkTable(table.comp, table.comp_off, table.dst_off, table.n_chunks,
+                       table.max_chunk_bytes, table.total_bytes, table.comp_bytes, 0)
+    _decode_check(t2, x, "same blocks, any window, chunk %d" % size)
+
+
+def test_declared_window_is_enforced():
+    """A block with a match farther back than the table's declared window
+    fails with BAD_OFFSET; the other chunks are unaffected."""
+    x = _repeats(4 * 65536, 9, 60000)
+    dst = np.arange(5, dtype=np.uint64) * np.uint64(65536)
+    ot = O.compress_table(x, dst)          # the oracle's compressor uses the full 64 KiB window
+    far = []
+    for i in range(4):
+        blk = ot.comp[int(ot.comp_off[i]):int(ot.comp_off[i + 1])]
+        far.append(max_match_distance(blk) > lt.SMALL_WINDOW)
+    assert any(far)
+    small = lt.ChunkTable.from_host(ot.comp, ot.comp_off, ot.dst_off, DEV, max_dist=lt.SMALL_WINDOW)
+    st = status_tensor(small.n_chunks)
+    out = lt.decode_lz4(small, status=st)
+    s = statuses(st, small.n_chunks)
+    got = out.cpu().numpy()
+    for i in range(4):
+        if far[i]:
+            assert s[i] == lt.CHUNK_BAD_OFFSET, (i, s[i])
+        else:
+            assert s[i] == 0 and np.array_equal(got[65536 * i:65536 * (i + 1)], x[65536 * i:65536 * (i + 1)])
+
+
 def test_decode_config4_full():
     a = synth.config4()
     _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV), a.data, "config4 packer")
@@ -312,6 +363,14 @@ def test_fused_int4_generated_streams():
     out = lt.fused_lz4_int4(table_from_oracle(t), t_u16(scales), t_i8(zp), (rows, cols), group, status=st)
     assert np.all(statuses(st, t.n) == 0)
     assert_same(host_u16(out), O.dequant_int4(e, scales, zp, group), "fused seqgen")
+
+
+def test_fused_int4_short_window_big_chunks():
+    """Fused INT4 with 256 KiB chunks in a short-window table (ring reuse)."""
+    w = synth.int4_weight(512, 4096, 128, 41)
+    packed = lt.pack_int4(w.codes)
+    table = lt.ChunkTable.build(packed, synth.uniform_chunks(packed.size, 262144), DEV)
+    _fused4(table, w, "short window, 256 KiB chunks")
 
 
 def test_fused_int8_config2():

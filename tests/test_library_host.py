@@ -14,6 +14,7 @@ import pytest
 
 import oracle as O
 import synth
+from lz4_blocks import max_match_distance
 import weight_dequantization_amd as lt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -35,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 1
+    assert lt.lib().lt_abi_version() == 2
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -69,6 +70,11 @@ def test_invalid_arguments_rejected_without_gpu():
     # int8 table size must equal rows*cols
     t = lt._Table(0x10000, 0x10000, 0x10000, 1, 16, 16, 100)
     assert L.lt_fused_lz4_int8(C.byref(t), fake, None, 4, 8, 8, fake, None, None) == lt.LT_ERR_INVALID_ARG
+    # a declared window beyond the format's, and a nonzero reserved field
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100, 65536, 0)
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100, 1024, 1)
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
     # empty tables are valid no-ops (no device work)
     t = lt._Table(0, 0, 0, 0, 0, 0, 0)
     assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_OK
@@ -127,3 +133,20 @@ def test_packer_mixed_chunks():
     w = synth.int4_weight(512, 8192, 128, 77, chunking="mixed")
     packed = lt.pack_int4(w.codes)
     _oracle_round_trip(packed, w.dst_off)
+
+
+@pytest.mark.parametrize("max_dist", [1, 4096, lt.SMALL_WINDOW, 65535])
+def test_packer_honours_declared_window(max_dist):
+    """Every match the packer writes reaches at most max_dist bytes back, and
+    the blocks still decode (oracle) to the input."""
+    rng = np.random.default_rng(max_dist)
+    n = 200000
+    base = rng.integers(0, 256, 40000, dtype=np.uint8)
+    x = np.concatenate([base, base[::-1], base, rng.integers(0, 3, n - 120000, dtype=np.uint8)])
+    dst_off = np.array([0, 65536, 131072, n], np.uint64)
+    comp, comp_off = lt.compress_chunks(x, dst_off, max_dist=max_dist)
+    for c in range(3):
+        blk = comp[int(comp_off[c]):int(comp_off[c + 1])]
+        assert max_match_distance(blk) <= max_dist
+    out, st = O.decode_table(O.Table(comp, comp_off, dst_off))
+    assert np.all(st == O.OK) and np.array_equal(out, x)

@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(_HERE, "liblt.so")
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE = range(5)
 CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE = range(6)
 MAX_CHUNK_BYTES = 1 << 20
+SMALL_WINDOW = 11264      # LT_SMALL_WINDOW: tables within it decode with a 16 KiB history
 
 
 class LtError(RuntimeError):
@@ -51,7 +52,8 @@ class LtDecodeError(RuntimeError):
 class _Table(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("comp_off", C.c_void_p), ("dst_off", C.c_void_p),
                 ("n_chunks", C.c_uint32), ("max_chunk_bytes", C.c_uint32),
-                ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64)]
+                ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64),
+                ("max_dist", C.c_uint32), ("reserved", C.c_uint32)]
 
 
 _L = None
@@ -74,7 +76,7 @@ def _lib():
             "lt_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
-            "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32]),
+            "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
             "lt_status_str": (C.c_char_p, [i32]),
             "lt_abi_version": (i32, []),
         }
@@ -110,7 +112,9 @@ def lz4_bound(n: int) -> int:
     return int(_lib().lt_lz4_bound(n))
 
 
-def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0):
+def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_dist: int = 0):
+    """LZ4-compress each chunk independently (matches reach at most max_dist
+    bytes back; 0 means the format's 65535).  Returns (comp, comp_off)."""
     src = np.ascontiguousarray(src, dtype=np.uint8)
     dst_off = np.ascontiguousarray(dst_off, dtype=np.uint64)
     n = dst_off.size - 1
@@ -119,7 +123,7 @@ def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0):
     comp = np.empty(max(cap, 1), np.uint8)
     comp_off = np.empty(n + 1, np.uint64)
     st = _lib().lt_compress_chunks(_np_ptr(src), _np_ptr(dst_off), n, _np_ptr(comp), cap,
-                                   _np_ptr(comp_off), threads)
+                                   _np_ptr(comp_off), threads, max_dist)
     if st != LT_OK:
         raise LtError(st, "lt_compress_chunks")
     return comp[:int(comp_off[-1])].copy(), comp_off
@@ -152,9 +156,11 @@ class ChunkTable:
     max_chunk_bytes: int
     total_bytes: int
     comp_bytes: int
+    max_dist: int = 0       # declared largest match distance (0: any)
 
     @classmethod
-    def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda"):
+    def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
+                  max_dist: int = 0):
         torch = _torch()
         comp_off = np.ascontiguousarray(comp_off, np.uint64)
         dst_off = np.ascontiguousarray(dst_off, np.uint64)
@@ -167,17 +173,23 @@ class ChunkTable:
                    torch.from_numpy(comp_off.view(np.int64).copy()).to(device),
                    torch.from_numpy(dst_off.view(np.int64).copy()).to(device),
                    n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
-                   int(comp_off[-1]) if comp_off.size else 0)
+                   int(comp_off[-1]) if comp_off.size else 0, max_dist)
 
     @classmethod
-    def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0):
-        """Compress `src` chunk by chunk on the host and upload the table."""
-        comp, comp_off = compress_chunks(src, dst_off, threads)
-        return cls.from_host(comp, comp_off, dst_off, device)
+    def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0,
+              max_dist: int = None):
+        """Compress `src` chunk by chunk on the host and upload the table.  By
+        default matches stay within SMALL_WINDOW bytes, which the table
+        declares, so the device decoder keeps a short history per chunk."""
+        if max_dist is None:
+            max_dist = SMALL_WINDOW
+        comp, comp_off = compress_chunks(src, dst_off, threads, max_dist)
+        return cls.from_host(comp, comp_off, dst_off, device, max_dist)
 
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
-                      self.n_chunks, self.max_chunk_bytes, self.total_bytes, self.comp_bytes)
+                      self.n_chunks, self.max_chunk_bytes, self.total_bytes, self.comp_bytes,
+                      self.max_dist, 0)
 
 
 def _check(st, where):

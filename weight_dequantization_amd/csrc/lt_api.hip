@@ -158,12 +158,19 @@ lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *c
   P.zp = zp;
   P.group = group;
   P.group_shift = shift_of(group);
+  P.dmax = t->max_dist ? t->max_dist : 65535u;
   hipStream_t s = (hipStream_t)stream;
   dim3 grid(t->n_chunks), block(lt::NTHREADS);
-  switch (mode) {
-    case lt::MODE_BYTES: hipLaunchKernelGGL(lt::chunk_kernel<lt::MODE_BYTES>, grid, block, 0, s, P); break;
-    case lt::MODE_INT4: hipLaunchKernelGGL(lt::chunk_kernel<lt::MODE_INT4>, grid, block, 0, s, P); break;
-    default: hipLaunchKernelGGL(lt::chunk_kernel<lt::MODE_INT8>, grid, block, 0, s, P); break;
+  // a declared short window lets each chunk keep a 16 KiB history, so more
+  // chunks share a CU
+  const bool small = P.dmax <= LT_SMALL_WINDOW;
+  switch (mode * 2 + (small ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 16>), grid, block, 0, s, P); break;
+    case 1: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 14>), grid, block, 0, s, P); break;
+    case 2: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 16>), grid, block, 0, s, P); break;
+    case 3: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 14>), grid, block, 0, s, P); break;
+    case 4: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 16>), grid, block, 0, s, P); break;
+    default: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
   }
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
@@ -173,6 +180,7 @@ bool table_ok(const lt_chunk_table *t) {
   if (t->n_chunks == 0) return t->total_bytes == 0;
   if (!t->comp || !t->comp_off || !t->dst_off) return false;
   if (t->max_chunk_bytes == 0 || t->max_chunk_bytes > LT_MAX_CHUNK_BYTES) return false;
+  if (t->max_dist > 65535u || t->reserved != 0) return false;
   if (t->n_chunks > 0x7FFFFFFFu) return false;
   return true;
 }

@@ -1,26 +1,37 @@
 // lt_lz4.hpp -- chunk-parallel LZ4 block decoding on gfx950, one workgroup
-// per independently compressed chunk, with three wave roles that form a
+// per independently compressed chunk, with four wave roles that form a
 // pipeline through LDS:
 //
-//   wave 0  parser  : walks the block's sequences, validates them, and emits
-//                     one small record per sequence (where its literals sit
-//                     in the input and in the decoded stream, the match
-//                     distance) into an LDS record ring;
-//   wave 1  feeder  : streams the chunk's compressed bytes from HBM into an
+//   wave 0  walker  : the only serial part.  It hops from token to token
+//                     (reading the length nibbles, the 255-run extension
+//                     bytes and the distance from a 16-byte register window)
+//                     and appends one raw entry per sequence (where the
+//                     token sits, literal count, match length, distance) to
+//                     a short LDS chain.  It checks nothing it does not need
+//                     to find the next token.
+//   wave 1  recorder: takes up to 64 chain entries at a time, one per lane,
+//                     validates them (distance within the decoded prefix and
+//                     the declared window, lengths within the chunk) and
+//                     turns them into records with absolute positions by a
+//                     wave-wide prefix scan, then publishes them to an LDS
+//                     record ring.
+//   wave 2  feeder  : streams the chunk's compressed bytes from HBM into an
 //                     8 KiB LDS input ring with LDS-DMA loads
 //                     (global_load_lds_dwordx4), several 1 KiB segments in
-//                     flight;
-//   waves 2+ builders: builder b owns the aligned 1 KiB tiles t = b, b + NB,
+//                     flight.
+//   waves 3+ builders: builder b owns the aligned 1 KiB tiles t = b, b + NB,
 //                     b + 2 NB, ... of the decoded stream.  From the records
-//                     it builds its tile in a 64 KiB LDS history ring, all 64
+//                     it builds its tile in an LDS history ring, all 64
 //                     lanes at once (each lane owns 16 bytes of the tile), and
 //                     then writes the tile out: as bytes (decode-only), or
 //                     unpacked and dequantized to fp16 (fused INT4 / INT8),
 //                     with coalesced 16-byte stores.
 //
-// Only the parser is serial, and it does the least work per sequence that
-// finding the next sequence allows; the tiles are built and written by NB
-// waves side by side.
+// The history ring holds 64 KiB of decoded bytes for any LZ4 block, or
+// 16 KiB when the chunk table declares that no match reaches further back
+// than LT_SMALL_WINDOW bytes; the smaller ring lets more workgroups share a
+// CU, and with it more chunks decode at once.  A match beyond the declared
+// window is reported as a bad offset.
 //
 // The LZ4 block format (the pages name LZ4 for compressed weight blocks but
 // do not define it; "GPU Compression Pipeline - TDD Roadmap", Phase 2.1 and
@@ -32,7 +43,7 @@
 // is what byte-serial copying gives when d < M.
 //
 // Building a tile.  Most tiles hold a few sequences whose matches are runs of
-// one byte (distance 1, the byte known to the parser) or copies from before
+// one byte (distance 1, the byte carried in the record) or copies from before
 // the part of the match that lies in the tile.  Such a tile is built in one
 // pass: each lane walks the pieces (literal run, match) that meet its 16
 // bytes, gathers each piece's bytes with aligned dword reads and
@@ -47,19 +58,29 @@
 // operations complete in program order, so a counter written after data is
 // seen after that data):
 //   in_avail     feeder   -> all     : input bytes present in the ring
-//   need[0]      parser   -> feeder  : first input byte the parser still reads
+//   need[0]      walker   -> feeder  : first input byte the walker still reads
 //   need[1 + b]  builder  -> feeder  : first input byte builder b still reads
-//   nrec, cov    parser   -> builders: records written; decoded bytes covered
-//   bk[b]        builder  -> parser  : first record builder b still reads
+//   wcnt, rcons  walker  <-> recorder: chain entries written / taken
+//   nrec, cov    recorder -> builders: records written and the decoded bytes
+//                                      they cover, published as one 8-byte word
+//   bk[b]        builder  -> recorder: first record builder b still reads
 //   next_tile[b] builder  -> builders: builder b's tiles below it are final
-//   pstate       parser   -> all     : running / done / failed
-// Every wait is bounded.  The parser consumes at least one input byte per
-// sequence and stops at the chunk's end or at the first error; builders stop
-// when the parser stops short of their next tile.  The ring sizes are chosen
-// so that a waiting wave never holds what the wave it waits for needs: the
-// record ring holds more records than one tile can overlap, and decoded
-// chunks are at most 1 MiB, so a length field's extra bytes (about 1/255 of
-// the length) fit in the input ring beside the oldest tile's literals.
+//   pstate       recorder -> all     : running / done / failed
+// Every wait is bounded.  The walker consumes at least one input byte per
+// sequence and stops at the chunk's end, at a malformed length, or when the
+// recorder has stopped; the recorder stops at the first invalid sequence;
+// builders stop when the records stop short of their next tile.  A literal
+// run longer than the input ring is handed over in two parts (its start is
+// announced before the walker waits for its end), so the builders that need
+// those literals keep consuming input while the walker waits.  The ring sizes
+// are chosen so that a waiting wave never holds what the wave it waits for
+// needs: the record ring holds more records than one tile can overlap, and
+// decoded chunks are at most 1 MiB, so a length field's extra bytes (about
+// 1/255 of the length) fit in the input ring beside the oldest tile's
+// literals.  A tile overwrites the history slot of the tile one ring length
+// back, so its builder first waits until every tile that may read that slot
+// is final: when the declared window stays NB tiles short of the ring only
+// tiles NB or more places back read it, otherwise any earlier tile may.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -68,21 +89,20 @@
 
 namespace lt {
 
-constexpr uint32_t HIST = 1u << 16;   // LZ4 distances reach 65535
-constexpr uint32_t HMASK = HIST - 1;
 constexpr uint32_t INR = 1u << 13;    // compressed-input ring
 constexpr uint32_t IMASK = INR - 1;
 constexpr uint32_t SEG = 1024;        // feeder unit: one 16-byte DMA load per lane
 constexpr uint32_t QMAX = INR / SEG;  // segments in flight at most
 constexpr uint32_t TILE = 1024;       // build / write-out unit (bytes of decoded stream)
-constexpr uint32_t HTILES = HIST / TILE;
-// Sequence records in flight (parser -> builders).  A 1 KiB tile overlaps at
-// most 257 records (every non-final sequence decodes to >= 4 bytes), and the
-// parser must be able to hold all of them while the oldest tile's builder
-// waits for the tile's coverage, so the ring holds more than 257.
-constexpr uint32_t RING = 320;
-constexpr int NB = 6;                 // builder waves
-constexpr int NWAVES = 2 + NB;        // parser, feeder, builders
+// Sequence records in flight (recorder -> builders).  A 1 KiB tile overlaps
+// at most 257 records (every non-final sequence decodes to >= 4 bytes), and
+// the recorder must be able to hold all of them while the oldest tile's
+// builder waits for the tile's coverage, so the ring holds more than 258.
+// (Two workgroups must fit in one CU's LDS, which bounds the rings.)
+constexpr uint32_t RING = 272;
+constexpr uint32_t CHAIN = 32;        // walker -> recorder entries in flight
+constexpr int NB = 5;                 // builder waves
+constexpr int NWAVES = 3 + NB;        // walker, recorder, feeder, builders
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr uint32_t NSLOT = 8;         // counter array length (>= NB + 1)
 constexpr uint32_t BULK_RECS = 16;    // most sequences in a tile built in one pass
@@ -93,21 +113,27 @@ enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4,
 enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2 };
 
 struct __attribute__((aligned(16))) Ctl {
-  uint32_t need[NSLOT];       // first input byte still read: [0] parser, [1 + b] builder b
+  uint32_t need[NSLOT];       // first input byte still read: [0] walker, [1 + b] builder b
   uint32_t bk[NSLOT];         // builder b: first record it may still read
   uint32_t next_tile[NSLOT];  // builder b: its next tile (all ones once it has left)
   uint32_t in_avail;          // feeder: input bytes present in the ring
-  uint32_t nrec;              // parser: records written
-  uint32_t cov;               // parser: decoded bytes fully described by records
-  uint32_t pstate;            // parser: running / done / failed
+  uint32_t pstate;            // recorder: running / done / failed
+  uint32_t nrec;              // recorder: records written ...
+  uint32_t cov;               // ... and the decoded bytes they cover (one 8-byte word)
+  uint32_t wcnt;              // walker: chain entries written
+  uint32_t rcons;             // recorder: chain entries taken
   uint32_t nfinished;         // builders that have left
   int32_t status;
 };
 
+// The history ring holds 2^HLOG decoded bytes: 64 KiB for any LZ4 block
+// (distances reach 65535), 16 KiB for tables that declare a short window.
+template <int HLOG>
 struct Smem {
-  uint8_t hist[HIST];
+  uint8_t hist[1u << HLOG];
   uint8_t inr[INR];
   uint4 recs[RING];
+  uint4 chain[CHAIN];
 };
 
 struct ChunkParams {
@@ -124,6 +150,7 @@ struct ChunkParams {
   const int8_t *zp;
   uint64_t group;
   uint32_t group_shift;      // log2(group) when group is a power of two, else 64
+  uint32_t dmax;             // largest match distance the table allows (65535: any)
 };
 
 // ------------------------------------------------------------ LDS sync
@@ -165,6 +192,26 @@ __device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t lane) 
   if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// nrec and cov are written together with one 8-byte store and read with one
+// 8-byte load, so a reader never sees coverage by records it does not count.
+__device__ __forceinline__ void publish_rec(Ctl &c, uint32_t nrec, uint32_t cov, uint32_t lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0)
+    __hip_atomic_store((uint64_t *)&c.nrec, ((uint64_t)cov << 32) | nrec, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ uint2 read_rec(Ctl &c) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const uint64_t v = __hip_atomic_load((uint64_t *)&c.nrec, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return make_uint2(__builtin_amdgcn_readfirstlane((uint32_t)v), __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)));
+}
+
+// a value every lane holds, stated so the compiler keeps it in a scalar register
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
@@ -257,7 +304,7 @@ __device__ __forceinline__ uint32_t merge_from(uint32_t acc, uint32_t v, int c) 
 
 // ----------------------------------------------------------- sequences
 
-// A sequence record, written by the parser into an LDS ring and read by the
+// A sequence record, written by the recorder into an LDS ring and read by the
 // builders: the decoded-stream position where the sequence's literals start,
 // the input position of the literals, their count, and the match (distance,
 // fill byte for distance 1 when known, flags).  A record's match ends where
@@ -270,65 +317,101 @@ __device__ __forceinline__ uint32_t ridx(uint32_t j) { return j % RING; }
 __device__ __forceinline__ uint32_t rec_dist(uint32_t info) { return info & 0xFFFFu; }
 __device__ __forceinline__ uint32_t rec_fill(uint32_t info) { return (info >> 16) & 0xFFu; }
 
-// ---------------------------------------------------------- the parser
+// --------------------------------------------------- walker and recorder
 
-// Wave 0.  Walks the block's sequences, validates every field and bound, and
-// emits one record per sequence.  Its only LDS round trip per sequence is the
-// parse window at the literal run's end, which also holds the distance, the
-// match length bytes and the next token.
-struct Parser {
-  Smem &sm;
+// The parse is split in two.  The walker follows the chain of sequence
+// starts, which is the only part of LZ4 decoding that is inherently serial:
+// from a token it needs the literal count (and its extra bytes), and from the
+// literal run's end the match length's extra bytes, to find the next token.
+// Reading the distance there as well, it writes one chain entry per sequence
+// {literal start, literal count, match length, distance | last literal byte
+// << 16 | flags << 24}.  The recorder takes up to 64 chain entries at once,
+// one lane per sequence: it forms the decoded positions with a wave prefix
+// sum, applies the checks that need them and writes the records the builders
+// consume.  It never reads the input.
+
+constexpr uint32_t W_LAST = 1u << 24;   // literal-only last sequence
+constexpr uint32_t W_END = 2u << 24;    // the walk stopped here; the status is in the match field
+constexpr uint32_t W_LIT = 4u << 24;    // a literal run whose match is still being read ...
+constexpr uint32_t W_CONT = 8u << 24;   // ... and, in the next entry, that match (M, distance)
+
+// Wave 0.  Structural checks only (everything that keeps the walk inside the
+// block); distances and decoded positions are the recorder's.  Input waits
+// always end: the feeder keeps filling the ring while the walk is open, and
+// the walker announces a literal run before it waits for the bytes after it,
+// so the builders can release the ring.  Only the chain wait can end with the
+// recorder gone (a failed chunk): then the walk stops.
+template <class SM>
+struct Walker {
+  SM &sm;
   Ctl &ctl;
   uint32_t lane;
-  uint32_t y;           // input position of the next byte to parse
+  uint32_t y;           // input position of the next token
   uint32_t y_end;
-  uint32_t op;          // decoded bytes described by finished sequences
   uint32_t N;
   uint32_t avail;       // cached ctl.in_avail
   uint32_t wy;          // window start (multiple of 4); window = [wy, wy + 256)
   uint32_t win;         // this lane's dword of the window
-  uint32_t nrec;        // records written
-  uint32_t rec_free;    // cached: records below this may be overwritten
-  uint32_t fill_ok;     // the byte at op - 1 is known ...
-  uint32_t fill;        // ... and is this
+  uint32_t cnt;         // chain entries written
+  uint32_t cons;        // cached ctl.rcons: entries the recorder has taken
+  uint32_t stop;        // the recorder is gone: the walk ends
+  uint32_t pend;        // the current literal run [pend_ys, + pend_L) is not announced yet
+  uint32_t split;       // it was announced on its own (W_LIT)
+  uint32_t pend_ys, pend_L;
+
+  __device__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
+    while (cnt - cons >= CHAIN) {
+      cons = lds_get(&ctl.rcons);
+      if (cnt - cons < CHAIN) break;
+      if (lds_get(&ctl.pstate) != ST_RUN) {
+        stop = 1;
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const uint32_t slot = cnt % CHAIN;
+    cnt = uni(cnt + 1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) {   // the entry first, then the count (one wave's LDS writes land in order)
+      sm.chain[slot] = make_uint4(ys, L, M, w);
+      __hip_atomic_store(&ctl.wcnt, cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
 
   __device__ void need_input(uint32_t upto) {
-    if (upto > y_end) upto = y_end;
+    upto = upto < y_end ? upto : y_end;
+    if (avail >= upto) return;
+    avail = lds_get(&ctl.in_avail);
+    if (avail >= upto) return;
+    if (pend) {
+      // announce the literal run before waiting: its builders consume it
+      // and release the input ring, which may be what the wait needs
+      pend = 0;
+      split = 1;
+      emit(pend_ys, pend_L, 0, W_LIT);
+    }
     while (avail < upto) {
+      __builtin_amdgcn_s_sleep(1);
       avail = lds_get(&ctl.in_avail);
-      if (avail < upto) __builtin_amdgcn_s_sleep(1);
     }
   }
 
-  // Nothing before the window start is parsed again (literals are read by
-  // the builders, which announce their own needs).
+  // Nothing before the window start is read again by the walker (the
+  // builders announce their own needs).
   __device__ void load_window(uint32_t p) {
-    wy = p & ~3u;
+    wy = uni(p & ~3u);
     lds_set(&ctl.need[0], wy, lane);
     need_input(wy + 256);
     win = *(const uint32_t *)(sm.inr + ((wy + 4 * lane) & IMASK));
-    wait_lds();   // on this path only, so byte_at never waits on stores
+    wait_lds();
   }
 
+  // byte p of the block (p < y_end)
   __device__ uint32_t byte_at(uint32_t p) {
     if (p < wy || p >= wy + 256) load_window(p);
-    uint32_t rel = p - wy;
-    uint32_t d = __builtin_amdgcn_readlane(win, rel >> 2);
-    return (d >> ((rel & 3) * 8)) & 0xFFu;
-  }
-
-  __device__ void wait_ring() {
-    while (nrec - rec_free >= RING) {
-      rec_free = min8(ctl.bk);
-      if (nrec - rec_free >= RING) __builtin_amdgcn_s_sleep(1);
-    }
-  }
-
-  // records and coverage for the builders (the record stores were issued
-  // earlier, so they land first)
-  __device__ void publish(uint32_t cov) {
-    lds_set(&ctl.nrec, nrec, lane);
-    lds_set(&ctl.cov, cov, lane);
+    const uint32_t rel = p - wy;
+    return uni((__builtin_amdgcn_readlane(win, rel >> 2) >> ((rel & 3) * 8)) & 0xFFu);
   }
 
   // bytes p .. p + 7 from the window (p >= wy, p + 12 <= wy + 256)
@@ -342,155 +425,273 @@ struct Parser {
     return ((uint64_t)hi << 32) | lo;
   }
 
-  // One sequence of the common shape -- at most two extra length bytes per
-  // length field, well inside the block, window reachable without waiting --
-  // parsed from two 8-byte peeks and written as one finished record.  Returns
-  // false, with the sequence untouched, when any of that does not hold or any
-  // check fails; the general step then parses (and diagnoses) it.
+  // Extra length bytes from q on (each 255 continues the run), added to
+  // len; q ends after the run.  The checks are the byte-serial ones: the
+  // block may not end inside the run, and a length past the chunk fails at
+  // once (which also bounds how far the walk reads ahead inside a run).
+  __device__ int32_t ext_run(uint32_t &q, uint32_t &len) {
+    for (;;) {
+      if (q >= y_end) return C_TRUNC;
+      const uint32_t b = byte_at(q);
+      q = uni(q + 1);
+      len = uni(len + b);
+      if (len > N) return C_OVERRUN;
+      if (b != 255) return C_OK;
+    }
+  }
+
+  // the entry of a finished sequence (announced on its own or not)
+  __device__ void finish(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
+    pend = 0;
+    if (split) emit(0, 0, M, w | W_CONT);
+    else emit(ys, L, M, w);
+  }
+
+  // One sequence of the common shape from two 8-byte peeks: at most two
+  // extra bytes per length field, well inside the block, window reachable
+  // without waiting.  Returns false, with nothing consumed, when that does
+  // not hold; the general step then walks the sequence.  Written with few
+  // branches: this is the decoder's only serial loop.
   __device__ bool fast_step() {
-    if (y < wy || y + 12 > wy + 256 || y + 8 > y_end) return false;
+    // token window: y - wy <= 244 also rules out y < wy (unsigned wrap)
+    if ((y - wy > 244u) | (y + 8 > y_end)) return false;
     const uint64_t q = peek8(y);
     const uint32_t token = (uint32_t)q & 0xFFu;
-    uint32_t L = token >> 4, hdr = 1;
-    if (L == 15) {
-      const uint32_t e1 = (uint32_t)(q >> 8) & 0xFFu, e2 = (uint32_t)(q >> 16) & 0xFFu;
-      if (e1 < 255) {
-        L = 15 + e1;
-        hdr = 2;
-      } else if (e2 < 255) {
-        L = 270 + e2;
-        hdr = 3;
-      } else {
-        return false;
-      }
-    }
-    const uint32_t ys = y + hdr;
-    if (L > N - op || L > y_end - ys || y_end - (ys + L) < 12) return false;
-    const uint32_t ye = ys + L;
-    if (nrec - rec_free >= RING) return false;
-    // the last literal byte, the distance, the match length bytes
-    const uint32_t p = L ? ye - 1 : ye;
-    if (p < wy || p + 12 > wy + 256) {
+    const uint32_t e1 = (uint32_t)(q >> 8) & 0xFFu, e2 = (uint32_t)(q >> 16) & 0xFFu;
+    const bool l15 = token >= 0xF0u;
+    const uint32_t L = l15 ? (e1 < 255 ? 15 + e1 : 270 + e2) : token >> 4;
+    const uint32_t ys = y + (l15 ? (e1 < 255 ? 2u : 3u) : 1u);
+    // at least 12 bytes after the literal run (so not the last sequence)
+    if ((l15 & (e1 == 255) & (e2 == 255)) | (y_end - ys < L + 12)) return false;
+    const uint32_t e = ys + L;
+    // window at the run's last byte: distance and match length bytes follow
+    const uint32_t p = L ? e - 1 : e;
+    if (p - wy > 244u) {
       const uint32_t w2 = p & ~3u;
       const uint32_t upto = w2 + 256 < y_end ? w2 + 256 : y_end;
       if (avail < upto) {
         avail = lds_get(&ctl.in_avail);
-        if (avail < upto) return false;   // the general step announces the literals first
+        if (avail < upto) return false;   // the general step waits
       }
-      wy = w2;
+      wy = uni(w2);
       lds_set(&ctl.need[0], wy, lane);
       win = *(const uint32_t *)(sm.inr + ((wy + 4 * lane) & IMASK));
       wait_lds();
     }
     const uint64_t pq = peek8(p);
+    const uint32_t lastlit = L ? (uint32_t)pq & 0xFFu : 0u;
     const uint64_t mq = pq >> (L ? 8 : 0);
-    const uint32_t dist = (uint32_t)mq & 0xFFFFu;
+    const uint32_t w = ((uint32_t)mq & 0xFFFFu) | (lastlit << 16);
     const uint32_t m1 = (uint32_t)(mq >> 16) & 0xFFu, m2 = (uint32_t)(mq >> 24) & 0xFFu;
-    uint32_t M = (token & 15) + 4, mext = 0;
-    if ((token & 15) == 15) {
-      if (m1 < 255) {
-        M += m1;
-        mext = 1;
-      } else if (m2 < 255) {
-        M += 255 + m2;
-        mext = 2;
-      } else {
-        return false;
+    const bool m15 = (token & 15) == 15;
+    uint32_t M = (token & 15) + 4 + (m15 ? (m1 < 255 ? m1 : 255 + m2) : 0u);
+    uint32_t ny = e + 2 + (m15 ? (m1 < 255 ? 1u : 2u) : 0u);
+    pend = L > 0;
+    split = 0;
+    pend_ys = ys;
+    pend_L = L;
+    if (m15 & (m1 == 255) & (m2 == 255)) {
+      // a longer run of extra bytes, read here byte by byte: the window
+      // has moved past the token, so the sequence cannot be handed back
+      const int32_t st = ext_run(ny, M);
+      if (st != C_OK) {
+        pend = 0;
+        emit(0, 0, (uint32_t)st, W_END);
+        stop = 1;
+        return true;
       }
     }
-    if (dist == 0 || dist > op + L || M > N - op - L) return false;
-    if (L) {
-      fill = (uint32_t)pq & 0xFFu;
-      fill_ok = 1;
-    }
-    uint32_t info = F_MATCH | dist;
-    if (dist == 1 && fill_ok) info |= F_FILL | (fill << 16);
-    if (dist != 1) fill_ok = 0;
-    if (lane == 0) sm.recs[ridx(nrec)] = make_uint4(op, ys, L, info);
-    nrec++;
-    op += L + M;
-    y = ye + 2 + mext;
-    publish(op);
+    finish(ys, L, M, w);
+    y = uni(ny);
     return true;
   }
 
-  // One sequence, byte by byte, with every check.  Returns false when the
-  // block ends (st: C_OK after the literal-only last sequence) or fails.
-  __device__ bool slow_step(int32_t &st) {
-    if (y >= y_end) { st = C_TRUNC; return false; }
-    const uint32_t token = byte_at(y);
-    y++;
-    uint32_t L = token >> 4;
-    if (L == 15) {
-      uint32_t b;
-      do {
-        if (y >= y_end) { st = C_TRUNC; return false; }
-        b = byte_at(y);
-        y++;
-        L += b;
-        // stop as soon as the run cannot fit: this also bounds how far the
-        // parser reads ahead of the builders inside a length field
-        if (L > N - op) { st = C_OVERRUN; return false; }
-      } while (b == 255);
+  // One sequence byte by byte, with the byte-serial checks.  Returns false
+  // when the walk ends: after the literal-only last sequence, at a
+  // structural error (an END entry carries the status), or when the
+  // recorder is gone.
+  __device__ bool slow_step() {
+    int32_t st = C_OK;
+    uint32_t ys = 0, L = 0, M = 0, w = 0, e = 0, token = 0;
+    if (y >= y_end) st = C_TRUNC;
+    if (st == C_OK) {
+      token = byte_at(y);
+      y = uni(y + 1);
+      L = token >> 4;
+      if (L == 15) st = ext_run(y, L);
     }
-    if (L > y_end - y) { st = C_TRUNC; return false; }
-    if (L > N - op) { st = C_OVERRUN; return false; }
-    const uint32_t ye = y + L;
-    // record, phase 1: the literal run
-    if (nrec - rec_free >= RING) wait_ring();
-    const uint32_t k = nrec;
-    if (lane == 0) sm.recs[ridx(k)] = make_uint4(op, y, L, ye == y_end ? F_LAST : 0u);
-    nrec++;
-    if (ye == y_end) {   // literal-only last sequence
-      op += L;
-      y = ye;
+    if (st == C_OK && L > y_end - y) st = C_TRUNC;
+    if (st == C_OK) {
+      ys = y;
+      e = uni(y + L);
+      if (e == y_end) {   // literal-only last sequence
+        emit(ys, L, 0, W_LAST);
+        return false;
+      }
+      if (y_end - e < 2) st = C_TRUNC;
+    }
+    if (st == C_OK) {
+      pend = L > 0;
+      split = 0;
+      pend_ys = ys;
+      pend_L = L;
+      const uint32_t lastlit = L ? byte_at(e - 1) : 0u;
+      const uint32_t d0 = byte_at(e), d1 = byte_at(e + 1);
+      w = d0 | (d1 << 8) | (lastlit << 16);
+      y = uni(e + 2);
+      M = (token & 15) + 4;
+      if ((token & 15) == 15) st = ext_run(y, M);
+    }
+    if (st != C_OK) {
+      pend = 0;
+      emit(0, 0, (uint32_t)st, W_END);
       return false;
     }
-    publish(op + L);
-    if (y_end - ye < 2) { st = C_TRUNC; return false; }
-    // the window at the run's end: last literal byte, distance, match
-    // length bytes, next token
-    const uint32_t wpos = L ? ye - 1 : ye;
-    if (wpos < wy || wpos + 16 > wy + 256) load_window(wpos);
-    if (L) {
-      fill = byte_at(ye - 1);
-      fill_ok = 1;
-    }
-    y = ye;
-    uint32_t dist = byte_at(y);
-    dist |= byte_at(y + 1) << 8;
-    y += 2;
-    if (dist == 0 || dist > op + L) { st = C_BADOFF; return false; }
-    uint32_t M = (token & 15) + 4;
-    if ((token & 15) == 15) {
-      uint32_t b;
-      do {
-        if (y >= y_end) { st = C_TRUNC; return false; }
-        b = byte_at(y);
-        y++;
-        M += b;
-        if (M > N - op - L) { st = C_OVERRUN; return false; }
-      } while (b == 255);
-    }
-    if (M > N - op - L) { st = C_OVERRUN; return false; }
-    // phase 2: the match
-    uint32_t info = F_MATCH | dist;
-    if (dist == 1 && fill_ok) info |= F_FILL | (fill << 16);
-    if (lane == 0) sm.recs[ridx(k)].w = info;
-    if (dist != 1) fill_ok = 0;
-    op += L + M;
-    return true;
+    finish(ys, L, M, w);
+    return stop == 0;
   }
 
-  __device__ int32_t run() {
-    int32_t st = C_OK;
+  __device__ void run() {
     for (;;) {
-      if (fast_step()) continue;
-      if (!slow_step(st)) break;
+      y = uni(y);
+      if (fast_step()) {
+        if (stop) break;
+        continue;
+      }
+      if (!slow_step()) break;
     }
-    if (st == C_OK && op != N) st = C_SIZE;
-    if (st == C_OK) publish(op);   // a failed chunk's builders stop at what was announced before
-    return st;
+    lds_set(&ctl.need[0], 0xFFFFFFFFu, lane);
+  }
+};
+
+// exclusive prefix sum of v over the wave's lanes
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane) {
+  uint32_t x = v;
+#pragma unroll
+  for (uint32_t d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(x, d, 64);
+    if (lane >= d) x += t;
+  }
+  return x - v;
+}
+
+// Wave 1.  Turns chain entries into records, 64 at a time.
+template <class SM>
+struct Recorder {
+  SM &sm;
+  uint32_t dmax;
+  Ctl &ctl;
+  uint32_t lane;
+  uint32_t N;
+  uint32_t taken;       // chain entries processed
+  uint32_t nrec;        // records written
+  uint32_t op;          // decoded bytes described by the records
+  uint32_t rec_free;    // cached: records below this may be overwritten
+  uint32_t fill_ok;     // the last record ends with a known byte (distance-1 run) ...
+  uint32_t fill;        // ... which is this
+  uint32_t pending;     // the last record's match is still to come (a W_CONT entry)
+
+  __device__ int32_t run() {
+    uint32_t avail_entries = 0;
+    for (;;) {
+      // entries to take
+      while (avail_entries == taken) {
+        avail_entries = lds_get(&ctl.wcnt);
+        if (avail_entries != taken) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (pending) {
+        // the match of the last record (announced literal run)
+        const uint4 ent = make_uint4(__builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].x),
+                                     __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].y),
+                                     __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].z),
+                                     __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].w));
+        if (ent.w & W_END) return (int32_t)ent.z;
+        const uint32_t M = ent.z, dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
+        if (dist == 0 || dist > op || dist > dmax) return C_BADOFF;
+        if (M > N - op) return C_OVERRUN;
+        uint32_t info = F_MATCH | dist;
+        if (dist == 1) info |= F_FILL | (lastlit << 16);   // the announced run has literals
+        if (lane == 0) sm.recs[(nrec - 1) % RING].w = info;
+        op += M;
+        fill_ok = dist == 1;
+        fill = lastlit;
+        pending = 0;
+        publish_rec(ctl, nrec, op, lane);
+        taken++;
+        lds_set(&ctl.rcons, taken, lane);
+        continue;
+      }
+      uint32_t n = avail_entries - taken;
+      n = n < 64 ? n : 64;
+      // record ring space
+      while (nrec - rec_free >= RING) {
+        rec_free = min8(ctl.bk);
+        if (nrec - rec_free < RING) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const uint32_t space = RING - (nrec - rec_free);
+      n = n < space ? n : space;
+      uint4 ent = make_uint4(0u, 0u, 0u, W_END);
+      if (lane < n) ent = sm.chain[(taken + lane) % CHAIN];
+      // a batch ends with an announced literal run (its match comes later)
+      const uint64_t lits = __ballot(lane < n && (ent.w & W_LIT) != 0);
+      if (lits) n = (uint32_t)__builtin_ctzll(lits) + 1;
+      const bool act = lane < n;
+      const uint32_t ys = ent.x, L = ent.y, M = ent.z;
+      const bool last = (ent.w & W_LAST) != 0, end = (ent.w & W_END) != 0;
+      const bool lit = (ent.w & W_LIT) != 0;
+      const uint32_t dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
+      // decoded positions
+      const uint32_t len = act && !end ? L + (last || lit ? 0u : M) : 0u;
+      const uint32_t o = op + wave_excl_scan(len, lane);
+      // checks that need the decoded position (the walker did the rest)
+      int32_t err = C_OK;
+      if (act) {
+        if (end) err = (int32_t)M;
+        else if (L > N - o) err = C_OVERRUN;
+        else if (last) err = (o + L == N) ? C_OK : C_SIZE;
+        else if (lit) err = C_OK;
+        else if (dist == 0 || dist > o + L || dist > dmax) err = C_BADOFF;
+        else if (M > N - o - L) err = C_OVERRUN;
+      }
+      const uint64_t bad = __ballot(err != C_OK);
+      const uint32_t f = bad ? (uint32_t)__builtin_ctzll(bad) : n;   // records before the first failure
+      // fill byte of distance-1 runs: the last literal, or the previous
+      // record's fill when this record has no literals
+      const uint32_t pfo = __shfl_up(dist == 1 && L > 0 && !lit ? 1u : 0u, 1, 64);
+      const uint32_t pfb = __shfl_up(lastlit, 1, 64);
+      uint32_t fok, fb;
+      if (L > 0) {
+        fok = 1;
+        fb = lastlit;
+      } else if (lane == 0) {
+        fok = fill_ok;
+        fb = fill;
+      } else {
+        fok = pfo;
+        fb = pfb;
+      }
+      uint32_t info = last ? F_LAST : (lit ? 0u : (F_MATCH | dist));
+      if (!last && !lit && dist == 1 && fok) info |= F_FILL | (fb << 16);
+      if (lane < f) sm.recs[(nrec + lane) % RING] = make_uint4(o, ys, L, info);
+      // state after the records written
+      if (f > 0) {
+        const uint32_t lf = f - 1;
+        const uint32_t l_o = __builtin_amdgcn_readlane(o, lf), l_len = __builtin_amdgcn_readlane(len, lf);
+        const uint32_t l_info = __builtin_amdgcn_readlane(info, lf);
+        op = l_o + l_len;
+        fill_ok = (l_info & F_FILL) ? 1u : 0u;
+        fill = rec_fill(l_info);
+        pending = __builtin_amdgcn_readlane(lit ? 1u : 0u, lf);
+        nrec += f;
+        publish_rec(ctl, nrec, op, lane);
+      }
+      taken += f;
+      if (f < n) return __builtin_amdgcn_readlane((uint32_t)err, f);
+      if (__ballot(act && last)) return C_OK;
+      lds_set(&ctl.rcons, taken, lane);
+    }
   }
 };
 
@@ -499,13 +700,14 @@ struct Parser {
 // Wave 1.  Streams the chunk's 16-byte aligned blocks into the input ring,
 // one 1 KiB segment (one LDS-DMA load per lane) at a time, keeping up to QMAX
 // segments in flight within the ring space that every reader has released.
-__device__ void feeder(Smem &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end) {
+template <class SM>
+__device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end) {
   const uint32_t nblk = (y_end + 15) / 16;
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
   uint32_t issued = 0, landed = 0;
   while (landed < nseg) {
-    // nobody reads input once the parser has stopped and every builder has left
-    if (lds_get_asm(&ctl.nfinished) == (uint32_t)NB && lds_get_asm(&ctl.pstate) != ST_RUN) break;
+    // nobody reads input once the walk has ended and every builder has left
+    if (lds_get_asm(&ctl.nfinished) == (uint32_t)NB && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
     const uint32_t used = min8(ctl.need);
     uint32_t limit = used / SEG + QMAX;
     if (limit > nseg) limit = nseg;
@@ -564,9 +766,10 @@ __device__ __forceinline__ void meta_ready(Meta4 &m, bool has_zp) {
   }
 }
 
-template <int MODE>
-__device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
+template <int MODE, int HLOG>
+__device__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
                            uint32_t t, uint32_t N, const Meta4 &m, bool fast) {
+  constexpr uint32_t HMASK = (1u << HLOG) - 1;
   uint32_t base = t * TILE;
   if constexpr (MODE == MODE_BYTES) {
     uint8_t *out = (uint8_t *)P.out + dst0;
@@ -647,9 +850,10 @@ __device__ void flush_tile(Smem &sm, uint32_t lane, const ChunkParams &P, uint64
 // ------------------------------------------------------------ builders
 
 // Waves 2 .. 2 + NB - 1.  Builder b builds and writes out tiles b, b + NB, ...
-template <int MODE>
+template <int MODE, int HLOG>
 struct Builder {
-  Smem &sm;
+  static constexpr uint32_t HIST = 1u << HLOG, HMASK = HIST - 1, HTILES = HIST / TILE;
+  Smem<HLOG> &sm;
   Ctl &ctl;
   const ChunkParams &P;
   uint64_t dst0;
@@ -665,9 +869,10 @@ struct Builder {
   uint32_t need_pub;   // announced in need[1 + b]
 
   __device__ void refresh() {
-    pst = lds_get(&ctl.pstate);   // read first: if done, cov and nrec below are final
-    cov = lds_get(&ctl.cov);      // before nrec: records up to cov are all counted
-    nrec = lds_get(&ctl.nrec);
+    pst = lds_get(&ctl.pstate);   // read first: if done, the records below are final
+    const uint2 r = read_rec(ctl);
+    nrec = r.x;
+    cov = r.y;
   }
 
   __device__ void need_input(uint32_t upto) {
@@ -721,7 +926,7 @@ struct Builder {
     }
   }
 
-  // wait until records cover [T, Tend); false if the parser stopped short
+  // wait until records cover [T, Tend); false if the records stopped short
   __device__ bool wait_cov(uint32_t T, uint32_t Tend) {
     while (cov < Tend) {
       refresh();
@@ -946,15 +1151,24 @@ struct Builder {
           }
         }
       }
-      // Beyond the first 64 KiB, sources up to 65535 bytes back share this
-      // tile's own ring slot: one pass reads them before its stores, but a
-      // second pass would read this tile's bytes instead.  Sequence by
-      // sequence, every such source lies ahead of the bytes written so far.
-      if (t >= HTILES && extra) hard = true;
-      // tiles before this one that are read, and (for chunks over 64 KiB)
-      // every tile that might still read the ring slot this one overwrites
+      // tiles before this one that are read
       uint32_t need_tiles = hard ? t : (src_need + TILE - 1) / TILE;
-      if (t >= HTILES) need_tiles = t;
+      if (t >= HTILES) {
+        // This tile overwrites the ring slot of tile t - HTILES.  When the
+        // table's distances stay NB tiles short of the ring, only tiles up
+        // to t - NB read that slot, and the builders' order leaves just the
+        // last NB - 1 tiles possibly unfinished.  Otherwise wait for every
+        // earlier tile; and since sources up to a ring length back then
+        // share this tile's own slot, build it sequence by sequence (every
+        // such source lies ahead of the bytes written so far) rather than
+        // in passes that would read their own stores.
+        if (P.dmax + NB * TILE <= HIST) {
+          need_tiles = need_tiles > t - NB + 1 ? need_tiles : t - NB + 1;
+        } else {
+          if (extra) hard = true;
+          need_tiles = t;
+        }
+      }
       if (!wait_done(need_tiles)) break;
       if (hard) {
         tile_exact(T, Tend);
@@ -963,7 +1177,7 @@ struct Builder {
         tile_bulk(T, Tend, rv, m, extra);
       }
       if (fast) meta_ready(cur, P.zp != nullptr);
-      flush_tile<MODE>(sm, lane, P, dst0, t, N, cur, fast);
+      flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
       lds_set(&ctl.next_tile[b], t + NB, lane);
     }
     lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
@@ -975,9 +1189,9 @@ struct Builder {
 
 // -------------------------------------------------------------- kernel
 
-template <int MODE>
+template <int MODE, int HLOG>
 __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem<HLOG> sm;
   __shared__ Ctl ctl;
   const uint32_t i = blockIdx.x;
   const uint32_t tid = threadIdx.x;
@@ -1010,21 +1224,25 @@ __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
     ctl.nrec = 0;
     ctl.cov = 0;
     ctl.pstate = ST_RUN;
+    ctl.wcnt = 0;
+    ctl.rcons = 0;
     ctl.nfinished = 0;
     ctl.status = 0;
   }
   __syncthreads();
 
   if (wave == 0) {
-    Parser Pa{sm, ctl, lane, head, y_end, 0, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0};
-    int32_t st = (y_end == head) ? C_TRUNC : Pa.run();
-    if (lane == 0) ctl.status = st;
-    lds_set(&ctl.need[0], 0xFFFFFFFFu, lane);
-    lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
+    Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0};
+    W.run();
   } else if (wave == 1) {
+    Recorder<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0, 0};
+    const int32_t st = R.run();
+    if (lane == 0) ctl.status = st;
+    lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
+  } else if (wave == 2) {
     feeder(sm, ctl, lane, S, y_end);
   } else {
-    Builder<MODE> B{sm, ctl, P, d0, lane, wave - 2, N, 0, 0, 0, ST_RUN, 0, 0, 0};
+    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave - 3, N, 0, 0, 0, ST_RUN, 0, 0, 0};
     B.run();
   }
   __syncthreads();

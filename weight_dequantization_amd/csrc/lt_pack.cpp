@@ -33,7 +33,7 @@ constexpr uint32_t kMinRun = 4;       // accepted length for distance-1 runs
 constexpr uint32_t kMinMatch = 8;     // accepted length for hashed matches
 constexpr uint32_t kLastLiterals = 5;
 constexpr uint32_t kMatchLimit = 12;  // no match may start in the last 12 bytes
-constexpr uint32_t kMaxDist = 65535;
+constexpr uint32_t kMaxDist = 65535;   // the format's limit; callers may ask for less
 constexpr int kHashBits = 15;
 
 inline uint32_t rd32(const uint8_t *p) {
@@ -69,7 +69,8 @@ struct Writer {
 };
 
 // Compress src[0, n) into out (capacity >= lt_lz4_bound(n)); returns size.
-uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vector<int32_t> &table) {
+uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vector<int32_t> &table,
+                        uint64_t max_dist) {
   Writer w{out, 0};
   if (n < kMatchLimit + 1) {
     w.sequence(src, n, 0, 0);
@@ -92,7 +93,7 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
     uint32_t h = hash32(rd32(src + i));
     int64_t c = table[h];
     table[h] = (int32_t)i;
-    if (c >= 0 && i - (uint64_t)c <= kMaxDist && i - (uint64_t)c > 1 && rd32(src + c) == rd32(src + i)) {
+    if (c >= 0 && i - (uint64_t)c <= max_dist && i - (uint64_t)c > 1 && rd32(src + c) == rd32(src + i)) {
       uint64_t len = 4;
       while (i + len < match_end && src[c + len] == src[i + len]) len++;
       if (len >= kMinMatch && len > best_len) {
@@ -139,8 +140,10 @@ lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed) 
 }
 
 lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
-                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads) {
+                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
+                             uint32_t max_dist) {
   if (!dst_off || !comp_off) return LT_ERR_INVALID_ARG;
+  const uint64_t window = (max_dist == 0 || max_dist > kMaxDist) ? kMaxDist : max_dist;
   if (n_chunks == 0) {
     comp_off[0] = 0;
     return LT_OK;
@@ -161,7 +164,8 @@ lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32
   auto work = [&](int t) {
     std::vector<int32_t> table(1u << kHashBits);
     for (uint32_t i = (uint32_t)t; i < n_chunks; i += (uint32_t)threads)
-      size[i] = compress_block(src + dst_off[i], dst_off[i + 1] - dst_off[i], scratch.data() + slot[i], table);
+      size[i] = compress_block(src + dst_off[i], dst_off[i + 1] - dst_off[i], scratch.data() + slot[i], table,
+                               window);
   };
   std::vector<std::thread> pool;
   for (int t = 1; t < threads; t++) pool.emplace_back(work, t);
