@@ -187,20 +187,39 @@ __device__ __forceinline__ uint32_t lds_get(uint32_t *p) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-__device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t lane) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Counter stores are made by lane 0 alone.  The exec mask is narrowed inside
+// the asm block rather than by a branch on the lane index, so the caller's
+// control flow stays uniform and a serial loop around a store stays a scalar
+// loop (a lane-dependent branch inside it would make the compiler treat the
+// loop's values as per-lane).  One wave's LDS operations complete in order,
+// so a store made here is seen after every LDS store the wave made before it.
+__device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t = 0) {
+  uint64_t sv;
+  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 1\n\tds_write_b32 %1, %2\n\ts_mov_b64 exec, %0"
+               : "=&s"(sv) : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// lane 0 stores a 16-byte entry and then a counter
+__device__ __forceinline__ void lds_set_entry(void *e, u32x4 v, uint32_t *p, uint32_t c) {
+  uint64_t sv;
+  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 1\n\tds_write_b128 %1, %2\n\t"
+               "ds_write_b32 %3, %4\n\ts_mov_b64 exec, %0"
+               : "=&s"(sv) : "v"(lds_addr(e)), "v"(v), "v"(lds_addr(p)), "v"(c) : "memory");
 }
 
 // nrec and cov are written together with one 8-byte store and read with one
 // 8-byte load, so a reader never sees coverage by records it does not count.
-__device__ __forceinline__ void publish_rec(Ctl &c, uint32_t nrec, uint32_t cov, uint32_t lane) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (lane == 0)
-    __hip_atomic_store((uint64_t *)&c.nrec, ((uint64_t)cov << 32) | nrec, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_WORKGROUP);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+__device__ __forceinline__ void publish_rec(Ctl &c, uint32_t nrec, uint32_t cov, uint32_t = 0) {
+  uint64_t sv;
+  const uint64_t v = ((uint64_t)cov << 32) | nrec;
+  asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 1\n\tds_write_b64 %1, %2\n\ts_mov_b64 exec, %0"
+               : "=&s"(sv) : "v"(lds_addr(&c.nrec)), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ uint2 read_rec(Ctl &c) {
@@ -212,10 +231,6 @@ __device__ __forceinline__ uint2 read_rec(Ctl &c) {
 
 // a value every lane holds, stated so the compiler keeps it in a scalar register
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
 
 // Minimum of an 8-entry counter array (16-byte aligned), read at once.  Like
 // every counter access of the feeder wave, it goes through inline asm: that
@@ -235,10 +250,6 @@ __device__ __forceinline__ uint32_t lds_get_asm(const uint32_t *p) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
   return __builtin_amdgcn_readfirstlane(v);
-}
-
-__device__ __forceinline__ void lds_set_asm(uint32_t *p, uint32_t v, uint32_t lane) {
-  if (lane == 0) asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
 }
 
 // ------------------------------------------------------ LDS byte moves
@@ -371,12 +382,8 @@ struct Walker {
     }
     const uint32_t slot = cnt % CHAIN;
     cnt = uni(cnt + 1);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (lane == 0) {   // the entry first, then the count (one wave's LDS writes land in order)
-      sm.chain[slot] = make_uint4(ys, L, M, w);
-      __hip_atomic_store(&ctl.wcnt, cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // the entry first, then the count (one wave's LDS writes land in order)
+    lds_set_entry(&sm.chain[slot], u32x4{ys, L, M, w}, &ctl.wcnt, cnt);
   }
 
   __device__ void need_input(uint32_t upto) {
@@ -725,7 +732,7 @@ __device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32
     }
     wait_vm_le(issued - landed - 1);   // the oldest segment in flight has landed
     landed++;
-    lds_set_asm(&ctl.in_avail, landed * SEG, lane);
+    lds_set(&ctl.in_avail, landed * SEG);
   }
   wait_vm<0>();   // no LDS-DMA write outlives this wave
 }
