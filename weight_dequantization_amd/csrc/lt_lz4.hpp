@@ -366,6 +366,9 @@ struct Walker {
   uint32_t cnt;         // chain entries written
   uint32_t cons;        // cached ctl.rcons: entries the recorder has taken
   uint32_t stop;        // the recorder is gone: the walk ends
+  uint64_t tw;          // bytes y .. y + 7 (when have_tw)
+  uint32_t have_tw;
+  uint32_t pub;         // last position published in need[0] by the fast step
   uint32_t pend;        // the current literal run [pend_ys, + pend_L) is not announced yet
   uint32_t split;       // it was announced on its own (W_LIT)
   uint32_t pend_ys, pend_L;
@@ -454,62 +457,83 @@ struct Walker {
     else emit(ys, L, M, w);
   }
 
-  // One sequence of the common shape from two 8-byte peeks: at most two
-  // extra bytes per length field, well inside the block, window reachable
-  // without waiting.  Returns false, with nothing consumed, when that does
-  // not hold; the general step then walks the sequence.  Written with few
-  // branches: this is the decoder's only serial loop.
+  // Bytes p .. p + 7 (p + 15) of the block, read straight from the input
+  // ring with one unaligned LDS read (the caller checks that they are
+  // present and do not wrap around the ring's end).
+  __device__ uint64_t ring8(uint32_t p) {
+    uint2 v;
+    __builtin_memcpy(&v, sm.inr + (p & IMASK), 8);
+    return ((uint64_t)uni(v.y) << 32) | uni(v.x);
+  }
+  __device__ uint4 ring16(uint32_t p) {
+    uint4 v;
+    __builtin_memcpy(&v, sm.inr + (p & IMASK), 16);
+    return make_uint4(uni(v.x), uni(v.y), uni(v.z), uni(v.w));
+  }
+
+  // Number of 255 bytes that open the 8-byte word x (8 when all are 255).
+  static __device__ uint32_t run255(uint64_t x) {
+    const uint64_t nz = ~x;
+    return nz ? (uint32_t)__builtin_ctzll(nz) / 8 : 8u;
+  }
+
+  // One sequence of the common shape: a literal count whose extra bytes end
+  // within the 8 bytes carried for the token, a match length whose extra
+  // bytes end within 8 bytes of its start, and the literal run's end at
+  // least 16 bytes before the block's end with its bytes already in the
+  // ring.  One 16-byte read from the literal run's last byte on yields that
+  // byte, the distance, the match length's extra bytes and the next token
+  // with the bytes that follow it, so a sequence costs one LDS round trip.
+  // Returns false, with nothing consumed, when the shape does not hold; the
+  // general step then walks the sequence.
   __device__ bool fast_step() {
-    // token window: y - wy <= 244 also rules out y < wy (unsigned wrap)
-    if ((y - wy > 244u) | (y + 8 > y_end)) return false;
-    const uint64_t q = peek8(y);
-    const uint32_t token = (uint32_t)q & 0xFFu;
-    const uint32_t e1 = (uint32_t)(q >> 8) & 0xFFu, e2 = (uint32_t)(q >> 16) & 0xFFu;
-    const bool l15 = token >= 0xF0u;
-    const uint32_t L = l15 ? (e1 < 255 ? 15 + e1 : 270 + e2) : token >> 4;
-    const uint32_t ys = y + (l15 ? (e1 < 255 ? 2u : 3u) : 1u);
-    // at least 12 bytes after the literal run (so not the last sequence)
-    if ((l15 & (e1 == 255) & (e2 == 255)) | (y_end - ys < L + 12)) return false;
-    const uint32_t e = ys + L;
-    // window at the run's last byte: distance and match length bytes follow
-    const uint32_t p = L ? e - 1 : e;
-    if (p - wy > 244u) {
-      const uint32_t w2 = p & ~3u;
-      const uint32_t upto = w2 + 256 < y_end ? w2 + 256 : y_end;
-      if (avail < upto) {
+    if (!have_tw) {
+      if (((y & IMASK) > INR - 8) | (y + 8 > y_end)) return false;
+      if (avail < y + 8) {
         avail = lds_get(&ctl.in_avail);
-        if (avail < upto) return false;   // the general step waits
+        if (avail < y + 8) return false;
       }
-      wy = uni(w2);
-      lds_set(&ctl.need[0], wy, lane);
-      win = *(const uint32_t *)(sm.inr + ((wy + 4 * lane) & IMASK));
-      wait_lds();
+      tw = ring8(y);
+      have_tw = 1;
     }
-    const uint64_t pq = peek8(p);
-    const uint32_t lastlit = L ? (uint32_t)pq & 0xFFu : 0u;
-    const uint64_t mq = pq >> (L ? 8 : 0);
-    const uint32_t w = ((uint32_t)mq & 0xFFFFu) | (lastlit << 16);
-    const uint32_t m1 = (uint32_t)(mq >> 16) & 0xFFu, m2 = (uint32_t)(mq >> 24) & 0xFFu;
-    const bool m15 = (token & 15) == 15;
-    uint32_t M = (token & 15) + 4 + (m15 ? (m1 < 255 ? m1 : 255 + m2) : 0u);
-    uint32_t ny = e + 2 + (m15 ? (m1 < 255 ? 1u : 2u) : 0u);
-    pend = L > 0;
+    // here y + 8 <= y_end and tw holds bytes y .. y + 7
+    const uint32_t token = (uint32_t)tw & 0xFFu;
+    const bool l15 = token >= 0xF0u;
+    const uint32_t nl = run255((tw >> 8) | (0xFFull << 56));   // bytes 1 .. 7
+    if (l15 & (nl >= 7)) return false;
+    const uint32_t L = l15 ? 15 + 255 * nl + ((uint32_t)(tw >> (8 * nl + 8)) & 0xFFu) : token >> 4;
+    const uint32_t ys = y + (l15 ? nl + 2 : 1u);
+    const uint32_t q = ys + L;          // the literal run's end
+    const uint32_t r0 = q - 1;          // read from its last byte on
+    if ((y_end - ys < L + 16) | ((r0 & IMASK) > INR - 16)) return false;
+    if (avail < r0 + 16) {
+      avail = lds_get(&ctl.in_avail);
+      if (avail < r0 + 16) return false;
+    }
+    if (r0 - pub >= SEG) {              // let the feeder reuse what lies behind
+      pub = uni(y);
+      lds_set(&ctl.need[0], pub);
+    }
+    const uint4 r = ring16(r0);         // bytes q - 1 .. q + 14
+    const uint64_t lo = ((uint64_t)r.y << 32) | r.x, hi = ((uint64_t)r.w << 32) | r.z;
+    const uint32_t lastlit = L ? r.x & 0xFFu : 0u;
+    const uint32_t w = ((r.x >> 8) & 0xFFFFu) | (lastlit << 16);
+    const uint32_t mn = token & 15u;
+    const bool m15 = mn == 15;
+    const uint64_t wm = (lo >> 24) | (hi << 40);   // bytes q + 2 .. q + 9
+    const uint32_t nm = run255(wm);
+    if (m15 & (nm >= 8)) return false;
+    const uint32_t mx = m15 ? nm + 1 : 0u;         // the match length's extra bytes
+    const uint32_t M = mn + 4 + (m15 ? 255 * nm + ((uint32_t)(wm >> (8 * nm)) & 0xFFu) : 0u);
+    // the next token sits o = 3 + mx bytes into the read; carry its 8 bytes
+    // when they are all there
+    const uint32_t o = 3 + mx, oc = o <= 7 ? o : 7u;
+    tw = (lo >> (8 * oc)) | (hi << (64 - 8 * oc));
+    have_tw = o <= 7;
+    y = uni(q + 2 + mx);
+    pend = 0;
     split = 0;
-    pend_ys = ys;
-    pend_L = L;
-    if (m15 & (m1 == 255) & (m2 == 255)) {
-      // a longer run of extra bytes, read here byte by byte: the window
-      // has moved past the token, so the sequence cannot be handed back
-      const int32_t st = ext_run(ny, M);
-      if (st != C_OK) {
-        pend = 0;
-        emit(0, 0, (uint32_t)st, W_END);
-        stop = 1;
-        return true;
-      }
-    }
-    finish(ys, L, M, w);
-    y = uni(ny);
+    emit(ys, L, M, w);
     return true;
   }
 
@@ -565,6 +589,7 @@ struct Walker {
         if (stop) break;
         continue;
       }
+      have_tw = 0;
       if (!slow_step()) break;
     }
     lds_set(&ctl.need[0], 0xFFFFFFFFu, lane);
@@ -1239,7 +1264,7 @@ __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
   __syncthreads();
 
   if (wave == 0) {
-    Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0};
+    Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     W.run();
   } else if (wave == 1) {
     Recorder<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0, 0};
