@@ -106,6 +106,12 @@ constexpr int NWAVES = 3 + NB;        // walker, recorder, feeder, builders
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr uint32_t NSLOT = 8;         // counter array length (>= NB + 1)
 constexpr uint32_t BULK_RECS = 16;    // most sequences in a tile built in one pass
+// Poll intervals (s_sleep units of 64 cycles).  Waiting waves share the CU's
+// scalar unit and LDS with the walkers, so they poll no faster than the
+// walk can change what they wait for.
+constexpr int SLEEP_COV = 6;          // builder waiting for records
+constexpr int SLEEP_DONE = 3;         // builder waiting for earlier tiles
+constexpr int SLEEP_FEED = 2;         // feeder waiting for ring space
 constexpr uint32_t LEN_CAP = 1u << 31;
 
 enum : uint32_t { ST_RUN = 0, ST_DONE = 1, ST_FAIL = 2 };
@@ -457,35 +463,192 @@ struct Walker {
     else emit(ys, L, M, w);
   }
 
-  // Bytes p .. p + 7 (p + 15) of the block, read straight from the input
-  // ring with one unaligned LDS read (the caller checks that they are
-  // present and do not wrap around the ring's end).
+  // Bytes p .. p + 7 of the block, read straight from the input ring with
+  // one unaligned LDS read (the caller checks that they are present and do
+  // not wrap around the ring's end).
   __device__ uint64_t ring8(uint32_t p) {
     uint2 v;
     __builtin_memcpy(&v, sm.inr + (p & IMASK), 8);
     return ((uint64_t)uni(v.y) << 32) | uni(v.x);
   }
-  __device__ uint4 ring16(uint32_t p) {
-    uint4 v;
-    __builtin_memcpy(&v, sm.inr + (p & IMASK), 16);
-    return make_uint4(uni(v.x), uni(v.y), uni(v.z), uni(v.w));
+
+  // The common-shape walk, written out in assembly: the compiler's version
+  // of this loop spends most of its instructions on branch and lane-mask
+  // bookkeeping, and the walk is the chunk's only serial work.
+  //
+  // A sequence of the common shape has a literal count whose extra bytes
+  // end within the 8 bytes carried for the token (tw), a match length whose
+  // extra bytes end within 8 bytes of its start, its literal run's end at
+  // least 16 bytes before the block's end, and those 16 bytes already in the
+  // ring.  Per sequence: the literal count from tw (a find-first-set on the
+  // inverted word measures the run of 255-bytes), one 16-byte LDS read from
+  // the literal run's last byte on (that byte, the distance, the match
+  // length's extra bytes, and the next token with the bytes after it), and
+  // the chain entry {literal start, literal count, match length, distance |
+  // last literal << 16}, collected in lane k of four registers and written
+  // to the chain for all collected sequences at once when the loop ends.
+  //
+  // Ends after nmax sequences (st 0), when the next token's eight bytes lie
+  // beyond the read (st 4: tw must be reloaded), when the ring does not
+  // hold the bytes yet (st 2), or at a sequence of another shape (st 1); in
+  // the last two cases that sequence is not consumed.  Every iteration
+  // advances y by at least 3 bytes, and a walk that crosses a KiB since the
+  // last publication publishes y in need[0].
+  __device__ uint32_t fast_run(uint32_t nmax, uint32_t &n) {
+    uint32_t st;
+    asm volatile(
+        "s_mov_b64 s[46:47], %[tw]\n\t"
+        "s_mov_b32 %[n], 0\n\t"
+        "s_mov_b32 %[st], 0\n"
+        "L_top%=:\n\t"
+        // literal count: token nibble, then the run of 255s in bytes 1..7
+        "s_and_b32 s48, s46, 0xff\n\t"
+        "s_lshr_b64 s[40:41], s[46:47], 8\n\t"
+        "s_or_b32 s41, s41, 0xff000000\n\t"
+        "s_not_b64 s[40:41], s[40:41]\n\t"
+        "s_ff1_i32_b64 s49, s[40:41]\n\t"
+        "s_lshr_b32 s49, s49, 3\n\t"
+        "s_cmpk_lt_u32 s48, 0xf0\n\t"
+        "s_cbranch_scc1 L_short%=\n\t"
+        "s_cmp_gt_u32 s49, 6\n\t"
+        "s_cbranch_scc1 L_bail%=\n\t"
+        "s_lshl_b32 s50, s49, 3\n\t"
+        "s_add_u32 s50, s50, 8\n\t"
+        "s_lshr_b64 s[40:41], s[46:47], s50\n\t"
+        "s_and_b32 s40, s40, 0xff\n\t"
+        "s_mul_i32 s51, s49, 0xff\n\t"
+        "s_add_u32 s51, s51, s40\n\t"
+        "s_add_u32 s51, s51, 15\n\t"            // L
+        "s_add_u32 s52, %[y], s49\n\t"
+        "s_add_u32 s52, s52, 2\n"               // literal start
+        "L_lit%=:\n\t"
+        "s_add_u32 s53, s52, s51\n\t"           // q: the literal run's end
+        "s_add_u32 s50, s53, 16\n\t"
+        "s_cmp_gt_u32 s50, %[yend]\n\t"
+        "s_cbranch_scc1 L_bail%=\n\t"
+        "s_sub_u32 s54, s53, 1\n\t"             // read from q - 1
+        "s_and_b32 s50, s54, 0x1fff\n\t"
+        "s_cmpk_gt_u32 s50, 0x1ff0\n\t"         // would wrap around the ring's end
+        "s_cbranch_scc1 L_bail%=\n\t"
+        "s_add_u32 s55, s54, 16\n\t"
+        "s_cmp_gt_u32 s55, %[avail]\n\t"
+        "s_cbranch_scc1 L_avail%=\n\t"
+        "s_add_u32 s50, s50, %[inr]\n\t"
+        "v_mov_b32 v44, s50\n\t"
+        "ds_read_b128 v[40:43], v44\n\t"
+        "s_sub_u32 s55, s54, %[pub]\n\t"
+        "s_cmpk_gt_u32 s55, 0x3ff\n\t"
+        "s_cbranch_scc1 L_pub%=\n"
+        "L_pubd%=:\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_readfirstlane_b32 s42, v40\n\t"
+        "v_readfirstlane_b32 s43, v41\n\t"
+        "v_readfirstlane_b32 s44, v42\n\t"
+        "v_readfirstlane_b32 s45, v43\n\t"
+        // match length: nibble, then the run of 255s in bytes q+2 .. q+9
+        "s_and_b32 s55, s48, 15\n\t"
+        "s_cmp_lg_u32 s55, 15\n\t"
+        "s_cbranch_scc1 L_nom%=\n\t"
+        "s_lshr_b64 s[40:41], s[42:43], 24\n\t"
+        "s_lshl_b32 s50, s44, 8\n\t"
+        "s_or_b32 s41, s41, s50\n\t"
+        "s_not_b64 s[58:59], s[40:41]\n\t"
+        "s_ff1_i32_b64 s49, s[58:59]\n\t"
+        "s_lshr_b32 s49, s49, 3\n\t"
+        "s_cmp_gt_u32 s49, 7\n\t"
+        "s_cbranch_scc1 L_bail%=\n\t"
+        "s_lshl_b32 s50, s49, 3\n\t"
+        "s_lshr_b64 s[58:59], s[40:41], s50\n\t"
+        "s_and_b32 s58, s58, 0xff\n\t"
+        "s_mul_i32 s56, s49, 0xff\n\t"
+        "s_add_u32 s56, s56, s58\n\t"
+        "s_add_u32 s56, s56, 19\n\t"            // M
+        "s_add_u32 s49, s49, 1\n"               // its extra bytes
+        "L_mdone%=:\n\t"
+        // distance | last literal << 16 (no literal: 0)
+        "s_bfe_u32 s57, s42, 0x100008\n\t"
+        "s_and_b32 s50, s42, 0xff\n\t"
+        "s_cmp_eq_u32 s51, 0\n\t"
+        "s_cselect_b32 s50, 0, s50\n\t"
+        "s_lshl_b32 s50, s50, 16\n\t"
+        "s_or_b32 s57, s57, s50\n\t"
+        "s_mov_b32 m0, %[n]\n\t"
+        "v_writelane_b32 v48, s52, m0\n\t"
+        "v_writelane_b32 v49, s51, m0\n\t"
+        "v_writelane_b32 v50, s56, m0\n\t"
+        "v_writelane_b32 v51, s57, m0\n\t"
+        "s_add_u32 %[n], %[n], 1\n\t"
+        // the next token: q + 2 + extra bytes, o = 3 + extra bytes into the read
+        "s_add_u32 %[y], s53, 2\n\t"
+        "s_add_u32 %[y], %[y], s49\n\t"
+        "s_add_u32 s50, s49, 3\n\t"
+        "s_cmp_gt_u32 s50, 7\n\t"
+        "s_cbranch_scc1 L_notw%=\n\t"
+        "s_lshl_b32 s50, s50, 3\n\t"
+        "s_lshr_b64 s[46:47], s[42:43], s50\n\t"
+        "s_sub_u32 s50, 64, s50\n\t"
+        "s_lshl_b64 s[40:41], s[44:45], s50\n\t"
+        "s_or_b64 s[46:47], s[46:47], s[40:41]\n\t"
+        "s_cmp_lt_u32 %[n], %[nmax]\n\t"
+        "s_cbranch_scc1 L_top%=\n\t"
+        "s_branch L_flush%=\n"
+        "L_short%=:\n\t"
+        "s_lshr_b32 s51, s48, 4\n\t"
+        "s_add_u32 s52, %[y], 1\n\t"
+        "s_branch L_lit%=\n"
+        "L_nom%=:\n\t"
+        "s_add_u32 s56, s55, 4\n\t"
+        "s_mov_b32 s49, 0\n\t"
+        "s_branch L_mdone%=\n"
+        "L_pub%=:\n\t"
+        "s_mov_b32 %[pub], %[y]\n\t"
+        "v_mov_b32 v45, %[y]\n\t"
+        "v_mov_b32 v46, %[need0]\n\t"
+        "s_mov_b64 s[58:59], exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "ds_write_b32 v46, v45\n\t"
+        "s_mov_b64 exec, s[58:59]\n\t"
+        "s_branch L_pubd%=\n"
+        "L_notw%=:\n\t"
+        "s_mov_b32 %[st], 4\n\t"
+        "s_branch L_flush%=\n"
+        "L_avail%=:\n\t"
+        "s_mov_b32 %[st], 2\n\t"
+        "s_branch L_flush%=\n"
+        "L_bail%=:\n\t"
+        "s_mov_b32 %[st], 1\n"
+        // entries of lanes 0 .. n-1 to chain slots cnt .. cnt+n-1, then the count
+        "L_flush%=:\n\t"
+        "s_cmp_eq_u32 %[n], 0\n\t"
+        "s_cbranch_scc1 L_end%=\n\t"
+        "v_add_u32 v45, %[cnt], %[vlane]\n\t"
+        "v_and_b32 v45, 31, v45\n\t"
+        "v_lshlrev_b32 v45, 4, v45\n\t"
+        "v_add_u32 v45, %[chain], v45\n\t"
+        "s_add_u32 %[cnt], %[cnt], %[n]\n\t"
+        "v_mov_b32 v46, %[cnt]\n\t"
+        "v_mov_b32 v47, %[wcnt]\n\t"
+        "s_bfm_b64 s[40:41], %[n], 0\n\t"
+        "s_mov_b64 s[58:59], exec\n\t"
+        "s_mov_b64 exec, s[40:41]\n\t"
+        "ds_write_b128 v45, v[48:51]\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "ds_write_b32 v47, v46\n\t"
+        "s_mov_b64 exec, s[58:59]\n"
+        "L_end%=:\n\t"
+        "s_mov_b64 %[tw], s[46:47]"
+        : [y] "+s"(y), [tw] "+s"(tw), [pub] "+s"(pub), [cnt] "+s"(cnt), [n] "=&s"(n), [st] "=&s"(st)
+        : [yend] "s"(y_end), [avail] "s"(avail), [inr] "s"(lds_addr(sm.inr)),
+          [need0] "s"(lds_addr(&ctl.need[0])), [nmax] "s"(nmax), [chain] "s"(lds_addr(sm.chain)),
+          [wcnt] "s"(lds_addr(&ctl.wcnt)), [vlane] "v"(lane)
+        : "s40", "s41", "s42", "s43", "s44", "s45", "s46", "s47", "s48", "s49", "s50", "s51", "s52",
+          "s53", "s54", "s55", "s56", "s57", "s58", "s59", "v40", "v41", "v42", "v43", "v44", "v45",
+          "v46", "v47", "v48", "v49", "v50", "v51", "m0", "scc", "memory");
+    return st;
   }
 
-  // Number of 255 bytes that open the 8-byte word x (8 when all are 255).
-  static __device__ uint32_t run255(uint64_t x) {
-    const uint64_t nz = ~x;
-    return nz ? (uint32_t)__builtin_ctzll(nz) / 8 : 8u;
-  }
-
-  // One sequence of the common shape: a literal count whose extra bytes end
-  // within the 8 bytes carried for the token, a match length whose extra
-  // bytes end within 8 bytes of its start, and the literal run's end at
-  // least 16 bytes before the block's end with its bytes already in the
-  // ring.  One 16-byte read from the literal run's last byte on yields that
-  // byte, the distance, the match length's extra bytes and the next token
-  // with the bytes that follow it, so a sequence costs one LDS round trip.
-  // Returns false, with nothing consumed, when the shape does not hold; the
-  // general step then walks the sequence.
+  // Walks common-shape sequences; false, with nothing consumed, when the
+  // next sequence needs the general step.
   __device__ bool fast_step() {
     if (!have_tw) {
       if (((y & IMASK) > INR - 8) | (y + 8 > y_end)) return false;
@@ -496,44 +659,24 @@ struct Walker {
       tw = ring8(y);
       have_tw = 1;
     }
-    // here y + 8 <= y_end and tw holds bytes y .. y + 7
-    const uint32_t token = (uint32_t)tw & 0xFFu;
-    const bool l15 = token >= 0xF0u;
-    const uint32_t nl = run255((tw >> 8) | (0xFFull << 56));   // bytes 1 .. 7
-    if (l15 & (nl >= 7)) return false;
-    const uint32_t L = l15 ? 15 + 255 * nl + ((uint32_t)(tw >> (8 * nl + 8)) & 0xFFu) : token >> 4;
-    const uint32_t ys = y + (l15 ? nl + 2 : 1u);
-    const uint32_t q = ys + L;          // the literal run's end
-    const uint32_t r0 = q - 1;          // read from its last byte on
-    if ((y_end - ys < L + 16) | ((r0 & IMASK) > INR - 16)) return false;
-    if (avail < r0 + 16) {
+    if (cnt - cons >= CHAIN) {
+      cons = lds_get(&ctl.rcons);
+      if (cnt - cons >= CHAIN) {
+        if (lds_get(&ctl.pstate) != ST_RUN) stop = 1;
+        else __builtin_amdgcn_s_sleep(1);
+        return true;
+      }
+    }
+    const uint32_t room = CHAIN - (cnt - cons);
+    uint32_t n;
+    const uint32_t st = fast_run(room < 4 ? room : 4u, n);
+    if (st == 4) have_tw = 0;
+    if (st == 2) {
+      const uint32_t a = avail;
       avail = lds_get(&ctl.in_avail);
-      if (avail < r0 + 16) return false;
+      return n > 0 || avail != a;
     }
-    if (r0 - pub >= SEG) {              // let the feeder reuse what lies behind
-      pub = uni(y);
-      lds_set(&ctl.need[0], pub);
-    }
-    const uint4 r = ring16(r0);         // bytes q - 1 .. q + 14
-    const uint64_t lo = ((uint64_t)r.y << 32) | r.x, hi = ((uint64_t)r.w << 32) | r.z;
-    const uint32_t lastlit = L ? r.x & 0xFFu : 0u;
-    const uint32_t w = ((r.x >> 8) & 0xFFFFu) | (lastlit << 16);
-    const uint32_t mn = token & 15u;
-    const bool m15 = mn == 15;
-    const uint64_t wm = (lo >> 24) | (hi << 40);   // bytes q + 2 .. q + 9
-    const uint32_t nm = run255(wm);
-    if (m15 & (nm >= 8)) return false;
-    const uint32_t mx = m15 ? nm + 1 : 0u;         // the match length's extra bytes
-    const uint32_t M = mn + 4 + (m15 ? 255 * nm + ((uint32_t)(wm >> (8 * nm)) & 0xFFu) : 0u);
-    // the next token sits o = 3 + mx bytes into the read; carry its 8 bytes
-    // when they are all there
-    const uint32_t o = 3 + mx, oc = o <= 7 ? o : 7u;
-    tw = (lo >> (8 * oc)) | (hi << (64 - 8 * oc));
-    have_tw = o <= 7;
-    y = uni(q + 2 + mx);
-    pend = 0;
-    split = 0;
-    emit(ys, L, M, w);
+    if (st == 1) return n > 0;
     return true;
   }
 
@@ -752,7 +895,7 @@ __device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32
       issued++;
     }
     if (issued == landed) {
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(SLEEP_FEED);
       continue;
     }
     wait_vm_le(issued - landed - 1);   // the oldest segment in flight has landed
@@ -920,7 +1063,7 @@ struct Builder {
       done = min8(ctl.next_tile);
       if (done >= tiles) break;
       if (lds_get(&ctl.pstate) == ST_FAIL) return false;
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(SLEEP_DONE);
     }
     return true;
   }
@@ -970,7 +1113,7 @@ struct Builder {
         find_k(T);
         announce(T);
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(SLEEP_COV);
     }
     return true;
   }
@@ -1144,12 +1287,15 @@ struct Builder {
   __device__ void run() {
     const uint32_t ntiles = (N + TILE - 1) / TILE;
     const bool fast = MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8;
+    // Each tile's scales and zero points are fetched one tile ahead, so their
+    // latency overlaps the build of the tile before.
+    Meta4 nxt{};
+    if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N);
     for (uint32_t t = b; t < ntiles; t += NB) {
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
-      // the tile's scales are fetched first, so their latency overlaps the build
-      Meta4 cur{};
-      if (fast) cur = int4_meta(P, dst0, t, lane, N);
+      Meta4 cur = nxt;
+      if (fast && t + NB < ntiles) nxt = int4_meta(P, dst0, t + NB, lane, N);
       if (!wait_cov(T, Tend)) break;
       find_k(T);
       announce(T);
