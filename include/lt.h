@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 2
+#define LT_ABI_VERSION 3
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -98,6 +98,19 @@ enum {
  *              65535; a compressor that keeps them shorter lets the decoder
  *              keep less history (see LT_SMALL_WINDOW).
  *   reserved   0
+ *   seq_off    DEVICE uint64[n_chunks + 1] or NULL: an optional sequence
+ *              index.  Chunk i's LZ4 sequences start at the block offsets
+ *              seq_pos[seq_off[i] .. seq_off[i+1]), in order (the first is
+ *              0); seq_off is non-decreasing and seq_off[n_chunks] <= n_seq.
+ *   seq_pos    DEVICE uint32[n_seq] or NULL (given exactly when seq_off is).
+ *   n_seq      entries in seq_pos (0 without an index).
+ * The index lets a chunk's sequences be parsed side by side instead of one
+ * after another (lt_index_chunks builds it from the blocks).  It is checked
+ * against the blocks: a listed sequence that does not end where the next
+ * listed one starts, or a block that goes on past its last listed
+ * sequence, makes the chunk fail with LT_CHUNK_BAD_TABLE.  Entries listed
+ * after a block's last sequence are not read.  A chunk with no entries is
+ * decoded without the index.
  * Entries that break these rules make that chunk fail with LT_CHUNK_BAD_TABLE
  * (checked on the device); the struct itself is read only during the call.
  */
@@ -111,6 +124,9 @@ typedef struct lt_chunk_table {
   uint64_t comp_bytes;
   uint32_t max_dist;
   uint32_t reserved;
+  const uint64_t *seq_off;
+  const uint32_t *seq_pos;
+  uint64_t n_seq;
 } lt_chunk_table;
 
 /*
@@ -184,6 +200,22 @@ lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed);
 lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
                              uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
                              uint32_t max_dist);
+
+/*
+ * lt_index_chunks -- HOST.  Builds the sequence index of a chunk table from
+ * its blocks (comp, comp_off as in lt_chunk_table): walks each block's
+ * sequences and lists where each one starts, relative to the block.
+ * seq_off (uint64[n_chunks+1]) always receives the prefix sums of the
+ * per-chunk counts; seq_pos (uint32[seq_cap]) receives the offsets when it
+ * is not NULL.  A block that breaks the format is listed up to the sequence
+ * that breaks it (the device then fails that chunk).  threads <= 0 means one
+ * per host core.  Returns LT_ERR_INVALID_ARG for NULL arrays, a
+ * non-monotone comp_off, or seq_pos given with seq_cap < seq_off[n_chunks]
+ * (seq_off is filled either way, so a first call with seq_pos NULL sizes
+ * the second).
+ */
+lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks,
+                          uint64_t *seq_off, uint32_t *seq_pos, uint64_t seq_cap, int threads);
 
 const char *lt_status_str(lt_status s);
 int lt_abi_version(void);

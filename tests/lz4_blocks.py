@@ -22,3 +22,40 @@ def max_match_distance(blk):
             while True:
                 v = b[y]; y += 1
                 if v != 255: break
+
+
+def sequence_starts(blk):
+    """Offsets of the sequences (tokens) of an LZ4 block, in order; the walk
+    stops after the literal-only last sequence or at the sequence that
+    breaks the format (that one is still listed)."""
+    b = [int(v) for v in blk]
+    n, y, out = len(b), 0, []
+    while y < n:
+        out.append(y)
+        t = b[y]
+        y += 1
+        L = t >> 4
+        if L == 15:
+            while True:
+                if y >= n:
+                    return out
+                v = b[y]
+                y += 1
+                L += v
+                if v != 255:
+                    break
+        if L > n - y:
+            return out
+        y += L
+        if y == n or n - y < 2:
+            return out
+        y += 2
+        if (t & 15) == 15:
+            while True:
+                if y >= n:
+                    return out
+                v = b[y]
+                y += 1
+                if v != 255:
+                    break
+    return out

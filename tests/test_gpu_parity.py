@@ -61,8 +61,8 @@ def statuses(st, n):
     return st[:n].cpu().numpy()
 
 
-def table_from_oracle(ot: O.Table):
-    return lt.ChunkTable.from_host(ot.comp, ot.comp_off, ot.dst_off, DEV)
+def table_from_oracle(ot: O.Table, index=False):
+    return lt.ChunkTable.from_host(ot.comp, ot.comp_off, ot.dst_off, DEV, index=index)
 
 
 # ------------------------------------------------------------ raw dequant
@@ -194,10 +194,14 @@ def _repeats(n, seed, reach):
 @pytest.mark.parametrize("size", [16384 + 16, 65536, 200000, 1 << 20])
 def test_decode_short_window_chunks(size):
     """Tables that declare a window within SMALL_WINDOW decode with a 16 KiB
-    history ring, which chunks over 16 KiB wrap many times."""
+    history ring, which chunks over 16 KiB wrap many times; the builders'
+    wait for earlier tiles follows the declared window."""
     x = _repeats(3 * size + 5, size, lt.SMALL_WINDOW)
     dst = np.array([0, size, 2 * size, 3 * size, 3 * size + 5], np.uint64)
-    table = lt.ChunkTable.build(x, dst, DEV)
+    for win in (lt.PACK_WINDOW, 1, 1024, 7000):
+        t = lt.ChunkTable.build(x, dst, DEV, max_dist=win)
+        _decode_check(t, x, "window %d, chunk %d" % (win, size))
+    table = lt.ChunkTable.build(x, dst, DEV, max_dist=lt.SMALL_WINDOW)
     assert table.max_dist == lt.SMALL_WINDOW
     _decode_check(table, x, "short window, chunk %d" % size)
     # the same blocks declared with any window (64 KiB history) decode alike
@@ -300,6 +304,77 @@ def test_decode_bad_table_entries():
     assert np.all((st == 0) <= (ost == 0))
 
 
+# --------------------------------------------------------- sequence index
+
+def test_index_decodes_oracle_and_generated_streams():
+    """Generator-built and oracle-compressed tables decode the same with the
+    sequence index; packer tables the same without it."""
+    rng = np.random.default_rng(17)
+    for trial in range(4):
+        n = int(rng.integers(1, 200))
+        sizes = list(16 * rng.integers(0, 70000 // 16, n))
+        sizes[-1] = int(rng.integers(0, 70000))
+        t, e = _seq_table(rng.integers(0, 2**62, n), sizes)
+        _decode_check(table_from_oracle(t, index=True), e, "seqgen indexed %d" % trial)
+    a = synth.config4()
+    _decode_check(table_from_oracle(O.compress_table(a.data, a.dst_off), index=True), a.data,
+                  "config4 oracle, indexed")
+    _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV, index=False), a.data, "config4 packer, walked")
+
+
+def _index_case(comp, comp_off, dst_off, data, seq_off, seq_pos, what, bad):
+    n = comp_off.size - 1
+    t = lt.ChunkTable.from_host(comp, comp_off, dst_off, DEV, max_dist=lt.SMALL_WINDOW)
+    t.set_index(seq_off, seq_pos)
+    st = status_tensor(n)
+    out = lt.decode_lz4(t, status=st)
+    s = statuses(st, n)
+    got = out.cpu().numpy()
+    for i in range(n):
+        lo, hi = int(dst_off[i]), int(dst_off[i + 1])
+        if i in bad:
+            assert s[i] != 0, "%s: chunk %d decoded with a wrong index" % (what, i)
+        else:
+            assert s[i] == 0 and np.array_equal(got[lo:hi], data[lo:hi]), "%s: chunk %d" % (what, i)
+
+
+def test_index_that_does_not_match_fails_its_chunk():
+    """A listed position off by one, a sequence missing from or added to the
+    list, a list that stops early, or one that runs past the entries fails
+    that chunk alone; a chunk with no entries is walked without the index."""
+    w = synth.int4_weight(256, 8192, 128, 23)
+    packed = lt.pack_int4(w.codes)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.SMALL_WINDOW)
+    so, sp = lt.index_chunks(comp, comp_off)
+    case = lambda o, p, what, bad: _index_case(comp, comp_off, w.dst_off, packed, o, p, what, bad)
+    case(so, sp, "exact", set())
+    p = sp.copy()
+    p[int(so[1]) + 5] += 1
+    case(so, p, "moved by one", {1})
+    k = int(so[2]) + 7
+    o = so.copy()
+    o[so > k] -= 1
+    case(o, np.delete(sp, k), "one missing", {2})
+    k = int(so[3]) + 3
+    o = so.copy()
+    o[so > k] += 1
+    case(o, np.insert(sp, k + 1, sp[k] + (sp[k + 1] - sp[k]) // 2), "one added", {3})
+    p = sp.copy()
+    p[int(so[4])] = 1
+    case(so, p, "first not at 0", {4})
+    cut = (int(so[6]) - int(so[5])) // 2
+    o = so.copy()
+    o[6:] -= cut
+    case(o, np.delete(sp, np.arange(int(so[6]) - cut, int(so[6]))), "stops early", {5})
+    n7 = int(so[8]) - int(so[7])
+    o = so.copy()
+    o[8:] -= n7
+    case(o, np.delete(sp, np.arange(int(so[7]), int(so[8]))), "no entries", set())
+    o = so.copy()
+    o[-1] += 1
+    case(o, sp, "past the entries", {so.size - 2})
+
+
 # ------------------------------------------------------------ fused paths
 
 def _fused4(table, w, what):
@@ -319,10 +394,12 @@ def test_fused_int4_config1_both_compressors():
 
 
 def test_fused_int4_config3_full():
-    """The benchmark's workload: 8192x28672, group 128, packer streams."""
+    """The benchmark's workload: 8192x28672, group 128, packer streams, with
+    the sequence index (the benchmark's table) and without it."""
     w = synth.config3()
     packed = lt.pack_int4(w.codes)
-    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "config3 packer")
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "config3 packer, indexed")
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV, index=False), w, "config3 packer, walked")
 
 
 def test_fused_int4_config3_oracle_stream():

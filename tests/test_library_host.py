@@ -14,7 +14,7 @@ import pytest
 
 import oracle as O
 import synth
-from lz4_blocks import max_match_distance
+from lz4_blocks import max_match_distance, sequence_starts
 import weight_dequantization_amd as lt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 2
+    assert lt.lib().lt_abi_version() == 3
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -74,6 +74,11 @@ def test_invalid_arguments_rejected_without_gpu():
     t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100, 65536, 0)
     assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
     t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100, 1024, 1)
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
+    # a sequence index needs both arrays
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100, 0, 0, 0x10000, None, 4)
+    assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
+    t = lt._Table(0x10000, 0x10000, 0x10000, 1, 8, 8, 100, 0, 0, None, 0x10000, 4)
     assert L.lt_decode_lz4(C.byref(t), fake, None, None) == lt.LT_ERR_INVALID_ARG
     # empty tables are valid no-ops (no device work)
     t = lt._Table(0, 0, 0, 0, 0, 0, 0)
@@ -150,3 +155,48 @@ def test_packer_honours_declared_window(max_dist):
         assert max_match_distance(blk) <= max_dist
     out, st = O.decode_table(O.Table(comp, comp_off, dst_off))
     assert np.all(st == O.OK) and np.array_equal(out, x)
+
+
+def _index_matches_walk(comp, comp_off):
+    seq_off, seq_pos = lt.index_chunks(comp, comp_off)
+    assert seq_off[0] == 0 and seq_off.size == comp_off.size
+    for i in range(comp_off.size - 1):
+        blk = comp[int(comp_off[i]):int(comp_off[i + 1])]
+        got = seq_pos[int(seq_off[i]):int(seq_off[i + 1])].tolist()
+        assert got == sequence_starts(blk), "chunk %d" % i
+    return seq_off, seq_pos
+
+
+def test_index_chunks_lists_every_sequence():
+    """The host index matches a walk of each block, for the packer's blocks,
+    the oracle compressor's and generated streams with extreme lengths."""
+    w = synth.int4_weight(64, 4096, 128, 5, chunking="mixed")
+    packed = lt.pack_int4(w.codes)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off)
+    _index_matches_walk(comp, comp_off)
+    t = O.compress_table(packed, w.dst_off)
+    _index_matches_walk(t.comp, t.comp_off)
+    streams = [O.seqgen(sd, n)[0] for sd, n in [(1, 0), (2, 15), (3, 300), (4, 70000), (5, 4096)]]
+    comp_off = np.cumsum([0] + [s.size for s in streams]).astype(np.uint64)
+    seq_off, _ = _index_matches_walk(np.concatenate(streams), comp_off)
+    assert seq_off[1] - seq_off[0] == 1          # an empty block is one token
+
+
+def test_index_chunks_malformed_and_args():
+    L = lt.lib()
+    blk = O.seqgen(9, 5000)[0]
+    for cut in (1, 2, blk.size // 2, blk.size - 1):
+        part = blk[:cut]
+        _index_matches_walk(part, np.array([0, cut], np.uint64))
+    seq_off = np.zeros(2, np.uint64)
+    comp_off = np.array([0, blk.size], np.uint64)
+    V = C.c_void_p
+    ptr = lambda a: a.ctypes.data_as(V)
+    assert L.lt_index_chunks(ptr(blk), ptr(comp_off), 1, None, None, 0, 1) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_index_chunks(ptr(blk), ptr(np.array([5, 0], np.uint64)), 1, ptr(seq_off), None, 0, 1) \
+        == lt.LT_ERR_INVALID_ARG
+    assert L.lt_index_chunks(ptr(blk), ptr(comp_off), 1, ptr(seq_off), None, 0, 1) == lt.LT_OK
+    small = np.zeros(1, np.uint32)
+    assert L.lt_index_chunks(ptr(blk), ptr(comp_off), 1, ptr(seq_off), ptr(small), 1, 1) \
+        == lt.LT_ERR_INVALID_ARG
+    assert seq_off[1] > 1                       # sized even when the buffer is short

@@ -15,7 +15,8 @@ Device entry points (asynchronous on torch's current stream):
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
 Host packer (numpy in, numpy out):
     pack_int4(codes) -> packed bytes (low nibble first)
-    compress_chunks(src, dst_off, threads=0) -> (comp, comp_off)
+    compress_chunks(src, dst_off, threads=0, max_dist=0) -> (comp, comp_off)
+    index_chunks(comp, comp_off, threads=0) -> (seq_off, seq_pos)
     ChunkTable.build(src_bytes, dst_off, device) -> table resident on the GPU
 """
 from __future__ import annotations
@@ -33,6 +34,7 @@ LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE = ra
 CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE = range(6)
 MAX_CHUNK_BYTES = 1 << 20
 SMALL_WINDOW = 11264      # LT_SMALL_WINDOW: tables within it decode with a 16 KiB history
+PACK_WINDOW = 4096        # the host packer's default match window (see ChunkTable.build)
 
 
 class LtError(RuntimeError):
@@ -53,7 +55,8 @@ class _Table(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("comp_off", C.c_void_p), ("dst_off", C.c_void_p),
                 ("n_chunks", C.c_uint32), ("max_chunk_bytes", C.c_uint32),
                 ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64),
-                ("max_dist", C.c_uint32), ("reserved", C.c_uint32)]
+                ("max_dist", C.c_uint32), ("reserved", C.c_uint32),
+                ("seq_off", C.c_void_p), ("seq_pos", C.c_void_p), ("n_seq", C.c_uint64)]
 
 
 _L = None
@@ -77,6 +80,7 @@ def _lib():
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
             "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
+            "lt_index_chunks": (i32, [vp, vp, u32, vp, vp, u64, i32]),
             "lt_status_str": (C.c_char_p, [i32]),
             "lt_abi_version": (i32, []),
         }
@@ -129,6 +133,25 @@ def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_
     return comp[:int(comp_off[-1])].copy(), comp_off
 
 
+def index_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0):
+    """The sequence index of a chunk table: (seq_off uint64[n+1], seq_pos
+    uint32[seq_off[-1]]), each chunk's sequence offsets within its block."""
+    comp = np.ascontiguousarray(comp, dtype=np.uint8)
+    comp_off = np.ascontiguousarray(comp_off, dtype=np.uint64)
+    n = comp_off.size - 1
+    seq_off = np.zeros(n + 1, np.uint64)
+    L = _lib()
+    st = L.lt_index_chunks(_np_ptr(comp), _np_ptr(comp_off), n, _np_ptr(seq_off), None, 0, threads)
+    if st != LT_OK:
+        raise LtError(st, "lt_index_chunks")
+    seq_pos = np.zeros(max(int(seq_off[-1]), 1), np.uint32)
+    st = L.lt_index_chunks(_np_ptr(comp), _np_ptr(comp_off), n, _np_ptr(seq_off), _np_ptr(seq_pos),
+                           seq_pos.size, threads)
+    if st != LT_OK:
+        raise LtError(st, "lt_index_chunks")
+    return seq_off, seq_pos[:int(seq_off[-1])]
+
+
 # --------------------------------------------------------------- device side
 
 def _torch():
@@ -157,10 +180,13 @@ class ChunkTable:
     total_bytes: int
     comp_bytes: int
     max_dist: int = 0       # declared largest match distance (0: any)
+    seq_off: object = None  # torch.int64 [n+1] (read as uint64), or None: no sequence index
+    seq_pos: object = None  # torch.int32 [n_seq] (read as uint32)
+    n_seq: int = 0
 
     @classmethod
     def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
-                  max_dist: int = 0):
+                  max_dist: int = 0, index: bool = False):
         torch = _torch()
         comp_off = np.ascontiguousarray(comp_off, np.uint64)
         dst_off = np.ascontiguousarray(dst_off, np.uint64)
@@ -169,27 +195,48 @@ class ChunkTable:
         comp_t = torch.from_numpy(np.ascontiguousarray(comp, np.uint8).copy()).to(device)
         if comp_t.numel() == 0:
             comp_t = torch.zeros(16, dtype=torch.uint8, device=device)
-        return cls(comp_t,
-                   torch.from_numpy(comp_off.view(np.int64).copy()).to(device),
-                   torch.from_numpy(dst_off.view(np.int64).copy()).to(device),
-                   n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
-                   int(comp_off[-1]) if comp_off.size else 0, max_dist)
+        t = cls(comp_t,
+                torch.from_numpy(comp_off.view(np.int64).copy()).to(device),
+                torch.from_numpy(dst_off.view(np.int64).copy()).to(device),
+                n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
+                int(comp_off[-1]) if comp_off.size else 0, max_dist)
+        if index and n > 0:
+            seq_off, seq_pos = index_chunks(comp, comp_off)
+            t.set_index(seq_off, seq_pos, device)
+        return t
+
+    def set_index(self, seq_off: np.ndarray, seq_pos: np.ndarray, device=None):
+        """Attach a sequence index (host arrays, as index_chunks returns)."""
+        torch = _torch()
+        device = device if device is not None else self.comp.device
+        seq_off = np.ascontiguousarray(seq_off, np.uint64)
+        seq_pos = np.ascontiguousarray(seq_pos, np.uint32)
+        self.n_seq = int(seq_pos.size)
+        if seq_pos.size == 0:
+            seq_pos = np.zeros(1, np.uint32)
+        self.seq_off = torch.from_numpy(seq_off.view(np.int64).copy()).to(device)
+        self.seq_pos = torch.from_numpy(seq_pos.view(np.int32).copy()).to(device)
 
     @classmethod
     def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0,
-              max_dist: int = None):
+              max_dist: int = None, index: bool = True):
         """Compress `src` chunk by chunk on the host and upload the table.  By
         default matches stay within SMALL_WINDOW bytes, which the table
-        declares, so the device decoder keeps a short history per chunk."""
+        declares, so the device decoder keeps a short history per chunk, and
+        the table carries the sequence index, so each chunk's sequences are
+        parsed side by side."""
         if max_dist is None:
-            max_dist = SMALL_WINDOW
+            max_dist = PACK_WINDOW
         comp, comp_off = compress_chunks(src, dst_off, threads, max_dist)
-        return cls.from_host(comp, comp_off, dst_off, device, max_dist)
+        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index)
 
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
                       self.n_chunks, self.max_chunk_bytes, self.total_bytes, self.comp_bytes,
-                      self.max_dist, 0)
+                      self.max_dist, 0,
+                      self.seq_off.data_ptr() if self.seq_off is not None else None,
+                      self.seq_pos.data_ptr() if self.seq_pos is not None else None,
+                      self.n_seq if self.seq_off is not None else 0)
 
 
 def _check(st, where):

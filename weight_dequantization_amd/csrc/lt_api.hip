@@ -159,6 +159,9 @@ lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *c
   P.group = group;
   P.group_shift = shift_of(group);
   P.dmax = t->max_dist ? t->max_dist : 65535u;
+  P.seq_off = t->seq_off;
+  P.seq_pos = t->seq_pos;
+  P.n_seq = t->seq_off ? t->n_seq : 0;
   hipStream_t s = (hipStream_t)stream;
   dim3 grid(t->n_chunks), block(lt::NTHREADS);
   // a declared short window lets each chunk keep a 16 KiB history, so more
@@ -181,6 +184,7 @@ bool table_ok(const lt_chunk_table *t) {
   if (!t->comp || !t->comp_off || !t->dst_off) return false;
   if (t->max_chunk_bytes == 0 || t->max_chunk_bytes > LT_MAX_CHUNK_BYTES) return false;
   if (t->max_dist > 65535u || t->reserved != 0) return false;
+  if ((t->seq_off == nullptr) != (t->seq_pos == nullptr)) return false;
   if (t->n_chunks > 0x7FFFFFFFu) return false;
   return true;
 }

@@ -89,10 +89,7 @@
 
 namespace lt {
 
-constexpr uint32_t INR = 1u << 13;    // compressed-input ring
-constexpr uint32_t IMASK = INR - 1;
 constexpr uint32_t SEG = 1024;        // feeder unit: one 16-byte DMA load per lane
-constexpr uint32_t QMAX = INR / SEG;  // segments in flight at most
 constexpr uint32_t TILE = 1024;       // build / write-out unit (bytes of decoded stream)
 // Sequence records in flight (recorder -> builders).  A 1 KiB tile overlaps
 // at most 257 records (every non-final sequence decodes to >= 4 bytes), and
@@ -134,8 +131,14 @@ struct __attribute__((aligned(16))) Ctl {
 
 // The history ring holds 2^HLOG decoded bytes: 64 KiB for any LZ4 block
 // (distances reach 65535), 16 KiB for tables that declare a short window.
+// The compressed-input ring is as large as two workgroups per CU allow with
+// the long history (8 KiB) and twice that with the short one: the longer
+// the ring, the further the feeder's loads run ahead of the builders.
 template <int HLOG>
 struct Smem {
+  static constexpr uint32_t INR = HLOG >= 16 ? 1u << 13 : 1u << 14;
+  static constexpr uint32_t IMASK = INR - 1;
+  static constexpr uint32_t QMAX = INR / SEG;   // segments in flight at most
   uint8_t hist[1u << HLOG];
   uint8_t inr[INR];
   uint4 recs[RING];
@@ -157,6 +160,9 @@ struct ChunkParams {
   uint64_t group;
   uint32_t group_shift;      // log2(group) when group is a power of two, else 64
   uint32_t dmax;             // largest match distance the table allows (65535: any)
+  const uint64_t *seq_off;   // optional sequence index (NULL: none)
+  const uint32_t *seq_pos;
+  uint64_t n_seq;            // entries in seq_pos
 };
 
 // ------------------------------------------------------------ LDS sync
@@ -210,6 +216,15 @@ __device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t = 0) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// lanes 0 .. n-1 (n <= 64) each store 16 bytes at their own address; the
+// exec mask is narrowed inside the asm block, as for lds_set
+__device__ __forceinline__ void lds_store_lanes(uint32_t addr, u32x4 v, uint32_t n) {
+  uint64_t sv, m;
+  asm volatile("s_bfm_b64 %1, %4, 0\n\ts_cmp_eq_u32 %4, 64\n\ts_cselect_b64 %1, -1, %1\n\t"
+               "s_mov_b64 %0, exec\n\ts_mov_b64 exec, %1\n\tds_write_b128 %2, %3\n\ts_mov_b64 exec, %0"
+               : "=&s"(sv), "=&s"(m) : "v"(addr), "v"(v), "s"(n) : "scc", "memory");
+}
 
 // lane 0 stores a 16-byte entry and then a counter
 __device__ __forceinline__ void lds_set_entry(void *e, u32x4 v, uint32_t *p, uint32_t c) {
@@ -360,6 +375,7 @@ constexpr uint32_t W_CONT = 8u << 24;   // ... and, in the next entry, that matc
 // recorder gone (a failed chunk): then the walk stops.
 template <class SM>
 struct Walker {
+  static constexpr uint32_t INR = SM::INR, IMASK = SM::IMASK;
   SM &sm;
   Ctl &ctl;
   uint32_t lane;
@@ -378,6 +394,10 @@ struct Walker {
   uint32_t pend;        // the current literal run [pend_ys, + pend_L) is not announced yet
   uint32_t split;       // it was announced on its own (W_LIT)
   uint32_t pend_ys, pend_L;
+  const uint32_t *ix;   // this chunk's sequence index (block offsets), or NULL
+  uint32_t icnt;        // its entries
+  uint32_t ij;          // the next entry to walk
+  uint32_t head;        // block offset 0 sits at input position head
 
   __device__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
     while (cnt - cons >= CHAIN) {
@@ -527,8 +547,8 @@ struct Walker {
         "s_cmp_gt_u32 s50, %[yend]\n\t"
         "s_cbranch_scc1 L_bail%=\n\t"
         "s_sub_u32 s54, s53, 1\n\t"             // read from q - 1
-        "s_and_b32 s50, s54, 0x1fff\n\t"
-        "s_cmpk_gt_u32 s50, 0x1ff0\n\t"         // would wrap around the ring's end
+        "s_and_b32 s50, s54, %[imask]\n\t"
+        "s_cmp_gt_u32 s50, %[rlast]\n\t"          // would wrap around the ring's end
         "s_cbranch_scc1 L_bail%=\n\t"
         "s_add_u32 s55, s54, 16\n\t"
         "s_cmp_gt_u32 s55, %[avail]\n\t"
@@ -640,7 +660,7 @@ struct Walker {
         : [y] "+s"(y), [tw] "+s"(tw), [pub] "+s"(pub), [cnt] "+s"(cnt), [n] "=&s"(n), [st] "=&s"(st)
         : [yend] "s"(y_end), [avail] "s"(avail), [inr] "s"(lds_addr(sm.inr)),
           [need0] "s"(lds_addr(&ctl.need[0])), [nmax] "s"(nmax), [chain] "s"(lds_addr(sm.chain)),
-          [wcnt] "s"(lds_addr(&ctl.wcnt)), [vlane] "v"(lane)
+          [wcnt] "s"(lds_addr(&ctl.wcnt)), [vlane] "v"(lane), [imask] "s"(IMASK), [rlast] "s"(INR - 16)
         : "s40", "s41", "s42", "s43", "s44", "s45", "s46", "s47", "s48", "s49", "s50", "s51", "s52",
           "s53", "s54", "s55", "s56", "s57", "s58", "s59", "v40", "v41", "v42", "v43", "v44", "v45",
           "v46", "v47", "v48", "v49", "v50", "v51", "m0", "scc", "memory");
@@ -725,15 +745,142 @@ struct Walker {
     return stop == 0;
   }
 
-  __device__ void run() {
+  // first byte != 255 among the low `bytes` bytes of w (== bytes when none)
+  static __device__ uint32_t first_not255(uint32_t w, uint32_t bytes) {
+    const uint32_t nz = ~w & (bytes >= 4 ? 0xFFFFFFFFu : ((1u << (8 * bytes)) - 1));
+    return nz ? (uint32_t)__builtin_ctz(nz) / 8 : bytes;
+  }
+
+  // Up to CHAIN listed sequences side by side, one per lane.  Lane l takes
+  // the sequence listed at entry ij + l, which starts at p and must end
+  // where entry ij + l + 1 starts (pn): it decodes the token and the literal
+  // count from the 16 bytes at p and the distance and match length from the
+  // 16 bytes at the literal run's last byte, all from the input ring.  The
+  // batch stops before the first sequence whose bytes are not all in the
+  // ring yet or whose length fields run past those 16 bytes, and before the
+  // last listed sequence (the general step checks the block's end).  A
+  // sequence that does not end where the next listed one starts means the
+  // index does not describe the block: the chunk fails.  Returns false,
+  // with nothing consumed, when the next sequence needs the general step.
+  __device__ bool index_batch() {
+    if (cnt - cons >= CHAIN) {
+      cons = lds_get(&ctl.rcons);
+      if (cnt - cons >= CHAIN) {
+        if (lds_get(&ctl.pstate) != ST_RUN) stop = 1;
+        else __builtin_amdgcn_s_sleep(1);
+        return true;
+      }
+    }
+    const uint32_t room = CHAIN - (cnt - cons), left = icnt - ij;
+    const uint32_t nmax = room < left - 1 ? room : left - 1;
+    if (nmax == 0) return false;
+    const uint32_t e = ij + (lane < nmax ? lane : nmax - 1);
+    const uint32_t p = head + ix[e], pn = head + ix[e + 1];
+    if (uni(p) != y) return false;                 // reported by the general step
+    const uint32_t hi = pn + 16 < y_end ? pn + 16 : y_end;
+    if (uni(hi) > avail) {
+      // the first sequence's bytes are not all here: wait for them when
+      // they fit well within the ring, else walk it with the general step
+      if (uni(pn) - y + 16 > INR / 2) return false;
+      avail = lds_get(&ctl.in_avail);
+      if (uni(hi) > avail) {
+        pub = y;
+        lds_set(&ctl.need[0], pub);
+        __builtin_amdgcn_s_sleep(1);
+        avail = lds_get(&ctl.in_avail);
+      }
+      return true;
+    }
+    // the token and the literal count's extra bytes
+    const uint4 a = gather16<IMASK>(sm.inr, p);
+    const uint32_t token = a.x & 0xFFu;
+    const bool l15 = token >= 0xF0u;
+    const uint32_t w0 = (a.x >> 8) | (a.y << 24), w1 = (a.y >> 8) | (a.z << 24);
+    const uint32_t w2 = (a.z >> 8) | (a.w << 24), w3 = a.w >> 8;
+    uint32_t nl = first_not255(w0, 4);
+    if (nl == 4) nl = 4 + first_not255(w1, 4);
+    if (nl == 8) nl = 8 + first_not255(w2, 4);
+    if (nl == 12) nl = 12 + first_not255(w3, 3);   // bytes 1 .. 15
+    const uint32_t nlc = nl < 14 ? nl : 14u;
+    const uint32_t lb = (nlc < 4 ? w0 >> (8 * nlc) : nlc < 8 ? w1 >> (8 * (nlc - 4))
+                         : nlc < 12 ? w2 >> (8 * (nlc - 8)) : w3 >> (8 * (nlc - 12))) & 0xFFu;
+    const uint32_t L = l15 ? 15 + 255 * nlc + lb : token >> 4;
+    const uint32_t ys = p + (l15 ? nlc + 2 : 1u);
+    const uint32_t q = ys + L;
+    // the literal run's last byte, the distance and the match length
+    const uint4 b = gather16<IMASK>(sm.inr, q - 1);
+    const uint32_t lastlit = L ? b.x & 0xFFu : 0u;
+    const uint32_t mn = token & 15u;
+    const uint32_t v0 = (b.x >> 24) | (b.y << 8), v1 = (b.y >> 24) | (b.z << 8);
+    const uint32_t v2 = (b.z >> 24) | (b.w << 8);
+    uint32_t nm = first_not255(v0, 4);
+    if (nm == 4) nm = 4 + first_not255(v1, 4);
+    if (nm == 8) nm = 8 + first_not255(v2, 4);   // bytes q + 2 .. q + 13
+    const uint32_t nmc = nm < 11 ? nm : 11u;
+    const uint32_t mb = (nmc < 4 ? v0 >> (8 * nmc) : nmc < 8 ? v1 >> (8 * (nmc - 4)) : v2 >> (8 * (nmc - 8))) & 0xFFu;
+    const bool m15 = mn == 15;
+    const uint32_t M = m15 ? 19 + 255 * nmc + mb : mn + 4;
+    const uint32_t nxt = q + 2 + (m15 ? nmc + 1 : 0u);
+    const bool hard = (l15 && nl > 13) || (m15 && nm > 10);
+    const bool ok = lane < nmax && hi <= avail && !hard;
+    const uint64_t stops = __ballot(!ok);
+    const uint32_t n = stops ? (uint32_t)__builtin_ctzll(stops) : 64u;
+    if (n == 0) return false;
+    const uint64_t bad = __ballot(nxt != pn) & (n >= 64 ? ~0ull : ((1ull << n) - 1));
+    if (bad) {
+      emit(0, 0, (uint32_t)C_TABLE, W_END);
+      stop = 1;
+      return true;
+    }
+    const uint32_t slot = lds_addr(&sm.chain[(cnt + lane) % CHAIN]);
+    lds_store_lanes(slot, u32x4{ys, L, M, ((b.x >> 8) & 0xFFFFu) | (lastlit << 16)}, n);
+    cnt = uni(cnt + n);
+    lds_set(&ctl.wcnt, cnt);
+    ij += n;
+    y = uni(__builtin_amdgcn_readlane(pn, n - 1));
+    if (y - pub >= SEG) {
+      pub = y;
+      lds_set(&ctl.need[0], pub);
+    }
+    return true;
+  }
+
+  // The walk guided by the sequence index: listed sequences in batches,
+  // the others (and the last) with the general step, each checked against
+  // its listed position.
+  __device__ void run_indexed() {
     for (;;) {
-      y = uni(y);
-      if (fast_step()) {
-        if (stop) break;
+      if (ij == icnt) {                 // the block goes on past the index
+        emit(0, 0, (uint32_t)C_TABLE, W_END);
+        return;
+      }
+      if (index_batch()) {
+        if (stop) return;
         continue;
       }
+      if (y != head + ix[ij]) {
+        emit(0, 0, (uint32_t)C_TABLE, W_END);
+        return;
+      }
+      ij++;
       have_tw = 0;
-      if (!slow_step()) break;
+      if (!slow_step()) return;
+    }
+  }
+
+  __device__ void run() {
+    if (icnt) {
+      run_indexed();
+    } else {
+      for (;;) {
+        y = uni(y);
+        if (fast_step()) {
+          if (stop) break;
+          continue;
+        }
+        have_tw = 0;
+        if (!slow_step()) break;
+      }
     }
     lds_set(&ctl.need[0], 0xFFFFFFFFu, lane);
   }
@@ -877,6 +1024,7 @@ struct Recorder {
 // segments in flight within the ring space that every reader has released.
 template <class SM>
 __device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end) {
+  constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
   const uint32_t nblk = (y_end + 15) / 16;
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
   uint32_t issued = 0, landed = 0;
@@ -1028,6 +1176,7 @@ __device__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, 
 template <int MODE, int HLOG>
 struct Builder {
   static constexpr uint32_t HIST = 1u << HLOG, HMASK = HIST - 1, HTILES = HIST / TILE;
+  static constexpr uint32_t IMASK = Smem<HLOG>::IMASK;
   Smem<HLOG> &sm;
   Ctl &ctl;
   const ChunkParams &P;
@@ -1332,16 +1481,18 @@ struct Builder {
       // tiles before this one that are read
       uint32_t need_tiles = hard ? t : (src_need + TILE - 1) / TILE;
       if (t >= HTILES) {
-        // This tile overwrites the ring slot of tile t - HTILES.  When the
-        // table's distances stay NB tiles short of the ring, only tiles up
-        // to t - NB read that slot, and the builders' order leaves just the
-        // last NB - 1 tiles possibly unfinished.  Otherwise wait for every
-        // earlier tile; and since sources up to a ring length back then
-        // share this tile's own slot, build it sequence by sequence (every
-        // such source lies ahead of the bytes written so far) rather than
-        // in passes that would read their own stores.
-        if (P.dmax + NB * TILE <= HIST) {
-          need_tiles = need_tiles > t - NB + 1 ? need_tiles : t - NB + 1;
+        // This tile overwrites the ring slot of tile t - HTILES, whose bytes
+        // only tiles up to t - HTILES + reach read (a match reaches at most
+        // reach tiles back): those must be final first.  When that bound
+        // does not stay short of this tile, wait for every earlier tile;
+        // and since sources up to a ring length back then share this tile's
+        // own slot, build it sequence by sequence (every such source lies
+        // ahead of the bytes written so far) rather than in passes that
+        // would read their own stores.
+        const uint32_t reach = (P.dmax + TILE - 1) / TILE;
+        if (reach < HTILES) {
+          const uint32_t fin = t - HTILES + reach + 1;
+          need_tiles = need_tiles > fin ? need_tiles : fin;
         } else {
           if (extra) hard = true;
           need_tiles = t;
@@ -1368,7 +1519,7 @@ struct Builder {
 // -------------------------------------------------------------- kernel
 
 template <int MODE, int HLOG>
-__global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) chunk_kernel(ChunkParams P) {
   __shared__ __attribute__((aligned(16))) Smem<HLOG> sm;
   __shared__ Ctl ctl;
   const uint32_t i = blockIdx.x;
@@ -1381,6 +1532,12 @@ __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
   bool bad = c0 > c1 || c1 > P.comp_bytes || d0 > d1 || d1 > P.total ||
              (i == 0 && d0 != 0) || (i == P.n - 1 && d1 != P.total) || (d0 & 15) != 0 ||
              d1 - d0 > (uint64_t)P.max_chunk || c1 - c0 > (uint64_t)LEN_CAP;
+  uint64_t s0 = 0, s1 = 0;
+  if (P.seq_off) {
+    s0 = P.seq_off[i];
+    s1 = P.seq_off[i + 1];
+    bad = bad || s0 > s1 || s1 > P.n_seq || s1 - s0 > (uint64_t)LEN_CAP;
+  }
   if (bad) {
     if (tid == 0 && P.status) P.status[i] = C_TABLE;
     return;
@@ -1410,7 +1567,8 @@ __global__ void __launch_bounds__(NTHREADS) chunk_kernel(ChunkParams P) {
   __syncthreads();
 
   if (wave == 0) {
-    Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
+                         P.seq_pos ? P.seq_pos + s0 : nullptr, (uint32_t)(s1 - s0), 0, head};
     W.run();
   } else if (wave == 1) {
     Recorder<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0, 0};

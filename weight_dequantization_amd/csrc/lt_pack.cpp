@@ -125,6 +125,52 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
   return w.pos;
 }
 
+// Calls visit(p) for the offset p of each sequence of the block b[0 .. n),
+// in order.  The walk ends after the literal-only last sequence, or at the
+// sequence that breaks the format (that one is still visited).
+template <class F>
+void walk_block(const uint8_t *b, uint64_t n, F &&visit) {
+  uint64_t p = 0;
+  while (p < n) {
+    visit(p);
+    const uint8_t token = b[p++];
+    uint64_t lit = token >> 4;
+    if (lit == 15) {
+      for (;;) {
+        if (p >= n) return;
+        const uint8_t v = b[p++];
+        lit += v;
+        if (v != 255) break;
+      }
+    }
+    if (lit > n - p) return;
+    p += lit;
+    if (p == n || n - p < 2) return;
+    p += 2;   // the distance
+    if ((token & 15) == 15) {
+      for (;;) {
+        if (p >= n) return;
+        if (b[p++] != 255) break;
+      }
+    }
+  }
+}
+
+// runs fn(i) for i in [0, n) on up to `threads` host threads
+template <class F>
+void parallel_chunks(uint32_t n, int threads, F &&fn) {
+  if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
+  threads = std::min<int>(threads, (int)n);
+  threads = std::min(threads, 256);
+  auto work = [&](int t) {
+    for (uint32_t i = (uint32_t)t; i < n; i += (uint32_t)threads) fn(i);
+  };
+  std::vector<std::thread> pool;
+  for (int t = 1; t < threads; t++) pool.emplace_back(work, t);
+  work(0);
+  for (auto &th : pool) th.join();
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +225,31 @@ lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32
     pos += size[i];
     comp_off[i + 1] = pos;
   }
+  return LT_OK;
+}
+
+lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks,
+                          uint64_t *seq_off, uint32_t *seq_pos, uint64_t seq_cap, int threads) {
+  if (!comp_off || !seq_off) return LT_ERR_INVALID_ARG;
+  seq_off[0] = 0;
+  if (n_chunks == 0) return LT_OK;
+  if (!comp) return LT_ERR_INVALID_ARG;
+  for (uint32_t i = 0; i < n_chunks; i++)
+    if (comp_off[i + 1] < comp_off[i] || comp_off[i + 1] - comp_off[i] > 0xFFFFFFFFull)
+      return LT_ERR_INVALID_ARG;
+  std::vector<uint64_t> count(n_chunks, 0);
+  parallel_chunks(n_chunks, threads, [&](uint32_t i) {
+    uint64_t c = 0;
+    walk_block(comp + comp_off[i], comp_off[i + 1] - comp_off[i], [&](uint64_t) { c++; });
+    count[i] = c;
+  });
+  for (uint32_t i = 0; i < n_chunks; i++) seq_off[i + 1] = seq_off[i] + count[i];
+  if (!seq_pos) return LT_OK;
+  if (seq_cap < seq_off[n_chunks]) return LT_ERR_INVALID_ARG;
+  parallel_chunks(n_chunks, threads, [&](uint32_t i) {
+    uint32_t *out = seq_pos + seq_off[i];
+    walk_block(comp + comp_off[i], comp_off[i + 1] - comp_off[i], [&](uint64_t p) { *out++ = (uint32_t)p; });
+  });
   return LT_OK;
 }
 
