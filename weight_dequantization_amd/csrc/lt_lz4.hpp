@@ -65,6 +65,7 @@
 //                                      they cover, published as one 8-byte word
 //   bk[b]        builder  -> recorder: first record builder b still reads
 //   next_tile[b] builder  -> builders: builder b's tiles below it are final
+//   tile_ctr     builders          : the next tile to take
 //   pstate       recorder -> all     : running / done / failed
 // Every wait is bounded.  The walker consumes at least one input byte per
 // sequence and stops at the chunk's end, at a malformed length, or when the
@@ -97,7 +98,6 @@ constexpr uint32_t TILE = 1024;       // build / write-out unit (bytes of decode
 // builder waits for the tile's coverage, so the ring holds more than 258.
 // (Two workgroups must fit in one CU's LDS, which bounds the rings.)
 constexpr uint32_t RING = 272;
-constexpr uint32_t CHAIN = 32;        // walker -> recorder entries in flight
 constexpr int NB = 5;                 // builder waves
 constexpr int NWAVES = 3 + NB;        // walker, recorder, feeder, builders
 constexpr int NTHREADS = 64 * NWAVES;
@@ -126,6 +126,7 @@ struct __attribute__((aligned(16))) Ctl {
   uint32_t wcnt;              // walker: chain entries written
   uint32_t rcons;             // recorder: chain entries taken
   uint32_t nfinished;         // builders that have left
+  uint32_t tile_ctr;          // builders: the next tile nobody has taken
   int32_t status;
 };
 
@@ -139,6 +140,9 @@ struct Smem {
   static constexpr uint32_t INR = HLOG >= 16 ? 1u << 13 : 1u << 14;
   static constexpr uint32_t IMASK = INR - 1;
   static constexpr uint32_t QMAX = INR / SEG;   // segments in flight at most
+  // walker -> recorder entries in flight (a longer chain lets the indexed
+  // walk hand over bigger batches)
+  static constexpr uint32_t CHAIN = HLOG >= 16 ? 32u : 128u;
   uint8_t hist[1u << HLOG];
   uint8_t inr[INR];
   uint4 recs[RING];
@@ -375,7 +379,7 @@ constexpr uint32_t W_CONT = 8u << 24;   // ... and, in the next entry, that matc
 // recorder gone (a failed chunk): then the walk stops.
 template <class SM>
 struct Walker {
-  static constexpr uint32_t INR = SM::INR, IMASK = SM::IMASK;
+  static constexpr uint32_t INR = SM::INR, IMASK = SM::IMASK, CHAIN = SM::CHAIN;
   SM &sm;
   Ctl &ctl;
   uint32_t lane;
@@ -398,6 +402,8 @@ struct Walker {
   uint32_t icnt;        // its entries
   uint32_t ij;          // the next entry to walk
   uint32_t head;        // block offset 0 sits at input position head
+  uint32_t wbase;       // entries wbase .. wbase + 63 sit in lane order in iw,
+  uint32_t iw, iw2;     // the next 64 in iw2 (loaded one window ahead)
 
   __device__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
     while (cnt - cons >= CHAIN) {
@@ -642,7 +648,7 @@ struct Walker {
         "s_cmp_eq_u32 %[n], 0\n\t"
         "s_cbranch_scc1 L_end%=\n\t"
         "v_add_u32 v45, %[cnt], %[vlane]\n\t"
-        "v_and_b32 v45, 31, v45\n\t"
+        "v_and_b32 v45, %[cmask], v45\n\t"
         "v_lshlrev_b32 v45, 4, v45\n\t"
         "v_add_u32 v45, %[chain], v45\n\t"
         "s_add_u32 %[cnt], %[cnt], %[n]\n\t"
@@ -660,7 +666,8 @@ struct Walker {
         : [y] "+s"(y), [tw] "+s"(tw), [pub] "+s"(pub), [cnt] "+s"(cnt), [n] "=&s"(n), [st] "=&s"(st)
         : [yend] "s"(y_end), [avail] "s"(avail), [inr] "s"(lds_addr(sm.inr)),
           [need0] "s"(lds_addr(&ctl.need[0])), [nmax] "s"(nmax), [chain] "s"(lds_addr(sm.chain)),
-          [wcnt] "s"(lds_addr(&ctl.wcnt)), [vlane] "v"(lane), [imask] "s"(IMASK), [rlast] "s"(INR - 16)
+          [wcnt] "s"(lds_addr(&ctl.wcnt)), [vlane] "v"(lane), [imask] "s"(IMASK), [rlast] "s"(INR - 16),
+          [cmask] "s"(CHAIN - 1)
         : "s40", "s41", "s42", "s43", "s44", "s45", "s46", "s47", "s48", "s49", "s50", "s51", "s52",
           "s53", "s54", "s55", "s56", "s57", "s58", "s59", "v40", "v41", "v42", "v43", "v44", "v45",
           "v46", "v47", "v48", "v49", "v50", "v51", "m0", "scc", "memory");
@@ -751,7 +758,7 @@ struct Walker {
     return nz ? (uint32_t)__builtin_ctz(nz) / 8 : bytes;
   }
 
-  // Up to CHAIN listed sequences side by side, one per lane.  Lane l takes
+  // Up to 64 listed sequences side by side, one per lane.  Lane l takes
   // the sequence listed at entry ij + l, which starts at p and must end
   // where entry ij + l + 1 starts (pn): it decodes the token and the literal
   // count from the 16 bytes at p and the distance and match length from the
@@ -772,12 +779,20 @@ struct Walker {
       }
     }
     const uint32_t room = CHAIN - (cnt - cons), left = icnt - ij;
-    const uint32_t nmax = room < left - 1 ? room : left - 1;
+    uint32_t nmax = room < left - 1 ? room : left - 1;
+    nmax = nmax < 64 ? nmax : 64u;
     if (nmax == 0) return false;
+    while (ij >= wbase + 64) {          // slide the index window
+      iw = iw2;
+      wbase += 64;
+      iw2 = ix[min(wbase + 64 + lane, icnt - 1)];
+    }
     const uint32_t e = ij + (lane < nmax ? lane : nmax - 1);
-    const uint32_t p = head + ix[e], pn = head + ix[e + 1];
+    const uint32_t p = head + entry(e), pn = head + entry(e + 1);
     if (uni(p) != y) return false;                 // reported by the general step
     const uint32_t hi = pn + 16 < y_end ? pn + 16 : y_end;
+    // the cached count may be behind: more may have landed since
+    if (__builtin_amdgcn_readlane(hi, nmax - 1) > avail) avail = lds_get(&ctl.in_avail);
     if (uni(hi) > avail) {
       // the first sequence's bytes are not all here: wait for them when
       // they fit well within the ring, else walk it with the general step
@@ -845,10 +860,21 @@ struct Walker {
     return true;
   }
 
+  // index entry x, for wbase <= x < wbase + 128 (from the two windows)
+  __device__ uint32_t entry(uint32_t x) {
+    const uint32_t d = x - wbase;
+    const uint32_t a = __builtin_amdgcn_ds_bpermute(4 * (d & 63), iw);
+    const uint32_t b = __builtin_amdgcn_ds_bpermute(4 * (d & 63), iw2);
+    return d < 64 ? a : b;
+  }
+
   // The walk guided by the sequence index: listed sequences in batches,
   // the others (and the last) with the general step, each checked against
   // its listed position.
   __device__ void run_indexed() {
+    wbase = 0;
+    iw = ix[min(lane, icnt - 1)];
+    iw2 = ix[min(64 + lane, icnt - 1)];
     for (;;) {
       if (ij == icnt) {                 // the block goes on past the index
         emit(0, 0, (uint32_t)C_TABLE, W_END);
@@ -900,6 +926,7 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane) {
 // Wave 1.  Turns chain entries into records, 64 at a time.
 template <class SM>
 struct Recorder {
+  static constexpr uint32_t CHAIN = SM::CHAIN;
   SM &sm;
   uint32_t dmax;
   Ctl &ctl;
@@ -1433,18 +1460,30 @@ struct Builder {
     }
   }
 
+  // the next untaken tile
+  __device__ uint32_t grab() {
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(&ctl.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+  }
+
   __device__ void run() {
     const uint32_t ntiles = (N + TILE - 1) / TILE;
     const bool fast = MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8;
     // Each tile's scales and zero points are fetched one tile ahead, so their
     // latency overlaps the build of the tile before.
+    // Tiles are taken in increasing order from a shared counter (builder b
+    // starts with tile b), each builder taking its next one when it starts
+    // the current, so a slow tile holds up only the builder that has it.
+    // Every tile below the smallest of the builders' current tiles is final.
     Meta4 nxt{};
     if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N);
-    for (uint32_t t = b; t < ntiles; t += NB) {
+    uint32_t u = grab();
+    for (uint32_t t = b; t < ntiles; t = u, u = grab()) {
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
       Meta4 cur = nxt;
-      if (fast && t + NB < ntiles) nxt = int4_meta(P, dst0, t + NB, lane, N);
+      if (fast && u < ntiles) nxt = int4_meta(P, dst0, u, lane, N);
       if (!wait_cov(T, Tend)) break;
       find_k(T);
       announce(T);
@@ -1455,9 +1494,12 @@ struct Builder {
       const uint32_t m = __builtin_popcountll(__ballot(jr < nrec && rv.x < Tend));
       // classify: one pass possible?  how many passes?  which input and
       // which earlier tiles are read?
+      // (the sources' bound also serves hard tiles when every record of the
+      // tile is in the 64 lanes; otherwise those wait for all earlier tiles)
       bool hard = m > BULK_RECS;
+      const bool seen = m < 64;
       uint32_t extra = 0, src_need = 0, in_end = 0;
-      if (!hard) {
+      if (seen) {
         for (uint32_t i = 0; i < m; i++) {
           const uint32_t x = __builtin_amdgcn_readlane(rv.x, i);
           const uint32_t yy = __builtin_amdgcn_readlane(rv.y, i);
@@ -1479,7 +1521,7 @@ struct Builder {
         }
       }
       // tiles before this one that are read
-      uint32_t need_tiles = hard ? t : (src_need + TILE - 1) / TILE;
+      uint32_t need_tiles = seen ? (src_need + TILE - 1) / TILE : t;
       if (t >= HTILES) {
         // This tile overwrites the ring slot of tile t - HTILES, whose bytes
         // only tiles up to t - HTILES + reach read (a match reaches at most
@@ -1507,7 +1549,7 @@ struct Builder {
       }
       if (fast) meta_ready(cur, P.zp != nullptr);
       flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
-      lds_set(&ctl.next_tile[b], t + NB, lane);
+      lds_set(&ctl.next_tile[b], u, lane);
     }
     lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
     lds_set(&ctl.bk[b], 0xFFFFFFFFu, lane);
@@ -1562,13 +1604,14 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     ctl.wcnt = 0;
     ctl.rcons = 0;
     ctl.nfinished = 0;
+    ctl.tile_ctr = NB;
     ctl.status = 0;
   }
   __syncthreads();
 
   if (wave == 0) {
     Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
-                         P.seq_pos ? P.seq_pos + s0 : nullptr, (uint32_t)(s1 - s0), 0, head};
+                         P.seq_pos ? P.seq_pos + s0 : nullptr, (uint32_t)(s1 - s0), 0, head, 0, 0, 0};
     W.run();
   } else if (wave == 1) {
     Recorder<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0, 0};

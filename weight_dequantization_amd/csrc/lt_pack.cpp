@@ -12,9 +12,11 @@
 //     to 65535), accepted from 8 bytes, so isolated 4-byte coincidences in
 //     near-random code bytes do not split long literal runs.
 // A hashed match is passed over when a run starting at the next byte covers
-// as much (a zero group after a nonzero byte, say): the run costs one more
-// literal byte, but the device decoder builds it without reading earlier
-// output, so the tiles of the decoded stream stay independent.
+// nearly as much (within kRunSlack bytes; a zero group after a nonzero byte,
+// say, which an earlier zero group followed by the same byte would match one
+// byte longer): the run costs a few more bytes, but the device decoder
+// builds it without reading earlier output, so the tiles of the decoded
+// stream stay independent.
 // It keeps the format's end-of-block rules (the last 5 bytes are literals and
 // no match starts within the last 12 bytes), so standard LZ4 block decoders
 // accept its output.
@@ -30,6 +32,7 @@
 namespace {
 
 constexpr uint32_t kMinRun = 4;       // accepted length for distance-1 runs
+constexpr uint32_t kRunSlack = 4;     // a run is preferred to a match at most this much longer
 constexpr uint32_t kMinMatch = 8;     // accepted length for hashed matches
 constexpr uint32_t kLastLiterals = 5;
 constexpr uint32_t kMatchLimit = 12;  // no match may start in the last 12 bytes
@@ -101,13 +104,17 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
         best_dist = i - (uint64_t)c;
       }
     }
-    if (best_dist > 1 && i + 1 + kMatchLimit <= n && src[i + 1] == src[i]) {
-      // A run of src[i] starting at i + 1 that covers as much as the hashed
-      // match (with src[i] as one more literal) is taken instead: a run
-      // decodes without reading earlier output.
-      uint64_t r = 0;
-      while (i + 1 + r < match_end && src[i + 1 + r] == src[i]) r++;
-      if (r >= kMinRun && r + 1 >= best_len) best_len = 0;
+    if (best_dist > 1 && i + 2 + kMatchLimit <= n) {
+      // A run starting at i + 1 (of src[i]) or at i + 2 (of src[i + 1]) that
+      // covers nearly as much as the hashed match, with the bytes before it
+      // as literals, is taken instead: a run decodes without reading earlier
+      // output.
+      for (uint64_t s0 = 1; s0 <= 2 && best_len; s0++) {
+        const uint8_t v = src[i + s0 - 1];
+        uint64_t r = 0;
+        while (i + s0 + r < match_end && src[i + s0 + r] == v) r++;
+        if (r >= kMinRun && r + s0 + kRunSlack >= best_len) best_len = 0;
+      }
     }
     if (best_len) {
       w.sequence(src + anchor, i - anchor, best_dist, best_len);
