@@ -1085,21 +1085,40 @@ __device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32
 struct Meta4 {
   uint32_t s[4];
   uint32_t z[4];
+  uint32_t g0;   // (few groups) the group lane 0 fetched
 };
 
-// scales / zero points of one INT4 tile (fast path: group is a power of two
-// >= 8, so each lane's 8 codes share one group).  The loads are issued here
-// and consumed only after the tile is built (see meta_ready).
+// The groups of INT4 dword k of lane `lane` in tile t (fast path: the group
+// is a power of two >= 8, so each lane's 8 codes share one group).
+__device__ __forceinline__ uint64_t int4_group(const ChunkParams &P, uint64_t dst0, uint32_t t,
+                                               uint32_t lane, uint32_t N, int k) {
+  uint32_t p = t * TILE + 256 * k + 4 * lane;
+  if (p >= N) p = 0;   // any valid group; unused
+  return (2 * (dst0 + p)) >> P.group_shift;
+}
+
+// Scales / zero points of one INT4 tile.  The loads are issued here and
+// consumed only after the tile is built (see meta_ready).  With groups of
+// 128 codes or more a tile spans at most 17 groups: lanes 0 .. 31 then
+// fetch groups g0 .. g0 + 31 with one load each of scale and zero point,
+// and meta_ready hands each lane its four; smaller groups fetch per lane.
 __device__ __forceinline__ Meta4 int4_meta(const ChunkParams &P, uint64_t dst0, uint32_t t,
-                                           uint32_t lane, uint32_t N) {
-  Meta4 m;
+                                           uint32_t lane, uint32_t N, bool few) {
+  Meta4 m{};
   // without zero points, read any valid byte and discard it (no branch)
   const int8_t *zsrc = P.zp ? P.zp : (const int8_t *)P.scales;
+  if (few) {
+    const uint64_t ng = (2 * P.total + (1ull << P.group_shift) - 1) >> P.group_shift;
+    m.g0 = (uint32_t)((2 * (dst0 + (uint64_t)t * TILE)) >> P.group_shift);
+    uint64_t g = (uint64_t)m.g0 + (lane & 31);
+    g = g < ng ? g : ng - 1;
+    m.s[0] = P.scales[g];
+    m.z[0] = (uint32_t)(uint8_t)zsrc[g];
+    return m;
+  }
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    uint32_t p = t * TILE + 256 * k + 4 * lane;
-    if (p >= N) p = 0;   // any valid group; unused
-    uint64_t g = (2 * (dst0 + p)) >> P.group_shift;
+    const uint64_t g = int4_group(P, dst0, t, lane, N, k);
     m.s[k] = P.scales[g];
     m.z[k] = (uint32_t)(int32_t)zsrc[g];
   }
@@ -1108,12 +1127,23 @@ __device__ __forceinline__ Meta4 int4_meta(const ChunkParams &P, uint64_t dst0, 
 
 // Make the tile's scale registers opaque here, so the compiler consumes (and
 // waits for) them at this point instead of right after issuing the loads.
-__device__ __forceinline__ void meta_ready(Meta4 &m, bool has_zp) {
+__device__ __forceinline__ void meta_ready(Meta4 &m, bool has_zp, const ChunkParams &P, uint64_t dst0,
+                                           uint32_t t, uint32_t lane, uint32_t N, bool few) {
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
-    asm volatile("" : "+v"(m.s[k]), "+v"(m.z[k]));
-    if (!has_zp) m.z[k] = 0;
+  for (int k = 0; k < 4; k++) asm volatile("" : "+v"(m.s[k]), "+v"(m.z[k]));
+  if (few) {
+    const uint32_t pk = (m.s[0] & 0xFFFFu) | (m.z[0] << 16);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t i = (uint32_t)int4_group(P, dst0, t, lane, N, k) - m.g0;
+      const uint32_t v = __builtin_amdgcn_ds_bpermute(4 * i, pk);
+      m.s[k] = v & 0xFFFFu;
+      m.z[k] = (uint32_t)(int32_t)(int8_t)(v >> 16);
+    }
   }
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+    if (!has_zp) m.z[k] = 0;
 }
 
 template <int MODE, int HLOG>
@@ -1476,14 +1506,15 @@ struct Builder {
     // starts with tile b), each builder taking its next one when it starts
     // the current, so a slow tile holds up only the builder that has it.
     // Every tile below the smallest of the builders' current tiles is final.
+    const bool few = fast && P.group_shift >= 7;
     Meta4 nxt{};
-    if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N);
+    if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N, few);
     uint32_t u = grab();
     for (uint32_t t = b; t < ntiles; t = u, u = grab()) {
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
       Meta4 cur = nxt;
-      if (fast && u < ntiles) nxt = int4_meta(P, dst0, u, lane, N);
+      if (fast && u < ntiles) nxt = int4_meta(P, dst0, u, lane, N, few);
       if (!wait_cov(T, Tend)) break;
       find_k(T);
       announce(T);
@@ -1500,24 +1531,31 @@ struct Builder {
       const bool seen = m < 64;
       uint32_t extra = 0, src_need = 0, in_end = 0;
       if (seen) {
-        for (uint32_t i = 0; i < m; i++) {
-          const uint32_t x = __builtin_amdgcn_readlane(rv.x, i);
-          const uint32_t yy = __builtin_amdgcn_readlane(rv.y, i);
-          const uint32_t L = __builtin_amdgcn_readlane(rv.z, i);
-          const uint32_t info = __builtin_amdgcn_readlane(rv.w, i);
-          const uint32_t re = __builtin_amdgcn_readlane(rv.x, i + 1);
-          const uint32_t le = x + L;
-          if (le > T) in_end = yy + ((le < Tend ? le : Tend) - x);
-          const uint32_t base = le > T ? le : T;
-          const uint32_t pend = re < Tend ? re : Tend;
-          if (base < pend && !(info & F_FILL)) {
-            const uint32_t dist = rec_dist(info);
-            if (dist < 16 || dist < pend - base) hard = true;   // overlapping copy
-            const uint32_t s_hi = pend - dist;                  // sources end here
-            if (s_hi > T) extra++;                              // reads this tile
-            const uint32_t s_fin = s_hi < T ? s_hi : T;
-            src_need = s_fin > src_need ? s_fin : src_need;
-          }
+        // lane i looks at record i (which ends where record i + 1 starts)
+        const uint32_t re = __shfl_down(rv.x, 1, 64);
+        const bool mine = lane < m;
+        const uint32_t le = rv.x + rv.z;
+        const bool lit = mine && le > T;   // literals in this tile
+        const uint32_t base = le > T ? le : T;
+        const uint32_t pend = re < Tend ? re : Tend;
+        const bool copy = mine && base < pend && !(rv.w & F_FILL);
+        const uint32_t dist = rec_dist(rv.w);
+        const uint32_t s_hi = pend - dist;   // the copy's sources end here
+        if (__ballot(copy && (dist < 16 || dist < pend - base))) hard = true;   // overlapping copy
+        extra = (uint32_t)__builtin_popcountll(__ballot(copy && s_hi > T));        // reads this tile
+        const uint64_t lits = __ballot(lit);
+        if (lits) {   // the last literal run in the tile ends the input it reads
+          const uint32_t li = 63 - __builtin_clzll(lits);
+          const uint32_t e = le < Tend ? le : Tend;
+          in_end = __builtin_amdgcn_readlane(rv.y + (e - rv.x), li);
+        }
+        uint64_t cps = __ballot(copy);
+        const uint32_t s_fin = s_hi < T ? s_hi : T;
+        while (cps) {   // earlier tiles read by copies
+          const uint32_t ci = __builtin_ctzll(cps);
+          cps &= cps - 1;
+          const uint32_t v = __builtin_amdgcn_readlane(s_fin, ci);
+          src_need = v > src_need ? v : src_need;
         }
       }
       // tiles before this one that are read
@@ -1547,7 +1585,7 @@ struct Builder {
         need_input(in_end);
         tile_bulk(T, Tend, rv, m, extra);
       }
-      if (fast) meta_ready(cur, P.zp != nullptr);
+      if (fast) meta_ready(cur, P.zp != nullptr, P, dst0, t, lane, N, few);
       flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
       lds_set(&ctl.next_tile[b], u, lane);
     }
