@@ -69,7 +69,8 @@ enum {
 
 /* Largest decoded chunk the device decoder accepts (bytes).  It bounds a
  * sequence's length-extension run (about size / 255 bytes) so that the
- * decoder's 8 KiB compressed-input ring always holds what is being parsed. */
+ * decoder's compressed-input ring (8 KiB, or 16 KiB for short-window
+ * tables) always holds what is being parsed. */
 #define LT_MAX_CHUNK_BYTES (1u << 20)
 
 /* Tables whose max_dist is at most this (bytes) are decoded with a 16 KiB

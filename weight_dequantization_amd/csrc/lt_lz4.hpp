@@ -3,12 +3,17 @@
 // pipeline through LDS:
 //
 //   wave 0  walker  : the only serial part.  It hops from token to token
-//                     (reading the length nibbles, the 255-run extension
-//                     bytes and the distance from a 16-byte register window)
+//                     (the length nibbles, the 255-run extension bytes and
+//                     the distance, read with one 16-byte LDS load per
+//                     sequence in an assembly loop for the common shapes)
 //                     and appends one raw entry per sequence (where the
-//                     token sits, literal count, match length, distance) to
-//                     a short LDS chain.  It checks nothing it does not need
-//                     to find the next token.
+//                     literals start, literal count, match length, distance)
+//                     to an LDS chain.  It checks nothing it does not need
+//                     to find the next token.  When the table carries a
+//                     sequence index (the input offset of every token), the
+//                     walker instead parses up to 64 listed sequences at once,
+//                     one per lane, and checks that each one ends where the
+//                     index says the next one starts.
 //   wave 1  recorder: takes up to 64 chain entries at a time, one per lane,
 //                     validates them (distance within the decoded prefix and
 //                     the declared window, lengths within the chunk) and
@@ -16,16 +21,17 @@
 //                     wave-wide prefix scan, then publishes them to an LDS
 //                     record ring.
 //   wave 2  feeder  : streams the chunk's compressed bytes from HBM into an
-//                     8 KiB LDS input ring with LDS-DMA loads
-//                     (global_load_lds_dwordx4), several 1 KiB segments in
-//                     flight.
-//   waves 3+ builders: builder b owns the aligned 1 KiB tiles t = b, b + NB,
-//                     b + 2 NB, ... of the decoded stream.  From the records
-//                     it builds its tile in an LDS history ring, all 64
-//                     lanes at once (each lane owns 16 bytes of the tile), and
-//                     then writes the tile out: as bytes (decode-only), or
-//                     unpacked and dequantized to fp16 (fused INT4 / INT8),
-//                     with coalesced 16-byte stores.
+//                     LDS input ring (8 KiB beside the long history, 16 KiB
+//                     beside the short one) with LDS-DMA loads
+//                     (global_load_lds_dwordx4), up to a ring's worth of
+//                     1 KiB segments in flight.
+//   waves 3+ builders: take the aligned 1 KiB tiles of the decoded stream in
+//                     increasing order from a shared counter.  From the
+//                     records a builder builds its tile in an LDS history
+//                     ring, all 64 lanes at once (each lane owns 16 bytes of
+//                     the tile), and then writes the tile out: as bytes
+//                     (decode-only), or unpacked and dequantized to fp16
+//                     (fused INT4 / INT8), with coalesced 16-byte stores.
 //
 // The history ring holds 64 KiB of decoded bytes for any LZ4 block, or
 // 16 KiB when the chunk table declares that no match reaches further back
@@ -64,8 +70,10 @@
 //   nrec, cov    recorder -> builders: records written and the decoded bytes
 //                                      they cover, published as one 8-byte word
 //   bk[b]        builder  -> recorder: first record builder b still reads
-//   next_tile[b] builder  -> builders: builder b's tiles below it are final
-//   tile_ctr     builders          : the next tile to take
+//   next_tile[b] builder  -> builders: the tile builder b holds (all ones
+//                                      once it has left); every tile below
+//                                      the smallest of these is final
+//   tile_ctr     builders          : the next tile nobody has taken
 //   pstate       recorder -> all     : running / done / failed
 // Every wait is bounded.  The walker consumes at least one input byte per
 // sequence and stops at the chunk's end, at a malformed length, or when the
@@ -80,8 +88,9 @@
 // 1/255 of the length) fit in the input ring beside the oldest tile's
 // literals.  A tile overwrites the history slot of the tile one ring length
 // back, so its builder first waits until every tile that may read that slot
-// is final: when the declared window stays NB tiles short of the ring only
-// tiles NB or more places back read it, otherwise any earlier tile may.
+// is final: with a declared window of w bytes (r = ceil(w / 1 KiB) tiles)
+// that stays short of the ring, the tiles up to r places after the old
+// one; otherwise every earlier tile.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1229,7 +1238,8 @@ __device__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, 
 
 // ------------------------------------------------------------ builders
 
-// Waves 2 .. 2 + NB - 1.  Builder b builds and writes out tiles b, b + NB, ...
+// Waves 3 .. 3 + NB - 1.  Builder b starts with tile b and then takes the
+// next untaken tile each time it starts one.
 template <int MODE, int HLOG>
 struct Builder {
   static constexpr uint32_t HIST = 1u << HLOG, HMASK = HIST - 1, HTILES = HIST / TILE;
