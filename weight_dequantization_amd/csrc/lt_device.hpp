@@ -53,6 +53,33 @@ __device__ __forceinline__ uint4 deq8_int4(uint32_t w, h2 c2, h2 s2) {
   return r;
 }
 
+// fp16 bit pattern of the integer k, |k| < 2048: exact.
+__device__ __forceinline__ uint32_t f16_bits_int(int k) {
+  _Float16 v = (_Float16)k;
+  return (uint32_t)__builtin_bit_cast(uint16_t, v);
+}
+
+// 8 INT4 codes -> 4 dwords of fp16 pairs, like deq8_int4, with two VALU
+// operations per pair before the arithmetic.  Byte j of w holds codes 2j
+// (low nibble) and 2j + 1 (high nibble).  One v_perm builds
+// [b_j, 0x64, b_j, 0x54] from w and the magic dword 0x54006400; masking then
+// keeps the low nibble under 0x64, where 0x6400 | c is 1024 + c, and the high
+// nibble at bits 4..7 under 0x54, where 0x5400 | (c << 4) is 64 + c
+// (exponent 2^6, mantissa step 1/16).  So c2 must hold {1024 + zp, 64 + zp};
+// both subtractions are exact.
+__device__ __forceinline__ uint32_t dual_magic(uint32_t w, uint32_t magic, uint32_t sel) {
+  return __builtin_amdgcn_perm(magic, w, sel) & 0xFFF0FF0Fu;
+}
+__device__ __forceinline__ uint4 deq8_int4_dual(uint32_t w, h2 c2, h2 s2) {
+  const uint32_t magic = 0x54006400u;   // pool bytes 5 = 0x64, 7 = 0x54
+  uint4 r;
+  r.x = deq_pair(dual_magic(w, magic, 0x07000500u), c2, s2);
+  r.y = deq_pair(dual_magic(w, magic, 0x07010501u), c2, s2);
+  r.z = deq_pair(dual_magic(w, magic, 0x07020502u), c2, s2);
+  r.w = deq_pair(dual_magic(w, magic, 0x07030503u), c2, s2);
+  return r;
+}
+
 // 4 INT8 codes (one dword, little-endian) -> 2 dwords of fp16 pairs.  Codes
 // are biased to unsigned (q + 128 = q ^ 0x80) so c2 must hold 1024 + 128 + zp.
 __device__ __forceinline__ uint2 deq4_int8(uint32_t w, h2 c2, h2 s2) {

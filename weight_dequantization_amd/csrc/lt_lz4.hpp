@@ -982,9 +982,11 @@ struct Recorder {
       }
       uint32_t n = avail_entries - taken;
       n = n < 64 ? n : 64;
-      // record ring space
+      // record ring space (with every builder gone, bk is all ones and
+      // nothing is read any more)
       while (nrec - rec_free >= RING) {
         rec_free = min8(ctl.bk);
+        if (rec_free == 0xFFFFFFFFu) rec_free = nrec;
         if (nrec - rec_free < RING) break;
         __builtin_amdgcn_s_sleep(1);
       }
@@ -1153,6 +1155,40 @@ __device__ __forceinline__ void meta_ready(Meta4 &m, bool has_zp, const ChunkPar
 #pragma unroll
   for (int k = 0; k < 4; k++)
     if (!has_zp) m.z[k] = 0;
+}
+
+// (few groups) lanes 0 .. 31 turn their group's scale and zero point into
+// the two packed constants of deq8_int4_dual: s[1] = {s, s} and
+// z[1] = {1024 + zp, 64 + zp}.
+__device__ __forceinline__ void meta_pack_few(Meta4 &m, bool has_zp) {
+  asm volatile("" : "+v"(m.s[0]), "+v"(m.z[0]));
+  const int z = has_zp ? (int)(int8_t)m.z[0] : 0;
+  m.s[1] = (m.s[0] & 0xFFFFu) * 0x10001u;
+  m.z[1] = f16_bits_int(1024 + z) | (f16_bits_int(64 + z) << 16);
+}
+
+// Write-out of a whole INT4 tile whose groups hold 128 codes or more (a
+// power of two).  Lane l's dword k holds codes 512 k + 8 l .. + 7 of the
+// tile, one group, whose constants come from lane (group - g0) by
+// ds_bpermute.  Each store instruction writes 1 KiB of contiguous fp16.
+template <int HLOG>
+__device__ __forceinline__ void flush_int4_few(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P,
+                                               uint64_t dst0, uint32_t T, const Meta4 &m) {
+  constexpr uint32_t HMASK = (1u << HLOG) - 1;
+  const uint8_t *src = sm.hist + (T & HMASK) + 4 * lane;   // a tile never wraps the ring
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) w[k] = *(const uint32_t *)(src + 256 * k);
+  const uint64_t e = 2 * (dst0 + T);   // the tile's first code
+  const uint32_t off = (uint32_t)(e & (P.group - 1)) + 8 * lane;
+  uint4 *out = (uint4 *)((uint16_t *)P.out + e) + lane;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const uint32_t i = (off + 512 * k) >> P.group_shift;
+    const h2 c2 = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, m.z[1]));
+    const h2 s2 = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, m.s[1]));
+    out[64 * k] = deq8_int4_dual(w[k], c2, s2);
+  }
 }
 
 template <int MODE, int HLOG>
@@ -1595,8 +1631,13 @@ struct Builder {
         need_input(in_end);
         tile_bulk(T, Tend, rv, m, extra);
       }
-      if (fast) meta_ready(cur, P.zp != nullptr, P, dst0, t, lane, N, few);
-      flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
+      if (few && Tend - T == TILE) {
+        meta_pack_few(cur, P.zp != nullptr);
+        flush_int4_few<HLOG>(sm, lane, P, dst0, T, cur);
+      } else {
+        if (fast) meta_ready(cur, P.zp != nullptr, P, dst0, t, lane, N, few);
+        flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
+      }
       lds_set(&ctl.next_tile[b], u, lane);
     }
     lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
