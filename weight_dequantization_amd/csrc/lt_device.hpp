@@ -67,8 +67,12 @@ __device__ __forceinline__ uint32_t f16_bits_int(int k) {
 // nibble at bits 4..7 under 0x54, where 0x5400 | (c << 4) is 64 + c
 // (exponent 2^6, mantissa step 1/16).  So c2 must hold {1024 + zp, 64 + zp};
 // both subtractions are exact.
+// (the selector goes in a scalar register, so the loop-invariant operands
+// cost one vector register, the magic dword, instead of one per selector)
 __device__ __forceinline__ uint32_t dual_magic(uint32_t w, uint32_t magic, uint32_t sel) {
-  return __builtin_amdgcn_perm(magic, w, sel) & 0xFFF0FF0Fu;
+  uint32_t t;
+  asm("v_perm_b32 %0, %1, %2, %3" : "=v"(t) : "v"(magic), "v"(w), "s"(sel));
+  return t & 0xFFF0FF0Fu;
 }
 __device__ __forceinline__ uint4 deq8_int4_dual(uint32_t w, h2 c2, h2 s2) {
   const uint32_t magic = 0x54006400u;   // pool bytes 5 = 0x64, 7 = 0x54

@@ -1476,8 +1476,72 @@ struct Builder {
 
   // ---- one-pass path
 
+  // One piece of a lane's 16-byte block [P, bend): the bytes that record j's
+  // literal run or match puts at [pos, pe), returned as a 16-byte vector
+  // aligned to P (the bytes before pos and from pe on are not meaningful).
+  // Advances pos to pe, and j past the record when the piece ends it; a lane
+  // already at bend stays put.  rve holds each record's end (the next
+  // record's start).  Block byte q comes from ring index q + delta: the input
+  // ring for literals, the history ring (q - dist) for matches; the 20 bytes
+  // that cover the block are read with one 16-byte and one 4-byte LDS load
+  // unless they wrap around the ring's end.
+  __device__ __forceinline__ uint4 piece(uint4 rv, uint32_t rve, uint32_t P, uint32_t bend, uint32_t inr_at,
+                                         uint32_t hist_at, uint32_t &pos, uint32_t &j) {
+    typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+    const uint32_t j4 = 4 * j;
+    const uint32_t os = __builtin_amdgcn_ds_bpermute(j4, rv.x);
+    const uint32_t src = __builtin_amdgcn_ds_bpermute(j4, rv.y);
+    const uint32_t L = __builtin_amdgcn_ds_bpermute(j4, rv.z);
+    const uint32_t info = __builtin_amdgcn_ds_bpermute(j4, rv.w);
+    const uint32_t re = __builtin_amdgcn_ds_bpermute(j4, rve);
+    const uint32_t le = os + L;
+    const bool lit = pos < le;
+    const uint32_t pe0 = lit ? le : re;
+    const uint32_t pe = pe0 < bend ? pe0 : bend;
+    const uint32_t si = P + (lit ? src - os : 0u - rec_dist(info));
+    const uint32_t mask = lit ? IMASK : HMASK;
+    const uint32_t base = lit ? inr_at : hist_at;
+    const uint32_t idx = si & mask & ~3u;
+    uint32_t d0, d1, d2, d3, d4;
+    if (idx + 20 <= mask + 1) {
+      const u32x4a q = *(const __attribute__((address_space(3))) u32x4a *)(uintptr_t)(base + idx);
+      d0 = q.x;
+      d1 = q.y;
+      d2 = q.z;
+      d3 = q.w;
+      d4 = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + idx + 16);
+    } else {
+      d0 = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + idx);
+      d1 = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + ((idx + 4) & mask));
+      d2 = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + ((idx + 8) & mask));
+      d3 = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + ((idx + 12) & mask));
+      d4 = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + ((idx + 16) & mask));
+    }
+    const uint32_t sh = si & 3u;
+    uint4 v = make_uint4(__builtin_amdgcn_alignbyte(d1, d0, sh), __builtin_amdgcn_alignbyte(d2, d1, sh),
+                         __builtin_amdgcn_alignbyte(d3, d2, sh), __builtin_amdgcn_alignbyte(d4, d3, sh));
+    if (!lit && (info & F_FILL)) {   // a run of the byte the record carries
+      const uint32_t fw = __builtin_amdgcn_perm(0u, info, 0x02020202u);
+      v = make_uint4(fw, fw, fw, fw);
+    }
+    const bool active = pos < bend;
+    j = (active && pe >= re) ? j + 1 : j;
+    pos = active ? pe : pos;
+    return v;
+  }
+
+  // keep the low clamp(s, 0, 32) bits of acc, the rest from v
+  __device__ __forceinline__ static uint32_t keep_low(uint32_t acc, uint32_t v, int s) {
+    int c;
+    asm("v_med3_i32 %0, %1, 0, 32" : "=v"(c) : "v"(s));
+    const uint32_t keep = ~(uint32_t)(~0ull << c);
+    return (acc & keep) | (v & ~keep);
+  }
+
   // Build [T, Tend) from the m records k .. k + m - 1 held in lanes 0 .. m - 1
-  // of rv (lane m holds the end of the last one), in 1 + extra passes.
+  // of rv (lane m holds the end of the last one), in 1 + extra passes.  Each
+  // lane builds its 16 bytes from the pieces that meet them, in order; the
+  // first piece covers the block's first byte.
   __device__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t m, uint32_t extra) {
     const uint32_t P = T + 16 * lane;
     const uint32_t bend = P + 16 < Tend ? P + 16 : Tend;
@@ -1487,47 +1551,18 @@ struct Builder {
       const uint32_t xi = __builtin_amdgcn_readlane(rv.x, i);
       j0 = (xi <= P) ? i : j0;
     }
+    const uint32_t rve = __shfl_down(rv.x, 1, 64);
     const uint32_t inr_at = lds_addr(sm.inr), hist_at = lds_addr(sm.hist);
     for (uint32_t pass = 0; pass <= extra; pass++) {
-      uint4 acc = make_uint4(0u, 0u, 0u, 0u);
       uint32_t pos = P, j = j0;
-      bool active = pos < bend;
-      while (__ballot(active)) {
-        const uint32_t os = __builtin_amdgcn_ds_bpermute(4 * j, rv.x);
-        const uint32_t src = __builtin_amdgcn_ds_bpermute(4 * j, rv.y);
-        const uint32_t L = __builtin_amdgcn_ds_bpermute(4 * j, rv.z);
-        const uint32_t info = __builtin_amdgcn_ds_bpermute(4 * j, rv.w);
-        const uint32_t re = __builtin_amdgcn_ds_bpermute(4 * (j + 1), rv.x);
-        if (active) {
-          const uint32_t le = os + L;
-          const bool lit = pos < le;
-          const uint32_t pe0 = lit ? le : re;
-          const uint32_t pe = pe0 < bend ? pe0 : bend;
-          // block byte q comes from ring index q + delta: the input ring for
-          // literals, the history ring (q - dist) for matches
-          const uint32_t base = lit ? inr_at : hist_at;
-          const uint32_t mask = lit ? IMASK : HMASK;
-          const uint32_t si = P + (lit ? src - os : 0u - rec_dist(info));
-          const uint32_t a = si & ~3u, sh = si & 3u;
-          uint32_t d[5];
-#pragma unroll
-          for (int q = 0; q < 5; q++)
-            d[q] = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(base + ((a + 4 * q) & mask));
-          uint4 v = make_uint4(__builtin_amdgcn_alignbyte(d[1], d[0], sh), __builtin_amdgcn_alignbyte(d[2], d[1], sh),
-                               __builtin_amdgcn_alignbyte(d[3], d[2], sh), __builtin_amdgcn_alignbyte(d[4], d[3], sh));
-          if (!lit && (info & F_FILL)) {
-            const uint32_t fw = rec_fill(info) * 0x01010101u;
-            v = make_uint4(fw, fw, fw, fw);
-          }
-          const int lo = (int)(pos - P);
-          acc.x = merge_from(acc.x, v.x, lo);
-          acc.y = merge_from(acc.y, v.y, lo - 4);
-          acc.z = merge_from(acc.z, v.z, lo - 8);
-          acc.w = merge_from(acc.w, v.w, lo - 12);
-          pos = pe;
-          if (pe >= re) j++;
-          active = pos < bend;
-        }
+      uint4 acc = piece(rv, rve, P, bend, inr_at, hist_at, pos, j);
+      while (__ballot(pos < bend)) {
+        const int c8 = (int)(8 * (pos - P));   // bytes before pos are kept
+        const uint4 v = piece(rv, rve, P, bend, inr_at, hist_at, pos, j);
+        acc.x = keep_low(acc.x, v.x, c8);
+        acc.y = keep_low(acc.y, v.y, c8 - 32);
+        acc.z = keep_low(acc.z, v.z, c8 - 64);
+        acc.w = keep_low(acc.w, v.w, c8 - 96);
       }
       // the last block of a chunk's last tile is stored only up to the end:
       // its ring slot beyond holds bytes that a later pass may still read
