@@ -167,13 +167,16 @@ lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *c
   // a declared short window lets each chunk keep a 16 KiB history, so more
   // chunks share a CU
   const bool small = P.dmax <= LT_SMALL_WINDOW;
+  if (mode == lt::MODE_INT4 && P.group_shift < 64 && group >= 128) mode = lt::MODE_INT4G;
   switch (mode * 2 + (small ? 1 : 0)) {
     case 0: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 16>), grid, block, 0, s, P); break;
     case 1: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 14>), grid, block, 0, s, P); break;
     case 2: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 16>), grid, block, 0, s, P); break;
     case 3: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 14>), grid, block, 0, s, P); break;
     case 4: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 16>), grid, block, 0, s, P); break;
-    default: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
+    case 5: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
+    case 6: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 16>), grid, block, 0, s, P); break;
+    default: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
   }
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }

@@ -122,7 +122,10 @@ constexpr uint32_t LEN_CAP = 1u << 31;
 
 enum : uint32_t { ST_RUN = 0, ST_DONE = 1, ST_FAIL = 2 };
 enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5 };
-enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2 };
+// MODE_INT4G is MODE_INT4 for groups that are a power of two of at least
+// 128 codes, where a tile spans at most 17 groups (its own kernel, with a
+// leaner scale / zero-point fetch).
+enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2, MODE_INT4G = 3 };
 
 struct __attribute__((aligned(16))) Ctl {
   uint32_t need[NSLOT];       // first input byte still read: [0] walker, [1 + b] builder b
@@ -359,6 +362,12 @@ constexpr uint32_t F_FILL = 2u << 24;   // distance 1 and bits 16..23 hold the b
 constexpr uint32_t F_LAST = 4u << 24;   // literal-only last sequence
 
 __device__ __forceinline__ uint32_t ridx(uint32_t j) { return j % RING; }
+// ring slot of record base + lane for a wave-uniform base: the modulo is
+// taken once on the scalar unit, the lane offset wraps at most once
+__device__ __forceinline__ uint32_t ridx_lane(uint32_t base, uint32_t lane) {
+  const uint32_t r = __builtin_amdgcn_readfirstlane(base % RING) + lane;
+  return r >= RING ? r - RING : r;
+}
 __device__ __forceinline__ uint32_t rec_dist(uint32_t info) { return info & 0xFFFFu; }
 __device__ __forceinline__ uint32_t rec_fill(uint32_t info) { return (info >> 16) & 0xFFu; }
 
@@ -1034,7 +1043,7 @@ struct Recorder {
       }
       uint32_t info = last ? F_LAST : (lit ? 0u : (F_MATCH | dist));
       if (!last && !lit && dist == 1 && fok) info |= F_FILL | (fb << 16);
-      if (lane < f) sm.recs[(nrec + lane) % RING] = make_uint4(o, ys, L, info);
+      if (lane < f) sm.recs[ridx_lane(nrec, lane)] = make_uint4(o, ys, L, info);
       // state after the records written
       if (f > 0) {
         const uint32_t lf = f - 1;
@@ -1157,6 +1166,25 @@ __device__ __forceinline__ void meta_ready(Meta4 &m, bool has_zp, const ChunkPar
     if (!has_zp) m.z[k] = 0;
 }
 
+// MODE_INT4G: lanes 0 .. 31 fetch the scale and zero point of groups
+// g0 .. g0 + 31 of tile t (the last valid group repeats past the end), from
+// a tile-uniform base and a per-lane offset.
+struct MetaG {
+  uint32_t s, z;
+};
+__device__ __forceinline__ MetaG int4g_meta(const ChunkParams &P, uint64_t dst0, uint32_t t, uint32_t lane31,
+                                            uint64_t ng) {
+  const uint64_t g0 = (2 * (dst0 + (uint64_t)t * TILE)) >> P.group_shift;
+  const uint64_t left = ng - g0;   // >= 1
+  const uint32_t li = lane31 < left ? lane31 : (uint32_t)left - 1;
+  // without zero points, read any valid byte and discard it (no branch)
+  const int8_t *zsrc = (P.zp ? P.zp : (const int8_t *)P.scales) + g0;
+  MetaG m;
+  m.s = P.scales[g0 + li];
+  m.z = (uint32_t)(uint8_t)zsrc[li];
+  return m;
+}
+
 // (few groups) lanes 0 .. 31 turn their group's scale and zero point into
 // the two packed constants of deq8_int4_dual: s[1] = {s, s} and
 // z[1] = {1024 + zp, 64 + zp}.
@@ -1211,7 +1239,7 @@ __device__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, 
         }
       }
     }
-  } else if constexpr (MODE == MODE_INT4) {
+  } else if constexpr (MODE == MODE_INT4 || MODE == MODE_INT4G) {
     uint16_t *out = (uint16_t *)P.out;
     const uint64_t G = P.group;
     uint32_t w[4];
@@ -1290,13 +1318,11 @@ struct Builder {
   uint32_t k;          // first record that may overlap the current tile (announced in bk[b])
   uint32_t nrec;       // cached ctl.nrec
   uint32_t cov;        // cached ctl.cov
-  uint32_t pst;        // cached ctl.pstate
   uint32_t avail;      // cached ctl.in_avail
   uint32_t done;       // cached: tiles below this are final
   uint32_t need_pub;   // announced in need[1 + b]
 
   __device__ void refresh() {
-    pst = lds_get(&ctl.pstate);   // read first: if done, the records below are final
     const uint2 r = read_rec(ctl);
     nrec = r.x;
     cov = r.y;
@@ -1327,7 +1353,7 @@ struct Builder {
     uint32_t kk = k;
     for (;;) {   // records from k on are protected by bk[b] <= k
       const uint32_t j = kk + lane;
-      const uint32_t x = (j < nrec) ? sm.recs[ridx(j)].x : 0xFFFFFFFFu;
+      const uint32_t x = (j < nrec) ? sm.recs[ridx_lane(kk, lane)].x : 0xFFFFFFFFu;
       const uint64_t bal = __ballot(x <= T);   // lanes 0 .. h
       const uint32_t h = 63 - __builtin_clzll(bal | 1ull);
       kk += h;
@@ -1353,12 +1379,37 @@ struct Builder {
     }
   }
 
-  // wait until records cover [T, Tend); false if the records stopped short
+  // announce() for record k already read: {start, input position, literal count}
+  __device__ void announce_rec(uint32_t T, uint32_t os, uint32_t src, uint32_t L) {
+    uint32_t off = T > os ? T - os : 0u;
+    off = off < L ? off : L;
+    const uint32_t nd = src + off;
+    if (nd > need_pub) {
+      need_pub = nd;
+      lds_set(&ctl.need[1 + b], nd, lane);
+    }
+  }
+
+  // the next untaken tile: the atomic is issued here and its result read by
+  // grab_take, so its latency overlaps the work in between
+  __device__ uint32_t grab_issue() {
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(&ctl.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return v;
+  }
+  __device__ uint32_t grab_take(uint32_t v) { return __builtin_amdgcn_readlane(v, 0); }
+
+  // wait until records cover [T, Tend); false if the records stopped short.
+  // The recorder publishes its final state after its last records, so
+  // records read after a final state has been seen are final.
   __device__ bool wait_cov(uint32_t T, uint32_t Tend) {
     while (cov < Tend) {
       refresh();
       if (cov >= Tend) break;
-      if (pst != ST_RUN) return false;
+      if (lds_get(&ctl.pstate) != ST_RUN) {
+        refresh();
+        return cov >= Tend;
+      }
       // move past the records that end before T (nrec may be newer than
       // cov, so the search looks at the records' starts, not at cov)
       if (nrec > 0) {
@@ -1539,10 +1590,11 @@ struct Builder {
   }
 
   // Build [T, Tend) from the m records k .. k + m - 1 held in lanes 0 .. m - 1
-  // of rv (lane m holds the end of the last one), in 1 + extra passes.  Each
+  // of rv (lane m holds the end of the last one; rve holds each record's end,
+  // the start of the next), in 1 + extra passes.  Each
   // lane builds its 16 bytes from the pieces that meet them, in order; the
   // first piece covers the block's first byte.
-  __device__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t m, uint32_t extra) {
+  __device__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t rve, uint32_t m, uint32_t extra) {
     const uint32_t P = T + 16 * lane;
     const uint32_t bend = P + 16 < Tend ? P + 16 : Tend;
     // the record under the block's first byte
@@ -1551,7 +1603,6 @@ struct Builder {
       const uint32_t xi = __builtin_amdgcn_readlane(rv.x, i);
       j0 = (xi <= P) ? i : j0;
     }
-    const uint32_t rve = __shfl_down(rv.x, 1, 64);
     const uint32_t inr_at = lds_addr(sm.inr), hist_at = lds_addr(sm.hist);
     for (uint32_t pass = 0; pass <= extra; pass++) {
       uint32_t pos = P, j = j0;
@@ -1571,16 +1622,10 @@ struct Builder {
     }
   }
 
-  // the next untaken tile
-  __device__ uint32_t grab() {
-    uint32_t v = 0;
-    if (lane == 0) v = __hip_atomic_fetch_add(&ctl.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return __builtin_amdgcn_readfirstlane(v);
-  }
-
   __device__ void run() {
     const uint32_t ntiles = (N + TILE - 1) / TILE;
-    const bool fast = MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8;
+    constexpr bool G = MODE == MODE_INT4G;
+    const bool fast = G || (MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8);
     // Each tile's scales and zero points are fetched one tile ahead, so their
     // latency overlaps the build of the tile before.
     // Tiles are taken in increasing order from a shared counter (builder b
@@ -1588,21 +1633,33 @@ struct Builder {
     // the current, so a slow tile holds up only the builder that has it.
     // Every tile below the smallest of the builders' current tiles is final.
     const bool few = fast && P.group_shift >= 7;
+    const uint32_t lane31 = lane & 31u;
+    const uint64_t ng = G ? (2 * P.total + P.group - 1) >> P.group_shift : 0;
     Meta4 nxt{};
-    if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N, few);
-    uint32_t u = grab();
-    for (uint32_t t = b; t < ntiles; t = u, u = grab()) {
+    MetaG nxg{};
+    if constexpr (G) {
+      if (b < ntiles) nxg = int4g_meta(P, dst0, b, lane31, ng);
+    } else {
+      if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N, few);
+    }
+    uint32_t u;
+    for (uint32_t t = b; t < ntiles; t = u) {
+      const uint32_t uv = grab_issue();
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
       Meta4 cur = nxt;
-      if (fast && u < ntiles) nxt = int4_meta(P, dst0, u, lane, N, few);
+      MetaG cug = nxg;
       if (!wait_cov(T, Tend)) break;
       find_k(T);
-      announce(T);
-      // records k .. k + 63 in lanes; missing ones read as {cov, 0, 0, 0}
+      // records k .. k + 63 in lanes, missing ones read as {cov, 0, 0, 0};
+      // lane i also reads where record k + i ends (the next one's start)
       const uint32_t jr = k + lane;
       uint4 rv = make_uint4(cov, 0u, 0u, 0u);
-      if (jr < nrec) rv = sm.recs[ridx(jr)];
+      uint32_t re = cov;
+      if (jr < nrec) rv = sm.recs[ridx_lane(k, lane)];
+      if (jr + 1 < nrec) re = sm.recs[ridx_lane(k + 1, lane)].x;
+      announce_rec(T, __builtin_amdgcn_readfirstlane(rv.x), __builtin_amdgcn_readfirstlane(rv.y),
+                   __builtin_amdgcn_readfirstlane(rv.z));
       const uint32_t m = __builtin_popcountll(__ballot(jr < nrec && rv.x < Tend));
       // classify: one pass possible?  how many passes?  which input and
       // which earlier tiles are read?
@@ -1611,9 +1668,7 @@ struct Builder {
       bool hard = m > BULK_RECS;
       const bool seen = m < 64;
       uint32_t extra = 0, src_need = 0, in_end = 0;
-      if (seen) {
-        // lane i looks at record i (which ends where record i + 1 starts)
-        const uint32_t re = __shfl_down(rv.x, 1, 64);
+      if (seen) {   // lane i looks at record i
         const bool mine = lane < m;
         const uint32_t le = rv.x + rv.z;
         const bool lit = mine && le > T;   // literals in this tile
@@ -1638,6 +1693,12 @@ struct Builder {
           const uint32_t v = __builtin_amdgcn_readlane(s_fin, ci);
           src_need = v > src_need ? v : src_need;
         }
+      }
+      u = grab_take(uv);
+      if constexpr (G) {
+        if (u < ntiles) nxg = int4g_meta(P, dst0, u, lane31, ng);
+      } else {
+        if (fast && u < ntiles) nxt = int4_meta(P, dst0, u, lane, N, few);
       }
       // tiles before this one that are read
       uint32_t need_tiles = seen ? (src_need + TILE - 1) / TILE : t;
@@ -1664,7 +1725,12 @@ struct Builder {
         tile_exact(T, Tend);
       } else {
         need_input(in_end);
-        tile_bulk(T, Tend, rv, m, extra);
+        tile_bulk(T, Tend, rv, re, m, extra);
+      }
+      if constexpr (G) {
+        cur.s[0] = cug.s;
+        cur.z[0] = cug.z;
+        cur.g0 = (uint32_t)((2 * (dst0 + T)) >> P.group_shift);
       }
       if (few && Tend - T == TILE) {
         meta_pack_few(cur, P.zp != nullptr);
@@ -1745,7 +1811,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   } else if (wave == 2) {
     feeder(sm, ctl, lane, S, y_end);
   } else {
-    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave - 3, N, 0, 0, 0, ST_RUN, 0, 0, 0};
+    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave - 3, N, 0, 0, 0, 0, 0, 0};
     B.run();
   }
   __syncthreads();
