@@ -931,14 +931,25 @@ struct Walker {
 };
 
 // exclusive prefix sum of v over the wave's lanes
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane) {
+// with DPP moves (no LDS traffic): inclusive sums within each 16-lane row
+// by shifts of 1, 2, 4 and 8 lanes (lanes shifted in from outside the row
+// read 0), then row 0's total added to row 1 and row 2's to row 3 (row
+// broadcast of lane 15), then rows 0..1's total added to rows 2 and 3 (row
+// broadcast of lane 31)
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t) {
   uint32_t x = v;
-#pragma unroll
-  for (uint32_t d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(x, d, 64);
-    if (lane >= d) x += t;
-  }
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x - v;
+}
+
+// the value of the lane below (lane 0 reads 0), by a DPP wave shift
+__device__ __forceinline__ uint32_t lane_below(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x138, 0xF, 0xF, true);   // wave_shr:1
 }
 
 // Wave 1.  Turns chain entries into records, 64 at a time.
@@ -1028,8 +1039,8 @@ struct Recorder {
       const uint32_t f = bad ? (uint32_t)__builtin_ctzll(bad) : n;   // records before the first failure
       // fill byte of distance-1 runs: the last literal, or the previous
       // record's fill when this record has no literals
-      const uint32_t pfo = __shfl_up(dist == 1 && L > 0 && !lit ? 1u : 0u, 1, 64);
-      const uint32_t pfb = __shfl_up(lastlit, 1, 64);
+      const uint32_t pfo = lane_below(dist == 1 && L > 0 && !lit ? 1u : 0u);
+      const uint32_t pfb = lane_below(lastlit);
       uint32_t fok, fb;
       if (L > 0) {
         fok = 1;
