@@ -389,6 +389,139 @@ constexpr uint32_t W_END = 2u << 24;    // the walk stopped here; the status is 
 constexpr uint32_t W_LIT = 4u << 24;    // a literal run whose match is still being read ...
 constexpr uint32_t W_CONT = 8u << 24;   // ... and, in the next entry, that match (M, distance)
 
+// exclusive prefix sum of v over the wave's lanes
+// with DPP moves (no LDS traffic): inclusive sums within each 16-lane row
+// by shifts of 1, 2, 4 and 8 lanes (lanes shifted in from outside the row
+// read 0), then row 0's total added to row 1 and row 2's to row 3 (row
+// broadcast of lane 15), then rows 0..1's total added to rows 2 and 3 (row
+// broadcast of lane 31)
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t) {
+  uint32_t x = v;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x - v;
+}
+
+// the value of the lane below (lane 0 reads 0), by a DPP wave shift
+__device__ __forceinline__ uint32_t lane_below(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x138, 0xF, 0xF, true);   // wave_shr:1
+}
+
+// Turns sequence entries into records: the recorder wave's work on entries
+// from the chain, and the walker's own when the chunk has a sequence index
+// (entries in registers, entry i in lane i).
+template <class SM>
+struct Rec {
+  SM &sm;
+  uint32_t dmax;
+  Ctl &ctl;
+  uint32_t lane;
+  uint32_t N;
+  uint32_t nrec;        // records written
+  uint32_t op;          // decoded bytes described by the records
+  uint32_t rec_free;    // cached: records below this may be overwritten
+  uint32_t fill_ok;     // the last record ends with a known byte (distance-1 run) ...
+  uint32_t fill;        // ... which is this
+  uint32_t pending;     // the last record's match is still to come (a W_CONT entry)
+
+  // the entry after an announced literal run (ent wave-uniform): its match,
+  // or the end of the walk.  Returns the chunk's final status, or -1.
+  __device__ int32_t cont(uint4 ent) {
+    if (ent.w & W_END) return (int32_t)ent.z;
+    const uint32_t M = ent.z, dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
+    if (dist == 0 || dist > op || dist > dmax) return C_BADOFF;
+    if (M > N - op) return C_OVERRUN;
+    uint32_t info = F_MATCH | dist;
+    if (dist == 1) info |= F_FILL | (lastlit << 16);   // the announced run has literals
+    if (lane == 0) sm.recs[(nrec - 1) % RING].w = info;
+    op += M;
+    fill_ok = dist == 1;
+    fill = lastlit;
+    pending = 0;
+    publish_rec(ctl, nrec, op, lane);
+    return -1;
+  }
+
+  // Up to n (1 .. 64) entries, entry i in lane i (none of them the one after
+  // an announced literal run).  Writes records for as many as the ring has
+  // room for, up to and including an announced literal run, and up to the
+  // first invalid one; returns how many it took, and in st the chunk's final
+  // status when the chunk ends with them (else -1).
+  __device__ uint32_t batch(uint4 ent, uint32_t n, int32_t &st) {
+    // record ring space (with every builder gone, bk is all ones and
+    // nothing is read any more)
+    while (nrec - rec_free >= RING) {
+      rec_free = min8(ctl.bk);
+      if (rec_free == 0xFFFFFFFFu) rec_free = nrec;
+      if (nrec - rec_free < RING) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const uint32_t space = RING - (nrec - rec_free);
+    n = n < space ? n : space;
+    // a batch ends with an announced literal run (its match comes later)
+    const uint64_t lits = __ballot(lane < n && (ent.w & W_LIT) != 0);
+    if (lits) n = (uint32_t)__builtin_ctzll(lits) + 1;
+    const bool act = lane < n;
+    const uint32_t ys = ent.x, L = ent.y, M = ent.z;
+    const bool last = (ent.w & W_LAST) != 0, end = (ent.w & W_END) != 0;
+    const bool lit = (ent.w & W_LIT) != 0;
+    const uint32_t dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
+    // decoded positions
+    const uint32_t len = act && !end ? L + (last || lit ? 0u : M) : 0u;
+    const uint32_t o = op + wave_excl_scan(len, lane);
+    // checks that need the decoded position (the walker did the rest)
+    int32_t err = C_OK;
+    if (act) {
+      if (end) err = (int32_t)M;
+      else if (L > N - o) err = C_OVERRUN;
+      else if (last) err = (o + L == N) ? C_OK : C_SIZE;
+      else if (lit) err = C_OK;
+      else if (dist == 0 || dist > o + L || dist > dmax) err = C_BADOFF;
+      else if (M > N - o - L) err = C_OVERRUN;
+    }
+    const uint64_t bad = __ballot(err != C_OK);
+    const uint32_t f = bad ? (uint32_t)__builtin_ctzll(bad) : n;   // records before the first failure
+    // fill byte of distance-1 runs: the last literal, or the previous
+    // record's fill when this record has no literals
+    const uint32_t pfo = lane_below(dist == 1 && L > 0 && !lit ? 1u : 0u);
+    const uint32_t pfb = lane_below(lastlit);
+    uint32_t fok, fb;
+    if (L > 0) {
+      fok = 1;
+      fb = lastlit;
+    } else if (lane == 0) {
+      fok = fill_ok;
+      fb = fill;
+    } else {
+      fok = pfo;
+      fb = pfb;
+    }
+    uint32_t info = last ? F_LAST : (lit ? 0u : (F_MATCH | dist));
+    if (!last && !lit && dist == 1 && fok) info |= F_FILL | (fb << 16);
+    if (lane < f) sm.recs[ridx_lane(nrec, lane)] = make_uint4(o, ys, L, info);
+    // state after the records written
+    if (f > 0) {
+      const uint32_t lf = f - 1;
+      const uint32_t l_o = __builtin_amdgcn_readlane(o, lf), l_len = __builtin_amdgcn_readlane(len, lf);
+      const uint32_t l_info = __builtin_amdgcn_readlane(info, lf);
+      op = l_o + l_len;
+      fill_ok = (l_info & F_FILL) ? 1u : 0u;
+      fill = rec_fill(l_info);
+      pending = __builtin_amdgcn_readlane(lit ? 1u : 0u, lf);
+      nrec += f;
+      publish_rec(ctl, nrec, op, lane);
+    }
+    st = -1;
+    if (f < n) st = (int32_t)__builtin_amdgcn_readlane((uint32_t)err, f);
+    else if (__ballot(act && last)) st = C_OK;
+    return f;
+  }
+};
+
 // Wave 0.  Structural checks only (everything that keeps the walk inside the
 // block); distances and decoded positions are the recorder's.  Input waits
 // always end: the feeder keeps filling the ring while the walk is open, and
@@ -422,8 +555,22 @@ struct Walker {
   uint32_t head;        // block offset 0 sits at input position head
   uint32_t wbase;       // entries wbase .. wbase + 63 sit in lane order in iw,
   uint32_t iw, iw2;     // the next 64 in iw2 (loaded one window ahead)
+  Rec<SM> rec;          // with an index the walker makes the records itself ...
+  uint32_t direct;      // ... (and no recorder wave runs)
+  int32_t fin;          // (direct) the chunk's final status once known, else -1
 
   __device__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
+    if (direct) {
+      int32_t st;
+      if (w & W_END) st = (int32_t)M;
+      else if (w & W_CONT) st = rec.cont(make_uint4(ys, L, M, w));
+      else rec.batch(make_uint4(ys, L, M, w), 1, st);
+      if (st >= 0) {
+        fin = st;
+        stop = 1;
+      }
+      return;
+    }
     while (cnt - cons >= CHAIN) {
       cons = lds_get(&ctl.rcons);
       if (cnt - cons < CHAIN) break;
@@ -729,7 +876,7 @@ struct Walker {
   // when the walk ends: after the literal-only last sequence, at a
   // structural error (an END entry carries the status), or when the
   // recorder is gone.
-  __device__ bool slow_step() {
+  __device__ __forceinline__ bool slow_step() {
     int32_t st = C_OK;
     uint32_t ys = 0, L = 0, M = 0, w = 0, e = 0, token = 0;
     if (y >= y_end) st = C_TRUNC;
@@ -788,7 +935,7 @@ struct Walker {
   // index does not describe the block: the chunk fails.  Returns false,
   // with nothing consumed, when the next sequence needs the general step.
   __device__ bool index_batch() {
-    if (cnt - cons >= CHAIN) {
+    if (!direct && cnt - cons >= CHAIN) {
       cons = lds_get(&ctl.rcons);
       if (cnt - cons >= CHAIN) {
         if (lds_get(&ctl.pstate) != ST_RUN) stop = 1;
@@ -796,7 +943,7 @@ struct Walker {
         return true;
       }
     }
-    const uint32_t room = CHAIN - (cnt - cons), left = icnt - ij;
+    const uint32_t room = direct ? 64u : CHAIN - (cnt - cons), left = icnt - ij;
     uint32_t nmax = room < left - 1 ? room : left - 1;
     nmax = nmax < 64 ? nmax : 64u;
     if (nmax == 0) return false;
@@ -865,12 +1012,24 @@ struct Walker {
       stop = 1;
       return true;
     }
-    const uint32_t slot = lds_addr(&sm.chain[(cnt + lane) % CHAIN]);
-    lds_store_lanes(slot, u32x4{ys, L, M, ((b.x >> 8) & 0xFFFFu) | (lastlit << 16)}, n);
-    cnt = uni(cnt + n);
-    lds_set(&ctl.wcnt, cnt);
-    ij += n;
-    y = uni(__builtin_amdgcn_readlane(pn, n - 1));
+    const uint32_t dw = ((b.x >> 8) & 0xFFFFu) | (lastlit << 16);
+    uint32_t took = n;
+    if (direct) {
+      int32_t st;
+      took = rec.batch(make_uint4(ys, L, M, dw), n, st);
+      if (st >= 0) {
+        fin = st;
+        stop = 1;
+        return true;
+      }
+    } else {
+      const uint32_t slot = lds_addr(&sm.chain[(cnt + lane) % CHAIN]);
+      lds_store_lanes(slot, u32x4{ys, L, M, dw}, n);
+      cnt = uni(cnt + n);
+      lds_set(&ctl.wcnt, cnt);
+    }
+    ij += took;
+    y = uni(__builtin_amdgcn_readlane(pn, took - 1));
     if (y - pub >= SEG) {
       pub = y;
       lds_set(&ctl.need[0], pub);
@@ -930,150 +1089,40 @@ struct Walker {
   }
 };
 
-// exclusive prefix sum of v over the wave's lanes
-// with DPP moves (no LDS traffic): inclusive sums within each 16-lane row
-// by shifts of 1, 2, 4 and 8 lanes (lanes shifted in from outside the row
-// read 0), then row 0's total added to row 1 and row 2's to row 3 (row
-// broadcast of lane 15), then rows 0..1's total added to rows 2 and 3 (row
-// broadcast of lane 31)
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t) {
-  uint32_t x = v;
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return x - v;
-}
-
-// the value of the lane below (lane 0 reads 0), by a DPP wave shift
-__device__ __forceinline__ uint32_t lane_below(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x138, 0xF, 0xF, true);   // wave_shr:1
-}
-
-// Wave 1.  Turns chain entries into records, 64 at a time.
+// Wave 1 (chunks without a sequence index).  Turns chain entries into
+// records, 64 at a time.
 template <class SM>
-struct Recorder {
-  static constexpr uint32_t CHAIN = SM::CHAIN;
-  SM &sm;
-  uint32_t dmax;
-  Ctl &ctl;
-  uint32_t lane;
-  uint32_t N;
-  uint32_t taken;       // chain entries processed
-  uint32_t nrec;        // records written
-  uint32_t op;          // decoded bytes described by the records
-  uint32_t rec_free;    // cached: records below this may be overwritten
-  uint32_t fill_ok;     // the last record ends with a known byte (distance-1 run) ...
-  uint32_t fill;        // ... which is this
-  uint32_t pending;     // the last record's match is still to come (a W_CONT entry)
-
-  __device__ int32_t run() {
-    uint32_t avail_entries = 0;
-    for (;;) {
-      // entries to take
-      while (avail_entries == taken) {
-        avail_entries = lds_get(&ctl.wcnt);
-        if (avail_entries != taken) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (pending) {
-        // the match of the last record (announced literal run)
-        const uint4 ent = make_uint4(__builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].x),
-                                     __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].y),
-                                     __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].z),
-                                     __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].w));
-        if (ent.w & W_END) return (int32_t)ent.z;
-        const uint32_t M = ent.z, dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
-        if (dist == 0 || dist > op || dist > dmax) return C_BADOFF;
-        if (M > N - op) return C_OVERRUN;
-        uint32_t info = F_MATCH | dist;
-        if (dist == 1) info |= F_FILL | (lastlit << 16);   // the announced run has literals
-        if (lane == 0) sm.recs[(nrec - 1) % RING].w = info;
-        op += M;
-        fill_ok = dist == 1;
-        fill = lastlit;
-        pending = 0;
-        publish_rec(ctl, nrec, op, lane);
-        taken++;
-        lds_set(&ctl.rcons, taken, lane);
-        continue;
-      }
-      uint32_t n = avail_entries - taken;
-      n = n < 64 ? n : 64;
-      // record ring space (with every builder gone, bk is all ones and
-      // nothing is read any more)
-      while (nrec - rec_free >= RING) {
-        rec_free = min8(ctl.bk);
-        if (rec_free == 0xFFFFFFFFu) rec_free = nrec;
-        if (nrec - rec_free < RING) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      const uint32_t space = RING - (nrec - rec_free);
-      n = n < space ? n : space;
-      uint4 ent = make_uint4(0u, 0u, 0u, W_END);
-      if (lane < n) ent = sm.chain[(taken + lane) % CHAIN];
-      // a batch ends with an announced literal run (its match comes later)
-      const uint64_t lits = __ballot(lane < n && (ent.w & W_LIT) != 0);
-      if (lits) n = (uint32_t)__builtin_ctzll(lits) + 1;
-      const bool act = lane < n;
-      const uint32_t ys = ent.x, L = ent.y, M = ent.z;
-      const bool last = (ent.w & W_LAST) != 0, end = (ent.w & W_END) != 0;
-      const bool lit = (ent.w & W_LIT) != 0;
-      const uint32_t dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
-      // decoded positions
-      const uint32_t len = act && !end ? L + (last || lit ? 0u : M) : 0u;
-      const uint32_t o = op + wave_excl_scan(len, lane);
-      // checks that need the decoded position (the walker did the rest)
-      int32_t err = C_OK;
-      if (act) {
-        if (end) err = (int32_t)M;
-        else if (L > N - o) err = C_OVERRUN;
-        else if (last) err = (o + L == N) ? C_OK : C_SIZE;
-        else if (lit) err = C_OK;
-        else if (dist == 0 || dist > o + L || dist > dmax) err = C_BADOFF;
-        else if (M > N - o - L) err = C_OVERRUN;
-      }
-      const uint64_t bad = __ballot(err != C_OK);
-      const uint32_t f = bad ? (uint32_t)__builtin_ctzll(bad) : n;   // records before the first failure
-      // fill byte of distance-1 runs: the last literal, or the previous
-      // record's fill when this record has no literals
-      const uint32_t pfo = lane_below(dist == 1 && L > 0 && !lit ? 1u : 0u);
-      const uint32_t pfb = lane_below(lastlit);
-      uint32_t fok, fb;
-      if (L > 0) {
-        fok = 1;
-        fb = lastlit;
-      } else if (lane == 0) {
-        fok = fill_ok;
-        fb = fill;
-      } else {
-        fok = pfo;
-        fb = pfb;
-      }
-      uint32_t info = last ? F_LAST : (lit ? 0u : (F_MATCH | dist));
-      if (!last && !lit && dist == 1 && fok) info |= F_FILL | (fb << 16);
-      if (lane < f) sm.recs[ridx_lane(nrec, lane)] = make_uint4(o, ys, L, info);
-      // state after the records written
-      if (f > 0) {
-        const uint32_t lf = f - 1;
-        const uint32_t l_o = __builtin_amdgcn_readlane(o, lf), l_len = __builtin_amdgcn_readlane(len, lf);
-        const uint32_t l_info = __builtin_amdgcn_readlane(info, lf);
-        op = l_o + l_len;
-        fill_ok = (l_info & F_FILL) ? 1u : 0u;
-        fill = rec_fill(l_info);
-        pending = __builtin_amdgcn_readlane(lit ? 1u : 0u, lf);
-        nrec += f;
-        publish_rec(ctl, nrec, op, lane);
-      }
-      taken += f;
-      if (f < n) return __builtin_amdgcn_readlane((uint32_t)err, f);
-      if (__ballot(act && last)) return C_OK;
-      lds_set(&ctl.rcons, taken, lane);
+__device__ __forceinline__ int32_t recorder(Rec<SM> &r, SM &sm, Ctl &ctl, uint32_t lane) {
+  constexpr uint32_t CHAIN = SM::CHAIN;
+  uint32_t taken = 0, avail_entries = 0;
+  for (;;) {
+    // entries to take
+    while (avail_entries == taken) {
+      avail_entries = lds_get(&ctl.wcnt);
+      if (avail_entries != taken) break;
+      __builtin_amdgcn_s_sleep(1);
     }
+    if (r.pending) {
+      const uint4 ent = make_uint4(__builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].x),
+                                   __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].y),
+                                   __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].z),
+                                   __builtin_amdgcn_readfirstlane(sm.chain[taken % CHAIN].w));
+      const int32_t st = r.cont(ent);
+      if (st >= 0) return st;
+      taken++;
+      lds_set(&ctl.rcons, taken, lane);
+      continue;
+    }
+    uint32_t n = avail_entries - taken;
+    n = n < 64 ? n : 64;
+    uint4 ent = make_uint4(0u, 0u, 0u, W_END);
+    if (lane < n) ent = sm.chain[(taken + lane) % CHAIN];
+    int32_t st;
+    taken += r.batch(ent, n, st);
+    if (st >= 0) return st;
+    lds_set(&ctl.rcons, taken, lane);
   }
-};
+}
 
 // -------------------------------------------------------------- feeder
 
@@ -1081,14 +1130,14 @@ struct Recorder {
 // one 1 KiB segment (one LDS-DMA load per lane) at a time, keeping up to QMAX
 // segments in flight within the ring space that every reader has released.
 template <class SM>
-__device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end) {
+__device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb) {
   constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
   const uint32_t nblk = (y_end + 15) / 16;
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
   uint32_t issued = 0, landed = 0;
   while (landed < nseg) {
     // nobody reads input once the walk has ended and every builder has left
-    if (lds_get_asm(&ctl.nfinished) == (uint32_t)NB && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
+    if (lds_get_asm(&ctl.nfinished) == nb && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
     const uint32_t used = min8(ctl.need);
     uint32_t limit = used / SEG + QMAX;
     if (limit > nseg) limit = nseg;
@@ -1792,10 +1841,14 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   const uint8_t *S = P.comp + (c0 - head);
   const uint32_t y_end = head + (uint32_t)(c1 - c0);
 
+  // with a sequence index the walker makes the records itself and wave 1
+  // becomes one more builder
+  const bool direct = P.seq_pos != nullptr && s1 > s0;
+  const uint32_t nb = (uint32_t)NB + (direct ? 1u : 0u);
   if (tid < NSLOT) {
-    ctl.need[tid] = tid <= (uint32_t)NB ? 0u : 0xFFFFFFFFu;
-    ctl.bk[tid] = tid < (uint32_t)NB ? 0u : 0xFFFFFFFFu;
-    ctl.next_tile[tid] = tid < (uint32_t)NB ? tid : 0xFFFFFFFFu;
+    ctl.need[tid] = tid <= nb ? 0u : 0xFFFFFFFFu;
+    ctl.bk[tid] = tid < nb ? 0u : 0xFFFFFFFFu;
+    ctl.next_tile[tid] = tid < nb ? tid : 0xFFFFFFFFu;
   }
   if (tid == 0) {
     ctl.in_avail = 0;
@@ -1805,24 +1858,31 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     ctl.wcnt = 0;
     ctl.rcons = 0;
     ctl.nfinished = 0;
-    ctl.tile_ctr = NB;
+    ctl.tile_ctr = nb;
     ctl.status = 0;
   }
   __syncthreads();
 
   if (wave == 0) {
     Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
-                         P.seq_pos ? P.seq_pos + s0 : nullptr, (uint32_t)(s1 - s0), 0, head, 0, 0, 0};
+                         direct ? P.seq_pos + s0 : nullptr, direct ? (uint32_t)(s1 - s0) : 0u, 0, head, 0, 0, 0,
+                         Rec<Smem<HLOG>>{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0}, direct ? 1u : 0u, -1};
     W.run();
-  } else if (wave == 1) {
-    Recorder<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0, 0};
-    const int32_t st = R.run();
+    if (direct) {
+      // every walk ends with a final status (the last sequence or an error)
+      const int32_t st = W.fin >= 0 ? W.fin : C_TABLE;
+      if (lane == 0) ctl.status = st;
+      lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
+    }
+  } else if (wave == 1 && !direct) {
+    Rec<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0};
+    const int32_t st = recorder(R, sm, ctl, lane);
     if (lane == 0) ctl.status = st;
     lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
   } else if (wave == 2) {
-    feeder(sm, ctl, lane, S, y_end);
-  } else {
-    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave - 3, N, 0, 0, 0, 0, 0, 0};
+    feeder(sm, ctl, lane, S, y_end, nb);
+  } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
+    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0};
     B.run();
   }
   __syncthreads();
