@@ -430,7 +430,7 @@ struct Rec {
 
   // the entry after an announced literal run (ent wave-uniform): its match,
   // or the end of the walk.  Returns the chunk's final status, or -1.
-  __device__ int32_t cont(uint4 ent) {
+  __device__ __forceinline__ int32_t cont(uint4 ent) {
     if (ent.w & W_END) return (int32_t)ent.z;
     const uint32_t M = ent.z, dist = ent.w & 0xFFFFu, lastlit = (ent.w >> 16) & 0xFFu;
     if (dist == 0 || dist > op || dist > dmax) return C_BADOFF;
@@ -451,7 +451,7 @@ struct Rec {
   // room for, up to and including an announced literal run, and up to the
   // first invalid one; returns how many it took, and in st the chunk's final
   // status when the chunk ends with them (else -1).
-  __device__ uint32_t batch(uint4 ent, uint32_t n, int32_t &st) {
+  __device__ __forceinline__ uint32_t batch(uint4 ent, uint32_t n, int32_t &st) {
     // record ring space (with every builder gone, bk is all ones and
     // nothing is read any more)
     while (nrec - rec_free >= RING) {
@@ -559,7 +559,7 @@ struct Walker {
   uint32_t direct;      // ... (and no recorder wave runs)
   int32_t fin;          // (direct) the chunk's final status once known, else -1
 
-  __device__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
+  __device__ __forceinline__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
     if (direct) {
       int32_t st;
       if (w & W_END) st = (int32_t)M;
@@ -586,7 +586,7 @@ struct Walker {
     lds_set_entry(&sm.chain[slot], u32x4{ys, L, M, w}, &ctl.wcnt, cnt);
   }
 
-  __device__ void need_input(uint32_t upto) {
+  __device__ __forceinline__ void need_input(uint32_t upto) {
     upto = upto < y_end ? upto : y_end;
     if (avail >= upto) return;
     avail = lds_get(&ctl.in_avail);
@@ -648,7 +648,7 @@ struct Walker {
   }
 
   // the entry of a finished sequence (announced on its own or not)
-  __device__ void finish(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
+  __device__ __forceinline__ void finish(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
     pend = 0;
     if (split) emit(0, 0, M, w | W_CONT);
     else emit(ys, L, M, w);
@@ -685,8 +685,15 @@ struct Walker {
   // the last two cases that sequence is not consumed.  Every iteration
   // advances y by at least 3 bytes, and a walk that crosses a KiB since the
   // last publication publishes y in need[0].
-  __device__ uint32_t fast_run(uint32_t nmax, uint32_t &n) {
+  __device__ __forceinline__ uint32_t fast_run(uint32_t nmax, uint32_t &n) {
     uint32_t st;
+    // every scalar operand must be wave-uniform in the compiler's view too
+    y = uni(y);
+    pub = uni(pub);
+    cnt = uni(cnt);
+    tw = ((uint64_t)uni((uint32_t)(tw >> 32)) << 32) | uni((uint32_t)tw);
+    const uint32_t yend = uni(y_end), av = uni(avail);
+    nmax = uni(nmax);
     asm volatile(
         "s_mov_b64 s[46:47], %[tw]\n\t"
         "s_mov_b32 %[n], 0\n\t"
@@ -829,9 +836,9 @@ struct Walker {
         "L_end%=:\n\t"
         "s_mov_b64 %[tw], s[46:47]"
         : [y] "+s"(y), [tw] "+s"(tw), [pub] "+s"(pub), [cnt] "+s"(cnt), [n] "=&s"(n), [st] "=&s"(st)
-        : [yend] "s"(y_end), [avail] "s"(avail), [inr] "s"(lds_addr(sm.inr)),
-          [need0] "s"(lds_addr(&ctl.need[0])), [nmax] "s"(nmax), [chain] "s"(lds_addr(sm.chain)),
-          [wcnt] "s"(lds_addr(&ctl.wcnt)), [vlane] "v"(lane), [imask] "s"(IMASK), [rlast] "s"(INR - 16),
+        : [yend] "s"(yend), [avail] "s"(av), [inr] "s"(uni(lds_addr(sm.inr))),
+          [need0] "s"(uni(lds_addr(&ctl.need[0]))), [nmax] "s"(nmax), [chain] "s"(uni(lds_addr(sm.chain))),
+          [wcnt] "s"(uni(lds_addr(&ctl.wcnt))), [vlane] "v"(lane), [imask] "s"(IMASK), [rlast] "s"(INR - 16),
           [cmask] "s"(CHAIN - 1)
         : "s40", "s41", "s42", "s43", "s44", "s45", "s46", "s47", "s48", "s49", "s50", "s51", "s52",
           "s53", "s54", "s55", "s56", "s57", "s58", "s59", "v40", "v41", "v42", "v43", "v44", "v45",
@@ -841,7 +848,7 @@ struct Walker {
 
   // Walks common-shape sequences; false, with nothing consumed, when the
   // next sequence needs the general step.
-  __device__ bool fast_step() {
+  __device__ __forceinline__ bool fast_step() {
     if (!have_tw) {
       if (((y & IMASK) > INR - 8) | (y + 8 > y_end)) return false;
       if (avail < y + 8) {
@@ -934,7 +941,7 @@ struct Walker {
   // sequence that does not end where the next listed one starts means the
   // index does not describe the block: the chunk fails.  Returns false,
   // with nothing consumed, when the next sequence needs the general step.
-  __device__ bool index_batch() {
+  __device__ __forceinline__ bool index_batch() {
     if (!direct && cnt - cons >= CHAIN) {
       cons = lds_get(&ctl.rcons);
       if (cnt - cons >= CHAIN) {
@@ -1048,7 +1055,7 @@ struct Walker {
   // The walk guided by the sequence index: listed sequences in batches,
   // the others (and the last) with the general step, each checked against
   // its listed position.
-  __device__ void run_indexed() {
+  __device__ __forceinline__ void run_indexed() {
     wbase = 0;
     iw = ix[min(lane, icnt - 1)];
     iw2 = ix[min(64 + lane, icnt - 1)];
@@ -1071,7 +1078,7 @@ struct Walker {
     }
   }
 
-  __device__ void run() {
+  __device__ __forceinline__ void run() {
     if (icnt) {
       run_indexed();
     } else {
@@ -1130,7 +1137,7 @@ __device__ __forceinline__ int32_t recorder(Rec<SM> &r, SM &sm, Ctl &ctl, uint32
 // one 1 KiB segment (one LDS-DMA load per lane) at a time, keeping up to QMAX
 // segments in flight within the ring space that every reader has released.
 template <class SM>
-__device__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb) {
+__device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb) {
   constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
   const uint32_t nblk = (y_end + 15) / 16;
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
@@ -1280,7 +1287,7 @@ __device__ __forceinline__ void flush_int4_few(Smem<HLOG> &sm, uint32_t lane, co
 }
 
 template <int MODE, int HLOG>
-__device__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
+__device__ __forceinline__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
                            uint32_t t, uint32_t N, const Meta4 &m, bool fast) {
   constexpr uint32_t HMASK = (1u << HLOG) - 1;
   uint32_t base = t * TILE;
@@ -1388,7 +1395,7 @@ struct Builder {
     cov = r.y;
   }
 
-  __device__ void need_input(uint32_t upto) {
+  __device__ __forceinline__ void need_input(uint32_t upto) {
     while (avail < upto) {
       avail = lds_get(&ctl.in_avail);
       if (avail < upto) __builtin_amdgcn_s_sleep(1);
@@ -1396,7 +1403,7 @@ struct Builder {
   }
 
   // wait until tiles [0, tiles) are final; false if the chunk failed first
-  __device__ bool wait_done(uint32_t tiles) {
+  __device__ __forceinline__ bool wait_done(uint32_t tiles) {
     while (done < tiles) {
       done = min8(ctl.next_tile);
       if (done >= tiles) break;
@@ -1409,7 +1416,7 @@ struct Builder {
   // Advance k to the last record starting at or before T, the one that
   // contains T once the records reach that far (records are sorted by
   // start), and announce that records below it are no longer read.
-  __device__ void find_k(uint32_t T) {
+  __device__ __forceinline__ void find_k(uint32_t T) {
     uint32_t kk = k;
     for (;;) {   // records from k on are protected by bk[b] <= k
       const uint32_t j = kk + lane;
@@ -1428,7 +1435,7 @@ struct Builder {
   // Announce the first input byte still read: the literal byte of record k
   // at position T, or the end of record k's literals when T lies past them
   // (later records' literals follow in the input).
-  __device__ void announce(uint32_t T) {
+  __device__ __forceinline__ void announce(uint32_t T) {
     const uint4 r = rec(k);
     uint32_t off = T > r.x ? T - r.x : 0u;
     off = off < r.z ? off : r.z;
@@ -1462,7 +1469,7 @@ struct Builder {
   // wait until records cover [T, Tend); false if the records stopped short.
   // The recorder publishes its final state after its last records, so
   // records read after a final state has been seen are final.
-  __device__ bool wait_cov(uint32_t T, uint32_t Tend) {
+  __device__ __forceinline__ bool wait_cov(uint32_t T, uint32_t Tend) {
     while (cov < Tend) {
       refresh();
       if (cov >= Tend) break;
@@ -1565,7 +1572,7 @@ struct Builder {
 
   // Build [T, Tend) record by record, starting at record k.  Every byte
   // before T must be final.
-  __device__ void tile_exact(uint32_t T, uint32_t Tend) {
+  __device__ __forceinline__ void tile_exact(uint32_t T, uint32_t Tend) {
     uint32_t j = k;
     for (;;) {
       uint4 r = rec(j);
@@ -1654,7 +1661,7 @@ struct Builder {
   // the start of the next), in 1 + extra passes.  Each
   // lane builds its 16 bytes from the pieces that meet them, in order; the
   // first piece covers the block's first byte.
-  __device__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t rve, uint32_t m, uint32_t extra) {
+  __device__ __forceinline__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t rve, uint32_t m, uint32_t extra) {
     const uint32_t P = T + 16 * lane;
     const uint32_t bend = P + 16 < Tend ? P + 16 : Tend;
     // the record under the block's first byte
@@ -1682,7 +1689,7 @@ struct Builder {
     }
   }
 
-  __device__ void run() {
+  __device__ __forceinline__ void run() {
     const uint32_t ntiles = (N + TILE - 1) / TILE;
     constexpr bool G = MODE == MODE_INT4G;
     const bool fast = G || (MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8);
