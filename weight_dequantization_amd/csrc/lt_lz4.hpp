@@ -1702,20 +1702,22 @@ struct Builder {
     const bool few = fast && P.group_shift >= 7;
     const uint32_t lane31 = lane & 31u;
     const uint64_t ng = G ? (2 * P.total + P.group - 1) >> P.group_shift : 0;
-    Meta4 nxt{};
-    MetaG nxg{};
+    // the loads of the next tile's scales and zero points are issued once
+    // the current tile's write-out has used them: loading into registers
+    // that a copy still has to read would make the compiler wait for every
+    // load and store in flight, the previous tile's stores included
+    Meta4 cur{};
+    MetaG cug{};
     if constexpr (G) {
-      if (b < ntiles) nxg = int4g_meta(P, dst0, b, lane31, ng);
+      if (b < ntiles) cug = int4g_meta(P, dst0, b, lane31, ng);
     } else {
-      if (fast && b < ntiles) nxt = int4_meta(P, dst0, b, lane, N, few);
+      if (fast && b < ntiles) cur = int4_meta(P, dst0, b, lane, N, few);
     }
     uint32_t u;
     for (uint32_t t = b; t < ntiles; t = u) {
       const uint32_t uv = grab_issue();
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
-      Meta4 cur = nxt;
-      MetaG cug = nxg;
       if (!wait_cov(T, Tend)) break;
       find_k(T);
       // records k .. k + 63 in lanes, missing ones read as {cov, 0, 0, 0};
@@ -1762,11 +1764,6 @@ struct Builder {
         }
       }
       u = grab_take(uv);
-      if constexpr (G) {
-        if (u < ntiles) nxg = int4g_meta(P, dst0, u, lane31, ng);
-      } else {
-        if (fast && u < ntiles) nxt = int4_meta(P, dst0, u, lane, N, few);
-      }
       // tiles before this one that are read
       uint32_t need_tiles = seen ? (src_need + TILE - 1) / TILE : t;
       if (t >= HTILES) {
@@ -1807,6 +1804,11 @@ struct Builder {
         flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
       }
       lds_set(&ctl.next_tile[b], u, lane);
+      if constexpr (G) {
+        if (u < ntiles) cug = int4g_meta(P, dst0, u, lane31, ng);
+      } else {
+        if (fast && u < ntiles) cur = int4_meta(P, dst0, u, lane, N, few);
+      }
     }
     lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
     lds_set(&ctl.bk[b], 0xFFFFFFFFu, lane);
