@@ -967,16 +967,18 @@ struct Walker {
     if (__builtin_amdgcn_readlane(hi, nmax - 1) > avail) avail = lds_get(&ctl.in_avail);
     if (uni(hi) > avail) {
       // the first sequence's bytes are not all here: wait for them when
-      // they fit well within the ring, else walk it with the general step
+      // they fit well within the ring (polling only the count, with the
+      // batch's setup kept), else walk it with the general step
       if (uni(pn) - y + 16 > INR / 2) return false;
       avail = lds_get(&ctl.in_avail);
       if (uni(hi) > avail) {
         pub = y;
         lds_set(&ctl.need[0], pub);
-        __builtin_amdgcn_s_sleep(1);
-        avail = lds_get(&ctl.in_avail);
+        do {
+          __builtin_amdgcn_s_sleep(1);
+          avail = lds_get(&ctl.in_avail);
+        } while (uni(hi) > avail);
       }
-      return true;
     }
     // the token and the literal count's extra bytes
     const uint4 a = gather16<IMASK>(sm.inr, p);
