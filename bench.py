@@ -181,7 +181,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
-            "kernel": "lt::chunk_kernel<1, 14>", "avg_launch_ms": round(avg_kern_ms, 5),
+            "kernel": "lt::chunk_kernel<3, 14>", "avg_launch_ms": round(avg_kern_ms, 5),
             "min_launch_ms": round(float(np.min(kern_ms)), 5),
             "bytes_per_launch": alg_bytes,
         },
