@@ -25,13 +25,56 @@ struct RawParams {
   uint64_t group;
   uint32_t group_shift;      // log2(group) if group is a power of two, else 64
   uint16_t *out;
+  uint64_t e_base;           // element index of src's first code (groups count from 0)
 };
 
 constexpr int RAW_THREADS = 256;
 constexpr int RAW_UNROLL = 4;   // dwords per thread
 
 __device__ __forceinline__ uint64_t grp(uint64_t e, const RawParams &P) {
+  e += P.e_base;
   return P.group_shift < 64 ? (e >> P.group_shift) : e / P.group;
+}
+
+// INT4 with groups that are a power of two of at least 64 codes, in tiles of
+// 1 KiB of packed codes (2048 codes, at most 33 groups): one wave per tile.
+// Lane l reads dword k = bytes 256 k + 4 l (each load instruction reads 256
+// contiguous bytes) and writes codes 512 k + 8 l .. + 7 as 16 bytes of fp16
+// (each store instruction writes 1 KiB contiguously).  Lanes 0 .. 63 fetch
+// the scale and zero point of groups g0 .. g0 + 63 once per tile, as the two
+// packed constants of deq8_int4_dual, and every lane takes its group's from
+// the lane that holds it (ds_bpermute).
+constexpr int RAWT_THREADS = 256;
+__global__ void __launch_bounds__(RAWT_THREADS) dequant_int4_tiles(RawParams P, uint64_t ntiles) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t nwaves = (uint64_t)gridDim.x * (RAWT_THREADS / 64);
+  const uint64_t ng = (2 * P.n_bytes + P.group - 1) >> P.group_shift;
+  // without zero points, read any valid byte and discard it (no branch)
+  const int8_t *zsrc = P.zp ? P.zp : (const int8_t *)P.scales;
+  const bool has_zp = P.zp != nullptr;
+  for (uint64_t w = (uint64_t)blockIdx.x * (RAWT_THREADS / 64) + (threadIdx.x >> 6); w < ntiles; w += nwaves) {
+    const uint8_t *src = P.src + 1024 * w + 4 * lane;
+    uint32_t d[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) d[k] = *(const uint32_t *)(src + 256 * k);
+    const uint64_t e = 2048 * w;   // the tile's first code
+    const uint64_t g0 = e >> P.group_shift;
+    const uint64_t left = ng - g0;   // >= 1
+    const uint32_t li = lane < left ? lane : (uint32_t)left - 1;
+    const uint32_t sv = P.scales[g0 + li];
+    const int z = has_zp ? (int)zsrc[g0 + li] : 0;
+    const uint32_t s2 = (sv & 0xFFFFu) * 0x10001u;
+    const uint32_t c2 = f16_bits_int(1024 + z) | (f16_bits_int(64 + z) << 16);
+    const uint32_t off = (uint32_t)(e & (P.group - 1)) + 8 * lane;
+    uint4 *out = (uint4 *)(P.out + e) + lane;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t i = (off + 512 * k) >> P.group_shift;
+      const h2 c = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, c2));
+      const h2 sc = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, s2));
+      out[64 * k] = deq8_int4_dual(d[k], c, sc);
+    }
+  }
 }
 
 // Each thread takes RAW_UNROLL dwords spaced a workgroup-width apart, so each
@@ -221,12 +264,26 @@ lt_status raw_common(bool int4, const uint8_t *src, const uint16_t *scales, cons
   P.group = group;
   P.group_shift = shift_of(group);
   P.out = out;
+  P.e_base = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (int4 && P.group_shift >= 6 && P.group_shift < 64 && P.n_bytes >= 1024) {
+    // whole 1 KiB tiles with per-tile group constants; the rest below
+    const uint64_t ntiles = P.n_bytes / 1024;
+    uint64_t blocks = (ntiles + lt::RAWT_THREADS / 64 - 1) / (lt::RAWT_THREADS / 64);
+    if (blocks > 2048) blocks = 2048;   // eight 4-wave blocks per CU, grid-strided
+    hipLaunchKernelGGL(lt::dequant_int4_tiles, dim3((uint32_t)blocks), dim3(lt::RAWT_THREADS), 0, s, P, ntiles);
+    const uint64_t done = ntiles * 1024;
+    if (done == P.n_bytes) return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+    P.src += done;
+    P.out += 2 * done;
+    P.e_base = 2 * done;
+    P.n_bytes -= done;
+  }
   uint64_t units = int4 ? P.n_bytes / 4 : P.n_bytes / 8;
   uint64_t per_block = (uint64_t)lt::RAW_THREADS * lt::RAW_UNROLL;
   uint64_t blocks = (units + per_block - 1) / per_block;
   if (blocks == 0) blocks = 1;
   if (blocks > 0x7FFFFFFFull) return LT_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
   if (int4)
     hipLaunchKernelGGL(lt::dequant_int4_kernel, dim3((uint32_t)blocks), dim3(lt::RAW_THREADS), 0, s, P);
   else
