@@ -44,7 +44,7 @@ __device__ __forceinline__ uint64_t grp(uint64_t e, const RawParams &P) {
 // the scale and zero point of groups g0 .. g0 + 63 once per tile, as the two
 // packed constants of deq8_int4_dual, and every lane takes its group's from
 // the lane that holds it (ds_bpermute).
-constexpr int RAWT_THREADS = 256;
+constexpr int RAWT_THREADS = 512;
 __global__ void __launch_bounds__(RAWT_THREADS) dequant_int4_tiles(RawParams P, uint64_t ntiles) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint64_t nwaves = (uint64_t)gridDim.x * (RAWT_THREADS / 64);
@@ -270,7 +270,9 @@ lt_status raw_common(bool int4, const uint8_t *src, const uint16_t *scales, cons
     // whole 1 KiB tiles with per-tile group constants; the rest below
     const uint64_t ntiles = P.n_bytes / 1024;
     uint64_t blocks = (ntiles + lt::RAWT_THREADS / 64 - 1) / (lt::RAWT_THREADS / 64);
-    if (blocks > 2048) blocks = 2048;   // eight 4-wave blocks per CU, grid-strided
+    // one tile per wave measures fastest (more waves in flight than a
+    // grid-strided loop keeps); the loop only serves grids past the limit
+    if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;
     hipLaunchKernelGGL(lt::dequant_int4_tiles, dim3((uint32_t)blocks), dim3(lt::RAWT_THREADS), 0, s, P, ntiles);
     const uint64_t done = ntiles * 1024;
     if (done == P.n_bytes) return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
