@@ -14,7 +14,10 @@ table, scales and zero points already resident in HBM.
 Metric: GB/s (1e9 B/s) of algorithmic bytes per step = compressed bytes read
 + fp16 bytes written (scales, zero points, the offset tables and the
 sequence index are reported separately as metadata), and the fraction of
-the 8.0 TB/s HBM peak.
+the 8.0 TB/s HBM peak.  Each step's time is the GPU time between HIP events
+around the launch; a 1 GiB fill before each step (outside the events) clears
+L2 and the last-level cache, so no step reads input a previous one left
+cached (--no-evict times the steps back to back instead).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
 
@@ -104,6 +107,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--extra", action="store_true")
     ap.add_argument("--cpu-chunks", type=int, default=1792)
+    ap.add_argument("--no-evict", action="store_true",
+                    help="launch the timed steps back to back, without clearing the caches between them")
+    ap.add_argument("--b2b", action="store_true",
+                    help="also time the steps back to back with warm caches, for reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode "
@@ -133,28 +140,44 @@ def main():
     def step():
         lt.fused_lz4_int4(table, scales, zp, shape, w.group, out=out, status=status)
 
-    for _ in range(args.warmup):
+    scratch = None if args.no_evict else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        if scratch is not None:
+            scratch.fill_(i & 255)
         step()
     torch.cuda.synchronize()
     lt.check_status(status)
 
+    # Each timed step is bracketed by HIP events on the launch stream.  Before
+    # each one (outside the events) a 1 GiB fill clears L2 and the 256 MB
+    # last-level cache, so no step reads input the previous one left cached.
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    lt.check_status(status)
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
+
+    def timed_steps(evict):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i, (a, b) in enumerate(ev):
+            if evict:
+                scratch.fill_(i & 255)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        lt.check_status(status)
+        return [a.elapsed_time(b) for a, b in ev], wall
+
+    kern_ms, wall = timed_steps(not args.no_evict)
     avg_kern_ms = float(np.mean(kern_ms))
+    ms_per_step = avg_kern_ms if not args.no_evict else wall * 1e3 / args.steps
     value = alg_bytes / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / (avg_kern_ms / 1e3) / 1e9
+    b2b_ms = None
+    if args.b2b and not args.no_evict:   # for reference: the same steps back to back, caches warm
+        b2b, b2b_wall = timed_steps(False)
+        b2b_ms = {"mean": round(float(np.mean(b2b)), 5), "wall_per_step": round(b2b_wall * 1e3 / args.steps, 5)}
 
     result = {
         "metric": "fused LZ4+INT4->fp16 GB/s (compressed in + fp16 out) and % of HBM peak, 1 GPU",
@@ -185,6 +208,11 @@ def main():
             "min_launch_ms": round(float(np.min(kern_ms)), 5),
             "bytes_per_launch": alg_bytes,
         },
+        "step_ms": {"mean": round(avg_kern_ms, 5), "median": round(float(np.median(kern_ms)), 5),
+                    "p10": round(float(np.percentile(kern_ms, 10)), 5),
+                    "p90": round(float(np.percentile(kern_ms, 90)), 5),
+                    "caches_cleared_before_each_step": not args.no_evict,
+                    "back_to_back_no_clearing": b2b_ms},
     }
 
     if args.extra:
