@@ -255,6 +255,64 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "raw_int4_GBps": round(raw_bytes / ms_raw / 1e6, 1), "raw_int4_ms": round(ms_raw, 4),
         "fill_fp16_GBps": round(2 * n_elem / ms_fill / 1e6, 1),
         "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
+        "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),
+    }
+
+
+def streamed_measurements(torch, lt, w, packed, scales, zp, dev, out, reps=10, per_half=512):
+    """The same layer with its chunk table in pinned host memory: the
+    streamed entry point (copies of one batch overlapped with the decode of
+    the one before) against copying the whole table first and then decoding,
+    and the plain host-to-device copy of the compressed bytes alone.  Host
+    wall clock around each call, synchronized on both sides, so every rate
+    here includes PCIe."""
+    import time as _t
+    n_elem = w.rows * w.cols
+    ht = lt.ChunkTable.build(packed, w.dst_off, "cpu", pin=True)
+    staging = torch.empty(ht.staging_bytes(per_half), dtype=torch.uint8, device=dev)
+    status = torch.full((ht.n_chunks,), -1, dtype=torch.int32, device=dev)
+    dt = lt.ChunkTable(torch.empty_like(ht.comp, device=dev), torch.empty_like(ht.comp_off, device=dev),
+                       torch.empty_like(ht.dst_off, device=dev), ht.n_chunks, ht.max_chunk_bytes,
+                       ht.total_bytes, ht.comp_bytes, ht.max_dist,
+                       torch.empty_like(ht.seq_off, device=dev), torch.empty_like(ht.seq_pos, device=dev),
+                       ht.n_seq)
+    shape = (w.rows, w.cols)
+
+    def streamed():
+        lt.stream_fused_lz4_int4(ht, scales, zp, shape, w.group, out=out, status=status, staging=staging)
+
+    def sequential():
+        for d, h in ((dt.comp, ht.comp), (dt.comp_off, ht.comp_off), (dt.dst_off, ht.dst_off),
+                     (dt.seq_off, ht.seq_off), (dt.seq_pos, ht.seq_pos)):
+            d.copy_(h, non_blocking=True)
+        lt.fused_lz4_int4(dt, scales, zp, shape, w.group, out=out, status=status)
+
+    def copy_only():
+        dt.comp.copy_(ht.comp, non_blocking=True)
+
+    def wall(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = _t.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append((_t.perf_counter() - t0) * 1e3)
+        return float(np.median(ts))
+
+    ms_stream = wall(streamed)
+    lt.check_status(status)
+    ms_seq = wall(sequential)
+    lt.check_status(status)
+    ms_copy = wall(copy_only)
+    inb = ht.comp_bytes + 2 * n_elem
+    return {
+        "chunks_per_half": per_half, "staging_bytes": staging.numel(),
+        "streamed_ms": round(ms_stream, 4), "copy_then_decode_ms": round(ms_seq, 4),
+        "h2d_copy_of_compressed_bytes_ms": round(ms_copy, 4),
+        "h2d_GBps": round(ht.comp_bytes / ms_copy / 1e6, 2),
+        "streamed_pcie_inclusive_GBps": round(inb / ms_stream / 1e6, 2),
     }
 
 

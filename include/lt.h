@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 3
+#define LT_ABI_VERSION 4
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -176,6 +176,42 @@ lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, con
 lt_status lt_fused_lz4_int8(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
                             uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                             int32_t *chunk_status, void *stream);
+
+/*
+ * Streamed decode ("GPU Compression Pipeline - TDD Roadmap", Phase 5.1: the
+ * transfer of one part overlaps the decompression of the part before, and
+ * the result equals the sequential one).  The table's arrays -- comp,
+ * comp_off, dst_off and, when present, seq_off and seq_pos -- are HOST
+ * arrays; for the copies to overlap the decode they must be pinned
+ * (hipHostMalloc, or torch's pin_memory).  comp_off[0] must be 0.  The
+ * staging buffer holds, in order, the table's offset arrays and sequence
+ * index (copied once, ahead of the first batch), then two halves for
+ * compressed bytes.  The chunks are cut into batches, each as large as a
+ * half holds; batch b is copied into half b % 2 on copy_stream, then
+ * decoded on stream, and half b % 2 is copied into again only after that
+ * decode has finished.  Output, chunk statuses and the validity rules are
+ * those of lt_decode_lz4 / lt_fused_lz4_int4 on the same table.
+ *   staging        DEVICE scratch owned by the caller, 256-byte aligned
+ *   staging_bytes  its size: with u(x) = x rounded up to 256, at least
+ *                  2*u(8(n+1)) [+ u(8(n+1)) + u(4 n_seq) with an index]
+ *                  for the table, plus two halves each holding
+ *                  u(largest chunk's compressed bytes + 16);
+ *                  LT_ERR_INVALID_ARG otherwise
+ *   copy_stream    the stream the host-to-device copies run on (it may
+ *                  equal stream, which then serializes copy and decode);
+ *                  its first copy waits for the work already on `stream`,
+ *                  so consecutive calls may share one staging buffer
+ * Calls return once everything is enqueued.  The host arrays and the
+ * staging buffer must stay untouched until the work on `stream` finishes.
+ * Events are created and destroyed within the call; nothing else is
+ * allocated.  LT_ERR_DEVICE if a copy or an event could not be enqueued.
+ */
+lt_status lt_stream_decode_lz4(const lt_chunk_table *host_table, uint8_t *dst, int32_t *chunk_status,
+                               uint8_t *staging, uint64_t staging_bytes, void *copy_stream, void *stream);
+lt_status lt_stream_fused_lz4_int4(const lt_chunk_table *host_table, const uint16_t *scales, const int8_t *zp,
+                                   uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                                   int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
+                                   void *copy_stream, void *stream);
 
 /* ---- host-side packer: builds the inputs above (no device work) ---- */
 

@@ -1,0 +1,236 @@
+"""Streamed copy-and-decode: the chunk table stays in pinned host memory and
+batches of chunks are copied to a device staging buffer while the batch
+before them decodes ("GPU Compression Pipeline - TDD Roadmap", Phase 5.1,
+the host-to-device streaming step).  The streamed result must be the same as
+the oracle's, bit for bit, and each chunk's status must be the one the
+resident-table entry point reports for it, at the same chunk index.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_dequantization_amd as lt
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def t_u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def t_i8(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int8)).to(DEV)
+
+
+def host_u16(t):
+    torch.cuda.synchronize()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+
+
+def assert_same(got, ref, what):
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "%s: %d of %d differ, first at %d: got %#x want %#x" % (
+        what, bad.size, ref.size, bad[0], got[bad[0]], ref[bad[0]])
+
+
+def status_tensor(n):
+    return torch.full((max(n, 1),), -1, dtype=torch.int32, device=DEV)
+
+
+def statuses(st, n):
+    torch.cuda.synchronize()
+    return st[:n].cpu().numpy()
+
+
+def host_table(comp, comp_off, dst_off, index, max_dist=0):
+    return lt.ChunkTable.from_host(comp, comp_off, dst_off, "cpu", max_dist=max_dist, index=index, pin=True)
+
+
+def staging_for(table, k):
+    return torch.empty(table.staging_bytes(k), dtype=torch.uint8, device=DEV)
+
+
+def _stream_fused4(table, w, k, what):
+    st = status_tensor(table.n_chunks)
+    out = lt.stream_fused_lz4_int4(table, t_u16(w.scales), t_i8(w.zp), (w.rows, w.cols), w.group,
+                                   status=st, staging=staging_for(table, k))
+    s = statuses(st, table.n_chunks)
+    assert np.all(s == 0), "%s: statuses %s" % (what, np.unique(s))
+    ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)
+    assert_same(host_u16(out), ref, what)
+
+
+def test_stream_fused_int4_config1_many_batches():
+    """One chunk per staging half (every batch waits for the decode two
+    batches back), and three per half; indexed and walked."""
+    w = synth.config1()
+    packed = lt.pack_int4(w.codes)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    for index in (True, False):
+        t = host_table(comp, comp_off, w.dst_off, index, lt.PACK_WINDOW)
+        for k in (1, 3):
+            print("config1 index=%s chunks/half=%d" % (index, k), flush=True)
+            _stream_fused4(t, w, k, "config1 streamed, index=%s, %d/half" % (index, k))
+
+
+def test_stream_fused_int4_config3_full():
+    """The benchmark's workload, 8192x28672 group 128, streamed through
+    64-chunk halves (about 28 batches), with and without the index."""
+    w = synth.config3()
+    packed = lt.pack_int4(w.codes)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    for index in (True, False):
+        print("config3 index=%s" % index, flush=True)
+        t = host_table(comp, comp_off, w.dst_off, index, lt.PACK_WINDOW)
+        _stream_fused4(t, w, 64, "config3 streamed, index=%s" % index)
+
+
+def test_stream_fused_int4_ragged_and_oracle_stream():
+    """Mixed chunk sizes with a ragged last chunk, from the oracle's own
+    compressor (its blocks use the format's whole window)."""
+    w = synth.int4_weight(512, 8192, 128, 31, chunking="mixed")
+    ot = O.compress_table(O.pack_int4(w.codes), w.dst_off)
+    for index in (False, True):
+        t = host_table(ot.comp, ot.comp_off, ot.dst_off, index)
+        _stream_fused4(t, w, 2, "mixed oracle stream, index=%s" % index)
+
+
+def _seq_table(seeds, sizes):
+    streams, expect = [], []
+    for sd, n in zip(seeds, sizes):
+        b, e = O.seqgen(int(sd), int(n))
+        streams.append(b)
+        expect.append(e)
+    comp_off = np.cumsum([0] + [b.size for b in streams]).astype(np.uint64)
+    dst_off = np.cumsum([0] + list(sizes)).astype(np.uint64)
+    return O.Table(np.concatenate(streams), comp_off, dst_off), np.concatenate(expect)
+
+
+def _stream_decode(t, k):
+    st = status_tensor(t.n_chunks)
+    got = lt.stream_decode_lz4(t, status=st, staging=staging_for(t, k))
+    return statuses(st, t.n_chunks), got.cpu().numpy()
+
+
+def _resident_decode(ot):
+    t = lt.ChunkTable.from_host(ot.comp, ot.comp_off, ot.dst_off, DEV)
+    st = status_tensor(t.n_chunks)
+    got = lt.decode_lz4(t, status=st)
+    return statuses(st, t.n_chunks), got.cpu().numpy()
+
+
+def test_stream_decode_generated_streams():
+    """Bytes mode on generated blocks (boundary lengths, distances up to
+    65535, overlapping matches, empty chunks, a ragged last chunk), against
+    the oracle's decode, at one and at three chunks per staging half."""
+    rng = np.random.default_rng(23)
+    for trial in range(3):
+        n = int(rng.integers(2, 120))
+        sizes = list(16 * rng.integers(0, 70000 // 16, n))
+        sizes[rng.integers(0, n)] = 0
+        sizes[-1] = int(rng.integers(0, 70000))
+        ot, e = _seq_table(rng.integers(0, 2**62, n), sizes)
+        for index in (False, True):
+            t = host_table(ot.comp, ot.comp_off, ot.dst_off, index)
+            for k in (1, 3):
+                print("seqgen trial %d index=%s chunks/half=%d" % (trial, index, k), flush=True)
+                s, got = _stream_decode(t, k)
+                assert np.all(s == 0), (trial, index, k, np.unique(s))
+                assert np.array_equal(got, e), (trial, index, k)
+
+
+def test_stream_decode_statuses_at_global_chunk_index():
+    """Corrupt blocks and a misaligned chunk start: each chunk's status, and
+    every chunk decoded OK, equal what the resident-table entry point gives,
+    so batch-local chunk numbers never leak into the status array."""
+    rng = np.random.default_rng(29)
+    s, _ = O.seqgen(99, 20000)
+    blocks = []
+    for k in range(40):
+        c = s.copy()
+        if k % 3 == 1:
+            c[rng.integers(0, c.size)] ^= np.uint8(rng.integers(1, 256))
+        if k % 7 == 5:
+            c = c[:c.size // 2]
+        blocks.append(c)
+    ot = O.Table(np.concatenate(blocks), np.cumsum([0] + [b.size for b in blocks]).astype(np.uint64),
+                 np.arange(len(blocks) + 1, dtype=np.uint64) * np.uint64(20000))
+    ot.dst_off[11] += np.uint64(8)
+    ref_s, ref = _resident_decode(ot)
+    assert np.any(ref_s != 0) and np.any(ref_s == 0)
+    t = host_table(ot.comp, ot.comp_off, ot.dst_off, False)
+    for k in (1, 4):
+        got_s, got = _stream_decode(t, k)
+        assert np.array_equal(got_s, ref_s), (k, got_s, ref_s)
+        for i in np.nonzero(ref_s == 0)[0]:
+            a, b = int(ot.dst_off[i]), int(ot.dst_off[i + 1])
+            assert np.array_equal(got[a:b], ref[a:b]), (k, i)
+
+
+def test_stream_empty_table_is_a_no_op():
+    t = host_table(np.zeros(0, np.uint8), np.zeros(1, np.uint64), np.zeros(1, np.uint64), False)
+    got = lt.stream_decode_lz4(t, staging=staging_for(t, 1))
+    torch.cuda.synchronize()
+    assert t.n_chunks == 0 and got.numel() == 0      # trimmed to total_bytes
+
+
+def test_stream_consecutive_calls_share_staging():
+    """Two tables streamed back to back through one small staging buffer,
+    with no synchronization between the calls: the second call's copies wait
+    for the first call's decodes, so both results are whole."""
+    w1 = synth.int4_weight(256, 8192, 128, 41, chunking="mixed")
+    w2 = synth.int4_weight(384, 4096, 64, 43)
+    tabs = []
+    for w in (w1, w2):
+        comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off, max_dist=lt.PACK_WINDOW)
+        tabs.append(host_table(comp, comp_off, w.dst_off, True, lt.PACK_WINDOW))
+    staging = torch.empty(max(t.staging_bytes(2) for t in tabs), dtype=torch.uint8, device=DEV)
+    outs, sts = [], []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t, w in zip(tabs, (w1, w2)):
+            st = status_tensor(t.n_chunks)
+            outs.append(lt.stream_fused_lz4_int4(t, t_u16(w.scales), t_i8(w.zp), (w.rows, w.cols), w.group,
+                                                 status=st, staging=staging))
+            sts.append((st, t.n_chunks))
+    for j, (o, (st, n)) in enumerate(zip(outs, sts)):
+        w = (w1, w2)[j % 2]
+        assert np.all(statuses(st, n) == 0), j
+        assert_same(host_u16(o), O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group), "call %d" % j)
+
+
+def test_stream_llama70b_layer_from_host():
+    """One layer of the 80-layer Llama-70B-shaped INT4 stack (7 projections,
+    LZ4 chunks of 16/64/256 KiB, the format's whole match window) held in
+    pinned host memory and expanded tensor by tensor through one staging
+    buffer into reused fp16 outputs, as a model too large for device memory
+    would load it; each tensor against the oracle in full."""
+    tabs = []
+    for t in range(len(synth.LLAMA70B_LAYER)):
+        w = synth.config5_tensor(3, t)
+        comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off)
+        tabs.append((w, host_table(comp, comp_off, w.dst_off, True)))
+    staging = torch.empty(max(ht.staging_bytes() for _, ht in tabs), dtype=torch.uint8, device=DEV)
+    outs = {}
+    for w, ht in tabs:
+        key = (w.rows, w.cols)
+        if key not in outs:
+            outs[key] = torch.empty(w.rows * w.cols, dtype=torch.float16, device=DEV)
+        print("layer 3 tensor %dx%d, %d chunks" % (w.rows, w.cols, ht.n_chunks), flush=True)
+        st = status_tensor(ht.n_chunks)
+        out = lt.stream_fused_lz4_int4(ht, t_u16(w.scales), t_i8(w.zp), key, w.group, out=outs[key],
+                                       status=st, staging=staging)
+        assert np.all(statuses(st, ht.n_chunks) == 0)
+        assert_same(host_u16(out), O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group),
+                    "layer 3 %dx%d" % key)

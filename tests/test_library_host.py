@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 3
+    assert lt.lib().lt_abi_version() == 4
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -200,3 +200,68 @@ def test_index_chunks_malformed_and_args():
     assert L.lt_index_chunks(ptr(blk), ptr(comp_off), 1, ptr(seq_off), ptr(small), 1, 1) \
         == lt.LT_ERR_INVALID_ARG
     assert seq_off[1] > 1                       # sized even when the buffer is short
+
+
+def test_streamed_arguments_rejected_without_gpu():
+    """The streamed entry points check the staging buffer and the host table
+    on the host and return LT_ERR_INVALID_ARG before any device work."""
+    L = lt.lib()
+    V = C.c_void_p
+    ptr = lambda a: a.ctypes.data_as(V)
+    fake = V(0x10000)
+    comp = np.zeros(4096, np.uint8)
+    comp_off = np.array([0, 1000, 3000], np.uint64)
+    dst_off = np.array([0, 4096, 8192], np.uint64)
+    seq_off = np.array([0, 3, 9], np.uint64)
+    seq_pos = np.zeros(9, np.uint32)
+
+    def table(coff=comp_off, soff=None, n_seq=0, n=2):
+        return lt._Table(ptr(comp), ptr(coff), ptr(dst_off), n, 4096, 8192, comp.size, 0, 0,
+                         None if soff is None else ptr(soff), None if soff is None else ptr(seq_pos), n_seq)
+
+    def dec(t, staging=fake, nbytes=1 << 20):
+        return L.lt_stream_decode_lz4(C.byref(t), fake, None, staging, nbytes, None, None)
+
+    inv = lt.LT_ERR_INVALID_ARG
+    assert dec(table(), staging=None) == inv
+    assert dec(table(), staging=V(0x10010)) == inv             # staging not 256-byte aligned
+    meta = 2 * 256                                             # two offset arrays of 3 entries
+    assert dec(table(), nbytes=meta + 256) == inv              # under two aligned halves
+    assert dec(table(), nbytes=meta + 2 * 1792) == inv         # the 2000-byte chunk needs 2048 per half
+    assert dec(table(np.array([8, 1000, 3000], np.uint64))) == inv      # must start at 0
+    assert dec(table(np.array([0, 3000, 1000], np.uint64))) == inv      # decreasing
+    assert dec(table(np.array([0, 1000, 5000], np.uint64))) == inv      # past comp_bytes
+    assert dec(table(soff=seq_off, n_seq=8)) == inv            # index past n_seq
+    assert dec(table(soff=np.array([0, 5, 4], np.uint64), n_seq=9)) == inv
+    # the device-table checks apply too
+    t = table()
+    t.reserved = 1
+    assert dec(t) == inv
+    assert L.lt_stream_decode_lz4(None, fake, None, fake, 1 << 20, None, None) == inv
+    assert L.lt_stream_decode_lz4(C.byref(table()), V(0x10008), None, fake, 1 << 20, None, None) == inv
+    # int4: 8192 packed bytes are 16384 codes
+    f = lambda rows, cols, g, sc=fake: L.lt_stream_fused_lz4_int4(C.byref(table()), sc, None, rows, cols, g,
+                                                                 fake, None, fake, 1 << 20, None, None)
+    assert f(4, 4096, 128, sc=None) == inv
+    assert f(4, 4096, 100) == inv
+    assert f(8, 4096, 128) == inv
+    # nothing to do: no device work, OK
+    empty = lt._Table(0, 0, 0, 0, 0, 0, 0)
+    assert L.lt_stream_decode_lz4(C.byref(empty), fake, None, None, 0, None, None) == lt.LT_OK
+
+
+def test_staging_bytes_holds_the_largest_window():
+    """ChunkTable.staging_bytes sizes each half for the largest run of k
+    consecutive chunks, with the library's 256-byte rounding."""
+    torch = pytest.importorskip("torch")
+    comp = np.zeros(10000, np.uint8)
+    comp_off = np.array([0, 100, 5100, 5200, 10000], np.uint64)
+    dst_off = np.array([0, 1, 2, 3, 4], np.uint64)
+    t = lt.ChunkTable.from_host(comp, comp_off, dst_off, device="cpu")
+    up = lambda x: (x + 255) // 256 * 256
+    meta = 2 * up(8 * 5)
+    assert t.staging_bytes(1) == meta + 2 * up(5000 + 16)
+    assert t.staging_bytes(2) == meta + 2 * up(5100 + 16)
+    assert t.staging_bytes(99) == meta + 2 * up(10000 + 16)
+    t.set_index(np.array([0, 1, 7, 8, 30], np.uint64), np.zeros(30, np.uint32))
+    assert t.staging_bytes(1) == meta + up(8 * 5) + up(4 * 30) + 2 * up(5000 + 16)

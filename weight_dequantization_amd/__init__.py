@@ -13,11 +13,16 @@ Device entry points (asynchronous on torch's current stream):
     dequant_int8(q, scales, zp, shape, group, out=None)      -> fp16 tensor
     fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
+Streamed entry points (the table in pinned host memory, copies overlapped
+with the decode on a second stream):
+    stream_decode_lz4(host_table, out=None, status=None, staging=None)
+    stream_fused_lz4_int4(host_table, scales, zp, shape, group, out=None, ...)
 Host packer (numpy in, numpy out):
     pack_int4(codes) -> packed bytes (low nibble first)
     compress_chunks(src, dst_off, threads=0, max_dist=0) -> (comp, comp_off)
     index_chunks(comp, comp_off, threads=0) -> (seq_off, seq_pos)
     ChunkTable.build(src_bytes, dst_off, device) -> table resident on the GPU
+    ChunkTable.build(src_bytes, dst_off, device="cpu", pin=True) -> pinned host table
 """
 from __future__ import annotations
 
@@ -77,6 +82,8 @@ def _lib():
             "lt_dequant_int8": (i32, [vp, vp, vp, u64, u64, u64, vp, vp]),
             "lt_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
+            "lt_stream_decode_lz4": (i32, [tp, vp, vp, vp, u64, vp, vp]),
+            "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
             "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
@@ -169,6 +176,16 @@ def _dptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _place(a: np.ndarray, device, pin: bool):
+    torch = _torch()
+    t = torch.from_numpy(a.copy())
+    if pin:
+        if torch.device(device).type != "cpu":
+            raise ValueError("pin=True places the table in host memory: use device='cpu'")
+        return t.pin_memory()
+    return t.to(device)
+
+
 @dataclass
 class ChunkTable:
     """A chunk table resident on the GPU (see lt_chunk_table in include/lt.h)."""
@@ -186,40 +203,57 @@ class ChunkTable:
 
     @classmethod
     def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
-                  max_dist: int = 0, index: bool = False):
-        torch = _torch()
+                  max_dist: int = 0, index: bool = False, pin: bool = False):
+        """Place a host-built table on `device`; with device="cpu" and
+        pin=True the arrays go to pinned host memory, the form the streamed
+        entry points read."""
         comp_off = np.ascontiguousarray(comp_off, np.uint64)
         dst_off = np.ascontiguousarray(dst_off, np.uint64)
         n = dst_off.size - 1
         sizes = np.diff(dst_off.astype(np.int64)) if n > 0 else np.zeros(0, np.int64)
-        comp_t = torch.from_numpy(np.ascontiguousarray(comp, np.uint8).copy()).to(device)
-        if comp_t.numel() == 0:
-            comp_t = torch.zeros(16, dtype=torch.uint8, device=device)
-        t = cls(comp_t,
-                torch.from_numpy(comp_off.view(np.int64).copy()).to(device),
-                torch.from_numpy(dst_off.view(np.int64).copy()).to(device),
+        comp = np.ascontiguousarray(comp, np.uint8)
+        if comp.size == 0:
+            comp = np.zeros(16, np.uint8)
+        t = cls(_place(comp, device, pin), _place(comp_off.view(np.int64), device, pin),
+                _place(dst_off.view(np.int64), device, pin),
                 n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
                 int(comp_off[-1]) if comp_off.size else 0, max_dist)
         if index and n > 0:
             seq_off, seq_pos = index_chunks(comp, comp_off)
-            t.set_index(seq_off, seq_pos, device)
+            t.set_index(seq_off, seq_pos, device, pin)
         return t
 
-    def set_index(self, seq_off: np.ndarray, seq_pos: np.ndarray, device=None):
+    def set_index(self, seq_off: np.ndarray, seq_pos: np.ndarray, device=None, pin: bool = None):
         """Attach a sequence index (host arrays, as index_chunks returns)."""
-        torch = _torch()
         device = device if device is not None else self.comp.device
+        pin = self.comp.device.type == "cpu" and self.comp.is_pinned() if pin is None else pin
         seq_off = np.ascontiguousarray(seq_off, np.uint64)
         seq_pos = np.ascontiguousarray(seq_pos, np.uint32)
         self.n_seq = int(seq_pos.size)
         if seq_pos.size == 0:
             seq_pos = np.zeros(1, np.uint32)
-        self.seq_off = torch.from_numpy(seq_off.view(np.int64).copy()).to(device)
-        self.seq_pos = torch.from_numpy(seq_pos.view(np.int32).copy()).to(device)
+        self.seq_off = _place(seq_off.view(np.int64), device, pin)
+        self.seq_pos = _place(seq_pos.view(np.int32), device, pin)
+
+    def staging_bytes(self, chunks_per_half: int = 512) -> int:
+        """A staging size for the streamed entry points: the table's offsets
+        and index, then two halves that each hold the compressed bytes of
+        the largest `chunks_per_half` consecutive chunks (the library's
+        layout: every piece rounded up to 256 bytes)."""
+        up = lambda x: (x + 255) // 256 * 256
+        n = self.n_chunks
+        if n == 0:
+            return 2 * 256
+        k = max(1, min(int(chunks_per_half), n))
+        co = self.comp_off.cpu().numpy().astype(np.int64)
+        meta = 2 * up(8 * (n + 1))
+        if self.seq_off is not None:
+            meta += up(8 * (n + 1)) + up(4 * int(self.seq_off[-1]))
+        return meta + 2 * up(int(np.max(co[k:] - co[:-k])) + 16)
 
     @classmethod
     def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0,
-              max_dist: int = None, index: bool = True):
+              max_dist: int = None, index: bool = True, pin: bool = False):
         """Compress `src` chunk by chunk on the host and upload the table.  By
         default matches stay within SMALL_WINDOW bytes, which the table
         declares, so the device decoder keeps a short history per chunk, and
@@ -228,7 +262,7 @@ class ChunkTable:
         if max_dist is None:
             max_dist = PACK_WINDOW
         comp, comp_off = compress_chunks(src, dst_off, threads, max_dist)
-        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index)
+        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin)
 
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
@@ -309,4 +343,62 @@ def fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, s
     _check(_lib().lt_fused_lz4_int8(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group,
                                     _dptr(out), _dptr(status), _stream_ptr(stream)),
            "lt_fused_lz4_int8")
+    return out.view(rows, cols)
+
+
+# ------------------------------------------------------------------ streamed
+
+_COPY_STREAMS = {}
+
+
+def _copy_stream(device):
+    torch = _torch()
+    key = torch.cuda.current_device() if device is None else torch.device(device).index
+    if key is None:
+        key = torch.cuda.current_device()
+    if key not in _COPY_STREAMS:
+        _COPY_STREAMS[key] = torch.cuda.Stream(device=key)      # default priority
+    return _COPY_STREAMS[key]
+
+
+def _stream_setup(table: ChunkTable, out_device, staging, copy_stream):
+    torch = _torch()
+    if table.comp.device.type != "cpu":
+        raise ValueError("the streamed entry points read a host table (ChunkTable.build(..., "
+                         "device='cpu', pin=True))")
+    if staging is None:
+        staging = torch.empty(table.staging_bytes(), dtype=torch.uint8, device=out_device)
+    if copy_stream is None:
+        copy_stream = _copy_stream(out_device)
+    return staging, copy_stream
+
+
+def stream_decode_lz4(table: ChunkTable, out=None, status=None, staging=None, copy_stream=None,
+                      stream=None, device="cuda"):
+    """Decode a host-resident table: batches are copied to the two halves of
+    `staging` on `copy_stream` while the previous batch decodes on `stream`.
+    The host arrays must stay unchanged until `stream` has passed this call."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(max(table.total_bytes, 1), dtype=torch.uint8, device=device)
+    staging, copy_stream = _stream_setup(table, out.device, staging, copy_stream)
+    t = table.as_c()
+    _check(_lib().lt_stream_decode_lz4(C.byref(t), _dptr(out), _dptr(status), _dptr(staging),
+                                       staging.numel(), _stream_ptr(copy_stream), _stream_ptr(stream)),
+           "lt_stream_decode_lz4")
+    return out[:table.total_bytes] if out.numel() > table.total_bytes else out
+
+
+def stream_fused_lz4_int4(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
+                          staging=None, copy_stream=None, stream=None):
+    """fused_lz4_int4 over a host-resident table, copies overlapped with the
+    decode as in stream_decode_lz4."""
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, scales.device)
+    staging, copy_stream = _stream_setup(table, out.device, staging, copy_stream)
+    t = table.as_c()
+    _check(_lib().lt_stream_fused_lz4_int4(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group,
+                                           _dptr(out), _dptr(status), _dptr(staging), staging.numel(),
+                                           _stream_ptr(copy_stream), _stream_ptr(stream)),
+           "lt_stream_fused_lz4_int4")
     return out.view(rows, cols)

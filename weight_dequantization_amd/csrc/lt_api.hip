@@ -185,8 +185,28 @@ uint32_t shift_of(uint64_t g) {
   return (g & (g - 1)) == 0 ? (uint32_t)__builtin_ctzll(g) : 64u;
 }
 
-lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *chunk_status,
-                        const uint16_t *scales, const int8_t *zp, uint64_t group, void *stream) {
+lt_status launch_params(int mode, lt::ChunkParams &P, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  dim3 grid(P.n), block(lt::NTHREADS);
+  // a declared short window lets each chunk keep a 16 KiB history, so more
+  // chunks share a CU
+  const bool small = P.dmax <= LT_SMALL_WINDOW;
+  if (mode == lt::MODE_INT4 && P.group_shift < 64 && P.group >= 128) mode = lt::MODE_INT4G;
+  switch (mode * 2 + (small ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 16>), grid, block, 0, s, P); break;
+    case 1: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 14>), grid, block, 0, s, P); break;
+    case 2: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 16>), grid, block, 0, s, P); break;
+    case 3: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 14>), grid, block, 0, s, P); break;
+    case 4: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 16>), grid, block, 0, s, P); break;
+    case 5: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
+    case 6: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 16>), grid, block, 0, s, P); break;
+    default: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
+  }
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+}
+
+lt::ChunkParams make_params(const lt_chunk_table *t, void *out, int32_t *chunk_status, const uint16_t *scales,
+                            const int8_t *zp, uint64_t group) {
   lt::ChunkParams P;
   P.comp = t->comp;
   P.comp_off = t->comp_off;
@@ -205,23 +225,132 @@ lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *c
   P.seq_off = t->seq_off;
   P.seq_pos = t->seq_pos;
   P.n_seq = t->seq_off ? t->n_seq : 0;
-  hipStream_t s = (hipStream_t)stream;
-  dim3 grid(t->n_chunks), block(lt::NTHREADS);
-  // a declared short window lets each chunk keep a 16 KiB history, so more
-  // chunks share a CU
-  const bool small = P.dmax <= LT_SMALL_WINDOW;
-  if (mode == lt::MODE_INT4 && P.group_shift < 64 && group >= 128) mode = lt::MODE_INT4G;
-  switch (mode * 2 + (small ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 16>), grid, block, 0, s, P); break;
-    case 1: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 14>), grid, block, 0, s, P); break;
-    case 2: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 16>), grid, block, 0, s, P); break;
-    case 3: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 14>), grid, block, 0, s, P); break;
-    case 4: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 16>), grid, block, 0, s, P); break;
-    case 5: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
-    case 6: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 16>), grid, block, 0, s, P); break;
-    default: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
+  P.comp_base = 0;
+  P.d_first = 0;
+  P.d_last = t->total_bytes;
+  return P;
+}
+
+lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *chunk_status,
+                        const uint16_t *scales, const int8_t *zp, uint64_t group, void *stream) {
+  lt::ChunkParams P = make_params(t, out, chunk_status, scales, zp, group);
+  return launch_params(mode, P, stream);
+}
+
+// ------------------------------------------------------------ streaming
+
+constexpr uint64_t kAlign = 256;
+uint64_t up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Staging layout for a host table t: first the whole table's offsets and
+// sequence index (copied once, before the first batch), then two halves
+// that take the compressed bytes of alternate batches.  Every piece starts
+// on a 256-byte boundary.
+uint64_t meta_bytes(const lt_chunk_table *t) {
+  const uint64_t n = t->n_chunks;
+  uint64_t b = 2 * up(8 * (n + 1));
+  if (t->seq_off) b += up(8 * (n + 1)) + up(4 * t->seq_off[n]);
+  return b;
+}
+
+// Bytes a half needs for the compressed bytes of chunks [c, e), plus one
+// 16-byte block the decoder may read past the last chunk.
+uint64_t batch_bytes(const lt_chunk_table *t, uint64_t c, uint64_t e) {
+  return up(t->comp_off[e] - t->comp_off[c] + 16);
+}
+
+// Copy-and-decode of a table whose arrays are in host memory: batches of
+// chunks go to the two halves of a device staging buffer in turn, the
+// copies on copy_stream and the decode on stream, each half reused once the
+// decode of the batch before it in that half has finished.  The offsets and
+// the index travel once, ahead of the first batch: many small copies per
+// batch cost more than the batch's compressed bytes.
+lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *chunk_status,
+                        const uint16_t *scales, const int8_t *zp, uint64_t group, uint8_t *staging,
+                        uint64_t staging_bytes, void *copy_stream, void *stream) {
+  if (t->n_chunks == 0) return LT_OK;
+  if (!staging || ((uintptr_t)staging & (kAlign - 1)) != 0) return LT_ERR_INVALID_ARG;
+  // host-side checks of what the batching relies on (the device checks the rest)
+  const uint64_t n = t->n_chunks;
+  if (t->comp_off[0] != 0 || t->comp_off[n] > t->comp_bytes) return LT_ERR_INVALID_ARG;
+  if (t->seq_off && (t->seq_off[0] != 0 || t->seq_off[n] > t->n_seq)) return LT_ERR_INVALID_ARG;
+  for (uint64_t i = 0; i < n; i++) {
+    if (t->comp_off[i + 1] < t->comp_off[i]) return LT_ERR_INVALID_ARG;
+    if (t->seq_off && t->seq_off[i + 1] < t->seq_off[i]) return LT_ERR_INVALID_ARG;
   }
-  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+  const uint64_t mb = meta_bytes(t);
+  if (staging_bytes < mb + 2 * kAlign) return LT_ERR_INVALID_ARG;
+  const uint64_t half = ((staging_bytes - mb) / 2) & ~(kAlign - 1);
+  for (uint64_t i = 0; i < n; i++)
+    if (batch_bytes(t, i, i + 1) > half) return LT_ERR_INVALID_ARG;   // a chunk must fit a half
+  hipStream_t cs = (hipStream_t)copy_stream, ds = (hipStream_t)stream;
+  uint64_t *m_coff = (uint64_t *)staging;
+  uint64_t *m_doff = (uint64_t *)(staging + up(8 * (n + 1)));
+  uint64_t *m_soff = (uint64_t *)(staging + 2 * up(8 * (n + 1)));
+  uint32_t *m_spos = (uint32_t *)(staging + 3 * up(8 * (n + 1)));
+  const uint64_t ns = t->seq_off ? t->seq_off[n] : 0;
+  hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, start = nullptr;
+  lt_status st = LT_OK;
+  for (int h = 0; h < 2 && st == LT_OK; h++) {
+    if (hipEventCreateWithFlags(&copied[h], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&done[h], hipEventDisableTiming) != hipSuccess)
+      st = LT_ERR_DEVICE;
+  }
+  // the first copy waits for the work already on stream, so a staging
+  // buffer reused by consecutive calls is not overwritten under a decode
+  if (st == LT_OK && (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess ||
+                      hipEventRecord(start, ds) != hipSuccess || hipStreamWaitEvent(cs, start, 0) != hipSuccess))
+    st = LT_ERR_DEVICE;
+  if (st == LT_OK) {
+    bool ok = hipMemcpyAsync(m_coff, t->comp_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess &&
+              hipMemcpyAsync(m_doff, t->dst_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess;
+    if (ok && t->seq_off)
+      ok = hipMemcpyAsync(m_soff, t->seq_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess &&
+           (ns == 0 || hipMemcpyAsync(m_spos, t->seq_pos, 4 * ns, hipMemcpyHostToDevice, cs) == hipSuccess);
+    if (!ok) st = LT_ERR_DEVICE;
+  }
+  uint64_t c = 0;
+  for (uint64_t batch = 0; st == LT_OK && c < n; batch++) {
+    // the batch: as many chunks as the half holds
+    uint64_t e = c + 1;
+    while (e < n && batch_bytes(t, c, e + 1) <= half) e++;
+    const int h = (int)(batch & 1);
+    uint8_t *p_comp = staging + mb + h * half;
+    const uint64_t cb = t->comp_off[e] - t->comp_off[c];
+    // copies into this half wait for the decode that last read it
+    if (batch >= 2 && hipStreamWaitEvent(cs, done[h], 0) != hipSuccess) { st = LT_ERR_DEVICE; break; }
+    if (hipMemcpyAsync(p_comp, t->comp + t->comp_off[c], cb, hipMemcpyHostToDevice, cs) != hipSuccess ||
+        hipEventRecord(copied[h], cs) != hipSuccess || hipStreamWaitEvent(ds, copied[h], 0) != hipSuccess) {
+      st = LT_ERR_DEVICE;
+      break;
+    }
+    // the kernel sees chunks c .. e-1 as 0 .. e-c-1: the offset arrays are
+    // the device copies from chunk c on, compressed offsets counted from
+    // the batch's first byte
+    lt::ChunkParams P = make_params(t, out, chunk_status ? chunk_status + c : nullptr, scales, zp, group);
+    P.comp = p_comp;
+    P.comp_off = m_coff + c;
+    P.dst_off = m_doff + c;
+    P.comp_bytes = cb;
+    P.comp_base = t->comp_off[c];
+    P.n = (uint32_t)(e - c);
+    P.d_first = t->dst_off[c];
+    P.d_last = t->dst_off[e];
+    if (t->seq_off) {
+      P.seq_off = m_soff + c;
+      P.seq_pos = m_spos;
+      P.n_seq = ns;
+    }
+    st = launch_params(mode, P, stream);
+    if (st == LT_OK && hipEventRecord(done[h], ds) != hipSuccess) st = LT_ERR_DEVICE;
+    c = e;
+  }
+  for (int h = 0; h < 2; h++) {   // destruction waits for nothing: pending events are released later
+    if (copied[h]) hipEventDestroy(copied[h]);
+    if (done[h]) hipEventDestroy(done[h]);
+  }
+  if (start) hipEventDestroy(start);
+  return st;
 }
 
 bool table_ok(const lt_chunk_table *t) {
@@ -248,6 +377,16 @@ lt_status fused_common(int mode, const lt_chunk_table *t, const uint16_t *scales
   }
   if (t->n_chunks == 0) return LT_OK;
   return launch_chunks(mode, t, out, chunk_status, scales, zp, group, stream);
+}
+
+lt_status stream_args(int mode, const lt_chunk_table *t, const uint16_t *scales, uint64_t rows, uint64_t cols,
+                      uint64_t group, const void *out) {
+  if (!table_ok(t) || !out || !aligned16(out)) return LT_ERR_INVALID_ARG;
+  if (mode == lt::MODE_BYTES) return LT_OK;
+  if (!scales || !shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
+  const uint64_t n = rows * cols;
+  if (n % 2 != 0 || t->total_bytes != n / 2) return LT_ERR_INVALID_ARG;
+  return LT_OK;
 }
 
 lt_status raw_common(bool int4, const uint8_t *src, const uint16_t *scales, const int8_t *zp,
@@ -323,6 +462,24 @@ lt_status lt_fused_lz4_int8(const lt_chunk_table *t, const uint16_t *scales, con
                             uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                             int32_t *chunk_status, void *stream) {
   return fused_common(lt::MODE_INT8, t, scales, zp, rows, cols, group, out, chunk_status, stream);
+}
+
+lt_status lt_stream_decode_lz4(const lt_chunk_table *host_table, uint8_t *dst, int32_t *chunk_status,
+                               uint8_t *staging, uint64_t staging_bytes, void *copy_stream, void *stream) {
+  const lt_status a = stream_args(lt::MODE_BYTES, host_table, nullptr, 0, 0, 0, dst);
+  if (a != LT_OK) return a;
+  return stream_common(lt::MODE_BYTES, host_table, dst, chunk_status, nullptr, nullptr, 1, staging, staging_bytes,
+                       copy_stream, stream);
+}
+
+lt_status lt_stream_fused_lz4_int4(const lt_chunk_table *host_table, const uint16_t *scales, const int8_t *zp,
+                                   uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                                   int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
+                                   void *copy_stream, void *stream) {
+  const lt_status a = stream_args(lt::MODE_INT4, host_table, scales, rows, cols, group, out);
+  if (a != LT_OK) return a;
+  return stream_common(lt::MODE_INT4, host_table, out, chunk_status, scales, zp, group, staging, staging_bytes,
+                       copy_stream, stream);
 }
 
 const char *lt_status_str(lt_status s) {
