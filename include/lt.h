@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 4
+#define LT_ABI_VERSION 5
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -178,12 +178,49 @@ lt_status lt_fused_lz4_int8(const lt_chunk_table *t, const uint16_t *scales, con
                             int32_t *chunk_status, void *stream);
 
 /*
+ * Chunk-range (partial) decode: only chunks [first, first + count) of a
+ * device-resident table, into a buffer that holds only their output
+ * (page "Openai/692db884-... (section 28)", the comparison with generic
+ * compressors: decode only the part an operation needs and skip the chunks
+ * it does not touch; here the chunk table is the index that makes a range
+ * addressable).
+ *   first, count      the range; first + count <= t->n_chunks; count 0 is
+ *                     a no-op
+ *   dst_first,        the range's bounds in the decoded stream: the values
+ *   dst_last          of dst_off[first] and dst_off[first + count], which the
+ *                     caller knows from building the table; dst_first a
+ *                     multiple of 16, dst_last <= t->total_bytes
+ *   dst / out         receives decoded bytes [dst_first, dst_last) at
+ *                     offset 0 (fused: the fp16 elements of those bytes, 2
+ *                     per byte for INT4, 1 for INT8); 16-byte aligned
+ *   chunk_status      count entries: entry k is chunk first + k
+ * rows, cols, group, scales, zp describe the WHOLE tensor, as for the
+ * full-table call; each element keeps its own group's scale.  The device
+ * checks every chunk of the range against dst_first / dst_last (the first
+ * chunk must start at dst_first, the last end at dst_last, none reach
+ * outside): a chunk that does not is LT_CHUNK_BAD_TABLE and writes nothing,
+ * so the output buffer is never overrun.  Output and statuses equal the
+ * corresponding part of the full-table call's.
+ */
+lt_status lt_decode_lz4_range(const lt_chunk_table *t, uint32_t first, uint32_t count, uint64_t dst_first,
+                              uint64_t dst_last, uint8_t *dst, int32_t *chunk_status, void *stream);
+lt_status lt_fused_lz4_int4_range(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                                  uint64_t rows, uint64_t cols, uint64_t group, uint32_t first, uint32_t count,
+                                  uint64_t dst_first, uint64_t dst_last, uint16_t *out, int32_t *chunk_status,
+                                  void *stream);
+lt_status lt_fused_lz4_int8_range(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                                  uint64_t rows, uint64_t cols, uint64_t group, uint32_t first, uint32_t count,
+                                  uint64_t dst_first, uint64_t dst_last, uint16_t *out, int32_t *chunk_status,
+                                  void *stream);
+
+/*
  * Streamed decode ("GPU Compression Pipeline - TDD Roadmap", Phase 5.1: the
  * transfer of one part overlaps the decompression of the part before, and
  * the result equals the sequential one).  The table's arrays -- comp,
  * comp_off, dst_off and, when present, seq_off and seq_pos -- are HOST
  * arrays; for the copies to overlap the decode they must be pinned
- * (hipHostMalloc, or torch's pin_memory).  comp_off[0] must be 0.  The
+ * (hipHostMalloc, or torch's pin_memory).  comp_off[0] must be 0, and
+ * comp_off, dst_off and seq_off must not decrease (checked on the host).  The
  * staging buffer holds, in order, the table's offset arrays and sequence
  * index (copied once, ahead of the first batch), then two halves for
  * compressed bytes.  The chunks are cut into batches, each as large as a

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 4
+    assert lt.lib().lt_abi_version() == 5
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -265,3 +265,36 @@ def test_staging_bytes_holds_the_largest_window():
     assert t.staging_bytes(99) == meta + 2 * up(10000 + 16)
     t.set_index(np.array([0, 1, 7, 8, 30], np.uint64), np.zeros(30, np.uint32))
     assert t.staging_bytes(1) == meta + up(8 * 5) + up(4 * 30) + 2 * up(5000 + 16)
+
+
+def test_range_arguments_rejected_without_gpu():
+    """Chunk-range calls check the range and its bounds on the host."""
+    L = lt.lib()
+    V = C.c_void_p
+    fake = V(0x10000)
+    inv = lt.LT_ERR_INVALID_ARG
+    t = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 8192, 100)
+    dec = lambda first, count, lo, hi, out=fake: L.lt_decode_lz4_range(C.byref(t), first, count, lo, hi, out,
+                                                                     None, None)
+    assert dec(3, 2, 0, 16) == inv                 # past the last chunk
+    assert dec(0, 1, 32, 16) == inv                # bounds reversed
+    assert dec(0, 1, 0, 8193) == inv               # past total_bytes
+    assert dec(0, 1, 8, 16) == inv                 # first bound not a multiple of 16
+    assert dec(0, 1, 0, 16, V(0x10004)) == inv     # unaligned output
+    assert dec(2, 0, 0, 0) == lt.LT_OK             # empty range: nothing to do
+    assert L.lt_decode_lz4_range(None, 0, 1, 0, 16, fake, None, None) == inv
+    f4 = lambda rows, cols, g, sc=fake: L.lt_fused_lz4_int4_range(C.byref(t), sc, None, rows, cols, g, 0, 1, 0,
+                                                                 16, fake, None, None)
+    assert f4(4, 4096, 128, sc=None) == inv
+    assert f4(4, 4096, 100) == inv
+    assert f4(8, 4096, 128) == inv                 # 8192 bytes hold 16384 codes
+    f8 = lambda rows, cols: L.lt_fused_lz4_int8_range(C.byref(t), fake, None, rows, cols, cols, 0, 1, 0, 16,
+                                                     fake, None, None)
+    assert f8(4, 4096) == inv                      # int8: one byte per element
+    # the streamed calls also require non-decreasing dst_off
+    comp = np.zeros(64, np.uint8)
+    coff = np.array([0, 10, 20], np.uint64)
+    doff = np.array([0, 32, 16], np.uint64)
+    ptr = lambda a: a.ctypes.data_as(V)
+    h = lt._Table(ptr(comp), ptr(coff), ptr(doff), 2, 4096, 32, 64)
+    assert L.lt_stream_decode_lz4(C.byref(h), fake, None, fake, 1 << 20, None, None) == inv

@@ -13,6 +13,10 @@ Device entry points (asynchronous on torch's current stream):
     dequant_int8(q, scales, zp, shape, group, out=None)      -> fp16 tensor
     fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
+Chunk ranges (only chunks first .. first+count-1, into a buffer for them):
+    decode_lz4_range(table, first, count, out=None, status=None)
+    fused_lz4_int4_range(table, scales, zp, shape, group, first, count, ...)
+    fused_lz4_int8_range(table, scales, zp, shape, group, first, count, ...)
 Streamed entry points (the table in pinned host memory, copies overlapped
 with the decode on a second stream):
     stream_decode_lz4(host_table, out=None, status=None, staging=None)
@@ -82,6 +86,9 @@ def _lib():
             "lt_dequant_int8": (i32, [vp, vp, vp, u64, u64, u64, vp, vp]),
             "lt_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
+            "lt_decode_lz4_range": (i32, [tp, u32, u32, u64, u64, vp, vp, vp]),
+            "lt_fused_lz4_int4_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
+            "lt_fused_lz4_int8_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
             "lt_stream_decode_lz4": (i32, [tp, vp, vp, vp, u64, vp, vp]),
             "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
@@ -200,6 +207,7 @@ class ChunkTable:
     seq_off: object = None  # torch.int64 [n+1] (read as uint64), or None: no sequence index
     seq_pos: object = None  # torch.int32 [n_seq] (read as uint32)
     n_seq: int = 0
+    host_dst_off: object = None   # numpy uint64 [n+1], kept for chunk-range calls
 
     @classmethod
     def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
@@ -218,6 +226,7 @@ class ChunkTable:
                 _place(dst_off.view(np.int64), device, pin),
                 n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
                 int(comp_off[-1]) if comp_off.size else 0, max_dist)
+        t.host_dst_off = dst_off.copy()
         if index and n > 0:
             seq_off, seq_pos = index_chunks(comp, comp_off)
             t.set_index(seq_off, seq_pos, device, pin)
@@ -344,6 +353,59 @@ def fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, s
                                     _dptr(out), _dptr(status), _stream_ptr(stream)),
            "lt_fused_lz4_int8")
     return out.view(rows, cols)
+
+
+# -------------------------------------------------------------- chunk range
+
+def _range_bounds(table: ChunkTable, first: int, count: int):
+    if first < 0 or count < 0 or first + count > table.n_chunks:
+        raise LtError(LT_ERR_INVALID_ARG, "chunk range")
+    d = table.host_dst_off
+    if d is None:
+        d = table.dst_off.cpu().numpy().view(np.uint64)
+    return int(d[first]), int(d[first + count])
+
+
+def decode_lz4_range(table: ChunkTable, first: int, count: int, out=None, status=None, stream=None):
+    """Decode chunks first .. first+count-1 only; `out` receives their bytes
+    from offset 0 (the decoded stream's bytes dst_off[first] ..
+    dst_off[first+count])."""
+    torch = _torch()
+    lo, hi = _range_bounds(table, first, count)
+    if out is None:
+        out = torch.empty(max(hi - lo, 1), dtype=torch.uint8, device=table.comp.device)
+    t = table.as_c()
+    _check(_lib().lt_decode_lz4_range(C.byref(t), first, count, lo, hi, _dptr(out), _dptr(status),
+                                      _stream_ptr(stream)), "lt_decode_lz4_range")
+    return out[:hi - lo] if out.numel() > hi - lo else out
+
+
+def _fused_range(fn, name, per_byte, table, scales, zp, shape, group, first, count, out, status, stream):
+    rows, cols = _shape(shape)
+    lo, hi = _range_bounds(table, first, count)
+    out = _out_f16(out, max(per_byte * (hi - lo), 1), table.comp.device)
+    t = table.as_c()
+    _check(fn(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group, first, count, lo, hi, _dptr(out),
+              _dptr(status), _stream_ptr(stream)), name)
+    n = per_byte * (hi - lo)
+    return out[:n] if out.numel() > n else out
+
+
+def fused_lz4_int4_range(table: ChunkTable, scales, zp, shape, group: int, first: int, count: int,
+                         out=None, status=None, stream=None):
+    """fused_lz4_int4 over chunks first .. first+count-1 only: `out` (flat)
+    receives elements 2*dst_off[first] .. 2*dst_off[first+count] of the
+    tensor; shape, scales and zero points describe the whole tensor."""
+    return _fused_range(_lib().lt_fused_lz4_int4_range, "lt_fused_lz4_int4_range", 2, table, scales, zp,
+                        shape, group, first, count, out, status, stream)
+
+
+def fused_lz4_int8_range(table: ChunkTable, scales, zp, shape, group: int, first: int, count: int,
+                         out=None, status=None, stream=None):
+    """fused_lz4_int8 over chunks first .. first+count-1 only (elements
+    dst_off[first] .. dst_off[first+count])."""
+    return _fused_range(_lib().lt_fused_lz4_int8_range, "lt_fused_lz4_int8_range", 1, table, scales, zp,
+                        shape, group, first, count, out, status, stream)
 
 
 # ------------------------------------------------------------------ streamed

@@ -275,7 +275,7 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   if (t->comp_off[0] != 0 || t->comp_off[n] > t->comp_bytes) return LT_ERR_INVALID_ARG;
   if (t->seq_off && (t->seq_off[0] != 0 || t->seq_off[n] > t->n_seq)) return LT_ERR_INVALID_ARG;
   for (uint64_t i = 0; i < n; i++) {
-    if (t->comp_off[i + 1] < t->comp_off[i]) return LT_ERR_INVALID_ARG;
+    if (t->comp_off[i + 1] < t->comp_off[i] || t->dst_off[i + 1] < t->dst_off[i]) return LT_ERR_INVALID_ARG;
     if (t->seq_off && t->seq_off[i + 1] < t->seq_off[i]) return LT_ERR_INVALID_ARG;
   }
   const uint64_t mb = meta_bytes(t);
@@ -379,6 +379,40 @@ lt_status fused_common(int mode, const lt_chunk_table *t, const uint16_t *scales
   return launch_chunks(mode, t, out, chunk_status, scales, zp, group, stream);
 }
 
+// A chunk range [first, first + count) of a device-resident table, decoded
+// into a buffer that holds only the range's output: the kernel addresses
+// output by global position, so the base pointer is moved back by the
+// range's first position (address arithmetic only; every write lands in
+// [out, out + range size), which the per-chunk bounds check guarantees).
+lt_status range_common(int mode, const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                       uint64_t rows, uint64_t cols, uint64_t group, uint32_t first, uint32_t count,
+                       uint64_t dst_first, uint64_t dst_last, void *out, int32_t *chunk_status, void *stream) {
+  if (!table_ok(t) || !out || !aligned16(out)) return LT_ERR_INVALID_ARG;
+  if ((uint64_t)first + count > t->n_chunks) return LT_ERR_INVALID_ARG;
+  if (dst_first > dst_last || dst_last > t->total_bytes || (dst_first & 15) != 0) return LT_ERR_INVALID_ARG;
+  uint64_t scale = 1;   // output bytes per decoded byte
+  if (mode != lt::MODE_BYTES) {
+    if (!scales || !shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
+    const uint64_t n = rows * cols;
+    if (mode == lt::MODE_INT4) {
+      if (n % 2 != 0 || t->total_bytes != n / 2) return LT_ERR_INVALID_ARG;
+      scale = 4;
+    } else {
+      if (t->total_bytes != n) return LT_ERR_INVALID_ARG;
+      scale = 2;
+    }
+  }
+  if (count == 0) return LT_OK;
+  lt::ChunkParams P = make_params(t, (void *)((uintptr_t)out - scale * dst_first), chunk_status, scales, zp, group);
+  P.comp_off = t->comp_off + first;
+  P.dst_off = t->dst_off + first;
+  if (t->seq_off) P.seq_off = t->seq_off + first;
+  P.n = count;
+  P.d_first = dst_first;
+  P.d_last = dst_last;
+  return launch_params(mode, P, stream);
+}
+
 lt_status stream_args(int mode, const lt_chunk_table *t, const uint16_t *scales, uint64_t rows, uint64_t cols,
                       uint64_t group, const void *out) {
   if (!table_ok(t) || !out || !aligned16(out)) return LT_ERR_INVALID_ARG;
@@ -462,6 +496,28 @@ lt_status lt_fused_lz4_int8(const lt_chunk_table *t, const uint16_t *scales, con
                             uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                             int32_t *chunk_status, void *stream) {
   return fused_common(lt::MODE_INT8, t, scales, zp, rows, cols, group, out, chunk_status, stream);
+}
+
+lt_status lt_decode_lz4_range(const lt_chunk_table *t, uint32_t first, uint32_t count, uint64_t dst_first,
+                              uint64_t dst_last, uint8_t *dst, int32_t *chunk_status, void *stream) {
+  return range_common(lt::MODE_BYTES, t, nullptr, nullptr, 0, 0, 0, first, count, dst_first, dst_last, dst,
+                      chunk_status, stream);
+}
+
+lt_status lt_fused_lz4_int4_range(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                                  uint64_t rows, uint64_t cols, uint64_t group, uint32_t first, uint32_t count,
+                                  uint64_t dst_first, uint64_t dst_last, uint16_t *out, int32_t *chunk_status,
+                                  void *stream) {
+  return range_common(lt::MODE_INT4, t, scales, zp, rows, cols, group, first, count, dst_first, dst_last, out,
+                      chunk_status, stream);
+}
+
+lt_status lt_fused_lz4_int8_range(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                                  uint64_t rows, uint64_t cols, uint64_t group, uint32_t first, uint32_t count,
+                                  uint64_t dst_first, uint64_t dst_last, uint16_t *out, int32_t *chunk_status,
+                                  void *stream) {
+  return range_common(lt::MODE_INT8, t, scales, zp, rows, cols, group, first, count, dst_first, dst_last, out,
+                      chunk_status, stream);
 }
 
 lt_status lt_stream_decode_lz4(const lt_chunk_table *host_table, uint8_t *dst, int32_t *chunk_status,

@@ -179,9 +179,10 @@ struct ChunkParams {
   const uint64_t *seq_off;   // optional sequence index (NULL: none)
   const uint32_t *seq_pos;
   uint64_t n_seq;            // entries in seq_pos
-  // A launch may cover a slice of a table (a batch of a streamed table):
-  // comp then holds the slice's compressed bytes, comp_off values count
-  // from comp_base, and the slice's chunks span dst_off d_first .. d_last.
+  // A launch may cover a slice of a table (a batch of a streamed table, a
+  // chunk range): comp_off values count from comp_base, and every chunk of
+  // the slice lies within dst_off d_first .. d_last, the first starting at
+  // d_first and the last ending at d_last.
   uint64_t comp_base;
   uint64_t d_first, d_last;
 };
@@ -1838,7 +1839,8 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   uint64_t c0 = P.comp_off[i], c1 = P.comp_off[i + 1];
   uint64_t d0 = P.dst_off[i], d1 = P.dst_off[i + 1];
   bool bad = c0 < P.comp_base || c0 > c1 || c1 - P.comp_base > P.comp_bytes || d0 > d1 || d1 > P.total ||
-             (i == 0 && d0 != P.d_first) || (i == P.n - 1 && d1 != P.d_last) || (d0 & 15) != 0 ||
+             d0 < P.d_first || d1 > P.d_last || (i == 0 && d0 != P.d_first) ||
+             (i == P.n - 1 && d1 != P.d_last) || (d0 & 15) != 0 ||
              d1 - d0 > (uint64_t)P.max_chunk || c1 - c0 > (uint64_t)LEN_CAP;
   c0 -= P.comp_base;
   c1 -= P.comp_base;
