@@ -15,6 +15,8 @@ What it computes (every function is the plain definition, written from):
   the roadmap's Phase 1.1 (INT4) and Phase 1.2 (INT8) worked examples.
 * fused = dequantize(decode(table)): the roadmap's CPU reference for its fused
   kernel (Phase 2.1).
+* CRC-32 of each chunk's compressed bytes, bit by bit from the polynomial: the
+  per-block checksum of the roadmap's container validation (Phase 6.1).
 """
 from __future__ import annotations
 
@@ -72,6 +74,8 @@ def lib():
             "ltref_fused_int8": (u32, [vp, u64, vp, vp, u32, u64, vp, vp, u64, u64, vp, vp, C.c_int]),
             "ltref_fused_int4_chunked": (u32, [vp, u64, vp, vp, u32, u64, vp, vp, u64, vp, vp, C.c_int]),
             "ltref_seqgen": (u64, [u64, u64, vp, u64, vp, u64, vp]),
+            "ltref_crc32": (u32, [vp, u64]),
+            "ltref_crc32_chunks": (None, [vp, vp, u32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -261,3 +265,22 @@ def fused_int4_chunked(t: Table, scales, zp, group: int, out: np.ndarray, thread
                                          t.n, t.total, _p(scales), _p(zp), group, _p(out),
                                          _p(status), threads)
     return int(bad), status[:t.n]
+
+
+# ----------------------------------------------------------------- CRC-32
+
+def crc32(data) -> int:
+    """CRC-32 (IEEE 802.3 / zlib polynomial) of a byte buffer, bit by bit."""
+    a = _c(np.frombuffer(bytes(data), np.uint8) if isinstance(data, (bytes, bytearray)) else data, np.uint8)
+    return int(lib().ltref_crc32(_p(a), a.size))
+
+
+def crc32_chunks(comp: np.ndarray, comp_off: np.ndarray) -> np.ndarray:
+    """One CRC-32 per chunk over its compressed bytes."""
+    comp = _c(comp, np.uint8)
+    comp_off = _c(comp_off, np.uint64)
+    n = comp_off.size - 1
+    out = np.zeros(max(n, 0), np.uint32)
+    if n > 0:
+        lib().ltref_crc32_chunks(_p(comp), _p(comp_off), n, _p(out))
+    return out

@@ -25,7 +25,12 @@
  *     roadmap's own CPU reference for its fused kernel (Phase 2.1 LZ4 + INT4
  *     Fused Kernel);
  *   - a random LZ4 sequence generator that builds a stream and its expected
- *     output side by side, independent of the compressor.
+ *     output side by side, independent of the compressor;
+ *   - CRC-32 (the IEEE 802.3 / zlib polynomial, bit-reflected, initial value
+ *     and final XOR all ones) of each chunk's compressed bytes, bit by bit
+ *     from the polynomial division: the per-block checksum the roadmap's
+ *     container validation asks for ("GPU Compression Pipeline - TDD
+ *     Roadmap", Phase 6.1), in a form whose definition is the polynomial.
  *
  * Floating point: the product (q - zp) * s has at most 19 significant bits, so
  * it is exact in fp64 (and in fp32); the only rounding is the final one to
@@ -548,4 +553,27 @@ uint64_t ltref_seqgen(uint64_t seed, uint64_t target, uint8_t *stream, uint64_t 
   free(lit);
   *out_len = op;
   return o;
+}
+
+/* ----------------------------------------------------------------- CRC-32 */
+
+/* CRC-32: the message, bits taken least significant first, times x^32, is
+ * divided by x^32 + x^26 + x^23 + x^22 + x^16 + x^12 + x^11 + x^10 + x^8 +
+ * x^7 + x^5 + x^4 + x^2 + x + 1; the register starts at all ones and the
+ * remainder is complemented.  In the reflected register the polynomial's
+ * low 32 coefficients read 0xEDB88320, and one step per message bit shifts
+ * the register right, subtracting (XOR) the polynomial when the bit shifted
+ * out is 1. */
+uint32_t ltref_crc32(const uint8_t *p, uint64_t n) {
+  uint32_t r = 0xFFFFFFFFu;
+  for (uint64_t i = 0; i < n; i++) {
+    r ^= p[i];
+    for (int b = 0; b < 8; b++) r = (r & 1u) ? (r >> 1) ^ 0xEDB88320u : (r >> 1);
+  }
+  return r ^ 0xFFFFFFFFu;
+}
+
+/* One CRC-32 per chunk over comp[comp_off[i] .. comp_off[i+1]). */
+void ltref_crc32_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n, uint32_t *crc) {
+  for (uint32_t i = 0; i < n; i++) crc[i] = ltref_crc32(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
 }
