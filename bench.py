@@ -256,7 +256,21 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "fill_fp16_GBps": round(2 * n_elem / ms_fill / 1e6, 1),
         "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
         "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),
+        "verify_crc32": verify_measurement(torch, lt, w, packed, dev, timed),
     }
+
+
+def verify_measurement(torch, lt, w, packed, dev, timed):
+    """lt_verify_chunks (CRC-32 of every chunk's compressed bytes against the
+    stored values) on the same table, as GB/s of compressed bytes."""
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev)
+    expect = torch.from_numpy(lt.checksum_chunks(comp, comp_off).view(np.int32)).to(dev)
+    got = torch.empty(table.n_chunks, dtype=torch.int32, device=dev)
+    status = torch.empty(table.n_chunks, dtype=torch.int32, device=dev)
+    ms = timed(lambda: lt.verify_chunks(table, expect, got, status))
+    lt.check_status(status)
+    return {"ms": round(ms, 4), "compressed_GBps": round(table.comp_bytes / ms / 1e6, 1)}
 
 
 def streamed_measurements(torch, lt, w, packed, scales, zp, dev, out, reps=10, per_half=512):

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 5
+#define LT_ABI_VERSION 6
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -64,7 +64,8 @@ enum {
   LT_CHUNK_BAD_OFFSET = 2,    /* match distance 0, or before the chunk start */
   LT_CHUNK_OVERRUN = 3,       /* a sequence would write past the chunk end */
   LT_CHUNK_SIZE_MISMATCH = 4, /* block decoded to fewer bytes than the chunk */
-  LT_CHUNK_BAD_TABLE = 5      /* the chunk's table entries are inconsistent */
+  LT_CHUNK_BAD_TABLE = 5,     /* the chunk's table entries are inconsistent */
+  LT_CHUNK_CHECKSUM = 6       /* lt_verify_chunks: stored bytes do not match their CRC-32 */
 };
 
 /* Largest decoded chunk the device decoder accepts (bytes).  It bounds a
@@ -214,6 +215,27 @@ lt_status lt_fused_lz4_int8_range(const lt_chunk_table *t, const uint16_t *scale
                                   void *stream);
 
 /*
+ * lt_verify_chunks -- per-chunk CRC-32 of the compressed bytes on the
+ * device, to validate stored blocks before they are decoded (the block
+ * checksum of the roadmap's container validation, "GPU Compression
+ * Pipeline - TDD Roadmap", Phase 6.1: a flipped stored byte must be
+ * reported as a checksum mismatch).  CRC-32 is the IEEE 802.3 / zlib CRC:
+ * polynomial 0x04C11DB7 bit-reflected, initial value and final XOR
+ * 0xFFFFFFFF; chunk i covers t->comp[comp_off[i] .. comp_off[i+1]).
+ *   expect        DEVICE uint32 [n_chunks] stored checksums, or NULL
+ *                 (compute only)
+ *   got           DEVICE uint32 [n_chunks], receives the computed values, or
+ *                 NULL
+ *   chunk_status  DEVICE int32 [n_chunks]: LT_CHUNK_OK, LT_CHUNK_CHECKSUM
+ *                 when expect[i] differs, LT_CHUNK_BAD_TABLE for offsets
+ *                 outside comp_bytes or decreasing (required with expect)
+ * Only comp, comp_off and comp_bytes of the table are read.  The host
+ * packer's lt_checksum_chunks computes the stored values.
+ */
+lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint32_t *got, int32_t *chunk_status,
+                           void *stream);
+
+/*
  * Streamed decode ("GPU Compression Pipeline - TDD Roadmap", Phase 5.1: the
  * transfer of one part overlaps the decompression of the part before, and
  * the result equals the sequential one).  The table's arrays -- comp,
@@ -251,6 +273,12 @@ lt_status lt_stream_fused_lz4_int4(const lt_chunk_table *host_table, const uint1
                                    void *copy_stream, void *stream);
 
 /* ---- host-side packer: builds the inputs above (no device work) ---- */
+
+/* CRC-32 of each chunk's compressed bytes (as lt_verify_chunks computes
+ * them on the device), on up to `threads` host threads (0: all).  crc has
+ * n_chunks entries. */
+lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint32_t *crc,
+                             int threads);
 
 /* Worst-case size of one LZ4 block holding n bytes. */
 uint64_t lt_lz4_bound(uint64_t n);

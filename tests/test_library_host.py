@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 5
+    assert lt.lib().lt_abi_version() == 6
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -298,3 +298,33 @@ def test_range_arguments_rejected_without_gpu():
     ptr = lambda a: a.ctypes.data_as(V)
     h = lt._Table(ptr(comp), ptr(coff), ptr(doff), 2, 4096, 32, 64)
     assert L.lt_stream_decode_lz4(C.byref(h), fake, None, fake, 1 << 20, None, None) == inv
+
+
+def test_checksum_chunks_matches_oracle():
+    """The host packer's per-chunk CRC-32 equals the oracle's (bit by bit from
+    the polynomial), on packer blocks and on arbitrary byte ranges."""
+    w = synth.int4_weight(64, 4096, 128, 6, chunking="mixed")
+    comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off)
+    assert np.array_equal(lt.checksum_chunks(comp, comp_off), O.crc32_chunks(comp, comp_off))
+    rng = np.random.default_rng(3)
+    buf = rng.integers(0, 256, 100000, dtype=np.uint8)
+    cuts = np.sort(rng.integers(0, buf.size, 60)).astype(np.uint64)
+    off = np.concatenate([[0], cuts, cuts[-1:], [buf.size]]).astype(np.uint64)   # includes an empty chunk
+    assert np.array_equal(lt.checksum_chunks(buf, off, threads=3), O.crc32_chunks(buf, off))
+    L = lt.lib()
+    V = C.c_void_p
+    ptr = lambda a: a.ctypes.data_as(V)
+    crc = np.zeros(2, np.uint32)
+    assert L.lt_checksum_chunks(ptr(buf), ptr(np.array([5, 1, 9], np.uint64)), 2, ptr(crc), 1) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_checksum_chunks(ptr(buf), None, 2, ptr(crc), 1) == lt.LT_ERR_INVALID_ARG
+
+
+def test_verify_arguments_rejected_without_gpu():
+    L = lt.lib()
+    fake = C.c_void_p(0x10000)
+    t = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 8192, 100)
+    assert L.lt_verify_chunks(None, None, fake, fake, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_verify_chunks(C.byref(t), None, None, None, None) == lt.LT_ERR_INVALID_ARG   # nowhere to report
+    assert L.lt_verify_chunks(C.byref(t), fake, fake, None, None) == lt.LT_ERR_INVALID_ARG   # expect needs status
+    empty = lt._Table(0, 0, 0, 0, 0, 0, 0)
+    assert L.lt_verify_chunks(C.byref(empty), None, fake, None, None) == lt.LT_OK

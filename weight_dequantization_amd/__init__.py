@@ -13,6 +13,8 @@ Device entry points (asynchronous on torch's current stream):
     dequant_int8(q, scales, zp, shape, group, out=None)      -> fp16 tensor
     fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
+Checksums (CRC-32 per chunk of the compressed bytes, on the device):
+    verify_chunks(table, expect=None) -> (got, status)
 Chunk ranges (only chunks first .. first+count-1, into a buffer for them):
     decode_lz4_range(table, first, count, out=None, status=None)
     fused_lz4_int4_range(table, scales, zp, shape, group, first, count, ...)
@@ -25,6 +27,7 @@ Host packer (numpy in, numpy out):
     pack_int4(codes) -> packed bytes (low nibble first)
     compress_chunks(src, dst_off, threads=0, max_dist=0) -> (comp, comp_off)
     index_chunks(comp, comp_off, threads=0) -> (seq_off, seq_pos)
+    checksum_chunks(comp, comp_off, threads=0) -> CRC-32 per chunk
     ChunkTable.build(src_bytes, dst_off, device) -> table resident on the GPU
     ChunkTable.build(src_bytes, dst_off, device="cpu", pin=True) -> pinned host table
 """
@@ -40,7 +43,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblt.so")
 
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE = range(5)
-CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE = range(6)
+(CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
+ CHUNK_CHECKSUM) = range(7)
 MAX_CHUNK_BYTES = 1 << 20
 SMALL_WINDOW = 11264      # LT_SMALL_WINDOW: tables within it decode with a 16 KiB history
 PACK_WINDOW = 4096        # the host packer's default match window (see ChunkTable.build)
@@ -90,6 +94,8 @@ def _lib():
             "lt_fused_lz4_int4_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int8_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
             "lt_stream_decode_lz4": (i32, [tp, vp, vp, vp, u64, vp, vp]),
+            "lt_verify_chunks": (i32, [tp, vp, vp, vp, vp]),
+            "lt_checksum_chunks": (i32, [vp, vp, u32, vp, i32]),
             "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
@@ -145,6 +151,18 @@ def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_
     if st != LT_OK:
         raise LtError(st, "lt_compress_chunks")
     return comp[:int(comp_off[-1])].copy(), comp_off
+
+
+def checksum_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0) -> np.ndarray:
+    """CRC-32 (zlib's) of each chunk's compressed bytes, uint32 [n]."""
+    comp = np.ascontiguousarray(comp, dtype=np.uint8)
+    comp_off = np.ascontiguousarray(comp_off, dtype=np.uint64)
+    n = comp_off.size - 1
+    crc = np.zeros(max(n, 1), np.uint32)
+    st = _lib().lt_checksum_chunks(_np_ptr(comp), _np_ptr(comp_off), max(n, 0), _np_ptr(crc), threads)
+    if st != LT_OK:
+        raise LtError(st, "lt_checksum_chunks")
+    return crc[:max(n, 0)]
 
 
 def index_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0):
@@ -353,6 +371,24 @@ def fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, s
                                     _dptr(out), _dptr(status), _stream_ptr(stream)),
            "lt_fused_lz4_int8")
     return out.view(rows, cols)
+
+
+# --------------------------------------------------------------- checksums
+
+def verify_chunks(table: ChunkTable, expect=None, got=None, status=None, stream=None):
+    """CRC-32 of each chunk's compressed bytes on the device.  With `expect`
+    (device uint32/int32 [n], as checksum_chunks computes) each chunk's
+    status is CHUNK_OK or CHUNK_CHECKSUM; returns (got, status)."""
+    torch = _torch()
+    dev = table.comp.device
+    if got is None:
+        got = torch.empty(max(table.n_chunks, 1), dtype=torch.int32, device=dev)
+    if status is None and expect is not None:
+        status = torch.empty(max(table.n_chunks, 1), dtype=torch.int32, device=dev)
+    t = table.as_c()
+    _check(_lib().lt_verify_chunks(C.byref(t), _dptr(expect), _dptr(got), _dptr(status), _stream_ptr(stream)),
+           "lt_verify_chunks")
+    return got, status
 
 
 # -------------------------------------------------------------- chunk range

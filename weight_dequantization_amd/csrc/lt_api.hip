@@ -12,6 +12,7 @@
 #include "lt.h"
 #include "lt_device.hpp"
 #include "lt_lz4.hpp"
+#include "lt_crc.hpp"
 
 namespace lt {
 
@@ -518,6 +519,24 @@ lt_status lt_fused_lz4_int8_range(const lt_chunk_table *t, const uint16_t *scale
                                   void *stream) {
   return range_common(lt::MODE_INT8, t, scales, zp, rows, cols, group, first, count, dst_first, dst_last, out,
                       chunk_status, stream);
+}
+
+lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint32_t *got, int32_t *chunk_status,
+                           void *stream) {
+  if (!table_ok(t)) return LT_ERR_INVALID_ARG;
+  if (!got && !chunk_status) return LT_ERR_INVALID_ARG;   // nothing to report into
+  if (expect && !chunk_status) return LT_ERR_INVALID_ARG;
+  if (t->n_chunks == 0) return LT_OK;
+  lt::CrcParams P;
+  P.comp = t->comp;
+  P.comp_off = t->comp_off;
+  P.comp_bytes = t->comp_bytes;
+  P.n = t->n_chunks;
+  P.expect = expect;
+  P.got = got;
+  P.status = chunk_status;
+  hipLaunchKernelGGL(lt::crc_kernel, dim3(t->n_chunks), dim3(lt::CRC_THREADS), 0, (hipStream_t)stream, P);
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
 
 lt_status lt_stream_decode_lz4(const lt_chunk_table *host_table, uint8_t *dst, int32_t *chunk_status,

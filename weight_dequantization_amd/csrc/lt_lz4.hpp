@@ -121,7 +121,7 @@ constexpr int SLEEP_FEED = 2;         // feeder waiting for ring space
 constexpr uint32_t LEN_CAP = 1u << 31;
 
 enum : uint32_t { ST_RUN = 0, ST_DONE = 1, ST_FAIL = 2 };
-enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5 };
+enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5, C_CHECKSUM = 6 };
 // MODE_INT4G is MODE_INT4 for groups that are a power of two of at least
 // 128 codes, where a tile spans at most 17 groups (its own kernel, with a
 // leaner scale / zero-point fetch).

@@ -178,6 +178,34 @@ void parallel_chunks(uint32_t n, int threads, F &&fn) {
   for (auto &th : pool) th.join();
 }
 
+// CRC-32 (IEEE 802.3 / zlib polynomial, reflected), eight bytes per step:
+// table k maps a byte to its register contribution when k zero bytes
+// follow it.
+struct CrcTables {
+  uint32_t t[8][256];
+  CrcTables() {
+    for (uint32_t v = 0; v < 256; v++) {
+      uint32_t c = v;
+      for (int b = 0; b < 8; b++) c = (c & 1u) ? (c >> 1) ^ 0xEDB88320u : c >> 1;
+      t[0][v] = c;
+    }
+    for (int k = 1; k < 8; k++)
+      for (uint32_t v = 0; v < 256; v++) t[k][v] = (t[k - 1][v] >> 8) ^ t[0][t[k - 1][v] & 255];
+  }
+};
+
+uint32_t crc32_bytes(const uint8_t *p, uint64_t n) {
+  static const CrcTables T;
+  uint32_t r = 0xFFFFFFFFu;
+  for (; n >= 8; n -= 8, p += 8) {
+    const uint32_t lo = r ^ rd32(p), hi = rd32(p + 4);
+    r = T.t[7][lo & 255] ^ T.t[6][(lo >> 8) & 255] ^ T.t[5][(lo >> 16) & 255] ^ T.t[4][lo >> 24] ^
+        T.t[3][hi & 255] ^ T.t[2][(hi >> 8) & 255] ^ T.t[1][(hi >> 16) & 255] ^ T.t[0][hi >> 24];
+  }
+  for (; n > 0; n--, p++) r = (r >> 8) ^ T.t[0][(r ^ *p) & 255];
+  return r ^ 0xFFFFFFFFu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +284,19 @@ lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_
   parallel_chunks(n_chunks, threads, [&](uint32_t i) {
     uint32_t *out = seq_pos + seq_off[i];
     walk_block(comp + comp_off[i], comp_off[i + 1] - comp_off[i], [&](uint64_t p) { *out++ = (uint32_t)p; });
+  });
+  return LT_OK;
+}
+
+lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint32_t *crc,
+                             int threads) {
+  if (!comp_off || !crc) return LT_ERR_INVALID_ARG;
+  if (n_chunks == 0) return LT_OK;
+  if (!comp) return LT_ERR_INVALID_ARG;
+  for (uint32_t i = 0; i < n_chunks; i++)
+    if (comp_off[i + 1] < comp_off[i]) return LT_ERR_INVALID_ARG;
+  parallel_chunks(n_chunks, threads, [&](uint32_t i) {
+    crc[i] = crc32_bytes(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
   });
   return LT_OK;
 }
