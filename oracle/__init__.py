@@ -15,6 +15,9 @@ What it computes (every function is the plain definition, written from):
   the roadmap's Phase 1.1 (INT4) and Phase 1.2 (INT8) worked examples.
 * fused = dequantize(decode(table)): the roadmap's CPU reference for its fused
   kernel (Phase 2.1).
+* zero-run coding of fp16 activations (per 1024-element block a nonzero bitmap,
+  then the nonzero values in order): the pages' zero-run encoding of ReLU
+  outputs, in the bitmap form the GPU decoder reads.
 * CRC-32 of each chunk's compressed bytes, bit by bit from the polynomial: the
   per-block checksum of the roadmap's container validation (Phase 6.1).
 """
@@ -75,6 +78,8 @@ def lib():
             "ltref_fused_int4_chunked": (u32, [vp, u64, vp, vp, u32, u64, vp, vp, u64, vp, vp, C.c_int]),
             "ltref_seqgen": (u64, [u64, u64, vp, u64, vp, u64, vp]),
             "ltref_crc32": (u32, [vp, u64]),
+            "ltref_zr_encode": (u64, [vp, u64, vp, vp, vp]),
+            "ltref_zr_decode": (None, [vp, vp, vp, u64, u64, vp, vp]),
             "ltref_crc32_chunks": (None, [vp, vp, u32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -284,3 +289,34 @@ def crc32_chunks(comp: np.ndarray, comp_off: np.ndarray) -> np.ndarray:
     if n > 0:
         lib().ltref_crc32_chunks(_p(comp), _p(comp_off), n, _p(out))
     return out
+
+
+# ------------------------------------------------------------- zero runs
+
+ZR_BLOCK = 1024
+
+
+def zr_encode(x: np.ndarray):
+    """Zero-run coding of fp16 bits: (bitmap uint32 [32 per block],
+    val_off uint64 [blocks+1], vals uint16 [nonzeros])."""
+    x = _c(x, np.uint16).ravel()
+    nb = (x.size + ZR_BLOCK - 1) // ZR_BLOCK
+    bitmap = np.zeros(max(32 * nb, 1), np.uint32)
+    val_off = np.zeros(nb + 1, np.uint64)
+    vals = np.zeros(max(x.size, 1), np.uint16)
+    m = lib().ltref_zr_encode(_p(x), x.size, _p(bitmap), _p(val_off), _p(vals))
+    return bitmap[:32 * nb], val_off, vals[:m].copy()
+
+
+def zr_decode(bitmap, val_off, vals, n: int, out=None):
+    """Inverse of zr_encode; returns (out uint16 [n], status int32 [blocks])."""
+    bitmap = _c(bitmap, np.uint32)
+    val_off = _c(val_off, np.uint64)
+    vals = _c(vals, np.uint16)
+    nb = (n + ZR_BLOCK - 1) // ZR_BLOCK
+    if out is None:
+        out = np.zeros(max(n, 1), np.uint16)
+    st = np.zeros(max(nb, 1), np.int32)
+    lib().ltref_zr_decode(_p(bitmap), _p(val_off), _p(vals if vals.size else np.zeros(1, np.uint16)), n,
+                          vals.size, _p(out), _p(st))
+    return out[:n], st[:nb]

@@ -26,6 +26,11 @@
  *     Fused Kernel);
  *   - a random LZ4 sequence generator that builds a stream and its expected
  *     output side by side, independent of the compressor;
+ *   - zero-run coding of fp16 activations (the pages' zero-run encoding for
+ *     ReLU outputs, "runs of zeros" stored instead of full arrays): per block
+ *     of 1024 elements a bitmap marks the nonzero elements, and the nonzero
+ *     values follow in element order; element bits are compared, so -0.0
+ *     counts as nonzero and the round trip is exact;
  *   - CRC-32 (the IEEE 802.3 / zlib polynomial, bit-reflected, initial value
  *     and final XOR all ones) of each chunk's compressed bytes, bit by bit
  *     from the polynomial division: the per-block checksum the roadmap's
@@ -576,4 +581,53 @@ uint32_t ltref_crc32(const uint8_t *p, uint64_t n) {
 /* One CRC-32 per chunk over comp[comp_off[i] .. comp_off[i+1]). */
 void ltref_crc32_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n, uint32_t *crc) {
   for (uint32_t i = 0; i < n; i++) crc[i] = ltref_crc32(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
+}
+
+/* ------------------------------------------------------------ zero runs */
+
+/* Block b covers elements [1024 b, min(1024 (b + 1), n)).  Bit k of bitmap
+ * word w stands for element 32 w + k and is 1 when that element's bits are
+ * not all zero.  val_off[b] counts the nonzero elements before block b;
+ * vals lists the nonzero elements in order.  Returns the nonzero count. */
+uint64_t ltref_zr_encode(const uint16_t *x, uint64_t n, uint32_t *bitmap, uint64_t *val_off, uint16_t *vals) {
+  const uint64_t nb = (n + 1023) / 1024;
+  uint64_t m = 0;
+  for (uint64_t b = 0; b < nb; b++) {
+    val_off[b] = m;
+    for (uint64_t w = 0; w < 32; w++) bitmap[32 * b + w] = 0;
+    for (uint64_t e = 1024 * b; e < n && e < 1024 * (b + 1); e++) {
+      if (x[e] != 0) {
+        bitmap[e / 32] |= 1u << (e % 32);
+        vals[m++] = x[e];
+      }
+    }
+  }
+  val_off[nb] = m;
+  return m;
+}
+
+/* Inverse of the above: each element is its next listed value when its bit
+ * is set, else zero.  Block status 0 when the block's bit count equals its
+ * val_off span within n_vals and no bit is set past n; otherwise 5 (the
+ * table's entries are inconsistent) and the block's output is left as it
+ * was. */
+void ltref_zr_decode(const uint32_t *bitmap, const uint64_t *val_off, const uint16_t *vals, uint64_t n,
+                     uint64_t n_vals, uint16_t *out, int32_t *status) {
+  const uint64_t nb = (n + 1023) / 1024;
+  for (uint64_t b = 0; b < nb; b++) {
+    uint64_t bits = 0, past = 0;
+    for (uint64_t e = 1024 * b; e < 1024 * (b + 1); e++) {
+      const int set = (bitmap[e / 32] >> (e % 32)) & 1u;
+      bits += set;
+      if (set && e >= n) past = 1;
+    }
+    if (past || val_off[b] > val_off[b + 1] || val_off[b + 1] > n_vals || val_off[b + 1] - val_off[b] != bits) {
+      if (status) status[b] = 5;
+      continue;
+    }
+    uint64_t m = val_off[b];
+    for (uint64_t e = 1024 * b; e < n && e < 1024 * (b + 1); e++)
+      out[e] = ((bitmap[e / 32] >> (e % 32)) & 1u) ? vals[m++] : 0;
+    if (status) status[b] = 0;
+  }
 }
