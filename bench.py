@@ -257,6 +257,32 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
         "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),
         "verify_crc32": verify_measurement(torch, lt, w, packed, dev, timed),
+        "activations_4096x14336": activation_measurements(torch, lt, dev, timed),
+    }
+
+
+def activation_measurements(torch, lt, dev, timed):
+    """The ReLU activation workload (4096x14336 fp16, about 90% zeros) two
+    ways: zero-run coded (bitmap + values) and LZ4 chunks, decode-only; the
+    coded size and GB/s of coded input + fp16 output."""
+    import synth
+    a = synth.config4()
+    x = a.data.view(np.uint16)
+    bitmap, val_off, vals = lt.encode_zero_runs(x)
+    z = lt.ZeroRunTensor.from_host(bitmap, val_off, vals, x.size, dev)
+    out = torch.empty(x.size, dtype=torch.float16, device=dev)
+    zr_in = bitmap.nbytes + val_off.nbytes + vals.nbytes
+    ms_zr = timed(lambda: lt.decode_zero_runs(z, out=out))
+    assert torch.equal(out.view(torch.int16).cpu(), torch.from_numpy(x.view(np.int16)))
+    table = lt.ChunkTable.build(a.data, a.dst_off, dev)
+    ob = out.view(torch.uint8)
+    ms_lz = timed(lambda: lt.decode_lz4(table, out=ob))
+    return {
+        "fp16_bytes": int(a.data.size),
+        "zero_runs": {"coded_bytes": int(zr_in), "ms": round(ms_zr, 4),
+                      "GBps": round((zr_in + a.data.size) / ms_zr / 1e6, 1)},
+        "lz4_decode_only": {"coded_bytes": int(table.comp_bytes), "ms": round(ms_lz, 4),
+                            "GBps": round((table.comp_bytes + a.data.size) / ms_lz / 1e6, 1)},
     }
 
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 6
+#define LT_ABI_VERSION 7
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -215,6 +215,37 @@ lt_status lt_fused_lz4_int8_range(const lt_chunk_table *t, const uint16_t *scale
                                   void *stream);
 
 /*
+ * Zero-run coding of fp16 activations (page "Openai/692db884-...
+ * (section 28)", zero-run encoding: the zero slices of ReLU outputs stored
+ * as runs of zeros instead of full arrays), in a block form every GPU wave
+ * decodes on its own: the tensor of n_elem fp16 elements is cut into blocks
+ * of LT_ZR_BLOCK elements (the last may be partial).
+ *   bitmap   uint32 [32 per block]: bit k of word w of block b is 1 when
+ *            element LT_ZR_BLOCK*b + 32w + k is nonzero (its 16 bits are
+ *            not all zero, so -0.0 is kept); bits past n_elem are 0
+ *   val_off  uint64 [blocks + 1]: nonzero elements before block b
+ *   vals     uint16 [n_vals]: the nonzero elements in order (fp16 bits)
+ */
+#define LT_ZR_BLOCK 1024
+typedef struct lt_zr_tensor {
+  const uint32_t *bitmap;
+  const uint64_t *val_off;
+  const uint16_t *vals;     /* may be NULL when n_vals == 0 */
+  uint64_t n_elem;
+  uint64_t n_vals;
+} lt_zr_tensor;
+
+/*
+ * lt_decode_zero_runs -- expand a zero-run coded tensor on the device.  All
+ * arrays of *z are DEVICE memory; out: DEVICE uint16 [n_elem], 16-byte
+ * aligned.  block_status (optional, DEVICE int32 [blocks]): LT_CHUNK_OK, or
+ * LT_CHUNK_BAD_TABLE when a block's bit count differs from its val_off
+ * span, val_off leaves [0, n_vals] or a bit past n_elem is set; such a
+ * block writes nothing.  Output equals the input of lt_encode_zero_runs.
+ */
+lt_status lt_decode_zero_runs(const lt_zr_tensor *z, uint16_t *out, int32_t *block_status, void *stream);
+
+/*
  * lt_verify_chunks -- per-chunk CRC-32 of the compressed bytes on the
  * device, to validate stored blocks before they are decoded (the block
  * checksum of the roadmap's container validation, "GPU Compression
@@ -273,6 +304,13 @@ lt_status lt_stream_fused_lz4_int4(const lt_chunk_table *host_table, const uint1
                                    void *copy_stream, void *stream);
 
 /* ---- host-side packer: builds the inputs above (no device work) ---- */
+
+/* Zero-run coding on the host (HOST arrays): bitmap [32 per block] and
+ * val_off [blocks + 1] are always written; vals (capacity vals_cap) only
+ * when not NULL, so a first call with vals NULL gives the size in
+ * val_off[blocks].  LT_ERR_INVALID_ARG when vals_cap is too small. */
+lt_status lt_encode_zero_runs(const uint16_t *x, uint64_t n, uint32_t *bitmap, uint64_t *val_off, uint16_t *vals,
+                              uint64_t vals_cap, int threads);
 
 /* CRC-32 of each chunk's compressed bytes (as lt_verify_chunks computes
  * them on the device), on up to `threads` host threads (0: all).  crc has

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 6
+    assert lt.lib().lt_abi_version() == 7
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -328,3 +328,41 @@ def test_verify_arguments_rejected_without_gpu():
     assert L.lt_verify_chunks(C.byref(t), fake, fake, None, None) == lt.LT_ERR_INVALID_ARG   # expect needs status
     empty = lt._Table(0, 0, 0, 0, 0, 0, 0)
     assert L.lt_verify_chunks(C.byref(empty), None, fake, None, None) == lt.LT_OK
+
+
+def test_encode_zero_runs_matches_oracle():
+    """The host zero-run encoder writes the oracle's bitmap, offsets and
+    values, for ReLU-shaped data at lengths around the block size and for
+    the activation workload's stress patterns."""
+    rng = np.random.default_rng(5)
+    for n in (0, 1, 31, 1023, 1024, 1025, 4097, 100001):
+        x = np.maximum(0, rng.standard_normal(n) - 1.3).astype(np.float16).view(np.uint16).copy()
+        if n > 40:
+            x[7] = 0x8000
+            x[33] = 0x0001
+        got = lt.encode_zero_runs(x, threads=3)
+        ref = O.zr_encode(x)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r), n
+    a = synth.activation(64, 4096, 4, stress_frac=0.05)
+    x = a.data.view(np.uint16)
+    for g, r in zip(lt.encode_zero_runs(x), O.zr_encode(x)):
+        assert np.array_equal(g, r)
+
+
+def test_zero_run_arguments_rejected_without_gpu():
+    L = lt.lib()
+    fake = C.c_void_p(0x10000)
+    z = lt._ZrTensor(0x10000, 0x10000, 0x10000, 4096, 10)
+    assert L.lt_decode_zero_runs(None, fake, None, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_decode_zero_runs(C.byref(z), C.c_void_p(0x10002), None, None) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_decode_zero_runs(C.byref(lt._ZrTensor(0x10000, None, 0x10000, 4096, 10)), fake, None, None) \
+        == lt.LT_ERR_INVALID_ARG
+    assert L.lt_decode_zero_runs(C.byref(lt._ZrTensor(0x10000, 0x10000, None, 4096, 10)), fake, None, None) \
+        == lt.LT_ERR_INVALID_ARG
+    assert L.lt_decode_zero_runs(C.byref(lt._ZrTensor(None, None, None, 0, 0)), fake, None, None) == lt.LT_OK
+    x = np.ones(10, np.uint16)
+    bm, vo, vals = np.zeros(32, np.uint32), np.zeros(2, np.uint64), np.zeros(4, np.uint16)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    assert L.lt_encode_zero_runs(p(x), 10, p(bm), p(vo), p(vals), 4, 1) == lt.LT_ERR_INVALID_ARG   # 10 values
+    assert L.lt_encode_zero_runs(p(x), 10, p(bm), p(vo), None, 0, 1) == lt.LT_OK and vo[1] == 10

@@ -13,6 +13,9 @@ Device entry points (asynchronous on torch's current stream):
     dequant_int8(q, scales, zp, shape, group, out=None)      -> fp16 tensor
     fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
+Zero-run coding of fp16 activations (bitmap + nonzero values per block):
+    encode_zero_runs(x) -> (bitmap, val_off, vals)        (host)
+    ZeroRunTensor.build(x, device); decode_zero_runs(z, out=None, status=None)
 Checksums (CRC-32 per chunk of the compressed bytes, on the device):
     verify_chunks(table, expect=None) -> (got, status)
 Chunk ranges (only chunks first .. first+count-1, into a buffer for them):
@@ -72,6 +75,13 @@ class _Table(C.Structure):
                 ("seq_off", C.c_void_p), ("seq_pos", C.c_void_p), ("n_seq", C.c_uint64)]
 
 
+class _ZrTensor(C.Structure):
+    _fields_ = [("bitmap", C.c_void_p), ("val_off", C.c_void_p), ("vals", C.c_void_p),
+                ("n_elem", C.c_uint64), ("n_vals", C.c_uint64)]
+
+
+ZR_BLOCK = 1024          # LT_ZR_BLOCK
+
 _L = None
 
 
@@ -95,6 +105,8 @@ def _lib():
             "lt_fused_lz4_int8_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
             "lt_stream_decode_lz4": (i32, [tp, vp, vp, vp, u64, vp, vp]),
             "lt_verify_chunks": (i32, [tp, vp, vp, vp, vp]),
+            "lt_decode_zero_runs": (i32, [C.POINTER(_ZrTensor), vp, vp, vp]),
+            "lt_encode_zero_runs": (i32, [vp, u64, vp, vp, vp, u64, i32]),
             "lt_checksum_chunks": (i32, [vp, vp, u32, vp, i32]),
             "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
@@ -163,6 +175,25 @@ def checksum_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0) ->
     if st != LT_OK:
         raise LtError(st, "lt_checksum_chunks")
     return crc[:max(n, 0)]
+
+
+def encode_zero_runs(x: np.ndarray, threads: int = 0):
+    """Zero-run coding of fp16 data (uint16 bits or float16): returns
+    (bitmap uint32 [32 per block], val_off uint64 [blocks+1], vals uint16)."""
+    x = np.ascontiguousarray(x).view(np.uint16).ravel()
+    nb = (x.size + ZR_BLOCK - 1) // ZR_BLOCK
+    bitmap = np.zeros(max(32 * nb, 1), np.uint32)
+    val_off = np.zeros(nb + 1, np.uint64)
+    L = _lib()
+    st = L.lt_encode_zero_runs(_np_ptr(x), x.size, _np_ptr(bitmap), _np_ptr(val_off), None, 0, threads)
+    if st != LT_OK:
+        raise LtError(st, "lt_encode_zero_runs")
+    vals = np.zeros(max(int(val_off[-1]), 1), np.uint16)
+    st = L.lt_encode_zero_runs(_np_ptr(x), x.size, _np_ptr(bitmap), _np_ptr(val_off), _np_ptr(vals), vals.size,
+                               threads)
+    if st != LT_OK:
+        raise LtError(st, "lt_encode_zero_runs")
+    return bitmap[:32 * nb], val_off, vals[:int(val_off[-1])]
 
 
 def index_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0):
@@ -371,6 +402,50 @@ def fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, s
                                     _dptr(out), _dptr(status), _stream_ptr(stream)),
            "lt_fused_lz4_int8")
     return out.view(rows, cols)
+
+
+# -------------------------------------------------------------- zero runs
+
+@dataclass
+class ZeroRunTensor:
+    """A zero-run coded fp16 tensor resident on the GPU (lt_zr_tensor)."""
+    bitmap: object          # torch.int32 [32 per block] (read as uint32)
+    val_off: object         # torch.int64 [blocks+1] (read as uint64)
+    vals: object            # torch.int16 [n_vals] (fp16 bits)
+    n_elem: int
+    n_vals: int
+
+    @classmethod
+    def build(cls, x: np.ndarray, device="cuda", threads: int = 0):
+        """Encode on the host (encode_zero_runs) and upload."""
+        bitmap, val_off, vals = encode_zero_runs(x, threads)
+        return cls.from_host(bitmap, val_off, vals, int(np.asarray(x).size), device)
+
+    @classmethod
+    def from_host(cls, bitmap, val_off, vals, n_elem: int, device="cuda"):
+        torch = _torch()
+        bitmap = np.ascontiguousarray(bitmap, np.uint32)
+        vals = np.ascontiguousarray(vals, np.uint16)
+        n_vals = int(vals.size)
+        return cls(torch.from_numpy((bitmap if bitmap.size else np.zeros(1, np.uint32)).view(np.int32).copy()).to(device),
+                   torch.from_numpy(np.ascontiguousarray(val_off, np.uint64).view(np.int64).copy()).to(device),
+                   torch.from_numpy((vals if vals.size else np.zeros(8, np.uint16)).view(np.int16).copy()).to(device),
+                   int(n_elem), n_vals)
+
+    def as_c(self) -> _ZrTensor:
+        return _ZrTensor(self.bitmap.data_ptr(), self.val_off.data_ptr(), self.vals.data_ptr(), self.n_elem,
+                         self.n_vals)
+
+
+def decode_zero_runs(z: ZeroRunTensor, out=None, status=None, stream=None):
+    """Expand a zero-run coded tensor into fp16 (flat [n_elem])."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(max(z.n_elem, 1), dtype=torch.float16, device=z.bitmap.device)
+    c = z.as_c()
+    _check(_lib().lt_decode_zero_runs(C.byref(c), _dptr(out), _dptr(status), _stream_ptr(stream)),
+           "lt_decode_zero_runs")
+    return out[:z.n_elem] if out.numel() > z.n_elem else out
 
 
 # --------------------------------------------------------------- checksums

@@ -13,6 +13,7 @@
 #include "lt_device.hpp"
 #include "lt_lz4.hpp"
 #include "lt_crc.hpp"
+#include "lt_zr.hpp"
 
 namespace lt {
 
@@ -519,6 +520,27 @@ lt_status lt_fused_lz4_int8_range(const lt_chunk_table *t, const uint16_t *scale
                                   void *stream) {
   return range_common(lt::MODE_INT8, t, scales, zp, rows, cols, group, first, count, dst_first, dst_last, out,
                       chunk_status, stream);
+}
+
+lt_status lt_decode_zero_runs(const lt_zr_tensor *z, uint16_t *out, int32_t *block_status, void *stream) {
+  static_assert(lt::ZR_BLOCK == LT_ZR_BLOCK, "block size");
+  if (!z || !out || !aligned16(out)) return LT_ERR_INVALID_ARG;
+  if (z->n_elem == 0) return LT_OK;
+  if (!z->bitmap || !z->val_off || (!z->vals && z->n_vals)) return LT_ERR_INVALID_ARG;
+  if (z->n_elem > (1ull << 48)) return LT_ERR_INVALID_ARG;
+  lt::ZrParams P;
+  P.bitmap = z->bitmap;
+  P.val_off = z->val_off;
+  P.vals = z->vals;
+  P.n = z->n_elem;
+  P.n_vals = z->n_vals;
+  P.nb = (z->n_elem + LT_ZR_BLOCK - 1) / LT_ZR_BLOCK;
+  P.out = out;
+  P.status = block_status;
+  const uint64_t grid = (P.nb + lt::ZR_WAVES - 1) / lt::ZR_WAVES;
+  if (grid > 0x7FFFFFFFull) return LT_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(lt::zr_decode_kernel, dim3((uint32_t)grid), dim3(64 * lt::ZR_WAVES), 0, (hipStream_t)stream, P);
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
 
 lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint32_t *got, int32_t *chunk_status,

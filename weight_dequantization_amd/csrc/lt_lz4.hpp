@@ -111,7 +111,11 @@ constexpr int NB = 5;                 // builder waves
 constexpr int NWAVES = 3 + NB;        // walker, recorder, feeder, builders
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr uint32_t NSLOT = 8;         // counter array length (>= NB + 1)
-constexpr uint32_t BULK_RECS = 16;    // most sequences in a tile built in one pass
+// A tile is built in passes (one, plus one per copy that reads the tile
+// itself) when it has at most BULK_RECS records, or when its passes number
+// at most one per BULK_RATIO records; otherwise record by record.
+constexpr uint32_t BULK_RECS = 16;
+constexpr uint32_t BULK_RATIO = 8;
 // Poll intervals (s_sleep units of 64 cycles).  Waiting waves share the CU's
 // scalar unit and LDS with the walkers, so they poll no faster than the
 // walk can change what they wait for.
@@ -491,10 +495,9 @@ struct Rec {
     }
     const uint64_t bad = __ballot(err != C_OK);
     const uint32_t f = bad ? (uint32_t)__builtin_ctzll(bad) : n;   // records before the first failure
-    // fill byte of distance-1 runs: the last literal, or the previous
-    // record's fill when this record has no literals
-    const uint32_t pfo = lane_below(dist == 1 && L > 0 && !lit ? 1u : 0u);
-    const uint32_t pfb = lane_below(lastlit);
+    // fill byte of distance-1 runs: the last literal, or, when this record
+    // has no literals, the byte the previous record's run repeats (so a
+    // chain of runs without literals between them carries it on)
     uint32_t fok, fb;
     if (L > 0) {
       fok = 1;
@@ -503,8 +506,22 @@ struct Rec {
       fok = fill_ok;
       fb = fill;
     } else {
-      fok = pfo;
-      fb = pfb;
+      fok = 0;
+      fb = 0;
+    }
+    {
+      const bool inherits = L == 0 && lane > 0;
+      const bool run = dist == 1 && !lit && !last;
+      for (;;) {
+        const uint32_t po = lane_below(run && fok ? 1u : 0u);
+        const uint32_t pb = lane_below(fb);
+        const bool take = inherits && !fok && po != 0;
+        if (!__ballot(take)) break;
+        if (take) {
+          fok = 1;
+          fb = pb;
+        }
+      }
     }
     uint32_t info = last ? F_LAST : (lit ? 0u : (F_MATCH | dist));
     if (!last && !lit && dist == 1 && fok) info |= F_FILL | (fb << 16);
@@ -1611,8 +1628,8 @@ struct Builder {
   // ring for literals, the history ring (q - dist) for matches; the 20 bytes
   // that cover the block are read with one 16-byte and one 4-byte LDS load
   // unless they wrap around the ring's end.
-  __device__ __forceinline__ uint4 piece(uint4 rv, uint32_t rve, uint32_t P, uint32_t bend, uint32_t inr_at,
-                                         uint32_t hist_at, uint32_t &pos, uint32_t &j) {
+  __device__ __forceinline__ uint4 piece(uint4 rv, uint32_t rve, uint32_t T, uint32_t P, uint32_t bend,
+                                         uint32_t inr_at, uint32_t hist_at, uint32_t &pos, uint32_t &j) {
     typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
     const uint32_t j4 = 4 * j;
     const uint32_t os = __builtin_amdgcn_ds_bpermute(j4, rv.x);
@@ -1649,6 +1666,13 @@ struct Builder {
     if (!lit && (info & F_FILL)) {   // a run of the byte the record carries
       const uint32_t fw = __builtin_amdgcn_perm(0u, info, 0x02020202u);
       v = make_uint4(fw, fw, fw, fw);
+    } else if (!lit && rec_dist(info) == 1) {
+      // a run of the byte before the run's part in this tile (the byte
+      // before the run, or the tile's previous byte, itself of the run)
+      const uint32_t at = (le > T ? le : T) - 1;
+      const uint32_t fw = (uint32_t)*(const __attribute__((address_space(3))) uint8_t *)(uintptr_t)(
+                              hist_at + (at & HMASK)) * 0x01010101u;
+      v = make_uint4(fw, fw, fw, fw);
     }
     const bool active = pos < bend;
     j = (active && pe >= re) ? j + 1 : j;
@@ -1681,10 +1705,10 @@ struct Builder {
     const uint32_t inr_at = lds_addr(sm.inr), hist_at = lds_addr(sm.hist);
     for (uint32_t pass = 0; pass <= extra; pass++) {
       uint32_t pos = P, j = j0;
-      uint4 acc = piece(rv, rve, P, bend, inr_at, hist_at, pos, j);
+      uint4 acc = piece(rv, rve, T, P, bend, inr_at, hist_at, pos, j);
       while (__ballot(pos < bend)) {
         const int c8 = (int)(8 * (pos - P));   // bytes before pos are kept
-        const uint4 v = piece(rv, rve, P, bend, inr_at, hist_at, pos, j);
+        const uint4 v = piece(rv, rve, T, P, bend, inr_at, hist_at, pos, j);
         acc.x = keep_low(acc.x, v.x, c8);
         acc.y = keep_low(acc.y, v.y, c8 - 32);
         acc.z = keep_low(acc.z, v.z, c8 - 64);
@@ -1740,10 +1764,10 @@ struct Builder {
       const uint32_t m = __builtin_popcountll(__ballot(jr < nrec && rv.x < Tend));
       // classify: one pass possible?  how many passes?  which input and
       // which earlier tiles are read?
-      // (the sources' bound also serves hard tiles when every record of the
-      // tile is in the 64 lanes; otherwise those wait for all earlier tiles)
-      bool hard = m > BULK_RECS;
+      // (the sources' bound also serves hard tiles; a tile of 64 records or
+      // more takes it from a scan of all its records)
       const bool seen = m < 64;
+      bool hard = !seen;
       uint32_t extra = 0, src_need = 0, in_end = 0;
       if (seen) {   // lane i looks at record i
         const bool mine = lane < m;
@@ -1753,9 +1777,12 @@ struct Builder {
         const uint32_t pend = re < Tend ? re : Tend;
         const bool copy = mine && base < pend && !(rv.w & F_FILL);
         const uint32_t dist = rec_dist(rv.w);
-        const uint32_t s_hi = pend - dist;   // the copy's sources end here
-        if (__ballot(copy && (dist < 16 || dist < pend - base))) hard = true;   // overlapping copy
+        // the copy's sources end here; a distance-1 run without its byte
+        // reads the one byte before base
+        const uint32_t s_hi = dist == 1 ? base : pend - dist;
+        if (__ballot(copy && dist > 1 && (dist < 16 || dist < pend - base))) hard = true;   // overlapping copy
         extra = (uint32_t)__builtin_popcountll(__ballot(copy && s_hi > T));        // reads this tile
+        if (m > BULK_RECS && BULK_RATIO * (1 + extra) > m) hard = true;
         const uint64_t lits = __ballot(lit);
         if (lits) {   // the last literal run in the tile ends the input it reads
           const uint32_t li = 63 - __builtin_clzll(lits);
@@ -1770,10 +1797,35 @@ struct Builder {
           const uint32_t v = __builtin_amdgcn_readlane(s_fin, ci);
           src_need = v > src_need ? v : src_need;
         }
+      } else {
+        // 64 records or more: built record by record, after the earlier
+        // tiles its copies read (every record of the tile is in the ring)
+        for (uint32_t w = 0;; w += 64) {
+          const uint32_t jw = k + w + lane;
+          uint4 r2 = make_uint4(cov, 0u, 0u, 0u);
+          uint32_t re2 = cov;
+          if (jw < nrec) r2 = sm.recs[ridx_lane(k + w, lane)];
+          if (jw + 1 < nrec) re2 = sm.recs[ridx_lane(k + w + 1, lane)].x;
+          const bool mine = jw < nrec && r2.x < Tend;
+          const uint32_t le = r2.x + r2.z;
+          const uint32_t base = le > T ? le : T;
+          const uint32_t pend = re2 < Tend ? re2 : Tend;
+          const bool copy = mine && base < pend && !(r2.w & F_FILL);
+          const uint32_t s_hi = rec_dist(r2.w) == 1 ? base : pend - rec_dist(r2.w);
+          const uint32_t s_fin = copy ? (s_hi < T ? s_hi : T) : 0u;
+          uint32_t v = s_fin;
+          for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t x = (uint32_t)__shfl_xor((int)v, o);
+            v = x > v ? x : v;
+          }
+          v = __builtin_amdgcn_readfirstlane(v);
+          src_need = v > src_need ? v : src_need;
+          if (__ballot(mine) != ~0ull) break;
+        }
       }
       u = grab_take(uv);
       // tiles before this one that are read
-      uint32_t need_tiles = seen ? (src_need + TILE - 1) / TILE : t;
+      uint32_t need_tiles = (src_need + TILE - 1) / TILE;
       if (t >= HTILES) {
         // This tile overwrites the ring slot of tile t - HTILES, whose bytes
         // only tiles up to t - HTILES + reach read (a match reaches at most

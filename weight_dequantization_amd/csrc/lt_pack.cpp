@@ -288,6 +288,38 @@ lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_
   return LT_OK;
 }
 
+lt_status lt_encode_zero_runs(const uint16_t *x, uint64_t n, uint32_t *bitmap, uint64_t *val_off, uint16_t *vals,
+                              uint64_t vals_cap, int threads) {
+  if (!val_off || (n && (!x || !bitmap))) return LT_ERR_INVALID_ARG;
+  const uint64_t nb = (n + LT_ZR_BLOCK - 1) / LT_ZR_BLOCK;
+  if (nb > 0xFFFFFFFFull) return LT_ERR_INVALID_ARG;
+  val_off[0] = 0;
+  if (nb == 0) return LT_OK;
+  std::vector<uint32_t> count(nb);
+  parallel_chunks((uint32_t)nb, threads, [&](uint32_t b) {
+    const uint64_t e0 = (uint64_t)b * LT_ZR_BLOCK, e1 = std::min<uint64_t>(e0 + LT_ZR_BLOCK, n);
+    uint32_t *w = bitmap + (uint64_t)b * (LT_ZR_BLOCK / 32);
+    for (int k = 0; k < LT_ZR_BLOCK / 32; k++) w[k] = 0;
+    uint32_t c = 0;
+    for (uint64_t e = e0; e < e1; e++)
+      if (x[e]) {
+        w[(e - e0) >> 5] |= 1u << ((e - e0) & 31);
+        c++;
+      }
+    count[b] = c;
+  });
+  for (uint64_t b = 0; b < nb; b++) val_off[b + 1] = val_off[b] + count[b];
+  if (!vals) return LT_OK;
+  if (vals_cap < val_off[nb]) return LT_ERR_INVALID_ARG;
+  parallel_chunks((uint32_t)nb, threads, [&](uint32_t b) {
+    const uint64_t e0 = (uint64_t)b * LT_ZR_BLOCK, e1 = std::min<uint64_t>(e0 + LT_ZR_BLOCK, n);
+    uint16_t *o = vals + val_off[b];
+    for (uint64_t e = e0; e < e1; e++)
+      if (x[e]) *o++ = x[e];
+  });
+  return LT_OK;
+}
+
 lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint32_t *crc,
                              int threads) {
   if (!comp_off || !crc) return LT_ERR_INVALID_ARG;
