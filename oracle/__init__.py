@@ -15,6 +15,8 @@ What it computes (every function is the plain definition, written from):
   the roadmap's Phase 1.1 (INT4) and Phase 1.2 (INT8) worked examples.
 * fused = dequantize(decode(table)): the roadmap's CPU reference for its fused
   kernel (Phase 2.1).
+* codebook dequantization: element e is entry q(e) of its group's 16-entry fp16
+  table (the pages' value dictionaries of small codes plus a lookup table).
 * zero-run coding of fp16 activations (per 1024-element block a nonzero bitmap,
   then the nonzero values in order): the pages' zero-run encoding of ReLU
   outputs, in the bitmap form the GPU decoder reads.
@@ -78,6 +80,7 @@ def lib():
             "ltref_fused_int4_chunked": (u32, [vp, u64, vp, vp, u32, u64, vp, vp, u64, vp, vp, C.c_int]),
             "ltref_seqgen": (u64, [u64, u64, vp, u64, vp, u64, vp]),
             "ltref_crc32": (u32, [vp, u64]),
+            "ltref_dequant_int4_lut": (None, [vp, u64, vp, u64, vp]),
             "ltref_zr_encode": (u64, [vp, u64, vp, vp, vp]),
             "ltref_zr_decode": (None, [vp, vp, vp, u64, u64, vp, vp]),
             "ltref_crc32_chunks": (None, [vp, vp, u32, vp]),
@@ -320,3 +323,15 @@ def zr_decode(bitmap, val_off, vals, n: int, out=None):
     lib().ltref_zr_decode(_p(bitmap), _p(val_off), _p(vals if vals.size else np.zeros(1, np.uint16)), n,
                           vals.size, _p(out), _p(st))
     return out[:n], st[:nb]
+
+
+# ------------------------------------------------------------- codebooks
+
+def dequant_int4_lut(packed, lut, group: int, n_elem: int | None = None) -> np.ndarray:
+    """out[e] = lut[e // group][q(e)]; lut uint16 [groups, 16] of fp16 bits."""
+    packed = _c(packed, np.uint8)
+    lut = _c(lut, np.uint16)
+    n = 2 * packed.size if n_elem is None else n_elem
+    out = np.empty(max(n, 1), np.uint16)
+    lib().ltref_dequant_int4_lut(_p(packed), n, _p(lut), group, _p(out))
+    return out[:n]

@@ -26,6 +26,10 @@
  *     Fused Kernel);
  *   - a random LZ4 sequence generator that builds a stream and its expected
  *     output side by side, independent of the compressor;
+ *   - codebook dequantization of INT4 codes: each group of `group` elements
+ *     has a 16-entry table of fp16 values and element e is entry q(e) of its
+ *     group's table (the pages' value dictionaries: small integer codes plus
+ *     a tiny lookup table);
  *   - zero-run coding of fp16 activations (the pages' zero-run encoding for
  *     ReLU outputs, "runs of zeros" stored instead of full arrays): per block
  *     of 1024 elements a bitmap marks the nonzero elements, and the nonzero
@@ -629,5 +633,18 @@ void ltref_zr_decode(const uint32_t *bitmap, const uint64_t *val_off, const uint
     for (uint64_t e = 1024 * b; e < n && e < 1024 * (b + 1); e++)
       out[e] = ((bitmap[e / 32] >> (e % 32)) & 1u) ? vals[m++] : 0;
     if (status) status[b] = 0;
+  }
+}
+
+/* ------------------------------------------------------------ codebooks */
+
+/* out[e] = lut[16 * (e / group) + q(e)], q(e) the 4-bit code of element e
+ * (low nibble first). */
+void ltref_dequant_int4_lut(const uint8_t *packed, uint64_t n_elem, const uint16_t *lut, uint64_t group,
+                            uint16_t *out) {
+  for (uint64_t e = 0; e < n_elem; e++) {
+    const uint8_t b = packed[e / 2];
+    const uint32_t q = (e % 2 == 0) ? (b & 15u) : (b >> 4);
+    out[e] = lut[16 * (e / group) + q];
   }
 }
