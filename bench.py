@@ -247,12 +247,16 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
     pk = torch.from_numpy(packed).to(dev)
     ms_raw = timed(lambda: lt.dequant_int4(pk, scales, zp, (w.rows, w.cols), w.group, out=out))
     raw_bytes = packed.size + 2 * n_elem
+    lut = torch.randint(0, 1 << 15, (n_elem // w.group, 16), dtype=torch.int16, device=dev)
+    ms_lut = timed(lambda: lt.dequant_int4_lut(pk, lut, (w.rows, w.cols), w.group, out=out))
+    lut_bytes = packed.size + 2 * n_elem + lut.numel() * 2
     ms_fill = timed(lambda: out.fill_(1.0))
     src = torch.empty(2 * n_elem, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     ms_copy = timed(lambda: dst.copy_(src))
     return {
         "raw_int4_GBps": round(raw_bytes / ms_raw / 1e6, 1), "raw_int4_ms": round(ms_raw, 4),
+        "codebook_int4_GBps": round(lut_bytes / ms_lut / 1e6, 1), "codebook_int4_ms": round(ms_lut, 4),
         "fill_fp16_GBps": round(2 * n_elem / ms_fill / 1e6, 1),
         "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
         "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 7
+#define LT_ABI_VERSION 8
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -157,6 +157,22 @@ lt_status lt_dequant_int4(const uint8_t *packed, const uint16_t *scales, const i
 lt_status lt_dequant_int8(const int8_t *q, const uint16_t *scales, const int8_t *zp,
                           uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                           void *stream);
+
+/*
+ * lt_dequant_int4_lut -- codebook dequantization of packed INT4 codes (the
+ * value dictionaries of page "Openai/692db884-... (section 28)": small
+ * integer codes plus a tiny lookup table, in place of the affine rule).
+ * Element e (row-major, low nibble first as lt_dequant_int4) becomes entry
+ * q(e) of the table of its group e / group:
+ *   lut    DEVICE uint16 [rows*cols/group][16] fp16 bits, 16-byte aligned;
+ *          group = rows*cols gives one dictionary for the whole tensor
+ *   packed DEVICE, 4-byte aligned; out DEVICE uint16 [rows*cols], 16-byte
+ *          aligned
+ * group must be at least 16 (a table per fewer codes outweighs the codes)
+ * and follow the shape rule of lt_dequant_int4.
+ */
+lt_status lt_dequant_int4_lut(const uint8_t *packed, const uint16_t *lut, uint64_t rows, uint64_t cols,
+                              uint64_t group, uint16_t *out, void *stream);
 
 /*
  * lt_fused_lz4_int4 -- LZ4 decode fused with INT4 unpack and dequantization

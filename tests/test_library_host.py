@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 7
+    assert lt.lib().lt_abi_version() == 8
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -366,3 +366,15 @@ def test_zero_run_arguments_rejected_without_gpu():
     p = lambda a: a.ctypes.data_as(C.c_void_p)
     assert L.lt_encode_zero_runs(p(x), 10, p(bm), p(vo), p(vals), 4, 1) == lt.LT_ERR_INVALID_ARG   # 10 values
     assert L.lt_encode_zero_runs(p(x), 10, p(bm), p(vo), None, 0, 1) == lt.LT_OK and vo[1] == 10
+
+
+def test_lut_arguments_rejected_without_gpu():
+    L = lt.lib()
+    fake = C.c_void_p(0x10000)
+    inv = lt.LT_ERR_INVALID_ARG
+    assert L.lt_dequant_int4_lut(fake, fake, 4, 64, 8, fake, None) == inv            # groups under 16
+    assert L.lt_dequant_int4_lut(fake, fake, 4, 64, 100, fake, None) == inv          # shape rule
+    assert L.lt_dequant_int4_lut(C.c_void_p(0x10002), fake, 4, 64, 16, fake, None) == inv   # packed alignment
+    assert L.lt_dequant_int4_lut(fake, C.c_void_p(0x10008), 4, 64, 16, fake, None) == inv   # table alignment
+    assert L.lt_dequant_int4_lut(fake, fake, 1, 17, 17, fake, None) == inv           # odd element count
+    assert L.lt_dequant_int4_lut(None, fake, 4, 64, 16, fake, None) == inv

@@ -11,6 +11,7 @@ Device entry points (asynchronous on torch's current stream):
     decode_lz4(table, out=None, status=None)                 -> uint8 tensor
     dequant_int4(packed, scales, zp, shape, group, out=None) -> fp16 tensor
     dequant_int8(q, scales, zp, shape, group, out=None)      -> fp16 tensor
+    dequant_int4_lut(packed, lut, shape, group, out=None)   -> fp16 tensor
     fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
 Zero-run coding of fp16 activations (bitmap + nonzero values per block):
@@ -98,6 +99,7 @@ def _lib():
             "lt_decode_lz4": (i32, [tp, vp, vp, vp]),
             "lt_dequant_int4": (i32, [vp, vp, vp, u64, u64, u64, vp, vp]),
             "lt_dequant_int8": (i32, [vp, vp, vp, u64, u64, u64, vp, vp]),
+            "lt_dequant_int4_lut": (i32, [vp, vp, u64, u64, u64, vp, vp]),
             "lt_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_decode_lz4_range": (i32, [tp, u32, u32, u64, u64, vp, vp, vp]),
@@ -379,6 +381,16 @@ def dequant_int8(q, scales, zp, shape, group: int, out=None, stream=None):
     out = _out_f16(out, rows * cols, q.device)
     _check(_lib().lt_dequant_int8(_dptr(q), _dptr(scales), _dptr(zp), rows, cols, group,
                                   _dptr(out), _stream_ptr(stream)), "lt_dequant_int8")
+    return out.view(rows, cols)
+
+
+def dequant_int4_lut(packed, lut, shape, group: int, out=None, stream=None):
+    """Codebook dequant: element e is lut[e // group][q(e)]; lut is a device
+    tensor of fp16 bits (int16/uint16/float16) [groups, 16]."""
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, packed.device)
+    _check(_lib().lt_dequant_int4_lut(_dptr(packed), _dptr(lut), rows, cols, group, _dptr(out),
+                                      _stream_ptr(stream)), "lt_dequant_int4_lut")
     return out.view(rows, cols)
 
 

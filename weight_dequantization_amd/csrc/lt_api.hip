@@ -79,6 +79,69 @@ __global__ void __launch_bounds__(RAWT_THREADS) dequant_int4_tiles(RawParams P, 
   }
 }
 
+// Codebook INT4 (a 16-entry fp16 table per group of at least 16 codes):
+// element e is entry q(e) of its group's table.  A workgroup takes 8192
+// codes, one 2048-code tile per wave in the lane layout above (each load
+// instruction reads 256 contiguous bytes, each store writes 1 KiB), and
+// first stages the at most 513 tables its codes use in LDS.
+struct LutParams {
+  const uint8_t *src;
+  const uint16_t *lut;
+  uint64_t n;                // codes
+  uint64_t group;
+  uint32_t group_shift;      // log2(group) if a power of two, else 64
+  uint16_t *out;
+};
+constexpr int LUT_THREADS = 256;
+constexpr uint32_t LUT_CODES = 2048 * (LUT_THREADS / 64);
+constexpr uint32_t LUT_ROWS = LUT_CODES / 16 + 2;
+
+__device__ __forceinline__ uint64_t lut_group(const LutParams &P, uint64_t e) {
+  return P.group_shift < 64 ? e >> P.group_shift : e / P.group;
+}
+
+__global__ void __launch_bounds__(LUT_THREADS) dequant_int4_lut_kernel(LutParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t tab[LUT_ROWS * 16];
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+  const uint64_t e0 = (uint64_t)blockIdx.x * LUT_CODES;
+  const uint64_t e1 = e0 + LUT_CODES < P.n ? e0 + LUT_CODES : P.n;
+  const uint64_t g0 = lut_group(P, e0);
+  const uint32_t rows = (uint32_t)(lut_group(P, e1 - 1) - g0 + 1);
+  const uint4 *lsrc = (const uint4 *)(P.lut + 16 * g0);
+  for (uint32_t i = threadIdx.x; i < 2 * rows; i += LUT_THREADS) ((uint4 *)tab)[i] = lsrc[i];
+  __syncthreads();
+  const uint64_t te = e0 + 2048 * wave;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const uint64_t eb = te + 512 * k + 8 * lane;   // this lane's 8 codes
+    if (eb >= P.n) break;
+    const bool whole = eb + 8 <= P.n;
+    uint32_t d = 0;
+    if (whole) {
+      d = *(const uint32_t *)(P.src + eb / 2);
+    } else {
+      for (uint32_t j = 0; 2 * j < P.n - eb; j++) d |= (uint32_t)P.src[eb / 2 + j] << (8 * j);
+    }
+    uint64_t g = lut_group(P, eb);
+    uint64_t next = (g + 1) * P.group;
+    uint32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      if (eb + i >= next) {   // groups of 16 or more: at most one step per 8 codes
+        g++;
+        next += P.group;
+      }
+      v[i] = tab[16 * (uint32_t)(g - g0) + ((d >> (4 * i)) & 15u)];
+    }
+    if (whole) {
+      *(uint4 *)(P.out + eb) = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+    } else {
+      for (int i = 0; i < 8; i++)
+        if (eb + i < P.n) P.out[eb + i] = (uint16_t)v[i];
+    }
+  }
+}
+
 // Each thread takes RAW_UNROLL dwords spaced a workgroup-width apart, so each
 // load instruction reads 1 KiB and each store instruction writes 4 KiB (int4)
 // contiguously across the workgroup.
@@ -486,6 +549,27 @@ lt_status lt_dequant_int4(const uint8_t *packed, const uint16_t *scales, const i
 lt_status lt_dequant_int8(const int8_t *q, const uint16_t *scales, const int8_t *zp, uint64_t rows,
                           uint64_t cols, uint64_t group, uint16_t *out, void *stream) {
   return raw_common(false, (const uint8_t *)q, scales, zp, rows, cols, group, out, stream);
+}
+
+lt_status lt_dequant_int4_lut(const uint8_t *packed, const uint16_t *lut, uint64_t rows, uint64_t cols,
+                              uint64_t group, uint16_t *out, void *stream) {
+  if (!packed || !lut || !out || !aligned16(out) || !aligned16(lut) || ((uintptr_t)packed & 3) != 0)
+    return LT_ERR_INVALID_ARG;
+  if (!shape_ok(rows, cols, group) || group < 16) return LT_ERR_INVALID_ARG;
+  const uint64_t n = rows * cols;
+  if (n % 2 != 0) return LT_ERR_INVALID_ARG;
+  lt::LutParams P;
+  P.src = packed;
+  P.lut = lut;
+  P.n = n;
+  P.group = group;
+  P.group_shift = shift_of(group);
+  P.out = out;
+  const uint64_t blocks = (n + lt::LUT_CODES - 1) / lt::LUT_CODES;
+  if (blocks > 0x7FFFFFFFull) return LT_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(lt::dequant_int4_lut_kernel, dim3((uint32_t)blocks), dim3(lt::LUT_THREADS), 0,
+                     (hipStream_t)stream, P);
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
 
 lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
