@@ -15,6 +15,9 @@ What it computes (every function is the plain definition, written from):
   the roadmap's Phase 1.1 (INT4) and Phase 1.2 (INT8) worked examples.
 * fused = dequantize(decode(table)): the roadmap's CPU reference for its fused
   kernel (Phase 2.1).
+* matrix-vector product with the dequantized matrix, y = W x in fp64 from the
+  fp16 weights that fused_int4 gives (decompress, then multiply: the pages'
+  decode-plus-GEMM benchmarks), by a library matrix product.
 * codebook dequantization: element e is entry q(e) of its group's 16-entry fp16
   table (the pages' value dictionaries of small codes plus a lookup table).
 * zero-run coding of fp16 activations (per 1024-element block a nonzero bitmap,
@@ -335,3 +338,13 @@ def dequant_int4_lut(packed, lut, group: int, n_elem: int | None = None) -> np.n
     out = np.empty(max(n, 1), np.uint16)
     lib().ltref_dequant_int4_lut(_p(packed), n, _p(lut), group, _p(out))
     return out[:n]
+
+
+# ---------------------------------------------------------- decode + GEMV
+
+def gemv_int4(t: Table, scales, zp, group: int, rows: int, cols: int, x_f16) -> np.ndarray:
+    """y = W x in fp64, W = fused_int4(t) as an fp16 rows x cols matrix and
+    x fp16 bits [cols]; returns (y float64 [rows], chunk statuses)."""
+    w, st = fused_int4(t, scales, zp, group, rows * cols)
+    W = f64_from_f16(w).reshape(rows, cols)
+    return W @ f64_from_f16(_c(x_f16, np.uint16)), st
