@@ -262,7 +262,22 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),
         "verify_crc32": verify_measurement(torch, lt, w, packed, dev, timed),
         "activations_4096x14336": activation_measurements(torch, lt, dev, timed),
+        "gemv": gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed),
     }
+
+
+def gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed):
+    """y = W x on the same layer: the fused decode-dequant-dot kernel (the
+    fp16 matrix never written) against the fused kernel writing W followed
+    by torch's fp16 matrix-vector product."""
+    table = lt.ChunkTable.build(packed, w.dst_off, dev)
+    x = torch.randn(w.cols, dtype=torch.float16, device=dev)
+    y = torch.empty(w.rows, dtype=torch.float32, device=dev)
+    ms_fused = timed(lambda: lt.fused_lz4_int4_gemv(table, scales, zp, (w.rows, w.cols), w.group, x, y=y))
+    W = out.view(w.rows, w.cols)
+    ms_two = timed(lambda: (lt.fused_lz4_int4(table, scales, zp, (w.rows, w.cols), w.group, out=out), torch.mv(W, x)))
+    return {"fused_ms": round(ms_fused, 4), "decode_then_mv_ms": round(ms_two, 4),
+            "fused_compressed_GBps": round(table.comp_bytes / ms_fused / 1e6, 1)}
 
 
 def activation_measurements(torch, lt, dev, timed):

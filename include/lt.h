@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 8
+#define LT_ABI_VERSION 9
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -185,6 +185,28 @@ lt_status lt_dequant_int4_lut(const uint8_t *packed, const uint16_t *lut, uint64
 lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
                             uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                             int32_t *chunk_status, void *stream);
+
+/*
+ * lt_fused_lz4_int4_gemv -- LZ4 decode and INT4 dequantization fused with a
+ * matrix-vector product, y = W x, W the rows x cols fp16 matrix that
+ * lt_fused_lz4_int4 would write (decompress-then-multiply, the decode plus
+ * GEMM benchmarks of page "Openai/691a41cd-... (section 38)"; a decoded
+ * tensor used in a matmul, "GPU Compression Pipeline - TDD Roadmap",
+ * Phase 4.1): each decoded tile of 2048 codes is dotted with x where it
+ * lies and never stored, so the fp16 matrix costs no memory traffic.
+ *   x  DEVICE fp16 [cols], 16-byte aligned
+ *   y  DEVICE fp32 [rows], 4-byte aligned: zeroed on `stream`, then each
+ *      tile adds its dot product (fp16 x fp16 products exact in fp32, fp32
+ *      sums: per lane, across the wave, then one atomic add per tile, so
+ *      the order of the sums, and the last bits of y, vary between calls)
+ * Requires group a power of two of at least 128 and cols a multiple of
+ * 2048 (LT_ERR_UNSUPPORTED otherwise); chunks whose decoded bytes do not
+ * start and end on 1 KiB boundaries fail with LT_CHUNK_BAD_TABLE and add
+ * nothing.  Other arguments as lt_fused_lz4_int4.
+ */
+lt_status lt_fused_lz4_int4_gemv(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                                 uint64_t rows, uint64_t cols, uint64_t group, const uint16_t *x, float *y,
+                                 int32_t *chunk_status, void *stream);
 
 /*
  * lt_fused_lz4_int8 -- LZ4 decode fused with INT8 dequantization; the

@@ -1,0 +1,91 @@
+"""LZ4 decode + INT4 dequant fused with a matrix-vector product, y = W x
+(decompress, then multiply: the pages' decode-plus-GEMM benchmarks), the
+fp16 matrix never stored.  One-hot vectors give exact columns of W, which
+must equal the oracle's bit for bit; random vectors must lie within the
+fp32 summation bound of the oracle's fp64 product."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_dequantization_amd as lt
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def t_u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+@pytest.fixture(scope="module")
+def layer():
+    w = synth.config3()
+    table = lt.ChunkTable.build(lt.pack_int4(w.codes), w.dst_off, DEV)
+    W = O.f64_from_f16(O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)).reshape(w.rows, w.cols)
+    return w, table, W
+
+
+def _gemv(w, table, x, status=None):
+    y = lt.fused_lz4_int4_gemv(table, t_u16(w.scales), torch.from_numpy(w.zp).to(DEV), (w.rows, w.cols), w.group,
+                               t_u16(x), status=status)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def test_one_hot_columns_exact(layer):
+    """x = e_j: y is column j of W exactly (one nonzero product per row)."""
+    w, table, W = layer
+    for j in (0, 1, 7, 2047, 2048, 14335, w.cols - 1):
+        x = np.zeros(w.cols, np.uint16)
+        x[j] = 0x3C00
+        y = _gemv(w, table, x)
+        assert np.array_equal(y, W[:, j]), j
+
+
+def test_random_vector_within_bound(layer):
+    """Summation depth: 16 two-product dot steps per lane, 6 wave levels and
+    14 tile additions per row; 64 unit roundoffs of the sum of |w x| bound
+    the difference from the fp64 product (products of fp16 are exact)."""
+    w, table, W = layer
+    rng = np.random.default_rng(0)
+    x = O.f16_from_f64(rng.standard_normal(w.cols))
+    st = torch.full((table.n_chunks,), -1, dtype=torch.int32, device=DEV)
+    y = _gemv(w, table, x, st)
+    assert np.all(st.cpu().numpy() == 0)
+    xd = O.f64_from_f16(x)
+    ref = W @ xd
+    bound = 64 * U32 * (np.abs(W) @ np.abs(xd)) + 1e-30
+    err = np.abs(y - ref)
+    assert np.all(err <= bound), (err / bound).max()
+    # the bound is not loose enough to hide one wrong column
+    assert np.median(np.abs(W[:, 5] * xd[5]) / bound) > 1.0
+
+
+def test_chunks_off_tile_boundaries_fail():
+    """A chunk that ends 16 bytes past a 1 KiB boundary and one that starts
+    there both fail without adding; y holds the first chunk's part."""
+    w = synth.int4_weight(64, 4096, 128, 21)
+    packed = lt.pack_int4(w.codes)
+    dst_off = np.array([0, 65536, 65552, packed.size], np.uint64)
+    table = lt.ChunkTable.build(packed, dst_off, DEV)
+    rng = np.random.default_rng(1)
+    x = O.f16_from_f64(rng.integers(-4, 5, w.cols).astype(np.float64))
+    st = torch.full((table.n_chunks,), -1, dtype=torch.int32, device=DEV)
+    y = _gemv(w, table, x, st)
+    s = st.cpu().numpy()
+    assert s[0] == 0 and np.all(s[1:] == lt.CHUNK_BAD_TABLE)
+    W = O.f64_from_f16(O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)).ravel()
+    W[2 * int(dst_off[1]):] = 0                         # only the first chunk's codes contribute
+    ref = W.reshape(w.rows, w.cols) @ O.f64_from_f16(x)
+    assert np.allclose(y, ref, rtol=0, atol=64 * U32 * np.abs(W).reshape(w.rows, w.cols).sum(1).max() * 4)

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 8
+    assert lt.lib().lt_abi_version() == 9
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 
@@ -378,3 +378,18 @@ def test_lut_arguments_rejected_without_gpu():
     assert L.lt_dequant_int4_lut(fake, C.c_void_p(0x10008), 4, 64, 16, fake, None) == inv   # table alignment
     assert L.lt_dequant_int4_lut(fake, fake, 1, 17, 17, fake, None) == inv           # odd element count
     assert L.lt_dequant_int4_lut(None, fake, 4, 64, 16, fake, None) == inv
+
+
+def test_gemv_arguments_rejected_without_gpu():
+    L = lt.lib()
+    fake = C.c_void_p(0x10000)
+    t = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 4 * 4096 // 2, 100)
+    g = lambda rows, cols, group, x=fake, y=fake: L.lt_fused_lz4_int4_gemv(C.byref(t), fake, None, rows, cols, group,
+                                                                          x, y, None, None)
+    assert g(4, 4096, 128, x=None) == lt.LT_ERR_INVALID_ARG
+    assert g(4, 4096, 128, y=C.c_void_p(0x10002)) == lt.LT_ERR_INVALID_ARG
+    assert g(8, 4096, 128) == lt.LT_ERR_INVALID_ARG            # table holds 4 x 4096 codes
+    assert g(4, 4096, 64) == lt.LT_ERR_UNSUPPORTED             # groups under 128
+    t2 = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 4 * 3072 // 2, 100)
+    assert L.lt_fused_lz4_int4_gemv(C.byref(t2), fake, None, 4, 3072, 1024, fake, fake, None, None) \
+        == lt.LT_ERR_UNSUPPORTED                                # rows not a multiple of 2048 codes

@@ -14,6 +14,7 @@ Device entry points (asynchronous on torch's current stream):
     dequant_int4_lut(packed, lut, shape, group, out=None)   -> fp16 tensor
     fused_lz4_int4(table, scales, zp, shape, group, out=None, status=None)
     fused_lz4_int8(table, scales, zp, shape, group, out=None, status=None)
+    fused_lz4_int4_gemv(table, scales, zp, shape, group, x) -> y = W x (fp32)
 Zero-run coding of fp16 activations (bitmap + nonzero values per block):
     encode_zero_runs(x) -> (bitmap, val_off, vals)        (host)
     ZeroRunTensor.build(x, device); decode_zero_runs(z, out=None, status=None)
@@ -102,6 +103,7 @@ def _lib():
             "lt_dequant_int4_lut": (i32, [vp, vp, u64, u64, u64, vp, vp]),
             "lt_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
+            "lt_fused_lz4_int4_gemv": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, vp]),
             "lt_decode_lz4_range": (i32, [tp, u32, u32, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int4_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
             "lt_fused_lz4_int8_range": (i32, [tp, vp, vp, u64, u64, u64, u32, u32, u64, u64, vp, vp, vp]),
@@ -403,6 +405,20 @@ def fused_lz4_int4(table: ChunkTable, scales, zp, shape, group: int, out=None, s
                                     _dptr(out), _dptr(status), _stream_ptr(stream)),
            "lt_fused_lz4_int4")
     return out.view(rows, cols)
+
+
+def fused_lz4_int4_gemv(table: ChunkTable, scales, zp, shape, group: int, x, y=None, status=None,
+                        stream=None):
+    """y = W x with W the fp16 matrix fused_lz4_int4 would write, never
+    stored: x fp16 [cols] on the device; returns y fp32 [rows]."""
+    torch = _torch()
+    rows, cols = _shape(shape)
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=table.comp.device)
+    t = table.as_c()
+    _check(_lib().lt_fused_lz4_int4_gemv(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group, _dptr(x),
+                                         _dptr(y), _dptr(status), _stream_ptr(stream)), "lt_fused_lz4_int4_gemv")
+    return y
 
 
 def fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,

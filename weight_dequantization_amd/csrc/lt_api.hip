@@ -142,6 +142,10 @@ __global__ void __launch_bounds__(LUT_THREADS) dequant_int4_lut_kernel(LutParams
   }
 }
 
+__global__ void __launch_bounds__(256) zero_f32(float *y, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256) y[i] = 0.0f;
+}
+
 // Each thread takes RAW_UNROLL dwords spaced a workgroup-width apart, so each
 // load instruction reads 1 KiB and each store instruction writes 4 KiB (int4)
 // contiguously across the workgroup.
@@ -265,7 +269,10 @@ lt_status launch_params(int mode, lt::ChunkParams &P, void *stream) {
     case 4: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 16>), grid, block, 0, s, P); break;
     case 5: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
     case 6: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 16>), grid, block, 0, s, P); break;
-    default: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
+    case 7: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
+    case 8: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMV, 16>), grid, block, 0, s, P); break;
+    case 9: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMV, 14>), grid, block, 0, s, P); break;
+    default: return LT_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
@@ -293,6 +300,9 @@ lt::ChunkParams make_params(const lt_chunk_table *t, void *out, int32_t *chunk_s
   P.comp_base = 0;
   P.d_first = 0;
   P.d_last = t->total_bytes;
+  P.gemv_x = nullptr;
+  P.gemv_y = nullptr;
+  P.cols = 0;
   return P;
 }
 
@@ -570,6 +580,27 @@ lt_status lt_dequant_int4_lut(const uint8_t *packed, const uint16_t *lut, uint64
   hipLaunchKernelGGL(lt::dequant_int4_lut_kernel, dim3((uint32_t)blocks), dim3(lt::LUT_THREADS), 0,
                      (hipStream_t)stream, P);
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+}
+
+lt_status lt_fused_lz4_int4_gemv(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
+                                 uint64_t rows, uint64_t cols, uint64_t group, const uint16_t *x, float *y,
+                                 int32_t *chunk_status, void *stream) {
+  if (!table_ok(t) || !scales || !x || !y || !aligned16(x) || ((uintptr_t)y & 3) != 0) return LT_ERR_INVALID_ARG;
+  if (!shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
+  const uint64_t n = rows * cols;
+  if (t->total_bytes != n / 2) return LT_ERR_INVALID_ARG;
+  if (cols % 2048 != 0 || shift_of(group) >= 64 || group < 128) return LT_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t zb = (rows + 255) / 256;
+  zb = zb < 4096 ? zb : 4096;
+  hipLaunchKernelGGL(lt::zero_f32, dim3((uint32_t)zb), dim3(256), 0, s, y, rows);
+  if (hipGetLastError() != hipSuccess) return LT_ERR_LAUNCH;
+  if (t->n_chunks == 0) return LT_OK;
+  lt::ChunkParams P = make_params(t, nullptr, chunk_status, scales, zp, group);
+  P.gemv_x = x;
+  P.gemv_y = y;
+  P.cols = cols;
+  return launch_params(lt::MODE_GEMV, P, stream);
 }
 
 lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,

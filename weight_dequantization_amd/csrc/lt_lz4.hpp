@@ -129,7 +129,9 @@ enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4,
 // MODE_INT4G is MODE_INT4 for groups that are a power of two of at least
 // 128 codes, where a tile spans at most 17 groups (its own kernel, with a
 // leaner scale / zero-point fetch).
-enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2, MODE_INT4G = 3 };
+// MODE_GEMV is MODE_INT4G whose whole tiles are dotted with a vector and
+// added to y instead of being written.
+enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2, MODE_INT4G = 3, MODE_GEMV = 4 };
 
 struct __attribute__((aligned(16))) Ctl {
   uint32_t need[NSLOT];       // first input byte still read: [0] walker, [1 + b] builder b
@@ -189,6 +191,12 @@ struct ChunkParams {
   // d_first and the last ending at d_last.
   uint64_t comp_base;
   uint64_t d_first, d_last;
+  // MODE_GEMV (INT4 groups of 128 codes or more, rows a multiple of 2048
+  // codes, chunks a multiple of 1 KiB): instead of writing fp16, each tile
+  // adds its dot product with x to y[row] (y zeroed beforehand).
+  const uint16_t *gemv_x;    // fp16 [cols]
+  float *gemv_y;             // fp32 [rows]
+  uint64_t cols;
 };
 
 // ------------------------------------------------------------ LDS sync
@@ -1291,7 +1299,7 @@ __device__ __forceinline__ void meta_pack_few(Meta4 &m, bool has_zp) {
 // power of two).  Lane l's dword k holds codes 512 k + 8 l .. + 7 of the
 // tile, one group, whose constants come from lane (group - g0) by
 // ds_bpermute.  Each store instruction writes 1 KiB of contiguous fp16.
-template <int HLOG>
+template <int MODE, int HLOG>
 __device__ __forceinline__ void flush_int4_few(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P,
                                                uint64_t dst0, uint32_t T, const Meta4 &m) {
   constexpr uint32_t HMASK = (1u << HLOG) - 1;
@@ -1301,6 +1309,27 @@ __device__ __forceinline__ void flush_int4_few(Smem<HLOG> &sm, uint32_t lane, co
   for (int k = 0; k < 4; k++) w[k] = *(const uint32_t *)(src + 256 * k);
   const uint64_t e = 2 * (dst0 + T);   // the tile's first code
   const uint32_t off = (uint32_t)(e & (P.group - 1)) + 8 * lane;
+  if constexpr (MODE == MODE_GEMV) {
+    // the tile is 2048 codes of one row: its fp16 weights dotted with x
+    const uint64_t row = e / P.cols;
+    const uint4 *xs = (const uint4 *)(P.gemv_x + (e - row * P.cols)) + lane;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t i = (off + 512 * k) >> P.group_shift;
+      const h2 c2 = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, m.z[1]));
+      const h2 s2 = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, m.s[1]));
+      const uint4 wv = deq8_int4_dual(w[k], c2, s2);
+      const uint4 xv = xs[64 * k];
+      acc = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), acc, false);
+    }
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) atomicAdd(P.gemv_y + row, acc);
+    return;
+  }
   uint4 *out = (uint4 *)((uint16_t *)P.out + e) + lane;
 #pragma unroll
   for (int k = 0; k < 4; k++) {
@@ -1331,6 +1360,8 @@ __device__ __forceinline__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const 
         }
       }
     }
+  } else if constexpr (MODE == MODE_GEMV) {
+    // never reached: the prologue admits only chunks of whole tiles
   } else if constexpr (MODE == MODE_INT4 || MODE == MODE_INT4G) {
     uint16_t *out = (uint16_t *)P.out;
     const uint64_t G = P.group;
@@ -1723,7 +1754,7 @@ struct Builder {
 
   __device__ __forceinline__ void run() {
     const uint32_t ntiles = (N + TILE - 1) / TILE;
-    constexpr bool G = MODE == MODE_INT4G;
+    constexpr bool G = MODE == MODE_INT4G || MODE == MODE_GEMV;
     const bool fast = G || (MODE == MODE_INT4 && P.group_shift < 64 && P.group >= 8);
     // Each tile's scales and zero points are fetched one tile ahead, so their
     // latency overlaps the build of the tile before.
@@ -1858,7 +1889,7 @@ struct Builder {
       }
       if (few && Tend - T == TILE) {
         meta_pack_few(cur, P.zp != nullptr);
-        flush_int4_few<HLOG>(sm, lane, P, dst0, T, cur);
+        flush_int4_few<MODE, HLOG>(sm, lane, P, dst0, T, cur);
       } else {
         if (fast) meta_ready(cur, P.zp != nullptr, P, dst0, t, lane, N, few);
         flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
@@ -1893,6 +1924,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   bool bad = c0 < P.comp_base || c0 > c1 || c1 - P.comp_base > P.comp_bytes || d0 > d1 || d1 > P.total ||
              d0 < P.d_first || d1 > P.d_last || (i == 0 && d0 != P.d_first) ||
              (i == P.n - 1 && d1 != P.d_last) || (d0 & 15) != 0 ||
+             (MODE == MODE_GEMV && ((d0 | d1) & (TILE - 1)) != 0) ||
              d1 - d0 > (uint64_t)P.max_chunk || c1 - c0 > (uint64_t)LEN_CAP;
   c0 -= P.comp_base;
   c1 -= P.comp_base;
