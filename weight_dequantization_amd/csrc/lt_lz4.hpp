@@ -1598,19 +1598,24 @@ struct Builder {
       uint32_t lo = a > Pp ? a - Pp : 0;
       uint32_t hi = end - Pp < 16 ? end - Pp : 16;
       uint32_t r = (Pp + lo - a) % dist;
-      uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+      // every byte's source index first (bytes outside [lo, hi) read any
+      // byte of the ring and are not stored), so the loads issue back to
+      // back, eight at a time, and wait once per eight
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (uint32_t q = 0; q < 16; q++) {
-        if (q >= lo && q < hi) {
-          uint32_t sv = (uint32_t)sm.hist[(a - dist + r) & HMASK] << (8 * (q & 3));
-          if (q < 4) w0 |= sv;
-          else if (q < 8) w1 |= sv;
-          else if (q < 12) w2 |= sv;
-          else w3 |= sv;
-          r = (r + 1 == dist) ? 0 : r + 1;
+      for (uint32_t h = 0; h < 2; h++) {
+        uint32_t b[8];
+#pragma unroll
+        for (uint32_t i = 0; i < 8; i++) {
+          const uint32_t q = 8 * h + i;
+          b[i] = sm.hist[(a - dist + r) & HMASK];
+          const uint32_t rn = (r + 1 == dist) ? 0 : r + 1;
+          r = q >= lo ? rn : r;
         }
+#pragma unroll
+        for (uint32_t i = 0; i < 8; i++) w[2 * h + i / 4] |= b[i] << (8 * (i & 3));
       }
-      st_block(sm.hist + (Pp & HMASK), make_uint4(w0, w1, w2, w3), lo, hi);
+      st_block(sm.hist + (Pp & HMASK), make_uint4(w[0], w[1], w[2], w[3]), lo, hi);
     }
   }
 
