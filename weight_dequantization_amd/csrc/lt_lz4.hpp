@@ -1619,10 +1619,28 @@ struct Builder {
     }
   }
 
+  // Up to 64 bytes, one per lane: lane i writes byte a + i.  A literal run
+  // reads the input ring at src + i; a match reads the history at
+  // a - dist + (i mod dist), which lies before a however the match
+  // overlaps itself (a match repeats with period dist).  One read and one
+  // write instruction, however short the piece.
+  __device__ __forceinline__ void lit_lanes(uint32_t src, uint32_t a, uint32_t n) {
+    if (lane < n) sm.hist[(a + lane) & HMASK] = sm.inr[(src + lane) & IMASK];
+  }
+  __device__ __forceinline__ void match_lanes(uint32_t dist, uint32_t a, uint32_t n) {
+    // lane mod dist for lane < 64: a multiply by ceil(2^16 / dist) is exact
+    // below dist 64, and from 64 on the lane is its own remainder
+    const uint32_t mq = 65535u / dist + 1u;
+    const uint32_t r = dist >= 64 ? lane : lane - dist * ((lane * mq) >> 16);
+    if (lane < n) sm.hist[(a + lane) & HMASK] = sm.hist[(a - dist + r) & HMASK];
+  }
+
   // the match bytes [a, a + n) of a record (the match started at or before a)
   __device__ void match_exact(uint32_t info, uint32_t a, uint32_t n) {
     const uint32_t dist = rec_dist(info);
-    if (dist == 1) {   // every byte of the run equals the one before a
+    if (n <= 64 && !(info & F_FILL)) {
+      match_lanes(dist, a, n);
+    } else if (dist == 1) {   // every byte of the run equals the one before a
       uint32_t bb = (info & F_FILL) ? rec_fill(info)
                                     : __builtin_amdgcn_readfirstlane(sm.hist[(a - 1) & HMASK]);
       fill_exact(a, bb, n);
@@ -1645,7 +1663,10 @@ struct Builder {
       uint32_t a = os > T ? os : T, e = le < Tend ? le : Tend;
       if (a < e) {
         need_input(src + (e - os));
-        copy_exact<IMASK>(sm.inr, src + (a - os), a, e - a);
+        if (e - a <= 64)
+          lit_lanes(src + (a - os), a, e - a);
+        else
+          copy_exact<IMASK>(sm.inr, src + (a - os), a, e - a);
       }
       a = le > T ? le : T;
       e = re < Tend ? re : Tend;
