@@ -114,10 +114,10 @@ constexpr uint32_t NSLOT = 8;         // counter array length (>= NB + 1)
 // A tile is built in passes (one, plus one per copy that reads the tile
 // itself) when it has at most BULK_RECS records, or when its passes number
 // at most one per BULK_RATIO records; otherwise record by record.  A pass
-// over a whole tile costs less than building one record alone, so passes
-// win whenever they do not outnumber the records.
+// over a whole tile costs about as much as two records built alone (short
+// pieces take one byte per lane there).
 constexpr uint32_t BULK_RECS = 16;
-constexpr uint32_t BULK_RATIO = 1;
+constexpr uint32_t BULK_RATIO = 2;
 // Poll intervals (s_sleep units of 64 cycles).  Waiting waves share the CU's
 // scalar unit and LDS with the walkers, so they poll no faster than the
 // walk can change what they wait for.
