@@ -104,9 +104,12 @@ constexpr uint32_t TILE = 1024;       // build / write-out unit (bytes of decode
 // Sequence records in flight (recorder -> builders).  A 1 KiB tile overlaps
 // at most 257 records (every non-final sequence decodes to >= 4 bytes), and
 // the recorder must be able to hold all of them while the oldest tile's
-// builder waits for the tile's coverage, so the ring holds more than 258.
-// (Two workgroups must fit in one CU's LDS, which bounds the rings.)
-constexpr uint32_t RING = 272;
+// builder waits for the tile's coverage, so the ring holds more than 258;
+// beyond that, a longer ring lets the walker run further ahead of the
+// builders on blocks of many short sequences.  (Four workgroups must fit
+// in one CU's LDS with the 16 KiB history, which bounds it: 40,848 bytes
+// each.)
+constexpr uint32_t RING = 368;
 constexpr int NB = 5;                 // builder waves
 constexpr int NWAVES = 3 + NB;        // walker, recorder, feeder, builders
 constexpr int NTHREADS = 64 * NWAVES;
