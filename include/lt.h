@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 9
+#define LT_ABI_VERSION 10
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -337,6 +337,11 @@ lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint
 lt_status lt_stream_decode_lz4(const lt_chunk_table *host_table, uint8_t *dst, int32_t *chunk_status,
                                uint8_t *staging, uint64_t staging_bytes, void *copy_stream, void *stream);
 lt_status lt_stream_fused_lz4_int4(const lt_chunk_table *host_table, const uint16_t *scales, const int8_t *zp,
+                                   uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                                   int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
+                                   void *copy_stream, void *stream);
+/* INT8 codes (t->total_bytes == rows*cols), as lt_fused_lz4_int8. */
+lt_status lt_stream_fused_lz4_int8(const lt_chunk_table *host_table, const uint16_t *scales, const int8_t *zp,
                                    uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                                    int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
                                    void *copy_stream, void *stream);

@@ -234,3 +234,16 @@ def test_stream_llama70b_layer_from_host():
         assert np.all(statuses(st, ht.n_chunks) == 0)
         assert_same(host_u16(out), O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group),
                     "layer 3 %dx%d" % key)
+
+
+def test_stream_fused_int8_config2():
+    """INT8 per-row weights (8192x8192, half the rows pruned) from pinned host
+    memory in 64-chunk batches, against the oracle."""
+    w = synth.config2()
+    comp, comp_off = lt.compress_chunks(w.q.view(np.uint8), w.dst_off, max_dist=lt.PACK_WINDOW)
+    t = host_table(comp, comp_off, w.dst_off, True, lt.PACK_WINDOW)
+    st = status_tensor(t.n_chunks)
+    out = lt.stream_fused_lz4_int8(t, t_u16(w.scales), None, (w.rows, w.cols), w.group, status=st,
+                                   staging=staging_for(t, 64))
+    assert np.all(statuses(st, t.n_chunks) == 0)
+    assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "config2 streamed int8")

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 9
+    assert lt.lib().lt_abi_version() == 10
     assert lt.lib().lt_status_str(1) == b"invalid argument"
 
 

@@ -113,6 +113,7 @@ def _lib():
             "lt_encode_zero_runs": (i32, [vp, u64, vp, vp, vp, u64, i32]),
             "lt_checksum_chunks": (i32, [vp, vp, u32, vp, i32]),
             "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
+            "lt_stream_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
             "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
@@ -590,16 +591,27 @@ def stream_decode_lz4(table: ChunkTable, out=None, status=None, staging=None, co
     return out[:table.total_bytes] if out.numel() > table.total_bytes else out
 
 
-def stream_fused_lz4_int4(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
-                          staging=None, copy_stream=None, stream=None):
-    """fused_lz4_int4 over a host-resident table, copies overlapped with the
-    decode as in stream_decode_lz4."""
+def _stream_fused(name, table, scales, zp, shape, group, out, status, staging, copy_stream, stream):
     rows, cols = _shape(shape)
     out = _out_f16(out, rows * cols, scales.device)
     staging, copy_stream = _stream_setup(table, out.device, staging, copy_stream)
     t = table.as_c()
-    _check(_lib().lt_stream_fused_lz4_int4(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group,
-                                           _dptr(out), _dptr(status), _dptr(staging), staging.numel(),
-                                           _stream_ptr(copy_stream), _stream_ptr(stream)),
-           "lt_stream_fused_lz4_int4")
+    _check(getattr(_lib(), name)(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group, _dptr(out),
+                                 _dptr(status), _dptr(staging), staging.numel(), _stream_ptr(copy_stream),
+                                 _stream_ptr(stream)), name)
     return out.view(rows, cols)
+
+
+def stream_fused_lz4_int4(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
+                          staging=None, copy_stream=None, stream=None):
+    """fused_lz4_int4 over a host-resident table, copies overlapped with the
+    decode as in stream_decode_lz4."""
+    return _stream_fused("lt_stream_fused_lz4_int4", table, scales, zp, shape, group, out, status, staging,
+                         copy_stream, stream)
+
+
+def stream_fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
+                          staging=None, copy_stream=None, stream=None):
+    """fused_lz4_int8 over a host-resident table, as stream_fused_lz4_int4."""
+    return _stream_fused("lt_stream_fused_lz4_int8", table, scales, zp, shape, group, out, status, staging,
+                         copy_stream, stream)

@@ -494,6 +494,7 @@ lt_status stream_args(int mode, const lt_chunk_table *t, const uint16_t *scales,
   if (mode == lt::MODE_BYTES) return LT_OK;
   if (!scales || !shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
   const uint64_t n = rows * cols;
+  if (mode == lt::MODE_INT8) return t->total_bytes == n ? LT_OK : LT_ERR_INVALID_ARG;
   if (n % 2 != 0 || t->total_bytes != n / 2) return LT_ERR_INVALID_ARG;
   return LT_OK;
 }
@@ -691,6 +692,16 @@ lt_status lt_stream_fused_lz4_int4(const lt_chunk_table *host_table, const uint1
   const lt_status a = stream_args(lt::MODE_INT4, host_table, scales, rows, cols, group, out);
   if (a != LT_OK) return a;
   return stream_common(lt::MODE_INT4, host_table, out, chunk_status, scales, zp, group, staging, staging_bytes,
+                       copy_stream, stream);
+}
+
+lt_status lt_stream_fused_lz4_int8(const lt_chunk_table *host_table, const uint16_t *scales, const int8_t *zp,
+                                   uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
+                                   int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
+                                   void *copy_stream, void *stream) {
+  const lt_status a = stream_args(lt::MODE_INT8, host_table, scales, rows, cols, group, out);
+  if (a != LT_OK) return a;
+  return stream_common(lt::MODE_INT8, host_table, out, chunk_status, scales, zp, group, staging, staging_bytes,
                        copy_stream, stream);
 }
 
