@@ -276,8 +276,27 @@ def gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed):
     ms_fused = timed(lambda: lt.fused_lz4_int4_gemv(table, scales, zp, (w.rows, w.cols), w.group, x, y=y))
     W = out.view(w.rows, w.cols)
     ms_two = timed(lambda: (lt.fused_lz4_int4(table, scales, zp, (w.rows, w.cols), w.group, out=out), torch.mv(W, x)))
-    return {"fused_ms": round(ms_fused, 4), "decode_then_mv_ms": round(ms_two, 4),
-            "fused_compressed_GBps": round(table.comp_bytes / ms_fused / 1e6, 1)}
+    res = {"fused_ms": round(ms_fused, 4), "decode_then_mv_ms": round(ms_two, 4),
+           "fused_compressed_GBps": round(table.comp_bytes / ms_fused / 1e6, 1)}
+    # one layer of the 80-layer Llama-70B-shaped stack (7 projections, mixed
+    # 16/64/256 KiB chunks), batch-1: the seven products back to back
+    import synth
+    layer = []
+    for t in range(len(synth.LLAMA70B_LAYER)):
+        wt = synth.config5_tensor(0, t)
+        tb = lt.ChunkTable.build(lt.pack_int4(wt.codes), wt.dst_off, dev)
+        layer.append((wt, tb, torch.from_numpy(wt.scales.view(np.int16)).to(dev), torch.from_numpy(wt.zp).to(dev),
+                      torch.randn(wt.cols, dtype=torch.float16, device=dev),
+                      torch.empty(wt.rows, dtype=torch.float32, device=dev)))
+
+    def run_layer():
+        for wt, tb, sc, z, xv, yv in layer:
+            lt.fused_lz4_int4_gemv(tb, sc, z, (wt.rows, wt.cols), wt.group, xv, y=yv)
+    ms_layer = timed(run_layer)
+    res["llama70b_layer_ms"] = round(ms_layer, 4)
+    res["llama70b_80_layers_ms"] = round(80 * ms_layer, 3)
+    res["llama70b_layer_compressed_bytes"] = int(sum(tb.comp_bytes for _, tb, *_ in layer))
+    return res
 
 
 def activation_measurements(torch, lt, dev, timed):

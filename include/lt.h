@@ -196,11 +196,12 @@ lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, con
  * lies and never stored, so the fp16 matrix costs no memory traffic.
  *   x  DEVICE fp16 [cols], 16-byte aligned
  *   y  DEVICE fp32 [rows], 4-byte aligned: zeroed on `stream`, then each
- *      tile adds its dot product (fp16 x fp16 products exact in fp32, fp32
- *      sums: per lane, across the wave, then one atomic add per tile, so
+ *      tile adds its dot products (fp16 x fp16 products exact in fp32, fp32
+ *      sums: per lane, across the wave, then one atomic add per tile and
+ *      row, so
  *      the order of the sums, and the last bits of y, vary between calls)
  * Requires group a power of two of at least 128 and cols a multiple of
- * 2048 (LT_ERR_UNSUPPORTED otherwise); chunks whose decoded bytes do not
+ * 512 (LT_ERR_UNSUPPORTED otherwise); chunks whose decoded bytes do not
  * start and end on 1 KiB boundaries fail with LT_CHUNK_BAD_TABLE and add
  * nothing.  Other arguments as lt_fused_lz4_int4.
  */

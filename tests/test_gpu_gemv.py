@@ -89,3 +89,28 @@ def test_chunks_off_tile_boundaries_fail():
     W[2 * int(dst_off[1]):] = 0                         # only the first chunk's codes contribute
     ref = W.reshape(w.rows, w.cols) @ O.f64_from_f16(x)
     assert np.allclose(y, ref, rtol=0, atol=64 * U32 * np.abs(W).reshape(w.rows, w.cols).sum(1).max() * 4)
+
+
+def test_llama70b_layer():
+    """One layer of the Llama-70B-shaped stack (q, k, v, o, gate, up, down;
+    chunks of 16/64/256 KiB drawn per chunk, the format's whole window):
+    y = W x for each projection within the summation bound, one-hot
+    columns exact."""
+    rng = np.random.default_rng(7)
+    for t in range(len(synth.LLAMA70B_LAYER)):
+        w = synth.config5_tensor(11, t)
+        print("layer 11 tensor %dx%d" % (w.rows, w.cols), flush=True)
+        comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off)
+        table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, DEV, index=True)
+        W = O.f64_from_f16(O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)).reshape(w.rows, w.cols)
+        x = O.f16_from_f64(rng.standard_normal(w.cols))
+        st = torch.full((table.n_chunks,), -1, dtype=torch.int32, device=DEV)
+        y = _gemv(w, table, x, st)
+        assert np.all(st.cpu().numpy() == 0)
+        xd = O.f64_from_f16(x)
+        bound = 64 * U32 * (np.abs(W) @ np.abs(xd)) + 1e-30
+        assert np.all(np.abs(y - W @ xd) <= bound), t
+        j = int(rng.integers(0, w.cols))
+        e = np.zeros(w.cols, np.uint16)
+        e[j] = 0x3C00
+        assert np.array_equal(_gemv(w, table, e), W[:, j]), (t, j)

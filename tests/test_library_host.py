@@ -390,6 +390,6 @@ def test_gemv_arguments_rejected_without_gpu():
     assert g(4, 4096, 128, y=C.c_void_p(0x10002)) == lt.LT_ERR_INVALID_ARG
     assert g(8, 4096, 128) == lt.LT_ERR_INVALID_ARG            # table holds 4 x 4096 codes
     assert g(4, 4096, 64) == lt.LT_ERR_UNSUPPORTED             # groups under 128
-    t2 = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 4 * 3072 // 2, 100)
-    assert L.lt_fused_lz4_int4_gemv(C.byref(t2), fake, None, 4, 3072, 1024, fake, fake, None, None) \
-        == lt.LT_ERR_UNSUPPORTED                                # rows not a multiple of 2048 codes
+    t2 = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 4 * 3328 // 2, 100)
+    assert L.lt_fused_lz4_int4_gemv(C.byref(t2), fake, None, 4, 3328, 128, fake, fake, None, None) \
+        == lt.LT_ERR_UNSUPPORTED                                # rows not a multiple of 512 codes

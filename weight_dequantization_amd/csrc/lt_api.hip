@@ -590,7 +590,7 @@ lt_status lt_fused_lz4_int4_gemv(const lt_chunk_table *t, const uint16_t *scales
   if (!shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
   const uint64_t n = rows * cols;
   if (t->total_bytes != n / 2) return LT_ERR_INVALID_ARG;
-  if (cols % 2048 != 0 || shift_of(group) >= 64 || group < 128) return LT_ERR_UNSUPPORTED;
+  if (cols % 512 != 0 || shift_of(group) >= 64 || group < 128) return LT_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   uint64_t zb = (rows + 255) / 256;
   zb = zb < 4096 ? zb : 4096;

@@ -196,9 +196,9 @@ struct ChunkParams {
   // d_first and the last ending at d_last.
   uint64_t comp_base;
   uint64_t d_first, d_last;
-  // MODE_GEMV (INT4 groups of 128 codes or more, rows a multiple of 2048
+  // MODE_GEMV (INT4 groups of 128 codes or more, rows a multiple of 512
   // codes, chunks a multiple of 1 KiB): instead of writing fp16, each tile
-  // adds its dot product with x to y[row] (y zeroed beforehand).
+  // adds its dot products with x to y (zeroed beforehand).
   const uint16_t *gemv_x;    // fp16 [cols]
   float *gemv_y;             // fp32 [rows]
   uint64_t cols;
@@ -1315,24 +1315,39 @@ __device__ __forceinline__ void flush_int4_few(Smem<HLOG> &sm, uint32_t lane, co
   const uint64_t e = 2 * (dst0 + T);   // the tile's first code
   const uint32_t off = (uint32_t)(e & (P.group - 1)) + 8 * lane;
   if constexpr (MODE == MODE_GEMV) {
-    // the tile is 2048 codes of one row: its fp16 weights dotted with x
-    const uint64_t row = e / P.cols;
-    const uint4 *xs = (const uint4 *)(P.gemv_x + (e - row * P.cols)) + lane;
-    float acc = 0.0f;
+    // the tile's fp16 weights dotted with x.  Rows are a multiple of 512
+    // codes, so each 512-code block k (lane l holds codes 512 k + 8 l ..)
+    // lies in one row; a tile inside one row sums all four blocks first.
+    const uint64_t row0 = e / P.cols, row3 = (e + 1536) / P.cols;
+    float acc[4];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
+      const uint64_t ek = e + 512 * k;
+      const uint64_t rk = ek / P.cols;
+      const uint4 xv = *((const uint4 *)(P.gemv_x + (ek - rk * P.cols)) + lane);
       const uint32_t i = (off + 512 * k) >> P.group_shift;
       const h2 c2 = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, m.z[1]));
       const h2 s2 = as_h2((uint32_t)__builtin_amdgcn_ds_bpermute(4 * i, m.s[1]));
       const uint4 wv = deq8_int4_dual(w[k], c2, s2);
-      const uint4 xv = xs[64 * k];
-      acc = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), acc, false);
+      float a = 0.0f;
+      a = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), a, false);
+      a = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), a, false);
+      a = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), a, false);
+      a = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), a, false);
+      acc[k] = a;
     }
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (lane == 0) atomicAdd(P.gemv_y + row, acc);
+    if (row0 == row3) {
+      float a = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+      if (lane == 0) atomicAdd(P.gemv_y + row0, a);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        float a = acc[k];
+        for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+        if (lane == 0) atomicAdd(P.gemv_y + (e + 512 * k) / P.cols, a);
+      }
+    }
     return;
   }
   uint4 *out = (uint4 *)((uint16_t *)P.out + e) + lane;
