@@ -123,7 +123,7 @@ def main():
     import weight_dequantization_amd as lt
 
     dev = torch.device("cuda:0")
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     packed = lt.pack_int4(w.codes)
     table = lt.ChunkTable.build(packed, w.dst_off, dev)
     scales = torch.from_numpy(w.scales.view(np.int16)).to(dev)
@@ -283,7 +283,7 @@ def gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed):
     import synth
     layer = []
     for t in range(len(synth.LLAMA70B_LAYER)):
-        wt = synth.config5_tensor(0, t)
+        wt = synth.llama70b_tensor(0, t)
         tb = lt.ChunkTable.build(lt.pack_int4(wt.codes), wt.dst_off, dev)
         layer.append((wt, tb, torch.from_numpy(wt.scales.view(np.int16)).to(dev), torch.from_numpy(wt.zp).to(dev),
                       torch.randn(wt.cols, dtype=torch.float16, device=dev),
@@ -329,7 +329,7 @@ def activation_measurements(torch, lt, dev, timed):
     ways: zero-run coded (bitmap + values) and LZ4 chunks, decode-only; the
     coded size and GB/s of coded input + fp16 output."""
     import synth
-    a = synth.config4()
+    a = synth.relu_4096x14336()
     x = a.data.view(np.uint16)
     bitmap, val_off, vals = lt.encode_zero_runs(x)
     z = lt.ZeroRunTensor.from_host(bitmap, val_off, vals, x.size, dev)

@@ -10,13 +10,13 @@ Workloads (shapes and value distributions) stand in for the real quantized
 model weights and captured activations that the pages measure on and that are
 not available here:
 
-* config 1  tiny INT4 weight 1024x1024, group 256, zero point 8, 30% all-zero groups
-* config 2  INT8 per-row 8192x8192, N(0,1)*32 rounded and clipped, half the rows pruned
-* config 3  INT4 MLP projection 8192x28672, group 128, zero points U{0..15},
-            codes rounded N(7.5, 3) clipped to 0..15, 20% all-zero groups
-* config 4  ReLU activations 4096x14336 fp16, max(0, N(0,1) - 1.3), with stress chunks
-* config 5  80 Llama-70B-shaped layers of INT4 projections, group 128, chunks of
-            16/64/256 KiB mixed per chunk
+* tiny_int4_1024       INT4 weight 1024x1024, group 256, zero point 8, 30% all-zero groups
+* int8_8192x8192       INT8 per-row 8192x8192, N(0,1)*32 rounded and clipped, half the rows pruned
+* mlp_int4_8192x28672  INT4 MLP projection 8192x28672, group 128, zero points U{0..15},
+                       codes rounded N(7.5, 3) clipped to 0..15, 20% all-zero groups
+* relu_4096x14336      ReLU activations 4096x14336 fp16, max(0, N(0,1) - 1.3), with stress chunks
+* llama70b_tensor      80 Llama-70B-shaped layers of INT4 projections, group 128, chunks of
+                       16/64/256 KiB mixed per chunk
 
 Scales are drawn in float64 and rounded to fp16 with numpy's round-to-nearest-even
 conversion; they are returned as raw fp16 bit patterns (uint16).
@@ -163,14 +163,14 @@ def int4_weight(rows, cols, group, seed, *, code_dist="normal", zero_frac=0.2,
     return Int4Weight(rows, cols, group, codes, scales, zp, dst_off, seed)
 
 
-def config1() -> Int4Weight:
+def tiny_int4_1024() -> Int4Weight:
     """Tiny INT4 weight: 1024x1024, group 256 along rows, zp 8, codes U{0..15},
     exactly round(0.3 * 4096) = 1229 all-zero groups, 64 KiB chunks."""
     return int4_weight(1024, 1024, 256, 1001, code_dist="uniform", zero_frac=0.30,
                        zp_mode=8, scale_lo=0.005, scale_hi=0.05)
 
 
-def config2() -> Int8Weight:
+def int8_8192x8192() -> Int8Weight:
     """INT8 per-channel: 8192x8192, q = clip(rint(N(0,1)*32), -127, 127),
     exactly 4096 zero rows, per-row fp16 scales U(1e-3, 1e-2), no zero point."""
     rng = np.random.default_rng(1002)
@@ -182,14 +182,14 @@ def config2() -> Int8Weight:
     return Int8Weight(R, C, C, q, scales, None, uniform_chunks(R * C), 1002)
 
 
-def config3() -> Int4Weight:
+def mlp_int4_8192x28672() -> Int4Weight:
     """Fused LZ4+INT4 MLP layer: 8192x28672, group 128, zp U{0..15},
     codes clip(rint(N(7.5, 3)), 0, 15), 20% all-zero groups, 64 KiB chunks."""
     return int4_weight(8192, 28672, 128, 1003)
 
 
-def config3_small(rows=256, cols=28672, seed=2003) -> Int4Weight:
-    """Config 3's distributions at a size the oracle checks in seconds."""
+def mlp_int4_small(rows=256, cols=28672, seed=2003) -> Int4Weight:
+    """The 8192x28672 layer's distributions at a size the oracle checks in seconds."""
     return int4_weight(rows, cols, 128, seed)
 
 
@@ -224,7 +224,7 @@ def activation(rows, cols, seed, *, stress_frac=0.01, chunk=CHUNK_64K) -> Activa
     return Activation((rows, cols), data, dst_off, stress, seed)
 
 
-def config4() -> Activation:
+def relu_4096x14336() -> Activation:
     """ReLU activations decode-only: 4096x14336 fp16, 1792 chunks of 64 KiB,
     18 random-byte chunks, 18 all-0xAB chunks, 18 chunks with one 0xAB run."""
     return activation(4096, 14336, 1004)
@@ -243,12 +243,12 @@ LLAMA70B_LAYER = (
 N_LAYERS_70B = 80
 
 
-def config5_tensor(layer: int, t: int) -> Int4Weight:
+def llama70b_tensor(layer: int, t: int) -> Int4Weight:
     """One INT4 projection of the 80-layer stack, seeded by (1005, layer, t);
-    distributions as config 3, chunk sizes drawn per chunk from 16/64/256 KiB."""
+    distributions as the 8192x28672 layer's, chunk sizes drawn per chunk from 16/64/256 KiB."""
     name, r, c = LLAMA70B_LAYER[t]
     return int4_weight(r, c, 128, [1005, layer, t], chunking="mixed")
 
 
-def config(k: int):
-    return {1: config1, 2: config2, 3: config3, 4: config4}[k]()
+WORKLOADS = {"tiny_int4_1024": tiny_int4_1024, "int8_8192x8192": int8_8192x8192,
+             "mlp_int4_8192x28672": mlp_int4_8192x28672, "relu_4096x14336": relu_4096x14336}

@@ -30,7 +30,7 @@ def t_u16(a):
 
 @pytest.fixture(scope="module")
 def layer():
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     table = lt.ChunkTable.build(lt.pack_int4(w.codes), w.dst_off, DEV)
     W = O.f64_from_f16(O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)).reshape(w.rows, w.cols)
     return w, table, W
@@ -98,7 +98,7 @@ def test_llama70b_layer():
     columns exact."""
     rng = np.random.default_rng(7)
     for t in range(len(synth.LLAMA70B_LAYER)):
-        w = synth.config5_tensor(11, t)
+        w = synth.llama70b_tensor(11, t)
         print("layer 11 tensor %dx%d" % (w.rows, w.cols), flush=True)
         comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off)
         table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, DEV, index=True)

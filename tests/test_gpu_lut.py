@@ -40,17 +40,17 @@ def _check(codes, lut, rows, cols, group, what):
     assert bad.size == 0, "%s: %d differ, first at %d" % (what, bad.size, bad[0])
 
 
-def test_config3_shape_random_tables():
+def test_mlp_8192x28672_shape_random_tables():
     """8192x28672, group 128, every table entry a random fp16 pattern."""
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     rng = np.random.default_rng(0)
     lut = rng.integers(0, 65536, (w.rows * w.cols // 128, 16)).astype(np.uint16)
-    _check(w.codes, lut, w.rows, w.cols, 128, "config3 shape")
+    _check(w.codes, lut, w.rows, w.cols, 128, "mlp_int4_8192x28672 shape")
 
 
 def test_affine_tables_equal_affine_dequant():
     """A table filled from (q - zp) * s gives lt_dequant_int4's output."""
-    w = synth.config1()
+    w = synth.tiny_int4_1024()
     q = np.arange(16, dtype=np.int64)
     vals = (q[None, :] - w.zp.astype(np.int64)[:, None]) * O.f64_from_f16(w.scales)[:, None]
     lut = O.f16_from_f64(vals.ravel()).reshape(-1, 16)

@@ -74,13 +74,13 @@ def _raw_int4(codes, scales, zp, rows, cols, group):
     assert_same(host_u16(out), ref, "dequant_int4 %dx%d g%d" % (rows, cols, group))
 
 
-def test_raw_int4_config1():
-    w = synth.config1()
+def test_raw_int4_tiny_int4():
+    w = synth.tiny_int4_1024()
     _raw_int4(w.codes, w.scales, w.zp, w.rows, w.cols, w.group)
 
 
-def test_raw_int4_config3_full():
-    w = synth.config3()
+def test_raw_int4_mlp_8192x28672_full():
+    w = synth.mlp_int4_8192x28672()
     _raw_int4(w.codes, w.scales, w.zp, w.rows, w.cols, w.group)
 
 
@@ -115,8 +115,8 @@ def _raw_int8(q, scales, zp, rows, cols, group):
     assert_same(host_u16(out), ref, "dequant_int8 %dx%d g%d" % (rows, cols, group))
 
 
-def test_raw_int8_config2():
-    w = synth.config2()
+def test_raw_int8_int8_8192():
+    w = synth.int8_8192x8192()
     _raw_int8(w.q, w.scales, w.zp, w.rows, w.cols, w.group)
 
 
@@ -233,10 +233,10 @@ def test_declared_window_is_enforced():
             assert s[i] == 0 and np.array_equal(got[65536 * i:65536 * (i + 1)], x[65536 * i:65536 * (i + 1)])
 
 
-def test_decode_config4_full():
-    a = synth.config4()
-    _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV), a.data, "config4 packer")
-    _decode_check(table_from_oracle(O.compress_table(a.data, a.dst_off)), a.data, "config4 oracle")
+def test_decode_relu_4096x14336_full():
+    a = synth.relu_4096x14336()
+    _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV), a.data, "relu_4096x14336 packer")
+    _decode_check(table_from_oracle(O.compress_table(a.data, a.dst_off)), a.data, "relu_4096x14336 oracle")
 
 
 def test_decode_stress_blocks():
@@ -316,10 +316,10 @@ def test_index_decodes_oracle_and_generated_streams():
         sizes[-1] = int(rng.integers(0, 70000))
         t, e = _seq_table(rng.integers(0, 2**62, n), sizes)
         _decode_check(table_from_oracle(t, index=True), e, "seqgen indexed %d" % trial)
-    a = synth.config4()
+    a = synth.relu_4096x14336()
     _decode_check(table_from_oracle(O.compress_table(a.data, a.dst_off), index=True), a.data,
-                  "config4 oracle, indexed")
-    _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV, index=False), a.data, "config4 packer, walked")
+                  "relu_4096x14336 oracle, indexed")
+    _decode_check(lt.ChunkTable.build(a.data, a.dst_off, DEV, index=False), a.data, "relu_4096x14336 packer, walked")
 
 
 def _index_case(comp, comp_off, dst_off, data, seq_off, seq_pos, what, bad):
@@ -386,25 +386,25 @@ def _fused4(table, w, what):
     assert_same(host_u16(out), ref, what)
 
 
-def test_fused_int4_config1_both_compressors():
-    w = synth.config1()
+def test_fused_int4_tiny_int4_both_compressors():
+    w = synth.tiny_int4_1024()
     packed = lt.pack_int4(w.codes)
-    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "config1 packer")
-    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "config1 oracle")
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "tiny_int4_1024 packer")
+    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "tiny_int4_1024 oracle")
 
 
-def test_fused_int4_config3_full():
+def test_fused_int4_mlp_8192x28672_full():
     """The benchmark's workload: 8192x28672, group 128, packer streams, with
     the sequence index (the benchmark's table) and without it."""
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     packed = lt.pack_int4(w.codes)
-    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "config3 packer, indexed")
-    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV, index=False), w, "config3 packer, walked")
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "mlp_int4_8192x28672 packer, indexed")
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV, index=False), w, "mlp_int4_8192x28672 packer, walked")
 
 
-def test_fused_int4_config3_oracle_stream():
-    w = synth.config3_small(rows=1024)
-    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "config3 oracle")
+def test_fused_int4_mlp_8192x28672_oracle_stream():
+    w = synth.mlp_int4_small(rows=1024)
+    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "mlp_int4_8192x28672 oracle")
 
 
 @pytest.mark.parametrize("rows,cols,group,chunk", [
@@ -450,13 +450,13 @@ def test_fused_int4_short_window_big_chunks():
     _fused4(table, w, "short window, 256 KiB chunks")
 
 
-def test_fused_int8_config2():
-    w = synth.config2()
+def test_fused_int8_int8_8192():
+    w = synth.int8_8192x8192()
     table = lt.ChunkTable.build(w.q.view(np.uint8), w.dst_off, DEV)
     st = status_tensor(table.n_chunks)
     out = lt.fused_lz4_int8(table, t_u16(w.scales), None, (w.rows, w.cols), w.group, status=st)
     assert np.all(statuses(st, table.n_chunks) == 0)
-    assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "config2 fused int8")
+    assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "int8_8192x8192 fused int8")
 
 
 def test_fused_int8_small_groups_zp():

@@ -72,15 +72,15 @@ def _int4_ranges(table, w, ref, what):
             assert_same(host_u16(out), ref[lo:hi], "%s chunks %d+%d" % (what, first, count))
 
 
-def test_int4_ranges_config3_full():
+def test_int4_ranges_mlp_8192x28672_full():
     """The 8192x28672 layer: single chunks at both ends, a 257-chunk middle
     range, the whole table; indexed and walked."""
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     packed = lt.pack_int4(w.codes)
     ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)
     for index in (True, False):
-        print("config3 index=%s" % index, flush=True)
-        _int4_ranges(lt.ChunkTable.build(packed, w.dst_off, DEV, index=index), w, ref, "config3 index=%s" % index)
+        print("mlp_int4_8192x28672 index=%s" % index, flush=True)
+        _int4_ranges(lt.ChunkTable.build(packed, w.dst_off, DEV, index=index), w, ref, "mlp_int4_8192x28672 index=%s" % index)
 
 
 def test_int4_ranges_mixed_chunks_oracle_stream():
@@ -94,8 +94,8 @@ def test_int4_ranges_mixed_chunks_oracle_stream():
         _int4_ranges(t, w, ref, "mixed index=%s" % index)
 
 
-def test_int8_ranges_config2():
-    w = synth.config2()
+def test_int8_ranges_int8_8192():
+    w = synth.int8_8192x8192()
     table = lt.ChunkTable.build(w.q.view(np.uint8), w.dst_off, DEV)
     ref = O.dequant_int8(w.q, w.scales, None, w.group)
     d = table.host_dst_off
@@ -105,14 +105,14 @@ def test_int8_ranges_config2():
                                       status=st)
         assert np.all(statuses(st, count) == 0), (first, count)
         if count:
-            assert_same(host_u16(out), ref[int(d[first]):int(d[first + count])], "config2 %d+%d" % (first, count))
+            assert_same(host_u16(out), ref[int(d[first]):int(d[first + count])], "int8_8192x8192 %d+%d" % (first, count))
 
 
-def test_decode_ranges_config4_with_guards():
+def test_decode_ranges_relu_4096x14336_with_guards():
     """Bytes mode on the activation workload (random-byte, 0xAB-run and
     sparse chunks): each range lands at offset 0 of its buffer and nothing
     is written past either end."""
-    a = synth.config4()
+    a = synth.relu_4096x14336()
     table = lt.ChunkTable.build(a.data, a.dst_off, DEV)
     d = table.host_dst_off
     guard = 4096

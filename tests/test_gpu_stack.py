@@ -1,4 +1,4 @@
-"""GPU parity over the 80-layer Llama-70B-shaped INT4 stack (config 5).
+"""GPU parity over the 80-layer Llama-70B-shaped INT4 stack (80 layers).
 
 Every one of the 80 layers x 7 projections (q, k, v, o, gate, up, down; INT4,
 group 128, LZ4 chunks of 16/64/256 KiB drawn per chunk) is resident on the
@@ -46,7 +46,7 @@ def test_llama70b_stack_layer_by_layer():
     distinct = {}
     for src_layer in (0, 79):
         for t in range(len(synth.LLAMA70B_LAYER)):
-            w = synth.config5_tensor(src_layer, t)
+            w = synth.llama70b_tensor(src_layer, t)
             packed = lt.pack_int4(w.codes)
             comp, comp_off = lt.compress_chunks(packed, w.dst_off)
             sizes = np.diff(w.dst_off.astype(np.int64))

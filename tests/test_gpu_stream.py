@@ -71,29 +71,29 @@ def _stream_fused4(table, w, k, what):
     assert_same(host_u16(out), ref, what)
 
 
-def test_stream_fused_int4_config1_many_batches():
+def test_stream_fused_int4_tiny_int4_many_batches():
     """One chunk per staging half (every batch waits for the decode two
     batches back), and three per half; indexed and walked."""
-    w = synth.config1()
+    w = synth.tiny_int4_1024()
     packed = lt.pack_int4(w.codes)
     comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
     for index in (True, False):
         t = host_table(comp, comp_off, w.dst_off, index, lt.PACK_WINDOW)
         for k in (1, 3):
-            print("config1 index=%s chunks/half=%d" % (index, k), flush=True)
-            _stream_fused4(t, w, k, "config1 streamed, index=%s, %d/half" % (index, k))
+            print("tiny_int4_1024 index=%s chunks/half=%d" % (index, k), flush=True)
+            _stream_fused4(t, w, k, "tiny_int4_1024 streamed, index=%s, %d/half" % (index, k))
 
 
-def test_stream_fused_int4_config3_full():
+def test_stream_fused_int4_mlp_8192x28672_full():
     """The benchmark's workload, 8192x28672 group 128, streamed through
     64-chunk halves (about 28 batches), with and without the index."""
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     packed = lt.pack_int4(w.codes)
     comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
     for index in (True, False):
-        print("config3 index=%s" % index, flush=True)
+        print("mlp_int4_8192x28672 index=%s" % index, flush=True)
         t = host_table(comp, comp_off, w.dst_off, index, lt.PACK_WINDOW)
-        _stream_fused4(t, w, 64, "config3 streamed, index=%s" % index)
+        _stream_fused4(t, w, 64, "mlp_int4_8192x28672 streamed, index=%s" % index)
 
 
 def test_stream_fused_int4_ragged_and_oracle_stream():
@@ -218,7 +218,7 @@ def test_stream_llama70b_layer_from_host():
     would load it; each tensor against the oracle in full."""
     tabs = []
     for t in range(len(synth.LLAMA70B_LAYER)):
-        w = synth.config5_tensor(3, t)
+        w = synth.llama70b_tensor(3, t)
         comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off)
         tabs.append((w, host_table(comp, comp_off, w.dst_off, True)))
     staging = torch.empty(max(ht.staging_bytes() for _, ht in tabs), dtype=torch.uint8, device=DEV)
@@ -236,14 +236,14 @@ def test_stream_llama70b_layer_from_host():
                     "layer 3 %dx%d" % key)
 
 
-def test_stream_fused_int8_config2():
+def test_stream_fused_int8_int8_8192():
     """INT8 per-row weights (8192x8192, half the rows pruned) from pinned host
     memory in 64-chunk batches, against the oracle."""
-    w = synth.config2()
+    w = synth.int8_8192x8192()
     comp, comp_off = lt.compress_chunks(w.q.view(np.uint8), w.dst_off, max_dist=lt.PACK_WINDOW)
     t = host_table(comp, comp_off, w.dst_off, True, lt.PACK_WINDOW)
     st = status_tensor(t.n_chunks)
     out = lt.stream_fused_lz4_int8(t, t_u16(w.scales), None, (w.rows, w.cols), w.group, status=st,
                                    staging=staging_for(t, 64))
     assert np.all(statuses(st, t.n_chunks) == 0)
-    assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "config2 streamed int8")
+    assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "int8_8192x8192 streamed int8")

@@ -32,11 +32,11 @@ def dev_u32(a):
     return torch.from_numpy(np.ascontiguousarray(a, np.uint32).view(np.int32)).to(DEV)
 
 
-def test_config3_checksums_and_single_flips():
+def test_mlp_8192x28672_checksums_and_single_flips():
     """The benchmark layer's 1792 packer blocks: computed values equal the
     oracle's; the host packer's values verify; one flipped byte in each of
     several chunks fails exactly those chunks."""
-    w = synth.config3()
+    w = synth.mlp_int4_8192x28672()
     comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off, max_dist=lt.PACK_WINDOW)
     table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, DEV)
     ref = O.crc32_chunks(comp, comp_off)

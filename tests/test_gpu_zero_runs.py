@@ -32,11 +32,11 @@ def status_tensor(n):
     return torch.full((max(n, 1),), -1, dtype=torch.int32, device=DEV)
 
 
-def test_config4_activation_round_trip():
+def test_relu_4096x14336_activation_round_trip():
     """The 4096x14336 ReLU activation workload (about 90% zeros, with
     random-byte and 0xAB stress chunks): bit-exact against the input and the
     oracle's decode."""
-    a = synth.config4()
+    a = synth.relu_4096x14336()
     x = a.data.view(np.uint16)
     bitmap, val_off, vals = lt.encode_zero_runs(x)
     z = lt.ZeroRunTensor.from_host(bitmap, val_off, vals, x.size, DEV)

@@ -116,8 +116,8 @@ def test_packer_blocks_decode_with_oracle_small():
     assert _oracle_round_trip(x, np.array([0, 65536], np.uint64)) < 300
 
 
-def test_packer_config1_and_config3_small():
-    for w in (synth.config1(), synth.config3_small()):
+def test_packer_tiny_and_mlp_small():
+    for w in (synth.tiny_int4_1024(), synth.mlp_int4_small()):
         packed = lt.pack_int4(w.codes)
         size = _oracle_round_trip(packed, w.dst_off)
         ref = O.compress_table(packed, w.dst_off).comp_bytes
@@ -126,12 +126,13 @@ def test_packer_config1_and_config3_small():
 
 
 @pytest.mark.slow
-def test_packer_full_configs():
-    for k in (2, 3, 4):
-        w = synth.config(k)
-        data = {2: lambda: w.q.view(np.uint8), 3: lambda: lt.pack_int4(w.codes), 4: lambda: w.data}[k]()
+def test_packer_full_workloads():
+    for name in ("int8_8192x8192", "mlp_int4_8192x28672", "relu_4096x14336"):
+        w = synth.WORKLOADS[name]()
+        data = {"int8_8192x8192": lambda: w.q.view(np.uint8), "mlp_int4_8192x28672": lambda: lt.pack_int4(w.codes),
+                "relu_4096x14336": lambda: w.data}[name]()
         size = _oracle_round_trip(data, w.dst_off)
-        print("config", k, "compressed", size, "of", data.size)
+        print(name, "compressed", size, "of", data.size)
 
 
 def test_packer_mixed_chunks():

@@ -5,7 +5,7 @@ its own LZ4 block; comp_off / dst_off are prefix sums.  Invariants:
 concat(decode(chunk_i)) == x, offsets monotone, dst_off[n] == len(x); the
 fused reference equals dequantize(decode(table)) and, for the round trip,
 dequantize(pack(codes)).  Synthetic workloads stand in for real weights and
-activations (configs 1-4 at full size; config 3's distributions also at a
+activations (the four single-tensor workloads at full size; the 8192x28672 layer's distributions also at a
 small size).
 """
 import hashlib
@@ -28,8 +28,8 @@ def _round_trip(data, dst_off):
     return t
 
 
-def test_config1_round_trip_and_fused():
-    w = synth.config1()
+def test_tiny_int4_round_trip_and_fused():
+    w = synth.tiny_int4_1024()
     packed = O.pack_int4(w.codes)
     t = _round_trip(packed, w.dst_off)
     assert t.n == 8
@@ -41,8 +41,8 @@ def test_config1_round_trip_and_fused():
     assert zg.sum() >= 1229
 
 
-def test_config3_small_fused_chunked_matches():
-    w = synth.config3_small()
+def test_mlp_small_fused_chunked_matches():
+    w = synth.mlp_int4_small()
     packed = O.pack_int4(w.codes)
     t = _round_trip(packed, w.dst_off)
     ref = O.dequant_int4(packed, w.scales, w.zp, w.group)
@@ -76,12 +76,12 @@ def test_bad_table_entries():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("k", [2, 3, 4])
-def test_full_configs_round_trip(k):
-    w = synth.config(k)
-    if k == 3:
+@pytest.mark.parametrize("name", ["int8_8192x8192", "mlp_int4_8192x28672", "relu_4096x14336"])
+def test_full_workloads_round_trip(name):
+    w = synth.WORKLOADS[name]()
+    if name == "mlp_int4_8192x28672":
         data = O.pack_int4(w.codes)
-    elif k == 2:
+    elif name == "int8_8192x8192":
         data = w.q.view(np.uint8)
     else:
         data = w.data
@@ -89,13 +89,14 @@ def test_full_configs_round_trip(k):
     assert t.n in (1024, 1792)
     ratio = t.comp_bytes / data.size
     # what the workloads are meant to look like (stated in the generators)
-    assert {2: 0.3 < ratio < 0.7, 3: 0.7 < ratio < 0.9, 4: 0.1 < ratio < 0.5}[k], ratio
+    assert {"int8_8192x8192": 0.3 < ratio < 0.7, "mlp_int4_8192x28672": 0.7 < ratio < 0.9,
+            "relu_4096x14336": 0.1 < ratio < 0.5}[name], ratio
 
 
 def test_compressed_stream_deterministic():
     """Parity of compressed bytes is unpinned beyond determinism (many valid
     encodings exist); the same input gives the same stream."""
-    w = synth.config1()
+    w = synth.tiny_int4_1024()
     packed = O.pack_int4(w.codes)
     a = O.compress_table(packed, w.dst_off)
     b = O.compress_table(packed, w.dst_off, threads=1)
