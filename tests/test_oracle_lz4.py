@@ -165,13 +165,34 @@ def test_flipped_bytes_never_write_outside():
 
 # ----------------------------------------------- generator-built streams
 
+def _seqgen_batch(seeds, targets):
+    """Streams from the sequence generator, decoded as one chunk table (one
+    block per stream) by the oracle's table decoder; returns the statuses,
+    the decoded bytes and the expected bytes."""
+    streams, expect = [], []
+    for s, t in zip(seeds, targets):
+        a, b = O.seqgen(int(s), int(t))
+        streams.append(a)
+        expect.append(b)
+    comp_off = np.concatenate([[0], np.cumsum([a.size for a in streams])]).astype(np.uint64)
+    dst_off = np.concatenate([[0], np.cumsum([b.size for b in expect])]).astype(np.uint64)
+    t = O.Table(np.concatenate(streams), comp_off, dst_off)
+    out, st = O.decode_table(t)
+    return st, out, np.concatenate(expect)
+
+
 def test_seqgen_fuzz():
-    for seed in range(3000):
-        target = [0, 1, 50, 700, 5000, 70000][seed % 6]
-        stream, expected = O.seqgen(seed, target)
-        st, out, produced = O.lz4_decode(stream, expected.size)
-        assert st == O.OK and produced == expected.size, seed
-        assert np.array_equal(out, expected), seed
+    """100,000 generator-built streams (sequence lists whose encoded bytes and
+    expected output are built side by side, independent of the compressor)
+    decode to their expected bytes."""
+    n = 100_000
+    seeds = np.arange(n)
+    targets = np.array([0, 1, 50, 700, 5000, 20000])[seeds % 6]
+    targets[seeds % 97 == 0] = 70000
+    for lo in range(0, n, 20_000):
+        st, out, exp = _seqgen_batch(seeds[lo:lo + 20_000], targets[lo:lo + 20_000])
+        assert np.all(st == O.OK), np.nonzero(st)[0][:5] + lo
+        assert np.array_equal(out, exp)
 
 
 # ------------------------------------------------------------ compressor
@@ -211,42 +232,41 @@ def test_store_sizes():
         assert s.size == want
 
 
-def _all_strings(alphabet, max_len):
-    for n in range(max_len + 1):
-        if n == 0:
-            yield np.zeros(0, np.uint8)
-            continue
-        k = len(alphabet)
-        for idx in range(k ** n):
-            digits = []
-            for _ in range(n):
-                digits.append(alphabet[idx % k])
-                idx //= k
-            yield np.array(digits, np.uint8)
+def _round_trip_all(n, alphabet):
+    """Every string of length n over `alphabet`, each compressed as its own
+    block by the oracle's table compressor and decoded back by its table
+    decoder (one chunk per string)."""
+    k = len(alphabet)
+    idx = np.arange(k ** n, dtype=np.int64)
+    digits = np.empty((idx.size, n), np.uint8)
+    a = np.asarray(alphabet, np.uint8)
+    for p in range(n):
+        digits[:, p] = a[(idx // k ** p) % k]
+    src = digits.ravel()
+    dst_off = (np.arange(idx.size + 1, dtype=np.uint64) * np.uint64(n))
+    t = O.compress_table(src, dst_off)
+    out, st = O.decode_table(t)
+    assert np.all(st == O.OK)
+    assert np.array_equal(out, src)
+    return t
 
 
 def test_compressor_brute_force_small():
-    """Every string of <= 14 bytes over {0x00, 0xAB} and every string of <= 2
+    """Every string of <= 14 bytes over {0x00, 0xAB} and every string of <= 3
     bytes over all 256 values round-trips."""
-    for x in _all_strings([0x00, 0xAB], 14):
-        c = O.lz4_compress(x)
-        st, out, _ = O.lz4_decode(c, x.size)
-        assert st == O.OK and np.array_equal(out, x), x
-    for x in _all_strings(list(range(256)), 2):
-        c = O.lz4_compress(x)
-        st, out, _ = O.lz4_decode(c, x.size)
-        assert st == O.OK and np.array_equal(out, x)
+    assert O.lz4_decode(O.lz4_compress(np.zeros(0, np.uint8)), 0)[0] == O.OK
+    for n in range(1, 15):
+        _round_trip_all(n, [0x00, 0xAB])
+    for n in range(1, 4):
+        _round_trip_all(n, list(range(256)))
 
 
 @pytest.mark.slow
-def test_compressor_brute_force_18():
-    """Every string of length <= 18 over {0x00, 0xAB} (524,287 strings)."""
-    for n in range(15, 19):
-        for idx in range(1 << n):
-            x = np.array([(0xAB if (idx >> b) & 1 else 0) for b in range(n)], np.uint8)
-            c = O.lz4_compress(x)
-            st, out, _ = O.lz4_decode(c, n)
-            assert st == O.OK and np.array_equal(out, x)
+def test_compressor_brute_force_20():
+    """Every string of length 15 ..= 20 over {0x00, 0xAB} (2,064,384 strings);
+    with the fast test, all 2,097,151 strings of length <= 20."""
+    for n in range(15, 21):
+        _round_trip_all(n, [0x00, 0xAB])
 
 
 def test_compressor_random_round_trips():

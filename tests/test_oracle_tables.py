@@ -101,3 +101,40 @@ def test_compressed_stream_deterministic():
     a = O.compress_table(packed, w.dst_off)
     b = O.compress_table(packed, w.dst_off, threads=1)
     assert hashlib.sha256(a.comp.tobytes()).hexdigest() == hashlib.sha256(b.comp.tobytes()).hexdigest()
+
+
+def test_int8_fused_is_dequant_of_decode():
+    """The INT8 fused reference is the composition dequant_int8(decode(table))
+    ("GPU Compression Pipeline - TDD Roadmap", Phase 1.2 INT8 dequantization
+    after the Phase 2.1 decode), on a per-row table whose round trip gives
+    back the codes, so it also equals dequant_int8 of the codes themselves;
+    a corrupted chunk fails with the decoder's status and the others stay
+    exact."""
+    rng = np.random.default_rng(31)
+    R, C = 96, 4096
+    q = np.clip(np.rint(rng.standard_normal(R * C) * 32.0), -127, 127).astype(np.int8)
+    q.reshape(R, C)[rng.choice(R, R // 2, replace=False)] = 0
+    scales = synth.fp16_bits(rng.uniform(1e-3, 1e-2, size=R))
+    zp = rng.integers(-128, 128, size=R, dtype=np.int8)
+    dst_off = synth.uniform_chunks(q.size, 16384)
+    t = _round_trip(q.view(np.uint8), dst_off)
+    for z in (None, zp):
+        fused, st = O.fused_int8(t, scales, z, C, q.size)
+        assert np.all(st == O.OK)
+        dec, _ = O.decode_table(t)
+        assert np.array_equal(fused, O.dequant_int8(dec.view(np.int8), scales, z, C))
+        assert np.array_equal(fused, O.dequant_int8(q, scales, z, C))
+    # per-tensor scale (group = rows * cols)
+    fused, st = O.fused_int8(t, scales[:1], None, q.size, q.size)
+    assert np.array_equal(fused, O.dequant_int8(q, scales[:1], None, q.size))
+    # a truncated block: that chunk's status matches the decoder's, the rest are exact
+    bad = O.Table(t.comp.copy(), t.comp_off.copy(), t.dst_off)
+    k = 5
+    bad.comp_off[k + 1:] -= np.uint64(1)
+    bad.comp = np.delete(bad.comp, int(t.comp_off[k + 1]) - 1)
+    fused, st = O.fused_int8(bad, scales, zp, C, q.size)
+    _, st_dec = O.decode_table(bad)
+    assert np.array_equal(st, st_dec) and st[k] != O.OK and np.count_nonzero(st) == 1
+    ref = O.dequant_int8(q, scales, zp, C)
+    a, b = int(t.dst_off[k]), int(t.dst_off[k + 1])
+    assert np.array_equal(np.delete(fused, np.s_[a:b]), np.delete(ref, np.s_[a:b]))
