@@ -95,6 +95,40 @@ def test_raw_int4_whole_domain():
     _raw_int4(codes, sc, zp, n_groups, 16, 16)
 
 
+def _group128_domain():
+    """Group-128 INT4 over the whole code and zero-point domain: every code
+    0..15 (eight times each, shuffled within its group) under every zero point
+    -128..127, for 1024 fp16 scales that cover every exponent field 0..30 with
+    both signs (subnormals and signed zeros included) at the mantissas 0, 1,
+    2, 0x0FF, 0x200, 0x3FE, 0x3FF, plus finite scales drawn at random.  8192
+    rows of 4096 codes (32 groups per row)."""
+    rng = np.random.default_rng(128)
+    fixed = [(sgn << 15) | (e << 10) | m for sgn in (0, 1) for e in range(31)
+             for m in (0, 1, 2, 0x0FF, 0x200, 0x3FE, 0x3FF)]
+    extra = rng.integers(0, 0x7C00, 1024 - len(fixed)) | (rng.integers(0, 2, 1024 - len(fixed)) << 15)
+    scales_1 = np.array(fixed + list(extra), np.uint16)
+    assert scales_1.size == 1024 and np.all((scales_1 & 0x7C00) != 0x7C00)
+    n_groups = 256 * scales_1.size
+    scales = np.repeat(scales_1, 256)
+    zp = np.tile(np.arange(-128, 128, dtype=np.int64).astype(np.int8), scales_1.size)
+    base = np.tile(np.arange(16, dtype=np.uint8), 8)
+    codes = base[np.argsort(rng.random((n_groups, 128)), axis=1)]
+    return codes.ravel(), scales, zp, 8192, 4096
+
+
+def test_int4_group128_whole_domain_tiles_and_fused():
+    """The 1 KiB-tile raw kernel and the fused group-128 write-out over every
+    code x every zero point x scales of every exponent, bit for bit."""
+    codes, scales, zp, rows, cols = _group128_domain()
+    _raw_int4(codes, scales, zp, rows, cols, 128)
+    w = synth.Int4Weight(rows, cols, 128, codes, scales, zp, synth.uniform_chunks(rows * cols // 2))
+    packed = lt.pack_int4(codes)
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "group-128 domain, packer, indexed")
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV, index=False), w, "group-128 domain, packer, walked")
+    w.zp = None
+    _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV), w, "group-128 domain, no zero points")
+
+
 @pytest.mark.parametrize("rows,cols,group", [
     (10, 36, 6), (10, 36, 12), (10, 36, 36), (10, 36, 360), (3, 2, 2), (1, 6, 6), (7, 10, 70),
     (33, 128, 128), (64, 4096, 4096 * 64), (17, 24, 8), (5, 1000, 1000),
@@ -403,8 +437,13 @@ def test_fused_int4_mlp_8192x28672_full():
 
 
 def test_fused_int4_mlp_8192x28672_oracle_stream():
-    w = synth.mlp_int4_small(rows=1024)
-    _fused4(table_from_oracle(O.compress_table(O.pack_int4(w.codes), w.dst_off)), w, "mlp_int4_8192x28672 oracle")
+    """The 8192x28672 layer in full as the oracle's greedy compressor encodes
+    it (64 KiB window, 4-byte minimum matches, no declared window), through
+    the fused entry point with and without the sequence index."""
+    w = synth.mlp_int4_8192x28672()
+    ot = O.compress_table(O.pack_int4(w.codes), w.dst_off)
+    _fused4(table_from_oracle(ot), w, "mlp_int4_8192x28672 oracle stream")
+    _fused4(table_from_oracle(ot, index=True), w, "mlp_int4_8192x28672 oracle stream, indexed")
 
 
 @pytest.mark.parametrize("rows,cols,group,chunk", [
@@ -472,3 +511,84 @@ def test_fused_int8_small_groups_zp():
     out = lt.fused_lz4_int8(table, t_u16(scales), t_i8(zp), (rows, cols), group, status=st)
     assert np.all(statuses(st, table.n_chunks) == 0)
     assert_same(host_u16(out), O.dequant_int8(q, scales, zp, group), "fused int8 g100")
+
+
+# ---------------------------------------------- corrupt blocks, fused modes
+
+def _corrupt_blocks(comp, comp_off, rng, n_bad):
+    """A copy of a table's blocks with n_bad of them damaged: truncated by a
+    few bytes, one byte flipped, or a byte inserted.  Returns the new blocks,
+    offsets and the damaged chunk indices."""
+    n = comp_off.size - 1
+    bad = sorted(rng.choice(n, size=n_bad, replace=False).tolist())
+    blocks = [comp[int(comp_off[i]):int(comp_off[i + 1])].copy() for i in range(n)]
+    for k, i in enumerate(bad):
+        b = blocks[i]
+        kind = k % 3
+        if kind == 0:
+            b = b[:max(0, b.size - 1 - int(rng.integers(0, 8)))]
+        elif kind == 1:
+            b[int(rng.integers(0, b.size))] ^= np.uint8(rng.integers(1, 256))
+        else:
+            b = np.insert(b, int(rng.integers(0, b.size)), np.uint8(rng.integers(0, 256)))
+        blocks[i] = b
+    off = np.concatenate([[0], np.cumsum([b.size for b in blocks])]).astype(np.uint64)
+    return np.concatenate(blocks), off, bad
+
+
+@pytest.mark.parametrize("mode", ["int4", "int8"])
+def test_fused_corrupt_blocks_status_and_guards(mode):
+    """Damaged blocks through the fused entry points, in an output buffer with
+    guard bands on both sides: nothing outside the output is written; a chunk
+    the oracle cannot decode fails; a chunk reported OK holds exactly the
+    dequantized oracle bytes; undamaged chunks are exact.  Tables from the
+    packer with its declared 4 KiB window, with and without the sequence
+    index (built from the damaged blocks), and with no declared window (where
+    a chunk is OK on the GPU exactly when it is for the oracle)."""
+    rng = np.random.default_rng(61 if mode == "int4" else 62)
+    if mode == "int4":
+        w = synth.int4_weight(384, 8192, 128, 63)
+        data = lt.pack_int4(w.codes)
+        n_elem, per = w.rows * w.cols, 2
+        scales, zp, group = w.scales, w.zp, w.group
+    else:
+        R, C = 256, 8192
+        q = np.clip(np.rint(rng.standard_normal(R * C) * 32.0), -127, 127).astype(np.int8)
+        q.reshape(R, C)[rng.choice(R, R // 2, replace=False)] = 0
+        data = q.view(np.uint8)
+        n_elem, per = R * C, 1
+        scales, zp, group = synth.fp16_bits(rng.uniform(1e-3, 1e-2, size=R)), None, C
+    dst_off = synth.uniform_chunks(data.size)
+    guard = 4096
+    for window in (lt.PACK_WINDOW, 0):
+        comp, comp_off = lt.compress_chunks(data, dst_off, max_dist=window)
+        bcomp, boff, bad = _corrupt_blocks(comp, comp_off, rng, 12)
+        ot = O.Table(bcomp, boff, dst_off)
+        odec, ost = O.decode_table(ot)
+        for index in (True, False):
+            table = lt.ChunkTable.from_host(bcomp, boff, dst_off, DEV, max_dist=window, index=index)
+            buf = torch.full((n_elem + 2 * guard,), -1, dtype=torch.int16, device=DEV)
+            out = buf[guard:guard + n_elem].view(torch.float16)
+            st = status_tensor(table.n_chunks)
+            if mode == "int4":
+                lt.fused_lz4_int4(table, t_u16(scales), t_i8(zp), (n_elem // 8192, 8192), group, out=out, status=st)
+            else:
+                lt.fused_lz4_int8(table, t_u16(scales), None, (n_elem // 8192, 8192), group, out=out, status=st)
+            s = statuses(st, table.n_chunks)
+            b = host_u16(buf)
+            what = "%s window %d index %s" % (mode, window, index)
+            assert np.all(b[:guard] == 0xFFFF) and np.all(b[guard + n_elem:] == 0xFFFF), what + ": write outside"
+            got = b[guard:guard + n_elem]
+            assert np.all(s[ost != 0] != 0), what + ": a chunk the oracle rejects decoded OK"
+            if window == 0:
+                assert np.array_equal(s == 0, ost == 0), what
+            if mode == "int4":
+                ref = O.dequant_int4(odec, scales, zp, group, n_elem)
+            else:
+                ref = O.dequant_int8(odec.view(np.int8), scales, None, group)
+            for i in range(table.n_chunks):
+                lo, hi = per * int(dst_off[i]), per * int(dst_off[i + 1])
+                if i not in bad:
+                    assert s[i] == 0, (what, i, s[i])
+                if s[i] == 0:
+                    assert np.array_equal(got[lo:hi], ref[lo:hi]), (what, i)

@@ -11,7 +11,9 @@ longer than a test may run, so two distinct layers are generated (the seeds of
 layers 0 and 79) and their compressed tables are copied into 80 separate
 device allocations (even layers from layer 0, odd layers from layer 79).
 Every launch is checked on sampled elements against the oracle applied to the
-generator's codes; layer 0's 7 tensors are also checked in full once.
+generator's codes; the 14 distinct tensors (layers 0 and 79) are also checked
+in full once, and a third layer is checked in full in the table form the
+benchmark uses (declared 4 KiB window, sequence index).
 """
 import numpy as np
 import pytest
@@ -99,15 +101,33 @@ def test_llama70b_stack_layer_by_layer():
             assert bad == 0, "layer %d tensor %s: %d of %d sampled outputs differ" % (
                 layer, synth.LLAMA70B_LAYER[t][0], bad, ref.size)
 
-    # full check of layer 0's tensors, once
+    # full check of both generated layers' tensors (layers 0 and 79: distinct
+    # seeds, so distinct 16/64/256 KiB chunk draws), once each
     for (src, t), d in distinct.items():
-        if src != 0:
-            continue
         w = d["w"]
         tb, sc, zp = base[(src, t)]
-        out = lt.fused_lz4_int4(tb, sc, zp, (w.rows, w.cols), 128)
-        torch.cuda.synchronize()
-        got = out.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
-        ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, 128)
-        bad = np.nonzero(got != ref)[0]
-        assert bad.size == 0, "layer %d tensor %d: %d differ, first %d" % (src, t, bad.size, bad[0])
+        _full_check(w, tb, sc, zp, "layer %d tensor %s" % (src, synth.LLAMA70B_LAYER[t][0]))
+
+
+def _full_check(w, tb, sc, zp, what):
+    st = torch.full((tb.n_chunks,), -1, dtype=torch.int32, device=DEV)
+    out = lt.fused_lz4_int4(tb, sc, zp, (w.rows, w.cols), 128, status=st)
+    torch.cuda.synchronize()
+    s = st.cpu().numpy()
+    assert np.all(s == 0), (what, np.unique(s))
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, 128)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "%s: %d differ, first %d" % (what, bad.size, bad[0])
+
+
+def test_llama70b_layer_in_the_default_table_form():
+    """One whole layer of the stack (layer 5's seeds) packed in the form the
+    benchmark uses (ChunkTable.build's defaults: the packer's 4 KiB declared
+    window and the sequence index), each projection checked in full."""
+    for t in range(len(synth.LLAMA70B_LAYER)):
+        w = synth.llama70b_tensor(5, t)
+        tb = lt.ChunkTable.build(lt.pack_int4(w.codes), w.dst_off, DEV)
+        assert tb.max_dist == lt.PACK_WINDOW and tb.seq_off is not None
+        _full_check(w, tb, torch.from_numpy(w.scales.view(np.int16)).to(DEV), torch.from_numpy(w.zp).to(DEV),
+                    "layer 5 tensor %s, default table" % synth.LLAMA70B_LAYER[t][0])

@@ -1171,21 +1171,72 @@ __device__ __forceinline__ int32_t recorder(Rec<SM> &r, SM &sm, Ctl &ctl, uint32
 
 // -------------------------------------------------------------- feeder
 
-// Wave 1.  Streams the chunk's 16-byte aligned blocks into the input ring,
+// Waits until at most K LDS-DMA segments are still in flight, publishes
+// in_avail = v, and returns the minimum of the eight need counters.  The
+// counters are read before the wait, in the same asm block, so the read
+// overlaps the segment's latency; an older minimum is a smaller one, so the
+// bound it gives is safe.  (The reads wait for their own results inside the
+// block, so their output registers are final when it ends.)
+template <int K>
+__device__ __forceinline__ uint32_t land_and_bound(const uint32_t *need, uint32_t *in_avail, uint32_t v) {
+  uint4 a, b;
+  uint64_t sv;
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %3 offset:16\n\t"
+      "s_waitcnt vmcnt(%6)\n\t"
+      "s_mov_b64 %2, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "ds_write_b32 %4, %5\n\t"
+      "s_mov_b64 exec, %2\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&s"(sv)
+      : "v"(lds_addr(need)), "v"(lds_addr(in_avail)), "v"(v), "n"(K)
+      : "memory");
+  const uint32_t m0 = min(min(a.x, a.y), min(a.z, a.w));
+  const uint32_t m1 = min(min(b.x, b.y), min(b.z, b.w));
+  return __builtin_amdgcn_readfirstlane(min(m0, m1));
+}
+
+// land_and_bound for a run-time count of loads still allowed in flight
+__device__ __forceinline__ uint32_t land_and_bound_k(uint32_t k, const uint32_t *need, uint32_t *in_avail,
+                                                     uint32_t v) {
+  switch (k) {
+    case 0: return land_and_bound<0>(need, in_avail, v);
+    case 1: return land_and_bound<1>(need, in_avail, v);
+    case 2: return land_and_bound<2>(need, in_avail, v);
+    case 3: return land_and_bound<3>(need, in_avail, v);
+    case 4: return land_and_bound<4>(need, in_avail, v);
+    case 5: return land_and_bound<5>(need, in_avail, v);
+    case 6: return land_and_bound<6>(need, in_avail, v);
+    case 7: return land_and_bound<7>(need, in_avail, v);
+    case 8: return land_and_bound<8>(need, in_avail, v);
+    case 9: return land_and_bound<9>(need, in_avail, v);
+    case 10: return land_and_bound<10>(need, in_avail, v);
+    case 11: return land_and_bound<11>(need, in_avail, v);
+    case 12: return land_and_bound<12>(need, in_avail, v);
+    case 13: return land_and_bound<13>(need, in_avail, v);
+    case 14: return land_and_bound<14>(need, in_avail, v);
+    default: return land_and_bound<15>(need, in_avail, v);
+  }
+}
+
+// Wave 2.  Streams the chunk's 16-byte aligned blocks into the input ring,
 // one 1 KiB segment (one LDS-DMA load per lane) at a time, keeping up to QMAX
 // segments in flight within the ring space that every reader has released.
+// Each landed segment costs one LDS round trip, overlapped with the wait for
+// the segment: the readers' bound is read while the segment is in flight,
+// and the exit check (every reader gone: a failed chunk) is made only when
+// nothing is in flight.
 template <class SM>
 __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb) {
   constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
+  static_assert(QMAX <= 16, "land_and_bound_k waits for up to 15 loads in flight");
   const uint32_t nblk = (y_end + 15) / 16;
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
   uint32_t issued = 0, landed = 0;
-  while (landed < nseg) {
-    // nobody reads input once the walk has ended and every builder has left
-    if (lds_get_asm(&ctl.nfinished) == nb && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
-    const uint32_t used = min8(ctl.need);
-    uint32_t limit = used / SEG + QMAX;
-    if (limit > nseg) limit = nseg;
+  uint32_t limit = QMAX < nseg ? QMAX : nseg;   // every reader starts at input byte 0
+  for (;;) {
     while (issued < limit && issued - landed < QMAX) {
       uint32_t blk = issued * (SEG / 16) + lane;
       if (blk >= nblk) blk = nblk - 1;   // stay within the chunk's blocks
@@ -1195,12 +1246,22 @@ __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const ui
       issued++;
     }
     if (issued == landed) {
-      __builtin_amdgcn_s_sleep(SLEEP_FEED);
+      if (landed == nseg) break;
+      // the window is closed and nothing is in flight: nobody reads input
+      // once the walk has ended and every builder has left
+      if (lds_get_asm(&ctl.nfinished) == nb && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
+      const uint32_t used = min8(ctl.need);
+      limit = used / SEG + QMAX;
+      if (limit > nseg) limit = nseg;
+      if (issued == limit) __builtin_amdgcn_s_sleep(SLEEP_FEED);
       continue;
     }
-    wait_vm_le(issued - landed - 1);   // the oldest segment in flight has landed
+    // the oldest segment in flight has landed once at most k loads remain
+    const uint32_t k = issued - landed - 1;
     landed++;
-    lds_set(&ctl.in_avail, landed * SEG);
+    const uint32_t used = land_and_bound_k(k, ctl.need, &ctl.in_avail, landed * SEG);
+    limit = used / SEG + QMAX;
+    if (limit > nseg) limit = nseg;
   }
   wait_vm<0>();   // no LDS-DMA write outlives this wave
 }
