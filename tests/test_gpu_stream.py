@@ -247,3 +247,30 @@ def test_stream_fused_int8_int8_8192():
                                    staging=staging_for(t, 64))
     assert np.all(statuses(st, t.n_chunks) == 0)
     assert_same(host_u16(out), O.dequant_int8(w.q, w.scales, None, w.group), "int8_8192x8192 streamed int8")
+
+
+def test_stream_on_a_side_stream_with_internal_staging():
+    """The binding allocates the staging buffer when none is given and drops
+    it on return while the copies and decodes still use it on their streams.
+    Here the decode runs on a side stream while the current stream at once
+    allocates buffers of the staging's size and fills them: the allocator
+    must not hand out the staging memory before that work is done, so the
+    result is still the oracle's."""
+    w = synth.int4_weight(512, 8192, 128, 57)
+    packed = lt.pack_int4(w.codes)
+    ht = lt.ChunkTable.build(packed, w.dst_off, "cpu", pin=True)
+    sc, zp = t_u16(w.scales), t_i8(w.zp)
+    ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    nbytes = ht.staging_bytes()
+    for rep in range(3):
+        st = status_tensor(ht.n_chunks)
+        out = torch.empty(w.rows * w.cols, dtype=torch.float16, device=DEV)
+        side.wait_stream(torch.cuda.current_stream())
+        lt.stream_fused_lz4_int4(ht, sc, zp, (w.rows, w.cols), w.group, out=out, status=st, stream=side)
+        junk = [torch.empty(nbytes, dtype=torch.uint8, device=DEV).fill_(0xA5 + k) for k in range(4)]
+        torch.cuda.synchronize()
+        del junk
+        assert np.all(statuses(st, ht.n_chunks) == 0), rep
+        assert_same(host_u16(out), ref, "side stream, internal staging, call %d" % rep)

@@ -564,15 +564,29 @@ def _copy_stream(device):
 
 
 def _stream_setup(table: ChunkTable, out_device, staging, copy_stream):
+    """(staging, copy_stream, owned): owned is True when the staging buffer
+    was allocated here (it must then be tied to the streams that use it)."""
     torch = _torch()
     if table.comp.device.type != "cpu":
         raise ValueError("the streamed entry points read a host table (ChunkTable.build(..., "
                          "device='cpu', pin=True))")
-    if staging is None:
+    owned = staging is None
+    if owned:
         staging = torch.empty(table.staging_bytes(), dtype=torch.uint8, device=out_device)
     if copy_stream is None:
         copy_stream = _copy_stream(out_device)
-    return staging, copy_stream
+    return staging, copy_stream, owned
+
+
+def _stream_release(staging, owned, copy_stream, stream):
+    """A staging buffer allocated by the binding is dropped when the call
+    returns, while the copies (copy_stream) and decodes (stream) still use it:
+    recording both streams keeps the caching allocator from handing its
+    memory to a new tensor before that work has finished."""
+    if owned:
+        torch = _torch()
+        staging.record_stream(copy_stream)
+        staging.record_stream(stream if stream is not None else torch.cuda.current_stream(staging.device))
 
 
 def stream_decode_lz4(table: ChunkTable, out=None, status=None, staging=None, copy_stream=None,
@@ -583,22 +597,24 @@ def stream_decode_lz4(table: ChunkTable, out=None, status=None, staging=None, co
     torch = _torch()
     if out is None:
         out = torch.empty(max(table.total_bytes, 1), dtype=torch.uint8, device=device)
-    staging, copy_stream = _stream_setup(table, out.device, staging, copy_stream)
+    staging, copy_stream, owned = _stream_setup(table, out.device, staging, copy_stream)
     t = table.as_c()
     _check(_lib().lt_stream_decode_lz4(C.byref(t), _dptr(out), _dptr(status), _dptr(staging),
                                        staging.numel(), _stream_ptr(copy_stream), _stream_ptr(stream)),
            "lt_stream_decode_lz4")
+    _stream_release(staging, owned, copy_stream, stream)
     return out[:table.total_bytes] if out.numel() > table.total_bytes else out
 
 
 def _stream_fused(name, table, scales, zp, shape, group, out, status, staging, copy_stream, stream):
     rows, cols = _shape(shape)
     out = _out_f16(out, rows * cols, scales.device)
-    staging, copy_stream = _stream_setup(table, out.device, staging, copy_stream)
+    staging, copy_stream, owned = _stream_setup(table, out.device, staging, copy_stream)
     t = table.as_c()
     _check(getattr(_lib(), name)(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group, _dptr(out),
                                  _dptr(status), _dptr(staging), staging.numel(), _stream_ptr(copy_stream),
                                  _stream_ptr(stream)), name)
+    _stream_release(staging, owned, copy_stream, stream)
     return out.view(rows, cols)
 
 
@@ -615,3 +631,4 @@ def stream_fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=
     """fused_lz4_int8 over a host-resident table, as stream_fused_lz4_int4."""
     return _stream_fused("lt_stream_fused_lz4_int8", table, scales, zp, shape, group, out, status, staging,
                          copy_stream, stream)
+
