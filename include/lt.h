@@ -47,14 +47,15 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 10
+#define LT_ABI_VERSION 11
 
 typedef enum lt_status {
   LT_OK = 0,
   LT_ERR_INVALID_ARG = 1, /* a pointer, size, shape or alignment is invalid */
   LT_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve */
   LT_ERR_LAUNCH = 3,      /* the HIP runtime refused the launch */
-  LT_ERR_DEVICE = 4       /* no usable gfx950 device for the current context */
+  LT_ERR_DEVICE = 4,      /* no usable gfx950 device for the current context */
+  LT_ERR_TOO_LARGE = 5    /* the request does not fit a fixed-size workspace */
 } lt_status;
 
 /* Per-chunk codes written to chunk_status[i] (DEVICE, int32). */
@@ -346,6 +347,30 @@ lt_status lt_stream_fused_lz4_int8(const lt_chunk_table *host_table, const uint1
                                    uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                                    int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
                                    void *copy_stream, void *stream);
+
+/*
+ * lt_stream_fused_lz4_int4_static -- lt_stream_fused_lz4_int4 for callers
+ * that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no staging argument and calls
+ * no allocating routine (no hipMalloc, hipFree or event creation): its
+ * staging workspace is a static device array of LT_STATIC_SCRATCH_BYTES
+ * that every GPU the library runs on holds until the process ends (its
+ * address is taken on each device's first call), and the copies and the
+ * decodes run in order on `stream` alone, so copy and decode do not overlap.
+ * Arguments, validity rules, output and chunk statuses are those of
+ * lt_stream_fused_lz4_int4 (host table, pinned for asynchronous copies).
+ * Returns LT_ERR_TOO_LARGE when the table's offsets and index plus twice the
+ * largest chunk's compressed bytes (each rounded up to 256 bytes, plus 16)
+ * exceed the workspace.  Every call on one GPU uses that GPU's one array, so
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering between them) race and give wrong results; calls
+ * in order on one stream are safe.  LT_ERR_DEVICE if the workspace's address
+ * cannot be taken or a copy cannot be enqueued.
+ */
+#define LT_STATIC_SCRATCH_BYTES (32u << 20)
+lt_status lt_stream_fused_lz4_int4_static(const lt_chunk_table *host_table, const uint16_t *scales,
+                                          const int8_t *zp, uint64_t rows, uint64_t cols, uint64_t group,
+                                          uint16_t *out, int32_t *chunk_status, void *stream);
 
 /* ---- host-side packer: builds the inputs above (no device work) ---- */
 

@@ -36,8 +36,9 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == 10
+    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 11
     assert lt.lib().lt_status_str(1) == b"invalid argument"
+    assert lt.lib().lt_status_str(lt.LT_ERR_TOO_LARGE) == b"request exceeds the static workspace"
 
 
 def test_invalid_arguments_rejected_without_gpu():
@@ -394,3 +395,23 @@ def test_gemv_arguments_rejected_without_gpu():
     t2 = lt._Table(0x10000, 0x10000, 0x10000, 4, 65536, 4 * 3328 // 2, 100)
     assert L.lt_fused_lz4_int4_gemv(C.byref(t2), fake, None, 4, 3328, 128, fake, fake, None, None) \
         == lt.LT_ERR_UNSUPPORTED                                # rows not a multiple of 512 codes
+
+
+def test_static_workspace_rejects_tables_that_do_not_fit():
+    """lt_stream_fused_lz4_int4_static checks on the host, before any device
+    call, that the table's offsets plus two halves of the largest chunk fit
+    its fixed workspace."""
+    L = lt.lib()
+    comp = np.zeros(16, np.uint8)
+    comp_off = np.array([0, 17 << 20], np.uint64)      # one chunk of 17 MiB compressed
+    dst_off = np.array([0, 16], np.uint64)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    t = lt._Table(p(comp).value, p(comp_off).value, p(dst_off).value, 1, 16, 16, 17 << 20)
+    fake = C.c_void_p(0x10000)
+    assert L.lt_stream_fused_lz4_int4_static(C.byref(t), fake, None, 1, 32, 32, fake, None, None) == \
+        lt.LT_ERR_TOO_LARGE
+    # the usual argument checks come first
+    assert L.lt_stream_fused_lz4_int4_static(C.byref(t), None, None, 1, 32, 32, fake, None, None) == \
+        lt.LT_ERR_INVALID_ARG
+    assert L.lt_stream_fused_lz4_int4_static(C.byref(t), fake, None, 1, 30, 30, fake, None, None) == \
+        lt.LT_ERR_INVALID_ARG

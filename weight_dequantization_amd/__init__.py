@@ -28,6 +28,8 @@ Streamed entry points (the table in pinned host memory, copies overlapped
 with the decode on a second stream):
     stream_decode_lz4(host_table, out=None, status=None, staging=None)
     stream_fused_lz4_int4(host_table, scales, zp, shape, group, out=None, ...)
+    stream_fused_lz4_int4_static(host_table, scales, zp, shape, group, out, ...)
+        (the same with the library's static workspace: allocates nothing)
 Host packer (numpy in, numpy out):
     pack_int4(codes) -> packed bytes (low nibble first)
     compress_chunks(src, dst_off, threads=0, max_dist=0) -> (comp, comp_off)
@@ -47,7 +49,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblt.so")
 
-LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE = range(5)
+ABI_VERSION = 11          # LT_ABI_VERSION of the library this binding speaks to
+LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE = range(6)
+STATIC_SCRATCH_BYTES = 32 << 20   # LT_STATIC_SCRATCH_BYTES
 (CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
  CHUNK_CHECKSUM) = range(7)
 MAX_CHUNK_BYTES = 1 << 20
@@ -114,6 +118,7 @@ def _lib():
             "lt_checksum_chunks": (i32, [vp, vp, u32, vp, i32]),
             "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_stream_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
+            "lt_stream_fused_lz4_int4_static": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
             "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
@@ -632,3 +637,21 @@ def stream_fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=
     return _stream_fused("lt_stream_fused_lz4_int8", table, scales, zp, shape, group, out, status, staging,
                          copy_stream, stream)
 
+
+def stream_fused_lz4_int4_static(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,
+                                 stream=None):
+    """fused_lz4_int4 over a host-resident table through the library's static
+    workspace (lt_stream_fused_lz4_int4_static): nothing is allocated by the
+    call, the copies and the decode run in order on `stream`, and calls that
+    overlap on one GPU race on the shared workspace."""
+    if table.comp.device.type != "cpu":
+        raise ValueError("the streamed entry points read a host table (ChunkTable.build(..., "
+                         "device='cpu', pin=True))")
+    rows, cols = _shape(shape)
+    if out is None:
+        raise ValueError("stream_fused_lz4_int4_static writes into a caller-owned `out` (it allocates nothing)")
+    t = table.as_c()
+    _check(_lib().lt_stream_fused_lz4_int4_static(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group,
+                                                  _dptr(out), _dptr(status), _stream_ptr(stream)),
+           "lt_stream_fused_lz4_int4_static")
+    return out.view(rows, cols)

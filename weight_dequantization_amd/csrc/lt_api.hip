@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lt.h"
 #include "lt_device.hpp"
 #include "lt_lz4.hpp"
@@ -359,6 +361,9 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   for (uint64_t i = 0; i < n; i++)
     if (batch_bytes(t, i, i + 1) > half) return LT_ERR_INVALID_ARG;   // a chunk must fit a half
   hipStream_t cs = (hipStream_t)copy_stream, ds = (hipStream_t)stream;
+  // on one stream the copies and decodes are ordered by the stream itself,
+  // and no event is needed (nor created)
+  const bool one = cs == ds;
   uint64_t *m_coff = (uint64_t *)staging;
   uint64_t *m_doff = (uint64_t *)(staging + up(8 * (n + 1)));
   uint64_t *m_soff = (uint64_t *)(staging + 2 * up(8 * (n + 1)));
@@ -366,15 +371,16 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   const uint64_t ns = t->seq_off ? t->seq_off[n] : 0;
   hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, start = nullptr;
   lt_status st = LT_OK;
-  for (int h = 0; h < 2 && st == LT_OK; h++) {
+  for (int h = 0; h < 2 && st == LT_OK && !one; h++) {
     if (hipEventCreateWithFlags(&copied[h], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&done[h], hipEventDisableTiming) != hipSuccess)
       st = LT_ERR_DEVICE;
   }
   // the first copy waits for the work already on stream, so a staging
   // buffer reused by consecutive calls is not overwritten under a decode
-  if (st == LT_OK && (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess ||
-                      hipEventRecord(start, ds) != hipSuccess || hipStreamWaitEvent(cs, start, 0) != hipSuccess))
+  if (st == LT_OK && !one &&
+      (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess || hipEventRecord(start, ds) != hipSuccess ||
+       hipStreamWaitEvent(cs, start, 0) != hipSuccess))
     st = LT_ERR_DEVICE;
   if (st == LT_OK) {
     bool ok = hipMemcpyAsync(m_coff, t->comp_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess &&
@@ -393,9 +399,9 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
     uint8_t *p_comp = staging + mb + h * half;
     const uint64_t cb = t->comp_off[e] - t->comp_off[c];
     // copies into this half wait for the decode that last read it
-    if (batch >= 2 && hipStreamWaitEvent(cs, done[h], 0) != hipSuccess) { st = LT_ERR_DEVICE; break; }
+    if (!one && batch >= 2 && hipStreamWaitEvent(cs, done[h], 0) != hipSuccess) { st = LT_ERR_DEVICE; break; }
     if (hipMemcpyAsync(p_comp, t->comp + t->comp_off[c], cb, hipMemcpyHostToDevice, cs) != hipSuccess ||
-        hipEventRecord(copied[h], cs) != hipSuccess || hipStreamWaitEvent(ds, copied[h], 0) != hipSuccess) {
+        (!one && (hipEventRecord(copied[h], cs) != hipSuccess || hipStreamWaitEvent(ds, copied[h], 0) != hipSuccess))) {
       st = LT_ERR_DEVICE;
       break;
     }
@@ -417,15 +423,46 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
       P.n_seq = ns;
     }
     st = launch_params(mode, P, stream);
-    if (st == LT_OK && hipEventRecord(done[h], ds) != hipSuccess) st = LT_ERR_DEVICE;
+    if (st == LT_OK && !one && hipEventRecord(done[h], ds) != hipSuccess) st = LT_ERR_DEVICE;
     c = e;
   }
   for (int h = 0; h < 2; h++) {   // destruction waits for nothing: pending events are released later
-    if (copied[h]) hipEventDestroy(copied[h]);
-    if (done[h]) hipEventDestroy(done[h]);
+    if (copied[h]) (void)hipEventDestroy(copied[h]);
+    if (done[h]) (void)hipEventDestroy(done[h]);
   }
-  if (start) hipEventDestroy(start);
+  if (start) (void)hipEventDestroy(start);
   return st;
+}
+
+// ------------------------------------------ staging without allocation
+
+// The staging workspace of lt_stream_fused_lz4_int4_static: one array per
+// device, in the code object, held until the process ends.  Its name is a
+// host-side stand-in; its device address is taken once per device with
+// hipGetSymbolAddress, and only that address is used.
+constexpr uint64_t kStaticScratch = LT_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[LT_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// the current device's copy of `scratch`, or NULL when its address cannot
+// be taken
+uint8_t *static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = (uint8_t *)p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 bool table_ok(const lt_chunk_table *t) {
@@ -705,6 +742,28 @@ lt_status lt_stream_fused_lz4_int8(const lt_chunk_table *host_table, const uint1
                        copy_stream, stream);
 }
 
+lt_status lt_stream_fused_lz4_int4_static(const lt_chunk_table *host_table, const uint16_t *scales,
+                                          const int8_t *zp, uint64_t rows, uint64_t cols, uint64_t group,
+                                          uint16_t *out, int32_t *chunk_status, void *stream) {
+  const lt_status a = stream_args(lt::MODE_INT4, host_table, scales, rows, cols, group, out);
+  if (a != LT_OK) return a;
+  const lt_chunk_table *t = host_table;
+  if (t->n_chunks == 0) return LT_OK;
+  // the table's offsets and index, and two halves that each hold the
+  // largest chunk's compressed bytes, must fit the static workspace
+  uint64_t big = 0;
+  for (uint64_t i = 0; i < t->n_chunks; i++) {
+    if (t->comp_off[i + 1] < t->comp_off[i]) return LT_ERR_INVALID_ARG;
+    const uint64_t c = t->comp_off[i + 1] - t->comp_off[i];
+    big = c > big ? c : big;
+  }
+  if (t->seq_off && t->seq_off[t->n_chunks] > t->n_seq) return LT_ERR_INVALID_ARG;
+  if (meta_bytes(t) + 2 * up(big + 16) > kStaticScratch) return LT_ERR_TOO_LARGE;
+  uint8_t *ws = static_scratch();
+  if (!ws) return LT_ERR_DEVICE;
+  return stream_common(lt::MODE_INT4, t, out, chunk_status, scales, zp, group, ws, kStaticScratch, stream, stream);
+}
+
 const char *lt_status_str(lt_status s) {
   switch (s) {
     case LT_OK: return "ok";
@@ -712,6 +771,7 @@ const char *lt_status_str(lt_status s) {
     case LT_ERR_UNSUPPORTED: return "unsupported";
     case LT_ERR_LAUNCH: return "kernel launch failed";
     case LT_ERR_DEVICE: return "no usable device";
+    case LT_ERR_TOO_LARGE: return "request exceeds the static workspace";
   }
   return "unknown status";
 }
