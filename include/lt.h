@@ -66,7 +66,8 @@ enum {
   LT_CHUNK_OVERRUN = 3,       /* a sequence would write past the chunk end */
   LT_CHUNK_SIZE_MISMATCH = 4, /* block decoded to fewer bytes than the chunk */
   LT_CHUNK_BAD_TABLE = 5,     /* the chunk's table entries are inconsistent */
-  LT_CHUNK_CHECKSUM = 6       /* lt_verify_chunks: stored bytes do not match their CRC-32 */
+  LT_CHUNK_CHECKSUM = 6,      /* lt_verify_chunks: stored bytes do not match their CRC-32 */
+  LT_CHUNK_STALLED = 7        /* a wait inside the decoder polled past its bound (see spin_limit) */
 };
 
 /* Largest decoded chunk the device decoder accepts (bytes).  It bounds a
@@ -100,7 +101,13 @@ enum {
  *              LT_CHUNK_BAD_OFFSET.  LZ4 blocks may use distances up to
  *              65535; a compressor that keeps them shorter lets the decoder
  *              keep less history (see LT_SMALL_WINDOW).
- *   reserved   0
+ *   spin_limit the number of polls each wave of the decoder may make while
+ *              it waits for another (for input, records, ring space or
+ *              earlier tiles) before it gives up and fails the chunk with
+ *              LT_CHUNK_STALLED; 0 means the library's default (2^24, far
+ *              above any legitimate wait: a protocol mistake then ends as a
+ *              failed chunk instead of a hung GPU).  Small values exist to
+ *              test that failure path; every wave still exits normally.
  *   seq_off    DEVICE uint64[n_chunks + 1] or NULL: an optional sequence
  *              index.  Chunk i's LZ4 sequences start at the block offsets
  *              seq_pos[seq_off[i] .. seq_off[i+1]), in order (the first is
@@ -126,7 +133,7 @@ typedef struct lt_chunk_table {
   uint64_t total_bytes;
   uint64_t comp_bytes;
   uint32_t max_dist;
-  uint32_t reserved;
+  uint32_t spin_limit;
   const uint64_t *seq_off;
   const uint32_t *seq_pos;
   uint64_t n_seq;

@@ -592,3 +592,56 @@ def test_fused_corrupt_blocks_status_and_guards(mode):
                     assert s[i] == 0, (what, i, s[i])
                 if s[i] == 0:
                     assert np.array_equal(got[lo:hi], ref[lo:hi]), (what, i)
+
+
+# ------------------------------------------------------- bounded waits
+
+@pytest.mark.parametrize("form", ["indexed", "walked", "full_window_bytes"])
+def test_bounded_waits_fail_their_chunk_and_exit(form):
+    """Every wait inside the decoder polls at most spin_limit times per wave;
+    a wave that runs out fails its chunk with CHUNK_STALLED and every wave
+    still leaves, so the kernel ends.  Forced from the host with tiny limits:
+    the launch completes, statuses are OK or STALLED only, chunks reported
+    OK hold the oracle's result, nothing outside the output is written; with
+    the default limit every chunk decodes."""
+    guard = 4096
+    if form == "full_window_bytes":
+        a = synth.activation(1024, 8192, 77)
+        ot = O.compress_table(a.data, a.dst_off)          # no declared window: 64 KiB history
+        data, n_out, per = a.data, a.data.size, 1
+    else:
+        w = synth.int4_weight(512, 28672, 128, 76)
+        data = lt.pack_int4(w.codes)
+        n_out, per = w.rows * w.cols, 2
+        ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)
+    for spin in (1, 3, 16, 256, 0):
+        if form == "full_window_bytes":
+            table = table_from_oracle(ot)
+            buf = torch.full((n_out + 2 * guard,), 0x5A, dtype=torch.uint8, device=DEV)
+        else:
+            table = lt.ChunkTable.build(data, w.dst_off, DEV, index=(form == "indexed"))
+            buf = torch.full((n_out + 2 * guard,), 0x5A5A, dtype=torch.int16, device=DEV)
+        table.spin_limit = spin
+        st = status_tensor(table.n_chunks)
+        out = buf[guard:guard + n_out]
+        if form == "full_window_bytes":
+            lt.decode_lz4(table, out=out, status=st)
+        else:
+            lt.fused_lz4_int4(table, t_u16(w.scales), t_i8(w.zp), (w.rows, w.cols), w.group,
+                              out=out.view(torch.float16), status=st)
+        s = statuses(st, table.n_chunks)
+        b = buf.cpu().numpy()
+        what = "%s, spin_limit %d" % (form, spin)
+        assert np.all(b[:guard] == b[0]) and np.all(b[guard + n_out:] == b[0]), what + ": write outside"
+        assert set(np.unique(s)) <= {lt.CHUNK_OK, lt.CHUNK_STALLED}, (what, np.unique(s))
+        if spin == 0:
+            assert np.all(s == lt.CHUNK_OK), what
+        if spin == 1 and form != "full_window_bytes":
+            assert np.any(s == lt.CHUNK_STALLED), what + ": no wait gave up"
+        got = b[guard:guard + n_out]
+        expect = data if form == "full_window_bytes" else ref
+        got = got if form == "full_window_bytes" else got.view(np.uint16)
+        d = table.host_dst_off
+        for i in np.nonzero(s == lt.CHUNK_OK)[0]:
+            lo, hi = per * int(d[i]), per * int(d[i + 1])
+            assert np.array_equal(got[lo:hi], expect[lo:hi]), (what, i)

@@ -53,7 +53,7 @@ ABI_VERSION = 11          # LT_ABI_VERSION of the library this binding speaks to
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE = range(6)
 STATIC_SCRATCH_BYTES = 32 << 20   # LT_STATIC_SCRATCH_BYTES
 (CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
- CHUNK_CHECKSUM) = range(7)
+ CHUNK_CHECKSUM, CHUNK_STALLED) = range(8)
 MAX_CHUNK_BYTES = 1 << 20
 SMALL_WINDOW = 11264      # LT_SMALL_WINDOW: tables within it decode with a 16 KiB history
 PACK_WINDOW = 4096        # the host packer's default match window (see ChunkTable.build)
@@ -77,7 +77,7 @@ class _Table(C.Structure):
     _fields_ = [("comp", C.c_void_p), ("comp_off", C.c_void_p), ("dst_off", C.c_void_p),
                 ("n_chunks", C.c_uint32), ("max_chunk_bytes", C.c_uint32),
                 ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64),
-                ("max_dist", C.c_uint32), ("reserved", C.c_uint32),
+                ("max_dist", C.c_uint32), ("spin_limit", C.c_uint32),
                 ("seq_off", C.c_void_p), ("seq_pos", C.c_void_p), ("n_seq", C.c_uint64)]
 
 
@@ -267,6 +267,7 @@ class ChunkTable:
     seq_pos: object = None  # torch.int32 [n_seq] (read as uint32)
     n_seq: int = 0
     host_dst_off: object = None   # numpy uint64 [n+1], kept for chunk-range calls
+    spin_limit: int = 0     # polls per decoder wave before a wait gives up (0: the library's default)
 
     @classmethod
     def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
@@ -335,7 +336,7 @@ class ChunkTable:
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
                       self.n_chunks, self.max_chunk_bytes, self.total_bytes, self.comp_bytes,
-                      self.max_dist, 0,
+                      self.max_dist, self.spin_limit,
                       self.seq_off.data_ptr() if self.seq_off is not None else None,
                       self.seq_pos.data_ptr() if self.seq_pos is not None else None,
                       self.n_seq if self.seq_off is not None else 0)

@@ -305,6 +305,7 @@ lt::ChunkParams make_params(const lt_chunk_table *t, void *out, int32_t *chunk_s
   P.gemv_x = nullptr;
   P.gemv_y = nullptr;
   P.cols = 0;
+  P.spin = t->spin_limit ? t->spin_limit : lt::SPIN_DEFAULT;
   return P;
 }
 
@@ -470,7 +471,7 @@ bool table_ok(const lt_chunk_table *t) {
   if (t->n_chunks == 0) return t->total_bytes == 0;
   if (!t->comp || !t->comp_off || !t->dst_off) return false;
   if (t->max_chunk_bytes == 0 || t->max_chunk_bytes > LT_MAX_CHUNK_BYTES) return false;
-  if (t->max_dist > 65535u || t->reserved != 0) return false;
+  if (t->max_dist > 65535u) return false;
   if ((t->seq_off == nullptr) != (t->seq_pos == nullptr)) return false;
   if (t->n_chunks > 0x7FFFFFFFu) return false;
   return true;

@@ -75,7 +75,10 @@
 //                                      the smallest of these is final
 //   tile_ctr     builders          : the next tile nobody has taken
 //   pstate       recorder -> all     : running / done / failed
-// Every wait is bounded.  The walker consumes at least one input byte per
+// Every wait ends, by the argument below; as a backstop against a protocol
+// mistake each wave's polls are also counted, and a wave that polls past its
+// budget fails the chunk (C_STALL) instead of hanging the GPU.  The walker
+// consumes at least one input byte per
 // sequence and stops at the chunk's end, at a malformed length, or when the
 // recorder has stopped; the recorder stops at the first invalid sequence;
 // builders stop when the records stop short of their next tile.  A literal
@@ -130,7 +133,18 @@ constexpr int SLEEP_FEED = 2;         // feeder waiting for ring space
 constexpr uint32_t LEN_CAP = 1u << 31;
 
 enum : uint32_t { ST_RUN = 0, ST_DONE = 1, ST_FAIL = 2 };
-enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5, C_CHECKSUM = 6 };
+enum : int32_t { C_OK = 0, C_TRUNC = 1, C_BADOFF = 2, C_OVERRUN = 3, C_SIZE = 4, C_TABLE = 5, C_CHECKSUM = 6,
+                 C_STALL = 7 };
+// Every wait ends.  The walker, the recorder and the feeder may each poll
+// at most this many times per chunk (or the table's spin_limit, when
+// nonzero) before they give up; a wave that gives up marks the chunk stalled
+// (it then reports C_STALL) and failed, and leaves its role.  Builders wait
+// only for those three and for older tiles (no cycle among builders), and
+// every builder wait also ends once the chunk has failed, so one wave giving
+// up lets every wave reach the kernel's end.  Legitimate waits take far
+// fewer polls (a whole 1 MiB chunk decodes in well under a million poll
+// intervals), so the bound only ends what would otherwise never end.
+constexpr uint32_t SPIN_DEFAULT = 1u << 24;
 // MODE_INT4G is MODE_INT4 for groups that are a power of two of at least
 // 128 codes, where a tile spans at most 17 groups (its own kernel, with a
 // leaner scale / zero-point fetch).
@@ -151,6 +165,7 @@ struct __attribute__((aligned(16))) Ctl {
   uint32_t nfinished;         // builders that have left
   uint32_t tile_ctr;          // builders: the next tile nobody has taken
   int32_t status;
+  uint32_t stall;             // any wave: a bounded wait gave up (the chunk fails with C_STALL)
 };
 
 // The history ring holds 2^HLOG decoded bytes: 64 KiB for any LZ4 block
@@ -202,6 +217,7 @@ struct ChunkParams {
   const uint16_t *gemv_x;    // fp16 [cols]
   float *gemv_y;             // fp32 [rows]
   uint64_t cols;
+  uint32_t spin;             // polls each wave may make per chunk (>= 1)
 };
 
 // ------------------------------------------------------------ LDS sync
@@ -291,6 +307,18 @@ __device__ __forceinline__ uint2 read_rec(Ctl &c) {
 
 // a value every lane holds, stated so the compiler keeps it in a scalar register
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// One poll of a bounded wait: true while this wave's poll budget lasts.  Once
+// it is spent the chunk is marked stalled and failed, and the caller leaves.
+__device__ __forceinline__ bool spin_ok(uint32_t &budget, Ctl &ctl) {
+  if (budget != 0) {
+    budget = uni(budget - 1);
+    return true;
+  }
+  lds_set(&ctl.stall, 1u);
+  lds_set(&ctl.pstate, ST_FAIL);
+  return false;
+}
 
 // Minimum of an 8-entry counter array (16-byte aligned), read at once.  Like
 // every counter access of the feeder wave, it goes through inline asm: that
@@ -450,6 +478,7 @@ struct Rec {
   uint32_t fill_ok;     // the last record ends with a known byte (distance-1 run) ...
   uint32_t fill;        // ... which is this
   uint32_t pending;     // the last record's match is still to come (a W_CONT entry)
+  uint32_t spin = 0;    // polls left (set from ChunkParams::spin)
 
   // the entry after an announced literal run (ent wave-uniform): its match,
   // or the end of the walk.  Returns the chunk's final status, or -1.
@@ -481,6 +510,10 @@ struct Rec {
       rec_free = min8(ctl.bk);
       if (rec_free == 0xFFFFFFFFu) rec_free = nrec;
       if (nrec - rec_free < RING) break;
+      if (!spin_ok(spin, ctl)) {
+        st = C_STALL;
+        return 0;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     const uint32_t space = RING - (nrec - rec_free);
@@ -594,6 +627,8 @@ struct Walker {
   Rec<SM> rec;          // with an index the walker makes the records itself ...
   uint32_t direct;      // ... (and no recorder wave runs)
   int32_t fin;          // (direct) the chunk's final status once known, else -1
+  uint32_t spin = 0;    // polls left (set from ChunkParams::spin)
+  uint32_t stalled = 0; // a wait for input gave up: the walk ends
 
   __device__ __forceinline__ void emit(uint32_t ys, uint32_t L, uint32_t M, uint32_t w) {
     if (direct) {
@@ -610,7 +645,7 @@ struct Walker {
     while (cnt - cons >= CHAIN) {
       cons = lds_get(&ctl.rcons);
       if (cnt - cons < CHAIN) break;
-      if (lds_get(&ctl.pstate) != ST_RUN) {
+      if (lds_get(&ctl.pstate) != ST_RUN || !spin_ok(spin, ctl)) {
         stop = 1;
         return;
       }
@@ -624,7 +659,7 @@ struct Walker {
 
   __device__ __forceinline__ void need_input(uint32_t upto) {
     upto = upto < y_end ? upto : y_end;
-    if (avail >= upto) return;
+    if (avail >= upto || stalled) return;
     avail = lds_get(&ctl.in_avail);
     if (avail >= upto) return;
     if (pend) {
@@ -635,6 +670,14 @@ struct Walker {
       emit(pend_ys, pend_L, 0, W_LIT);
     }
     while (avail < upto) {
+      if (!spin_ok(spin, ctl)) {
+        // the bytes never came: the walk ends (what it reads from here on
+        // is not input, but every read stays inside the ring and the walk
+        // stops at its next step)
+        stalled = 1;
+        stop = 1;
+        return;
+      }
       __builtin_amdgcn_s_sleep(1);
       avail = lds_get(&ctl.in_avail);
     }
@@ -897,7 +940,7 @@ struct Walker {
     if (cnt - cons >= CHAIN) {
       cons = lds_get(&ctl.rcons);
       if (cnt - cons >= CHAIN) {
-        if (lds_get(&ctl.pstate) != ST_RUN) stop = 1;
+        if (lds_get(&ctl.pstate) != ST_RUN || !spin_ok(spin, ctl)) stop = 1;
         else __builtin_amdgcn_s_sleep(1);
         return true;
       }
@@ -981,7 +1024,7 @@ struct Walker {
     if (!direct && cnt - cons >= CHAIN) {
       cons = lds_get(&ctl.rcons);
       if (cnt - cons >= CHAIN) {
-        if (lds_get(&ctl.pstate) != ST_RUN) stop = 1;
+        if (lds_get(&ctl.pstate) != ST_RUN || !spin_ok(spin, ctl)) stop = 1;
         else __builtin_amdgcn_s_sleep(1);
         return true;
       }
@@ -1011,6 +1054,12 @@ struct Walker {
         pub = y;
         lds_set(&ctl.need[0], pub);
         do {
+          if (!spin_ok(spin, ctl)) {
+            stalled = 1;
+            stop = 1;
+            fin = C_STALL;
+            return true;
+          }
           __builtin_amdgcn_s_sleep(1);
           avail = lds_get(&ctl.in_avail);
         } while (uni(hi) > avail);
@@ -1130,6 +1179,7 @@ struct Walker {
         if (!slow_step()) break;
       }
     }
+    if (stalled && direct) fin = C_STALL;
     lds_set(&ctl.need[0], 0xFFFFFFFFu, lane);
   }
 };
@@ -1145,6 +1195,8 @@ __device__ __forceinline__ int32_t recorder(Rec<SM> &r, SM &sm, Ctl &ctl, uint32
     while (avail_entries == taken) {
       avail_entries = lds_get(&ctl.wcnt);
       if (avail_entries != taken) break;
+      // the recorder owns pstate: a failed state here is a stalled wave's
+      if (lds_get(&ctl.pstate) == ST_FAIL || !spin_ok(r.spin, ctl)) return C_STALL;
       __builtin_amdgcn_s_sleep(1);
     }
     if (r.pending) {
@@ -1229,7 +1281,8 @@ __device__ __forceinline__ uint32_t land_and_bound_k(uint32_t k, const uint32_t 
 // and the exit check (every reader gone: a failed chunk) is made only when
 // nothing is in flight.
 template <class SM>
-__device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb) {
+__device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb,
+                                       uint32_t spin) {
   constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
   static_assert(QMAX <= 16, "land_and_bound_k waits for up to 15 loads in flight");
   const uint32_t nblk = (y_end + 15) / 16;
@@ -1253,7 +1306,10 @@ __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const ui
       const uint32_t used = min8(ctl.need);
       limit = used / SEG + QMAX;
       if (limit > nseg) limit = nseg;
-      if (issued == limit) __builtin_amdgcn_s_sleep(SLEEP_FEED);
+      if (issued == limit) {
+        if (!spin_ok(spin, ctl)) break;
+        __builtin_amdgcn_s_sleep(SLEEP_FEED);
+      }
       continue;
     }
     // the oldest segment in flight has landed once at most k loads remain
@@ -1532,11 +1588,16 @@ struct Builder {
     cov = r.y;
   }
 
-  __device__ __forceinline__ void need_input(uint32_t upto) {
+  // false if the chunk failed first (the feeder gave up)
+  __device__ __forceinline__ bool need_input(uint32_t upto) {
     while (avail < upto) {
       avail = lds_get(&ctl.in_avail);
-      if (avail < upto) __builtin_amdgcn_s_sleep(1);
+      if (avail < upto) {
+        if (lds_get(&ctl.pstate) == ST_FAIL) return false;
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
+    return true;
   }
 
   // wait until tiles [0, tiles) are final; false if the chunk failed first
@@ -1731,8 +1792,8 @@ struct Builder {
   }
 
   // Build [T, Tend) record by record, starting at record k.  Every byte
-  // before T must be final.
-  __device__ __forceinline__ void tile_exact(uint32_t T, uint32_t Tend) {
+  // before T must be final.  False if a wait for input gave up.
+  __device__ __forceinline__ bool tile_exact(uint32_t T, uint32_t Tend) {
     uint32_t j = k;
     for (;;) {
       uint4 r = rec(j);
@@ -1741,7 +1802,7 @@ struct Builder {
       const uint32_t le = os + L;
       uint32_t a = os > T ? os : T, e = le < Tend ? le : Tend;
       if (a < e) {
-        need_input(src + (e - os));
+        if (!need_input(src + (e - os))) return false;
         if (e - a <= 64)
           lit_lanes(src + (a - os), a, e - a);
         else
@@ -1750,7 +1811,7 @@ struct Builder {
       a = le > T ? le : T;
       e = re < Tend ? re : Tend;
       if (a < e) match_exact(info, a, e - a);   // LDS ops of one wave stay in order
-      if (re >= Tend || j + 1 >= nrec) return;
+      if (re >= Tend || j + 1 >= nrec) return true;
       j++;
     }
   }
@@ -1984,9 +2045,9 @@ struct Builder {
       }
       if (!wait_done(need_tiles)) break;
       if (hard) {
-        tile_exact(T, Tend);
+        if (!tile_exact(T, Tend)) break;
       } else {
-        need_input(in_end);
+        if (!need_input(in_end)) break;
         tile_bulk(T, Tend, rv, re, m, extra);
       }
       if constexpr (G) {
@@ -2071,6 +2132,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     ctl.nfinished = 0;
     ctl.tile_ctr = nb;
     ctl.status = 0;
+    ctl.stall = 0;
   }
   __syncthreads();
 
@@ -2078,6 +2140,8 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
                          direct ? P.seq_pos + s0 : nullptr, direct ? (uint32_t)(s1 - s0) : 0u, 0, head, 0, 0, 0,
                          Rec<Smem<HLOG>>{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0}, direct ? 1u : 0u, -1};
+    W.spin = P.spin;
+    W.rec.spin = P.spin;
     W.run();
     if (direct) {
       // every walk ends with a final status (the last sequence or an error)
@@ -2087,17 +2151,18 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     }
   } else if (wave == 1 && !direct) {
     Rec<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0};
+    R.spin = P.spin;
     const int32_t st = recorder(R, sm, ctl, lane);
     if (lane == 0) ctl.status = st;
     lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
   } else if (wave == 2) {
-    feeder(sm, ctl, lane, S, y_end, nb);
+    feeder(sm, ctl, lane, S, y_end, nb, P.spin);
   } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
     Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0};
     B.run();
   }
   __syncthreads();
-  if (tid == 0 && P.status) P.status[i] = ctl.status;
+  if (tid == 0 && P.status) P.status[i] = ctl.stall ? C_STALL : ctl.status;
 }
 
 }  // namespace lt
