@@ -1,0 +1,107 @@
+"""The chunk decoder's LDS protocol, modelled on the CPU under random
+interleavings (tests/protocol_model.py), over the workloads' own blocks:
+the 8192x28672 layer's distributions (host packer, 4 KiB declared window,
+16 KiB history class), the ReLU activations with their stress chunks (host
+packer in the 16 KiB class; the oracle's greedy compressor in the 64 KiB
+class), generator-built streams with far and overlapping matches and chunks
+over 64 KiB, and all-literal and long-run blocks; each with and without the
+sequence index and on several schedules.  Every read must see landed,
+unoverwritten input, live records and final history; no schedule may
+deadlock; the decode must equal the expected bytes.  The model is also
+shown to catch planted protocol mistakes.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+import weight_dequantization_amd as lt
+from protocol_model import Chunk, ProtocolError
+
+
+def _chunks(comp, comp_off, dst_off, src, picks):
+    so, sp = lt.index_chunks(comp, comp_off)
+    for i in picks:
+        blk = comp[int(comp_off[i]):int(comp_off[i + 1])]
+        yield (i, blk, src[int(dst_off[i]):int(dst_off[i + 1])].tobytes(), sp[int(so[i]):int(so[i + 1])])
+
+
+def _run(blk, expect, idx, hlog, dmax, seeds, what):
+    for seed in seeds:
+        for indexed in (True, False):
+            c = Chunk(blk, len(expect), index=idx if indexed else None, hlog=hlog, dmax=dmax, head=seed % 16,
+                      seed=seed)
+            st, out, _ = c.run()
+            assert st == 0, (what, seed, indexed, st)
+            assert out == expect, (what, seed, indexed)
+            assert all(v == 1 for v in c.built), (what, seed, indexed)
+
+
+def test_weight_layer_chunks():
+    w = synth.mlp_int4_small(rows=64)
+    packed = lt.pack_int4(w.codes)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    n = w.dst_off.size - 1
+    for i, blk, expect, idx in _chunks(comp, comp_off, w.dst_off, packed, range(0, n, max(1, n // 6))):
+        _run(blk, expect, idx, 14, lt.PACK_WINDOW, (1, 2, 3), "weight chunk %d" % i)
+
+
+def test_activation_chunks_with_stress_blocks():
+    a = synth.activation(1024, 8192, 1104)
+    picks = sorted(set(a.stress["random"] + a.stress["all_ab"] + a.stress["ab_run"] + [0, 1, 100]))
+    comp, comp_off = lt.compress_chunks(a.data, a.dst_off, max_dist=lt.PACK_WINDOW)
+    for i, blk, expect, idx in _chunks(comp, comp_off, a.dst_off, a.data, picks):
+        _run(blk, expect, idx, 14, lt.PACK_WINDOW, (4, 5), "activation chunk %d, packer" % i)
+    ot = O.compress_table(a.data, a.dst_off)
+    for i, blk, expect, idx in _chunks(ot.comp, ot.comp_off, a.dst_off, a.data, picks):
+        _run(blk, expect, idx, 16, 65535, (6, 7), "activation chunk %d, oracle compressor" % i)
+
+
+@pytest.mark.parametrize("target", [5000, 70000, 262144])
+def test_generated_streams(target):
+    for seed in range(3):
+        blk, expect = O.seqgen(1000 + seed + target, target)
+        idx = lt.index_chunks(blk, np.array([0, blk.size], np.uint64))[1]
+        _run(blk, expect.tobytes(), idx, 16, 65535, (seed,), "seqgen %d/%d" % (target, seed))
+
+
+def test_all_literal_and_long_run_blocks():
+    r = np.random.default_rng(9).integers(0, 256, 65536, dtype=np.uint8)
+    x = np.full(65536, 0xAB, np.uint8)
+    for data, what in ((r, "random"), (x, "0xAB")):
+        for blk in (O.lz4_compress(data), O.lz4_store(data)):
+            idx = lt.index_chunks(blk, np.array([0, blk.size], np.uint64))[1]
+            _run(blk, data.tobytes(), idx, 16, 65535, (1, 2), what)
+            _run(blk, data.tobytes(), idx, 14, 65535, (3,), what + " (16 KiB class, any window)")
+
+
+def _fault_caught(fault, blk, expect, idx, hlog, dmax, seeds):
+    """How many schedules of a model with a planted mistake end in a
+    detected violation, a deadlock or a wrong decode."""
+    caught = 0
+    for seed in range(seeds):
+        c = Chunk(blk, len(expect), index=idx, hlog=hlog, dmax=dmax, seed=seed, fault=fault)
+        try:
+            _, out, _ = c.run()
+            caught += out != expect
+        except ProtocolError:
+            caught += 1
+    return caught
+
+
+def test_model_catches_planted_mistakes():
+    w = synth.mlp_int4_small(rows=8)
+    packed = lt.pack_int4(w.codes)[:65536]
+    blk = O.lz4_compress(packed)
+    idx = lt.index_chunks(blk, np.array([0, blk.size], np.uint64))[1]
+    for fault in ("no_window", "early_need"):
+        assert _fault_caught(fault, blk, packed.tobytes(), idx, 14, 65535, 4) == 4, fault
+    g, e = O.seqgen(5, 262144)
+    gidx = lt.index_chunks(g, np.array([0, g.size], np.uint64))[1]
+    assert _fault_caught("no_slot_rule", g, e.tobytes(), gidx, 16, 65535, 3) == 3
+    # a 20,000-byte literal run, longer than the 8 KiB input ring, then a match
+    r = np.random.default_rng(3).integers(0, 256, 20000, dtype=np.uint8)
+    d = np.concatenate([r, r[:3000]])
+    db = O.lz4_compress(d)
+    assert _fault_caught("no_split", db, d.tobytes(), None, 16, 65535, 2) == 2
+    assert _fault_caught(None, db, d.tobytes(), None, 16, 65535, 2) == 0
