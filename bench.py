@@ -19,10 +19,17 @@ around the launch; a 1 GiB fill before each step (outside the events) clears
 L2 and the last-level cache, so no step reads input a previous one left
 cached (--no-evict times the steps back to back instead).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|2|5] [--no-cpu] [--extra]
 
-Prints one JSON line.  --extra adds measurements of the raw (uncompressed)
-INT4 path and of plain fill/copy ceilings under "extra".
+Prints one JSON line and exits non-zero when any GPU output checked in the
+run differs from the oracle's or between routes.  The line also times the
+same layer as plain LZ4 ("plain_lz4": the packer's blocks without the
+sequence index, and greedy-parse blocks with a 64 KiB window), reports the
+device footprint with the index counted in, and times the CPU oracle on the
+table the GPU decodes at all host cores and at one thread.  --extra adds
+the raw (uncompressed) INT4 path, plain fill/copy ceilings and the other
+entry points under "extra".  --config 2 measures the 8192x8192 INT8 matrix
+(fused and two-pass); --config 5 the 80-layer Llama-70B-shaped stack.
 """
 from __future__ import annotations
 
@@ -66,37 +73,110 @@ def stored_traffic():
     return int(kv["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w, out_gpu, chunks: int, threads: int):
-    """The CPU oracle (as it stands) on a bounded sample of the workload: the
-    first `chunks` 64 KiB chunks of the same layer (all 1792 by default), compressed by the oracle's
-    own compressor, decoded and dequantized with `threads` host threads.  The
-    sample's outputs are also compared with the GPU's."""
-    import oracle as O
-    packed = O.pack_int4(w.codes)
-    n = min(chunks, w.dst_off.size - 1)
-    d_end = int(w.dst_off[n])
-    dst_off = w.dst_off[:n + 1].copy()
-    t = O.compress_table(packed[:d_end], dst_off, threads=threads)
-    n_elem = 2 * d_end
-    n_groups = -(-n_elem // w.group)
-    scales, zp = w.scales[:n_groups], w.zp[:n_groups]
-    out = np.zeros(n_elem, np.uint16)
-    O.fused_int4_chunked(t, scales, zp, w.group, out, threads)        # warm caches
-    times = []
-    for _ in range(5):
-        t0 = time.perf_counter()
-        bad, _ = O.fused_int4_chunked(t, scales, zp, w.group, out, threads)
-        times.append(time.perf_counter() - t0)
-        assert bad == 0
-    sec = sorted(times)[2]
-    alg = t.comp_bytes + 2 * n_elem
-    mismatches = int(np.count_nonzero(out != out_gpu[:n_elem]))
+def _threads_all() -> int:
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(n, 64))
+
+
+def cpu_baseline(run, alg_bytes, out_gpu, n_elem, sample, runs_one=3, runs_all=5):
+    """The CPU oracle (as it stands) on the same table the GPU decodes:
+    `run(threads)` decodes and dequantizes it into a host buffer and returns
+    (buffer, bad chunks).  Timed at all host cores (the reported value) and
+    at one thread; the outputs are compared with the GPU's, element by
+    element."""
+    threads = _threads_all()
+
+    def timed(th, runs):
+        out, bad = run(th)                       # warm caches
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            out, bad = run(th)
+            ts.append(time.perf_counter() - t0)
+            assert bad == 0
+        return out, float(np.median(ts))
+
+    out, sec = timed(threads, runs_all)
+    mismatches = int(np.count_nonzero(out[:n_elem] != out_gpu[:n_elem]))
+    _, sec1 = timed(1, runs_one)
     return {
-        "value": round(alg / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": "first %d of %d chunks (%d elements, %.1f MB algorithmic), oracle-compressed, "
-                  "median of 5 runs, %.2f s each" % (n, w.dst_off.size - 1, n_elem, alg / 1e6, sec),
+        "value": round(alg_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "%s; median of %d runs, %.3f s each" % (sample, runs_all, sec),
+        "one_thread": {"value": round(alg_bytes / sec1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                       "sample": "the same, median of %d runs, %.2f s each" % (runs_one, sec1)},
         "gpu_mismatches_on_sample": mismatches,
     }
+
+
+def timed_launches(torch, fn, steps, scratch, stream):
+    """Kernel time of `steps` calls of fn, each bracketed by HIP events on
+    `stream`; with `scratch`, a fill of it before each call (outside the
+    events) clears the caches.  Returns (per-call ms, wall seconds)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        if scratch is not None:
+            scratch.fill_(i & 255)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def footprint(comp_bytes, n_chunks, n_seq, meta_bytes, n_elem, packed_bytes):
+    """The compressed tensor's size in device memory, with the sequence
+    index and the offset tables counted in, against fp16 and packed INT4."""
+    index = 8 * (n_chunks + 1) + 4 * n_seq if n_seq else 0
+    offsets = 16 * (n_chunks + 1)
+    total = comp_bytes + index + offsets + meta_bytes
+    return {"compressed_bytes": comp_bytes, "sequence_index_bytes": index, "offset_table_bytes": offsets,
+            "scale_zero_point_bytes": meta_bytes, "total_bytes": total,
+            "fp16_over_total": round(2 * n_elem / total, 4),
+            "packed_over_total": round((packed_bytes + meta_bytes) / total, 4)}
+
+
+def plain_lz4_forms(torch, lt, packed, comp, comp_off, w, scales, zp, dev, out_ref, scratch, stream, steps):
+    """The same layer as plain LZ4, without the sequence index: (i) the
+    packer's blocks (4096-byte window) and (ii) the greedy parse's blocks
+    (4-byte matches, 64 KiB window), the blocks a general-purpose LZ4
+    compressor writes; (iii) the greedy blocks with the index added at load.
+    Each is timed like the headline and its output compared bit for bit
+    with the headline's."""
+    n_elem = w.rows * w.cols
+    gcomp, gcomp_off = lt.compress_chunks(packed, w.dst_off, greedy=True)
+    forms = (
+        ("packer_blocks_no_index", lambda: lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev, lt.PACK_WINDOW)),
+        ("greedy_64k_window_no_index", lambda: lt.ChunkTable.from_host(gcomp, gcomp_off, w.dst_off, dev, 0)),
+        ("greedy_64k_window_indexed", lambda: lt.ChunkTable.from_host(gcomp, gcomp_off, w.dst_off, dev, 0, index=True)),
+    )
+    n_seq = {False: int(lt.index_chunks(comp, comp_off)[1].size),
+             True: int(lt.index_chunks(gcomp, gcomp_off)[1].size)}
+    out = torch.empty_like(out_ref)
+    res, bad_total = {}, 0
+    for name, make in forms:
+        tb = make()
+        status = torch.full((tb.n_chunks,), -1, dtype=torch.int32, device=dev)
+
+        def fn():
+            lt.fused_lz4_int4(tb, scales, zp, (w.rows, w.cols), w.group, out=out, status=status)
+        out.fill_(0)
+        fn()
+        torch.cuda.synchronize()
+        lt.check_status(status)
+        bad = int((out.view(torch.int16) != out_ref.view(torch.int16)).sum().item())
+        bad_total += bad
+        ms, _ = timed_launches(torch, fn, steps, scratch, stream)
+        lt.check_status(status)
+        alg = tb.comp_bytes + 2 * n_elem
+        kern = float(np.mean(ms))
+        res[name] = {"compressed_bytes": tb.comp_bytes, "sequences": n_seq["greedy" in name],
+                     "kernel_ms": round(kern, 5), "GBps": round(alg / kern / 1e6, 2),
+                     "frac": round(alg / kern / 1e6 / HBM_PEAK_GBS, 4), "mismatches_vs_headline": bad}
+        del tb
+    return res, bad_total
 
 
 def main():
@@ -104,9 +184,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=(2, 3, 5),
+                    help="3: the 8192x28672 INT4 layer (default); 2: the 8192x8192 INT8 matrix; "
+                         "5: the 80-layer Llama-70B-shaped INT4 stack")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--extra", action="store_true")
-    ap.add_argument("--cpu-chunks", type=int, default=1792)
     ap.add_argument("--no-evict", action="store_true",
                     help="launch the timed steps back to back, without clearing the caches between them")
     ap.add_argument("--b2b", action="store_true",
@@ -116,7 +198,14 @@ def main():
         print("bench.py measures one GPU: this path has no multi-GPU mode "
               "(chunks shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.config == 2:
+        sys.exit(bench_int8(args))
+    if args.config == 5:
+        sys.exit(bench_stack(args))
+    sys.exit(bench_int4_layer(args))
 
+
+def bench_int4_layer(args) -> int:
     import torch
 
     import synth
@@ -125,7 +214,8 @@ def main():
     dev = torch.device("cuda:0")
     w = synth.mlp_int4_8192x28672()
     packed = lt.pack_int4(w.codes)
-    table = lt.ChunkTable.build(packed, w.dst_off, dev)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev, lt.PACK_WINDOW, index=True)
     scales = torch.from_numpy(w.scales.view(np.int16)).to(dev)
     zp = torch.from_numpy(w.zp).to(dev)
     n_elem = w.rows * w.cols
@@ -152,31 +242,15 @@ def main():
     # each one (outside the events) a 1 GiB fill clears L2 and the 256 MB
     # last-level cache, so no step reads input the previous one left cached.
     stream = torch.cuda.current_stream()
-
-    def timed_steps(evict):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i, (a, b) in enumerate(ev):
-            if evict:
-                scratch.fill_(i & 255)
-            a.record(stream)
-            step()
-            b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        lt.check_status(status)
-        return [a.elapsed_time(b) for a, b in ev], wall
-
-    kern_ms, wall = timed_steps(not args.no_evict)
+    kern_ms, wall = timed_launches(torch, step, args.steps, scratch, stream)
+    lt.check_status(status)
     avg_kern_ms = float(np.mean(kern_ms))
     ms_per_step = avg_kern_ms if not args.no_evict else wall * 1e3 / args.steps
     value = alg_bytes / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / (avg_kern_ms / 1e3) / 1e9
     b2b_ms = None
     if args.b2b and not args.no_evict:   # for reference: the same steps back to back, caches warm
-        b2b, b2b_wall = timed_steps(False)
+        b2b, b2b_wall = timed_launches(torch, step, args.steps, None, stream)
         b2b_ms = {"mean": round(float(np.mean(b2b)), 5), "wall_per_step": round(b2b_wall * 1e3 / args.steps, 5)}
 
     result = {
@@ -200,6 +274,8 @@ def main():
             "compressed_bytes": table.comp_bytes, "fp16_bytes": 2 * n_elem,
             "algorithmic_bytes": alg_bytes, "metadata_bytes": int(meta_bytes),
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "footprint": footprint(table.comp_bytes, table.n_chunks, table.n_seq,
+                                   2 * w.scales.size + w.zp.size, n_elem, packed.size),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -214,18 +290,257 @@ def main():
                     "caches_cleared_before_each_step": not args.no_evict,
                     "back_to_back_no_clearing": b2b_ms},
     }
+    plain, bad_plain = plain_lz4_forms(torch, lt, packed, comp, comp_off, w, scales, zp, dev, out, scratch,
+                                       stream, max(5, args.steps // 5))
+    result["plain_lz4"] = plain
 
     if args.extra:
         result["extra"] = extra_measurements(torch, lt, w, packed, scales, zp, dev)
 
+    bad_cpu = 0
     if not args.no_cpu:
+        import oracle as O
         out_host = out.view(torch.int16).cpu().numpy().view(np.uint16)
-        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-        threads = max(1, min(threads, 64))
-        result["cpu_baseline"] = cpu_baseline(w, out_host, args.cpu_chunks, threads)
+        t = O.Table(comp, comp_off, w.dst_off)
+        host = np.zeros(n_elem, np.uint16)
+
+        def run(th):
+            bad, _ = O.fused_int4_chunked(t, w.scales, w.zp, w.group, host, th)
+            return host, bad
+        result["cpu_baseline"] = cpu_baseline(
+            run, alg_bytes, out_host, n_elem,
+            "the whole layer: all %d chunks of the table the GPU decodes (%d elements, %.1f MB algorithmic)"
+            % (table.n_chunks, n_elem, alg_bytes / 1e6))
+        bad_cpu = result["cpu_baseline"]["gpu_mismatches_on_sample"]
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    if bad_cpu or bad_plain:
+        print("GPU output differs: %d elements from the oracle, %d across the plain-LZ4 forms"
+              % (bad_cpu, bad_plain), file=sys.stderr)
+        return 1
+    return 0
+
+
+def bench_int8(args) -> int:
+    """The 8192x8192 INT8 matrix (per-row scales, half the rows zero), 64 KiB
+    chunks in the default table form: the fused kernel against the two-pass
+    route (decode to INT8 bytes, then dequantize)."""
+    import torch
+
+    import synth
+    import weight_dequantization_amd as lt
+
+    dev = torch.device("cuda:0")
+    w = synth.int8_8192x8192()
+    qb = w.q.view(np.uint8)
+    comp, comp_off = lt.compress_chunks(qb, w.dst_off, max_dist=lt.PACK_WINDOW)
+    table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev, lt.PACK_WINDOW, index=True)
+    scales = torch.from_numpy(w.scales.view(np.int16)).to(dev)
+    n_elem = w.rows * w.cols
+    shape = (w.rows, w.cols)
+    out = torch.empty(n_elem, dtype=torch.float16, device=dev)
+    out2 = torch.empty_like(out)
+    qbuf = torch.empty(n_elem, dtype=torch.uint8, device=dev)
+    status = torch.full((table.n_chunks,), -1, dtype=torch.int32, device=dev)
+    status2 = torch.full_like(status, -1)
+    alg = table.comp_bytes + 2 * n_elem
+
+    def fused():
+        lt.fused_lz4_int8(table, scales, None, shape, w.group, out=out, status=status)
+
+    def decode():
+        lt.decode_lz4(table, out=qbuf, status=status2)
+
+    def dequant():
+        lt.dequant_int8(qbuf.view(torch.int8), scales, None, shape, w.group, out=out2)
+
+    scratch = None if args.no_evict else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fused(); decode(); dequant()
+    torch.cuda.synchronize()
+    lt.check_status(status)
+    lt.check_status(status2)
+    bad_two = int((out.view(torch.int16) != out2.view(torch.int16)).sum().item())
+    ms_f, _ = timed_launches(torch, fused, args.steps, scratch, stream)
+    ms_d, _ = timed_launches(torch, decode, args.steps, scratch, stream)
+    ms_q, _ = timed_launches(torch, dequant, args.steps, scratch, stream)
+    lt.check_status(status)
+    kf, kd, kq = float(np.mean(ms_f)), float(np.mean(ms_d)), float(np.mean(ms_q))
+    value = alg / kf / 1e6
+    result = {
+        "metric": "fused LZ4+INT8->fp16 GB/s (compressed in + fp16 out) and % of HBM peak, 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(kf, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; q = clip(rint(N(0,1)*32), +-127), 4096 of 8192 rows zero, "
+                "per-row fp16 scales U(1e-3, 1e-2))",
+        "config": {"workload": "fused LZ4+INT8 -> fp16, 8192x8192, per-row scales, no zero point, 64 KiB LZ4 "
+                               "chunks (host packer, declared match window 4096 B, sequence index)",
+                   "chunks": table.n_chunks, "compressed_bytes": table.comp_bytes, "fp16_bytes": 2 * n_elem,
+                   "algorithmic_bytes": alg,
+                   "footprint": footprint(table.comp_bytes, table.n_chunks, table.n_seq, 2 * w.scales.size,
+                                          n_elem, n_elem)},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "lt::chunk_kernel<2, 14>", "avg_launch_ms": round(kf, 5), "bytes_per_launch": alg},
+        "two_pass": {"decode_ms": round(kd, 5), "dequant_ms": round(kq, 5), "total_ms": round(kd + kq, 5),
+                     "GBps": round(alg / (kd + kq) / 1e6, 2), "fused_speedup": round((kd + kq) / kf, 3),
+                     "mismatches_vs_fused": bad_two},
+        "step_ms": {"caches_cleared_before_each_step": not args.no_evict},
+    }
+    bad_cpu = 0
+    if not args.no_cpu:
+        import oracle as O
+        t = O.Table(comp, comp_off, w.dst_off)
+        out_host = out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+        def run(th):
+            o, st = O.fused_int8(t, w.scales, None, w.group, n_elem, th)
+            return o, int(np.count_nonzero(st))
+        result["cpu_baseline"] = cpu_baseline(
+            run, alg, out_host, n_elem, "the whole matrix: all %d chunks of the table the GPU decodes"
+            % table.n_chunks)
+        bad_cpu = result["cpu_baseline"]["gpu_mismatches_on_sample"]
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    if bad_cpu or bad_two:
+        print("GPU output differs: %d elements from the oracle, %d between the routes" % (bad_cpu, bad_two),
+              file=sys.stderr)
+        return 1
+    return 0
+
+
+def bench_stack(args) -> int:
+    """The 80-layer Llama-70B-shaped INT4 stack (q, k, v, o, gate, up, down
+    per layer; group 128; 16/64/256 KiB chunks drawn per chunk), resident on
+    the device in the default table form and expanded layer by layer into
+    seven reused fp16 buffers: one lt_fused_lz4_int4 launch per tensor, 560
+    per pass.  Two distinct layers are generated (the seeds of layers 0 and
+    79) and copied on the device into 80 separate allocations (even layers
+    from layer 0, odd from layer 79); 80 layers of host generation would
+    take far longer than a benchmark may run.  Each layer's seven launches
+    are bracketed by HIP events; no cache clearing is needed, as each layer
+    reads and writes about 2 GB."""
+    import torch
+
+    import synth
+    import weight_dequantization_amd as lt
+
+    dev = torch.device("cuda:0")
+    names = [n for n, _, _ in synth.LLAMA70B_LAYER]
+    base, host = {}, {}
+    for src in (0, 79):
+        for t in range(len(names)):
+            w = synth.llama70b_tensor(src, t)
+            packed = lt.pack_int4(w.codes)
+            comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+            tb = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev, lt.PACK_WINDOW, index=True)
+            base[(src, t)] = (tb, torch.from_numpy(w.scales.view(np.int16)).to(dev), torch.from_numpy(w.zp).to(dev))
+            if src == 0 and t == 6:
+                host["down"] = (w, comp, comp_off)
+            del packed
+            print("stack: layer %d %s packed and resident" % (src, names[t]), file=sys.stderr, flush=True)
+    layers = []
+    for layer in range(synth.N_LAYERS_70B):
+        src = 0 if layer % 2 == 0 else 79
+        tensors = []
+        for t in range(len(names)):
+            tb, sc, zp = base[(src, t)]
+            c = lt.ChunkTable(tb.comp.clone(), tb.comp_off.clone(), tb.dst_off.clone(), tb.n_chunks,
+                              tb.max_chunk_bytes, tb.total_bytes, tb.comp_bytes, tb.max_dist,
+                              tb.seq_off.clone(), tb.seq_pos.clone(), tb.n_seq)
+            tensors.append((c, sc.clone(), zp.clone()))
+        layers.append(tensors)
+    shapes = [(r, c) for _, r, c in synth.LLAMA70B_LAYER]
+    outs = [torch.empty(r * c, dtype=torch.float16, device=dev) for r, c in shapes]
+    nmax = max(tb.n_chunks for L in layers for tb, _, _ in L)
+    statuses = [torch.full((nmax,), -1, dtype=torch.int32, device=dev) for _ in shapes]
+    stream = torch.cuda.current_stream()
+
+    def run_layer(L):
+        for t, (tb, sc, zp) in enumerate(L):
+            lt.fused_lz4_int4(tb, sc, zp, shapes[t], 128, out=outs[t], status=statuses[t])
+
+    def check():
+        for t, (tb, _, _) in enumerate(layers[-1]):
+            lt.check_status(statuses[t][:tb.n_chunks])
+
+    print("stack: 80 layers resident, warming up", file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):
+        for L in layers:
+            run_layer(L)
+    torch.cuda.synchronize()
+    check()
+    passes = max(1, min(args.steps, 5))
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+          for _ in range(passes)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for p in range(passes):
+        for L, (a, b) in zip(layers, ev[p]):
+            a.record(stream)
+            run_layer(L)
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    check()
+    per_layer = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
+    layer_comp = [sum(tb.comp_bytes for tb, _, _ in L) for L in layers]
+    n_elem_layer = sum(r * c for r, c in shapes)
+    alg_layer = np.array([cb + 2 * n_elem_layer for cb in layer_comp], np.float64)
+    gbps = alg_layer[None, :] / per_layer / 1e6
+    ms_pass = float(per_layer.sum(axis=1).mean())
+    alg_pass = float(alg_layer.sum())
+    value = alg_pass / ms_pass / 1e6
+    result = {
+        "metric": "fused LZ4+INT4->fp16 GB/s over the 80-layer stack (compressed in + fp16 out), 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": passes, "warmup": max(1, args.warmup),
+        "ms_per_step": round(ms_pass, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic (seeded; two generated layers copied to 80 device allocations)",
+        "config": {"workload": "80 Llama-70B-shaped INT4 layers (q, k, v, o 8192x8192 / 8192x1024; gate, up, "
+                               "down 8192x28672), group 128, 16/64/256 KiB LZ4 chunks (host packer, declared "
+                               "window 4096 B, sequence index), 560 fused launches per pass",
+                   "compressed_bytes_resident": int(sum(layer_comp)), "fp16_bytes_per_layer": 2 * n_elem_layer},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "lt::chunk_kernel<3, 14>", "bytes_per_launch": None},
+        "per_layer": {"ms_mean": round(float(per_layer.mean()), 5), "ms_min": round(float(per_layer.min()), 5),
+                      "ms_max": round(float(per_layer.max()), 5), "GBps_mean": round(float(gbps.mean()), 2),
+                      "frac_mean": round(float(gbps.mean()) / HBM_PEAK_GBS, 4),
+                      "wall_ms_per_pass": round(wall * 1e3 / passes, 3)},
+    }
+    bad_cpu = 0
+    if not args.no_cpu:
+        import oracle as O
+        w, comp, comp_off = host["down"]
+        tb, sc, zp = base[(0, 6)]
+        st = torch.full((tb.n_chunks,), -1, dtype=torch.int32, device=dev)
+        o = lt.fused_lz4_int4(tb, sc, zp, (w.rows, w.cols), 128, status=st)
+        torch.cuda.synchronize()
+        lt.check_status(st)
+        out_host = o.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+        n_elem = w.rows * w.cols
+        t = O.Table(comp, comp_off, w.dst_off)
+        buf = np.zeros(n_elem, np.uint16)
+
+        def run(th):
+            bad, _ = O.fused_int4_chunked(t, w.scales, w.zp, w.group, buf, th)
+            return buf, bad
+        result["cpu_baseline"] = cpu_baseline(
+            run, int(comp_off[-1]) + 2 * n_elem, out_host, n_elem,
+            "layer 0's down projection (8192x28672, %d chunks of 16/64/256 KiB), the table the GPU decodes"
+            % (comp_off.size - 1), runs_one=1, runs_all=3)
+        bad_cpu = result["cpu_baseline"]["gpu_mismatches_on_sample"]
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    if bad_cpu:
+        print("GPU output differs from the oracle in %d elements" % bad_cpu, file=sys.stderr)
+        return 1
+    return 0
 
 
 def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):

@@ -405,7 +405,8 @@ lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed);
 
 /*
  * lt_compress_chunks -- HOST.  Compresses src[dst_off[i] .. dst_off[i+1]) for
- * each of n_chunks chunks as an independent LZ4 block and concatenates them
+ * each of n_chunks chunks as an independent LZ4 block (the public block
+ * format, which the pages name without defining) and concatenates them
  * into comp (capacity comp_cap); comp_off (uint64[n_chunks+1]) receives the
  * prefix sums.  threads <= 0 means one per host core.  Matches reach at most
  * max_dist bytes back (0 or anything above 65535 means 65535); the table
@@ -416,6 +417,19 @@ lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed);
 lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
                              uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
                              uint32_t max_dist);
+
+/*
+ * lt_compress_chunks_greedy -- HOST.  As lt_compress_chunks (same arguments,
+ * layout and errors), with the plain greedy LZ4 parse of a general-purpose
+ * block compressor: every hashed match of 4 bytes or more at any distance
+ * from 1 to max_dist is taken and extended.  lt_compress_chunks accepts
+ * hashed matches of 8 bytes or more and prefers runs of one byte, which
+ * gives the device decoder longer sequences to work on; this form gives
+ * the blocks a standard compressor would write, for tables not made here.
+ */
+lt_status lt_compress_chunks_greedy(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
+                                    uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
+                                    uint32_t max_dist);
 
 /*
  * lt_index_chunks -- HOST.  Builds the sequence index of a chunk table from

@@ -59,3 +59,27 @@ def sequence_starts(blk):
                 if v != 255:
                     break
     return out
+
+
+def matches(blk):
+    """(distance, length) of every match of a valid LZ4 block, in order."""
+    b = [int(v) for v in blk]
+    y, out = 0, []
+    while True:
+        t = b[y]; y += 1
+        L = t >> 4
+        if L == 15:
+            while True:
+                v = b[y]; y += 1; L += v
+                if v != 255: break
+        y += L
+        if y >= len(b):
+            return out
+        d = b[y] | (b[y + 1] << 8)
+        y += 2
+        M = (t & 15) + 4
+        if (t & 15) == 15:
+            while True:
+                v = b[y]; y += 1; M += v
+                if v != 255: break
+        out.append((d, M))

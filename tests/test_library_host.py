@@ -14,7 +14,7 @@ import pytest
 
 import oracle as O
 import synth
-from lz4_blocks import max_match_distance, sequence_starts
+from lz4_blocks import matches, max_match_distance, sequence_starts
 import weight_dequantization_amd as lt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -155,6 +155,48 @@ def test_packer_honours_declared_window(max_dist):
         assert max_match_distance(blk) <= max_dist
     out, st = O.decode_table(O.Table(comp, comp_off, dst_off))
     assert np.all(st == O.OK) and np.array_equal(out, x)
+
+
+@pytest.mark.parametrize("max_dist", [1, 4096, 65535])
+def test_greedy_packer_round_trips_within_its_window(max_dist):
+    """The greedy parse's blocks decode (oracle) to the input and keep every
+    match within max_dist, on random, zero, short-alphabet and repeated data
+    and on chunks of 0 to 13 bytes."""
+    rng = np.random.default_rng(40 + max_dist)
+    base = rng.integers(0, 256, 30000, dtype=np.uint8)
+    parts = [base, np.zeros(5000, np.uint8), rng.integers(0, 3, 30000, dtype=np.uint8), base,
+             rng.integers(0, 256, 13, dtype=np.uint8)]
+    x = np.concatenate(parts)
+    dst_off = np.array([0, 0, 12, 25, 40000, 70000, x.size], np.uint64)
+    comp, comp_off = lt.compress_chunks(x, dst_off, max_dist=max_dist, greedy=True)
+    for c in range(dst_off.size - 1):
+        blk = comp[int(comp_off[c]):int(comp_off[c + 1])]
+        assert all(d <= max_dist for d, _ in matches(blk))
+    out, st = O.decode_table(O.Table(comp, comp_off, dst_off))
+    assert np.all(st == O.OK) and np.array_equal(out, x)
+
+
+def test_greedy_packer_takes_the_short_matches_the_default_leaves():
+    """Data whose only repeats are 5-byte strings: the greedy parse codes
+    them as matches of 4 to 7 bytes, the default parse (8-byte minimum,
+    runs aside) leaves them as literals; on the layer's codes the greedy
+    parse writes about as many sequences as the oracle's greedy compressor."""
+    rng = np.random.default_rng(5)
+    x = rng.integers(0, 256, 65536, dtype=np.uint8)
+    for k in range(200, 65000, 37):
+        x[k:k + 5] = x[k - 150:k - 145]
+    dst_off = np.array([0, x.size], np.uint64)
+    g = matches(lt.compress_chunks(x, dst_off, greedy=True)[0])
+    d = matches(lt.compress_chunks(x, dst_off)[0])
+    assert sum(1 for dist, m in g if m < 8 and dist > 1) > 1000
+    assert all(m >= 8 or dist == 1 for dist, m in d)
+    w = synth.mlp_int4_small(rows=64)
+    packed = lt.pack_int4(w.codes)
+    gc, go = lt.compress_chunks(packed, w.dst_off, greedy=True)
+    oc = O.compress_table(packed, w.dst_off)
+    ng = lt.index_chunks(gc, go)[1].size
+    no = lt.index_chunks(oc.comp, oc.comp_off)[1].size
+    assert 0.9 * no <= ng <= 1.1 * no, (ng, no)
 
 
 def _index_matches_walk(comp, comp_off):

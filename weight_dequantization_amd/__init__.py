@@ -122,6 +122,7 @@ def _lib():
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
             "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
+            "lt_compress_chunks_greedy": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
             "lt_index_chunks": (i32, [vp, vp, u32, vp, vp, u64, i32]),
             "lt_status_str": (C.c_char_p, [i32]),
             "lt_abi_version": (i32, []),
@@ -158,9 +159,12 @@ def lz4_bound(n: int) -> int:
     return int(_lib().lt_lz4_bound(n))
 
 
-def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_dist: int = 0):
+def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_dist: int = 0,
+                    greedy: bool = False):
     """LZ4-compress each chunk independently (matches reach at most max_dist
-    bytes back; 0 means the format's 65535).  Returns (comp, comp_off)."""
+    bytes back; 0 means the format's 65535).  greedy=True gives the plain
+    greedy parse of a general-purpose compressor (4-byte matches, no run
+    preference) instead of the packer's own.  Returns (comp, comp_off)."""
     src = np.ascontiguousarray(src, dtype=np.uint8)
     dst_off = np.ascontiguousarray(dst_off, dtype=np.uint64)
     n = dst_off.size - 1
@@ -168,10 +172,11 @@ def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_
     cap = int(np.sum(sizes + sizes // 255 + 16)) + 16
     comp = np.empty(max(cap, 1), np.uint8)
     comp_off = np.empty(n + 1, np.uint64)
-    st = _lib().lt_compress_chunks(_np_ptr(src), _np_ptr(dst_off), n, _np_ptr(comp), cap,
-                                   _np_ptr(comp_off), threads, max_dist)
+    fn = "lt_compress_chunks_greedy" if greedy else "lt_compress_chunks"
+    st = getattr(_lib(), fn)(_np_ptr(src), _np_ptr(dst_off), n, _np_ptr(comp), cap,
+                             _np_ptr(comp_off), threads, max_dist)
     if st != LT_OK:
-        raise LtError(st, "lt_compress_chunks")
+        raise LtError(st, fn)
     return comp[:int(comp_off[-1])].copy(), comp_off
 
 
@@ -322,15 +327,16 @@ class ChunkTable:
 
     @classmethod
     def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0,
-              max_dist: int = None, index: bool = True, pin: bool = False):
+              max_dist: int = None, index: bool = True, pin: bool = False, greedy: bool = False):
         """Compress `src` chunk by chunk on the host and upload the table.  By
-        default matches stay within SMALL_WINDOW bytes, which the table
+        default matches stay within PACK_WINDOW bytes, which the table
         declares, so the device decoder keeps a short history per chunk, and
         the table carries the sequence index, so each chunk's sequences are
-        parsed side by side."""
+        parsed side by side.  greedy=True packs with the plain greedy parse
+        (compress_chunks)."""
         if max_dist is None:
             max_dist = PACK_WINDOW
-        comp, comp_off = compress_chunks(src, dst_off, threads, max_dist)
+        comp, comp_off = compress_chunks(src, dst_off, threads, max_dist, greedy)
         return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin)
 
     def as_c(self) -> _Table:

@@ -72,6 +72,13 @@ struct Writer {
 };
 
 // Compress src[0, n) into out (capacity >= lt_lz4_bound(n)); returns size.
+// Greedy is the plain LZ4 parse: at each position the hashed candidate is
+// taken when its first 4 bytes match (any distance from 1 to max_dist),
+// extended forward, every position inside it is indexed, and the scan
+// resumes after it.  The default parse
+// instead accepts hashed matches of 8 bytes or more and prefers runs
+// (distance 1), which a decoder builds without reading earlier output.
+template <bool Greedy>
 uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vector<int32_t> &table,
                         uint64_t max_dist) {
   Writer w{out, 0};
@@ -85,7 +92,7 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
   while (i + kMatchLimit <= n) {
     uint64_t best_len = 0, best_dist = 0;
     // distance-1 run
-    if (i > 0 && src[i] == src[i - 1]) {
+    if (!Greedy && i > 0 && src[i] == src[i - 1]) {
       uint64_t len = 0;
       while (i + len < match_end && src[i + len] == src[i - 1]) len++;
       if (len >= kMinRun) {
@@ -96,15 +103,16 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
     uint32_t h = hash32(rd32(src + i));
     int64_t c = table[h];
     table[h] = (int32_t)i;
-    if (c >= 0 && i - (uint64_t)c <= max_dist && i - (uint64_t)c > 1 && rd32(src + c) == rd32(src + i)) {
+    if (c >= 0 && i - (uint64_t)c <= max_dist && i - (uint64_t)c > (Greedy ? 0u : 1u) &&
+        rd32(src + c) == rd32(src + i)) {
       uint64_t len = 4;
       while (i + len < match_end && src[c + len] == src[i + len]) len++;
-      if (len >= kMinMatch && len > best_len) {
+      if (len >= (Greedy ? 4u : kMinMatch) && len > best_len) {
         best_len = len;
         best_dist = i - (uint64_t)c;
       }
     }
-    if (best_dist > 1 && i + 2 + kMatchLimit <= n) {
+    if (!Greedy && best_dist > 1 && i + 2 + kMatchLimit <= n) {
       // A run starting at i + 1 (of src[i]) or at i + 2 (of src[i + 1]) that
       // covers nearly as much as the hashed match, with the bytes before it
       // as literals, is taken instead: a run decodes without reading earlier
@@ -119,9 +127,10 @@ uint64_t compress_block(const uint8_t *src, uint64_t n, uint8_t *out, std::vecto
     if (best_len) {
       w.sequence(src + anchor, i - anchor, best_dist, best_len);
       uint64_t stop = i + best_len;
-      // index a few positions inside the match so later repeats find it
-      for (uint64_t j = std::max<uint64_t>(i + 1, stop > 2 ? stop - 2 : 0); j < stop && j + kMatchLimit <= n; j++)
-        table[hash32(rd32(src + j))] = (int32_t)j;
+      // index positions inside the match so later repeats find it (the
+      // greedy parse indexes all of them, the default only the last two)
+      const uint64_t j0 = Greedy ? i + 1 : std::max<uint64_t>(i + 1, stop > 2 ? stop - 2 : 0);
+      for (uint64_t j = j0; j < stop && j + kMatchLimit <= n; j++) table[hash32(rd32(src + j))] = (int32_t)j;
       i = stop;
       anchor = i;
     } else {
@@ -220,9 +229,13 @@ lt_status lt_pack_int4(const uint8_t *codes, uint64_t n_codes, uint8_t *packed) 
   return LT_OK;
 }
 
-lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
-                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
-                             uint32_t max_dist) {
+}  // extern "C"
+
+namespace {
+
+template <bool Greedy>
+lt_status compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks, uint8_t *comp,
+                          uint64_t comp_cap, uint64_t *comp_off, int threads, uint32_t max_dist) {
   if (!dst_off || !comp_off) return LT_ERR_INVALID_ARG;
   const uint64_t window = (max_dist == 0 || max_dist > kMaxDist) ? kMaxDist : max_dist;
   if (n_chunks == 0) {
@@ -245,8 +258,8 @@ lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32
   auto work = [&](int t) {
     std::vector<int32_t> table(1u << kHashBits);
     for (uint32_t i = (uint32_t)t; i < n_chunks; i += (uint32_t)threads)
-      size[i] = compress_block(src + dst_off[i], dst_off[i + 1] - dst_off[i], scratch.data() + slot[i], table,
-                               window);
+      size[i] = compress_block<Greedy>(src + dst_off[i], dst_off[i + 1] - dst_off[i], scratch.data() + slot[i],
+                                       table, window);
   };
   std::vector<std::thread> pool;
   for (int t = 1; t < threads; t++) pool.emplace_back(work, t);
@@ -261,6 +274,22 @@ lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32
     comp_off[i + 1] = pos;
   }
   return LT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lt_status lt_compress_chunks(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
+                             uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
+                             uint32_t max_dist) {
+  return compress_chunks<false>(src, dst_off, n_chunks, comp, comp_cap, comp_off, threads, max_dist);
+}
+
+lt_status lt_compress_chunks_greedy(const uint8_t *src, const uint64_t *dst_off, uint32_t n_chunks,
+                                    uint8_t *comp, uint64_t comp_cap, uint64_t *comp_off, int threads,
+                                    uint32_t max_dist) {
+  return compress_chunks<true>(src, dst_off, n_chunks, comp, comp_cap, comp_off, threads, max_dist);
 }
 
 lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks,
