@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 11
+#define LT_ABI_VERSION 12
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -114,6 +114,16 @@ enum {
  *              0); seq_off is non-decreasing and seq_off[n_chunks] <= n_seq.
  *   seq_pos    DEVICE uint32[n_seq] or NULL (given exactly when seq_off is).
  *   n_seq      entries in seq_pos (0 without an index).
+ *   order      DEVICE uint32[n_chunks] or NULL: the order in which the
+ *              chunks are started, the k-th workgroup of a launch taking
+ *              chunk order[k] (NULL: chunk k).  It should be a permutation
+ *              of 0 .. n_chunks-1; an entry >= n_chunks is skipped, a chunk
+ *              listed twice is decoded twice (the same bytes), and a chunk
+ *              not listed is neither decoded nor given a status.  A launch
+ *              lasts at least as long as its slowest chunk, so tables whose
+ *              chunks differ in size start the largest first
+ *              (lt_order_chunks).  Chunk-range and streamed calls decode in
+ *              table order and ignore it.
  * The index lets a chunk's sequences be parsed side by side instead of one
  * after another (lt_index_chunks builds it from the blocks).  It is checked
  * against the blocks: a listed sequence that does not end where the next
@@ -137,6 +147,7 @@ typedef struct lt_chunk_table {
   const uint64_t *seq_off;
   const uint32_t *seq_pos;
   uint64_t n_seq;
+  const uint32_t *order;
 } lt_chunk_table;
 
 /*
@@ -393,6 +404,12 @@ lt_status lt_encode_zero_runs(const uint16_t *x, uint64_t n, uint32_t *bitmap, u
  * n_chunks entries. */
 lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint32_t *crc,
                              int threads);
+
+/* The order field of a table (HOST arrays): order (uint32[n_chunks])
+ * receives 0 .. n_chunks-1 sorted by decreasing decoded size
+ * (dst_off[i+1] - dst_off[i]); chunks of one size keep table order.
+ * LT_ERR_INVALID_ARG for a non-monotone dst_off. */
+lt_status lt_order_chunks(const uint64_t *dst_off, uint32_t n_chunks, uint32_t *order);
 
 /* Worst-case size of one LZ4 block holding n bytes. */
 uint64_t lt_lz4_bound(uint64_t n);

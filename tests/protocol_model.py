@@ -5,7 +5,8 @@ LDS counters: a feeder that streams the compressed block into an input ring
 with asynchronous DMA, a walker that parses sequences (one per lane with a
 sequence index, else one after another, handing entries to a recorder wave),
 and builder waves that take 1 KiB tiles of the decoded stream in order,
-build them in a history ring and write them out.  This module re-states
+build them in a history ring and write them out; a builder announces a tile
+as built before its write-out, and as written out after it.  This module re-states
 that protocol in Python, role by role, with the same counters, ring sizes,
 window rule, record-ring rule, tile order and history-slot reuse rule, and
 runs it under random interleavings: every role is a generator that yields
@@ -19,14 +20,18 @@ It checks what the protocol must guarantee, at the moment of every access:
   - every history byte a tile's match reads belongs to a final tile (or to
     bytes of the same tile built before it), in the slot that holds it;
   - a tile overwrites a history slot only after every tile that reads the
-    slot's previous tile is final;
+    slot's previous tile is built and the previous tile is written out;
+  - a tile's write-out reads only its own bytes (its slot is not reused
+    while the write-out runs);
   - no interleaving deadlocks (a step bound far above the work);
 and at the end that the decoded chunk equals the expected bytes.
 
 `fault` plants one protocol mistake in the model (test of the model
 itself): "no_window" (the feeder ignores the readers' bound), "early_need"
 (a builder releases its tile's input before building it), "no_slot_rule"
-(a builder skips the history-slot reuse wait), "no_split" (the walker
+(a builder skips the history-slot reuse wait), "no_write_rule" (a
+builder overwrites a slot without waiting for the old tile's write-out),
+"no_split" (the walker
 waits for the bytes after a literal run without announcing the run).
 
 The model follows the kernel's structure, not its instruction-level
@@ -126,6 +131,7 @@ class Chunk:
         self.need = [0 if i <= self.nb else FF for i in range(8)]
         self.bk = [0 if i < self.nb else FF for i in range(8)]
         self.next_tile = [i if i < self.nb else FF for i in range(8)]
+        self.built_to = [i if i < self.nb else FF for i in range(8)]   # the kernel's built[]
         self.nrec = 0
         self.cov = 0
         self.wcnt = 0
@@ -142,7 +148,8 @@ class Chunk:
         self.hist = bytearray(self.HIST)
         self.hist_tile = [-1] * self.HTILES     # tile held by each history slot
         self.hist_owner = [-1] * self.HIST      # tile whose byte each history byte holds
-        self.final = [False] * self.ntiles
+        self.final = [False] * self.ntiles        # history bytes final (built)
+        self.written = [False] * self.ntiles      # written out too
         self.out = bytearray(n_out)
         self.built = [0] * self.ntiles
         self.inflight = []                      # [segment, steps until it lands]
@@ -566,7 +573,7 @@ class Chunk:
         k = 0
         nrec = cov = 0
         avail = 0
-        done = 0
+        done = fdone = 0
         need_pub = 0
         reach = (self.dmax + TILE - 1) // TILE
         t = b
@@ -656,15 +663,20 @@ class Chunk:
             if seen and m > 16 and 2 * (1 + extra) > m:
                 hard = True
             need_tiles = (src_need + TILE - 1) // TILE
+            written = 0
             if t >= self.HTILES and self.fault != "no_slot_rule":
                 if reach < self.HTILES:
                     need_tiles = max(need_tiles, t - self.HTILES + reach + 1)
                 else:
                     need_tiles = t
-            while done < need_tiles:
-                done = min(self.next_tile)
+                if self.fault != "no_write_rule":
+                    written = t - self.HTILES + 1
+            while done < need_tiles or fdone < written:
+                done = min(self.built_to)
                 yield
-                if done >= need_tiles:
+                fdone = min(self.next_tile)
+                yield
+                if done >= need_tiles and fdone >= written:
                     break
                 if self.pstate == ST_FAIL:
                     ok = False
@@ -690,6 +702,8 @@ class Chunk:
                 if pending:
                     raise ProtocolError("%s overwrote tile %d's history while tiles %s still read it" % (
                         who, old, pending[:4]))
+                if not self.written[old]:
+                    raise ProtocolError("%s overwrote tile %d's history before its write-out" % (who, old))
             self.hist_tile[slot] = t
             for j in js:
                 o, ys, L, dist, fill, flags = rec(j)
@@ -717,15 +731,26 @@ class Chunk:
                         raise ProtocolError("%s tile %d read byte %d of tile %d (final %s, byte holds tile %d)" % (
                             who, t, src, st_, self.final[st_], own))
                     self.hist[q % self.HIST] = self.hist[src % self.HIST]
-            for q in range(T, Tend):
-                self.out[q] = self.hist[q % self.HIST]
             self.built[t] += 1
             self.final[t] = True
+            self.built_to[b] = u
+            yield
+            # the write-out reads the tile's slot, in two steps; tiles that
+            # copy from it may be built meanwhile
+            for a, e in ((T, min(T + TILE // 2, Tend)), (min(T + TILE // 2, Tend), Tend)):
+                for q in range(a, e):
+                    if self.hist_owner[q % self.HIST] != t:
+                        raise ProtocolError("%s write-out of tile %d read byte %d after tile %d overwrote it" % (
+                            who, t, q, self.hist_owner[q % self.HIST]))
+                    self.out[q] = self.hist[q % self.HIST]
+                yield
+            self.written[t] = True
             self.next_tile[b] = u
             yield
             t = u
         self.need[1 + b] = FF
         self.bk[b] = FF
+        self.built_to[b] = FF
         self.next_tile[b] = FF
         yield
         self.nfinished += 1

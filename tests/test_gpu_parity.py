@@ -436,6 +436,36 @@ def test_fused_int4_mlp_8192x28672_full():
     _fused4(lt.ChunkTable.build(packed, w.dst_off, DEV, index=False), w, "mlp_int4_8192x28672 packer, walked")
 
 
+def test_launch_order_mixed_chunks_and_partial_orders():
+    """A table of 16/64/256 KiB chunks decoded in its launch order (largest
+    first), fused and decode-only, equals the oracle; an order that leaves
+    a chunk out and holds an entry past the last chunk decodes every listed
+    chunk, skips the bad entry, and leaves the missing chunk's output and
+    status untouched."""
+    w = synth.int4_weight(1024, 8192, 128, 78, chunking="mixed")
+    packed = lt.pack_int4(w.codes)
+    tb = lt.ChunkTable.build(packed, w.dst_off, DEV)
+    sizes = np.diff(w.dst_off.astype(np.int64))
+    assert tb.order is not None and len(set(sizes[:-1].tolist())) == 3
+    order = tb.order.cpu().numpy().view(np.uint32)
+    assert np.all(np.diff(sizes[order]) <= 0)
+    _fused4(tb, w, "mixed chunks, largest first")
+    _decode_check(tb, packed, "mixed chunks decode-only, largest first")
+    gone = int(order[1])
+    partial = np.concatenate([order[order != gone], [tb.n_chunks + 7]]).astype(np.uint32)
+    tb.order = torch.from_numpy(partial.view(np.int32)).to(DEV)
+    st = status_tensor(tb.n_chunks)
+    out = torch.full((w.rows * w.cols,), 3.0, dtype=torch.float16, device=DEV)
+    lt.fused_lz4_int4(tb, t_u16(w.scales), t_i8(w.zp), (w.rows, w.cols), w.group, out=out, status=st)
+    s = statuses(st, tb.n_chunks)
+    assert s[gone] == -1 and np.all(np.delete(s, gone) == 0)
+    got = host_u16(out)
+    ref = O.dequant_int4(O.pack_int4(w.codes), w.scales, w.zp, w.group)
+    e0, e1 = 2 * int(w.dst_off[gone]), 2 * int(w.dst_off[gone + 1])
+    assert np.all(got[e0:e1] == np.float16(3.0).view(np.uint16))
+    assert_same(np.concatenate([got[:e0], got[e1:]]), np.concatenate([ref[:e0], ref[e1:]]), "partial order")
+
+
 def test_fused_int4_mlp_8192x28672_oracle_stream():
     """The 8192x28672 layer in full as the oracle's greedy compressor encodes
     it (64 KiB window, 4-byte minimum matches, no declared window), through

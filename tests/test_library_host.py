@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 11
+    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 12
     assert lt.lib().lt_status_str(1) == b"invalid argument"
     assert lt.lib().lt_status_str(lt.LT_ERR_TOO_LARGE) == b"request exceeds the static workspace"
 
@@ -455,3 +455,21 @@ def test_static_workspace_rejects_tables_that_do_not_fit():
         lt.LT_ERR_INVALID_ARG
     assert L.lt_stream_fused_lz4_int4_static(C.byref(t), fake, None, 1, 30, 30, fake, None, None) == \
         lt.LT_ERR_INVALID_ARG
+
+
+def test_order_chunks_starts_the_largest_first():
+    """The launch order is a permutation of the chunks by decreasing decoded
+    size, chunks of one size in table order."""
+    rng = np.random.default_rng(8)
+    n = 500
+    sizes = rng.choice([16384, 65536, 262144], n)
+    dst_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.uint64)
+    order = lt.order_chunks(dst_off)
+    assert sorted(order.tolist()) == list(range(n))
+    assert order.tolist() == sorted(range(n), key=lambda i: (-int(sizes[i]), i))
+    assert lt.order_chunks(np.zeros(1, np.uint64)).size == 0
+    assert lt.order_chunks(np.arange(0, 5 * 65536, 65536, dtype=np.uint64)).tolist() == [0, 1, 2, 3]
+    bad = dst_off.copy()
+    bad[3] = bad[5]
+    with pytest.raises(lt.LtError):
+        lt.order_chunks(bad)

@@ -90,12 +90,20 @@ def _fault_caught(fault, blk, expect, idx, hlog, dmax, seeds):
 
 
 def test_model_catches_planted_mistakes():
-    w = synth.mlp_int4_small(rows=8)
-    packed = lt.pack_int4(w.codes)[:65536]
-    blk = O.lz4_compress(packed)
-    idx = lt.index_chunks(blk, np.array([0, blk.size], np.uint64))[1]
+    """Each planted protocol mistake is caught on some schedule (each case
+    pairs a history class with a window its blocks keep to)."""
+    w = synth.mlp_int4_small(rows=64)
+    packed = lt.pack_int4(w.codes)
+    p64, p256 = packed[:65536], packed[:262144]
+    b64, o64 = lt.compress_chunks(p64, np.array([0, p64.size], np.uint64), max_dist=lt.PACK_WINDOW)
+    i64 = lt.index_chunks(b64, o64)[1]
     for fault in ("no_window", "early_need"):
-        assert _fault_caught(fault, blk, packed.tobytes(), idx, 14, 65535, 4) == 4, fault
+        assert _fault_caught(fault, b64, p64.tobytes(), i64, 14, lt.PACK_WINDOW, 4) >= 3, fault
+    # a slot reused while the tile that held it is still being written out
+    b256, o256 = lt.compress_chunks(p256, np.array([0, p256.size], np.uint64), max_dist=lt.PACK_WINDOW)
+    i256 = lt.index_chunks(b256, o256)[1]
+    assert _fault_caught("no_write_rule", b256, p256.tobytes(), i256, 14, lt.PACK_WINDOW, 10) >= 1
+    assert _fault_caught(None, b256, p256.tobytes(), i256, 14, lt.PACK_WINDOW, 3) == 0
     g, e = O.seqgen(5, 262144)
     gidx = lt.index_chunks(g, np.array([0, g.size], np.uint64))[1]
     assert _fault_caught("no_slot_rule", g, e.tobytes(), gidx, 16, 65535, 3) == 3

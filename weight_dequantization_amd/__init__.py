@@ -49,7 +49,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblt.so")
 
-ABI_VERSION = 11          # LT_ABI_VERSION of the library this binding speaks to
+ABI_VERSION = 12          # LT_ABI_VERSION of the library this binding speaks to
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE = range(6)
 STATIC_SCRATCH_BYTES = 32 << 20   # LT_STATIC_SCRATCH_BYTES
 (CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
@@ -78,7 +78,8 @@ class _Table(C.Structure):
                 ("n_chunks", C.c_uint32), ("max_chunk_bytes", C.c_uint32),
                 ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64),
                 ("max_dist", C.c_uint32), ("spin_limit", C.c_uint32),
-                ("seq_off", C.c_void_p), ("seq_pos", C.c_void_p), ("n_seq", C.c_uint64)]
+                ("seq_off", C.c_void_p), ("seq_pos", C.c_void_p), ("n_seq", C.c_uint64),
+                ("order", C.c_void_p)]
 
 
 class _ZrTensor(C.Structure):
@@ -124,6 +125,7 @@ def _lib():
             "lt_compress_chunks": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
             "lt_compress_chunks_greedy": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
             "lt_index_chunks": (i32, [vp, vp, u32, vp, vp, u64, i32]),
+            "lt_order_chunks": (i32, [vp, u32, vp]),
             "lt_status_str": (C.c_char_p, [i32]),
             "lt_abi_version": (i32, []),
         }
@@ -230,6 +232,18 @@ def index_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0):
     return seq_off, seq_pos[:int(seq_off[-1])]
 
 
+def order_chunks(dst_off: np.ndarray) -> np.ndarray:
+    """A table's launch order (uint32 [n]): chunks by decreasing decoded
+    size, chunks of one size in table order."""
+    dst_off = np.ascontiguousarray(dst_off, np.uint64)
+    n = dst_off.size - 1
+    order = np.zeros(max(n, 1), np.uint32)
+    st = _lib().lt_order_chunks(_np_ptr(dst_off), max(n, 0), _np_ptr(order))
+    if st != LT_OK:
+        raise LtError(st, "lt_order_chunks")
+    return order[:n]
+
+
 # --------------------------------------------------------------- device side
 
 def _torch():
@@ -273,13 +287,15 @@ class ChunkTable:
     n_seq: int = 0
     host_dst_off: object = None   # numpy uint64 [n+1], kept for chunk-range calls
     spin_limit: int = 0     # polls per decoder wave before a wait gives up (0: the library's default)
+    order: object = None    # torch.int32 [n] (read as uint32): launch order, or None: table order
 
     @classmethod
     def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
-                  max_dist: int = 0, index: bool = False, pin: bool = False):
+                  max_dist: int = 0, index: bool = False, pin: bool = False, order: bool = False):
         """Place a host-built table on `device`; with device="cpu" and
         pin=True the arrays go to pinned host memory, the form the streamed
-        entry points read."""
+        entry points read.  index adds the sequence index, order the launch
+        order (order_chunks) when the chunks differ in size."""
         comp_off = np.ascontiguousarray(comp_off, np.uint64)
         dst_off = np.ascontiguousarray(dst_off, np.uint64)
         n = dst_off.size - 1
@@ -295,6 +311,8 @@ class ChunkTable:
         if index and n > 0:
             seq_off, seq_pos = index_chunks(comp, comp_off)
             t.set_index(seq_off, seq_pos, device, pin)
+        if order and n > 0 and np.unique(sizes).size > 1:   # one size: table order already
+            t.order = _place(order_chunks(dst_off).view(np.int32), device, pin)
         return t
 
     def set_index(self, seq_off: np.ndarray, seq_pos: np.ndarray, device=None, pin: bool = None):
@@ -327,17 +345,19 @@ class ChunkTable:
 
     @classmethod
     def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0,
-              max_dist: int = None, index: bool = True, pin: bool = False, greedy: bool = False):
+              max_dist: int = None, index: bool = True, pin: bool = False, greedy: bool = False,
+              order: bool = True):
         """Compress `src` chunk by chunk on the host and upload the table.  By
         default matches stay within PACK_WINDOW bytes, which the table
         declares, so the device decoder keeps a short history per chunk, and
         the table carries the sequence index, so each chunk's sequences are
-        parsed side by side.  greedy=True packs with the plain greedy parse
+        parsed side by side, and a launch order that starts the largest
+        chunks first.  greedy=True packs with the plain greedy parse
         (compress_chunks)."""
         if max_dist is None:
             max_dist = PACK_WINDOW
         comp, comp_off = compress_chunks(src, dst_off, threads, max_dist, greedy)
-        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin)
+        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin, order)
 
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
@@ -345,7 +365,8 @@ class ChunkTable:
                       self.max_dist, self.spin_limit,
                       self.seq_off.data_ptr() if self.seq_off is not None else None,
                       self.seq_pos.data_ptr() if self.seq_pos is not None else None,
-                      self.n_seq if self.seq_off is not None else 0)
+                      self.n_seq if self.seq_off is not None else 0,
+                      self.order.data_ptr() if self.order is not None else None)
 
 
 def _check(st, where):

@@ -306,6 +306,7 @@ lt::ChunkParams make_params(const lt_chunk_table *t, void *out, int32_t *chunk_s
   P.gemv_y = nullptr;
   P.cols = 0;
   P.spin = t->spin_limit ? t->spin_limit : lt::SPIN_DEFAULT;
+  P.order = t->order;
   return P;
 }
 
@@ -410,6 +411,7 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
     // the device copies from chunk c on, compressed offsets counted from
     // the batch's first byte
     lt::ChunkParams P = make_params(t, out, chunk_status ? chunk_status + c : nullptr, scales, zp, group);
+    P.order = nullptr;   // batches are decoded in table order
     P.comp = p_comp;
     P.comp_off = m_coff + c;
     P.dst_off = m_doff + c;
@@ -517,6 +519,7 @@ lt_status range_common(int mode, const lt_chunk_table *t, const uint16_t *scales
   }
   if (count == 0) return LT_OK;
   lt::ChunkParams P = make_params(t, (void *)((uintptr_t)out - scale * dst_first), chunk_status, scales, zp, group);
+  P.order = nullptr;   // a range is decoded in table order
   P.comp_off = t->comp_off + first;
   P.dst_off = t->dst_off + first;
   if (t->seq_off) P.seq_off = t->seq_off + first;

@@ -70,9 +70,14 @@
 //   nrec, cov    recorder -> builders: records written and the decoded bytes
 //                                      they cover, published as one 8-byte word
 //   bk[b]        builder  -> recorder: first record builder b still reads
-//   next_tile[b] builder  -> builders: the tile builder b holds (all ones
-//                                      once it has left); every tile below
-//                                      the smallest of these is final
+//   built[b]     builder  -> builders: the tile builder b holds, moved on
+//                                      as soon as that tile's history bytes
+//                                      are final; every tile below the
+//                                      smallest of these is built
+//   next_tile[b] builder  -> builders: the same, moved on only after the
+//                                      tile's write-out (which reads its
+//                                      history slot) as well; all ones once
+//                                      b has left
 //   tile_ctr     builders          : the next tile nobody has taken
 //   pstate       recorder -> all     : running / done / failed
 // Every wait ends, by the argument below; as a backstop against a protocol
@@ -89,11 +94,13 @@
 // needs: the record ring holds more records than one tile can overlap, and
 // decoded chunks are at most 1 MiB, so a length field's extra bytes (about
 // 1/255 of the length) fit in the input ring beside the oldest tile's
-// literals.  A tile overwrites the history slot of the tile one ring length
-// back, so its builder first waits until every tile that may read that slot
-// is final: with a declared window of w bytes (r = ceil(w / 1 KiB) tiles)
-// that stays short of the ring, the tiles up to r places after the old
-// one; otherwise every earlier tile.
+// literals.  A tile's copies read only built tiles; its write-out is not on
+// that path, so the next tile's build can start while it runs.  A tile
+// overwrites the history slot of the tile one ring length back, so its
+// builder first waits until the old tile's write-out is done and every tile
+// that may read that slot is built: with a declared window of w bytes
+// (r = ceil(w / 1 KiB) tiles) that stays short of the ring, the tiles up to
+// r places after the old one; otherwise every earlier tile.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -110,7 +117,7 @@ constexpr uint32_t TILE = 1024;       // build / write-out unit (bytes of decode
 // builder waits for the tile's coverage, so the ring holds more than 258;
 // beyond that, a longer ring lets the walker run further ahead of the
 // builders on blocks of many short sequences.  (Four workgroups must fit
-// in one CU's LDS with the 16 KiB history, which bounds it: 40,848 bytes
+// in one CU's LDS with the 16 KiB history, which bounds it: 40,880 bytes
 // each.)
 constexpr uint32_t RING = 368;
 constexpr int NB = 5;                 // builder waves
@@ -156,6 +163,7 @@ struct __attribute__((aligned(16))) Ctl {
   uint32_t need[NSLOT];       // first input byte still read: [0] walker, [1 + b] builder b
   uint32_t bk[NSLOT];         // builder b: first record it may still read
   uint32_t next_tile[NSLOT];  // builder b: its next tile (all ones once it has left)
+  uint32_t built[NSLOT];      // builder b: its first tile whose history bytes are not final
   uint32_t in_avail;          // feeder: input bytes present in the ring
   uint32_t pstate;            // recorder: running / done / failed
   uint32_t nrec;              // recorder: records written ...
@@ -186,6 +194,9 @@ struct Smem {
   uint4 recs[RING];
   uint4 chain[CHAIN];
 };
+
+// four workgroups of the 16 KiB-history class share one CU's 160 KiB of LDS
+static_assert(sizeof(Smem<14>) + sizeof(Ctl) <= 160u * 1024u / 4u, "LDS per workgroup");
 
 struct ChunkParams {
   const uint8_t *comp;
@@ -218,6 +229,7 @@ struct ChunkParams {
   float *gemv_y;             // fp32 [rows]
   uint64_t cols;
   uint32_t spin;             // polls each wave may make per chunk (>= 1)
+  const uint32_t *order;     // workgroup k decodes chunk order[k] (NULL: chunk k)
 };
 
 // ------------------------------------------------------------ LDS sync
@@ -1579,7 +1591,8 @@ struct Builder {
   uint32_t nrec;       // cached ctl.nrec
   uint32_t cov;        // cached ctl.cov
   uint32_t avail;      // cached ctl.in_avail
-  uint32_t done;       // cached: tiles below this are final
+  uint32_t done;       // cached: tiles below this are built
+  uint32_t fdone;      // cached: tiles below this are built and written out
   uint32_t need_pub;   // announced in need[1 + b]
 
   __device__ void refresh() {
@@ -1601,10 +1614,13 @@ struct Builder {
   }
 
   // wait until tiles [0, tiles) are final; false if the chunk failed first
-  __device__ __forceinline__ bool wait_done(uint32_t tiles) {
-    while (done < tiles) {
-      done = min8(ctl.next_tile);
-      if (done >= tiles) break;
+  // Wait until the tiles below `tiles` are built and those below `written`
+  // are written out too; false if the chunk failed first.
+  __device__ __forceinline__ bool wait_done(uint32_t tiles, uint32_t written) {
+    while (done < tiles || fdone < written) {
+      done = min8(ctl.built);
+      fdone = min8(ctl.next_tile);
+      if (done >= tiles && fdone >= written) break;
       if (lds_get(&ctl.pstate) == ST_FAIL) return false;
       __builtin_amdgcn_s_sleep(SLEEP_DONE);
     }
@@ -2025,11 +2041,14 @@ struct Builder {
       u = grab_take(uv);
       // tiles before this one that are read
       uint32_t need_tiles = (src_need + TILE - 1) / TILE;
+      uint32_t written = 0;
       if (t >= HTILES) {
-        // This tile overwrites the ring slot of tile t - HTILES, whose bytes
-        // only tiles up to t - HTILES + reach read (a match reaches at most
-        // reach tiles back): those must be final first.  When that bound
-        // does not stay short of this tile, wait for every earlier tile;
+        // This tile overwrites the ring slot of tile t - HTILES, whose
+        // write-out reads it and whose bytes only tiles up to
+        // t - HTILES + reach read (a match reaches at most reach tiles
+        // back): the first must be written out and those built first.  When
+        // that bound does not stay short of this tile, wait for every
+        // earlier tile;
         // and since sources up to a ring length back then share this tile's
         // own slot, build it sequence by sequence (every such source lies
         // ahead of the bytes written so far) rather than in passes that
@@ -2043,13 +2062,17 @@ struct Builder {
           need_tiles = t;
         }
       }
-      if (!wait_done(need_tiles)) break;
+      if (t >= HTILES) written = t - HTILES + 1;
+      if (!wait_done(need_tiles, written)) break;
       if (hard) {
         if (!tile_exact(T, Tend)) break;
       } else {
         if (!need_input(in_end)) break;
         tile_bulk(T, Tend, rv, re, m, extra);
       }
+      // the tile's history bytes are final: tiles that copy from it may
+      // start while it is written out
+      lds_set(&ctl.built[b], u, lane);
       if constexpr (G) {
         cur.s[0] = cug.s;
         cur.z[0] = cug.z;
@@ -2071,6 +2094,7 @@ struct Builder {
     }
     lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
     lds_set(&ctl.bk[b], 0xFFFFFFFFu, lane);
+    lds_set(&ctl.built[b], 0xFFFFFFFFu, lane);
     lds_set(&ctl.next_tile[b], 0xFFFFFFFFu, lane);
     if (lane == 0) __hip_atomic_fetch_add(&ctl.nfinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
@@ -2082,7 +2106,11 @@ template <int MODE, int HLOG>
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) chunk_kernel(ChunkParams P) {
   __shared__ __attribute__((aligned(16))) Smem<HLOG> sm;
   __shared__ Ctl ctl;
-  const uint32_t i = blockIdx.x;
+  uint32_t i = blockIdx.x;
+  if (P.order) {
+    i = __builtin_amdgcn_readfirstlane(P.order[i]);
+    if (i >= P.n) return;   // the whole workgroup, before any barrier
+  }
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const uint32_t lane = tid & 63;
@@ -2121,6 +2149,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     ctl.need[tid] = tid <= nb ? 0u : 0xFFFFFFFFu;
     ctl.bk[tid] = tid < nb ? 0u : 0xFFFFFFFFu;
     ctl.next_tile[tid] = tid < nb ? tid : 0xFFFFFFFFu;
+    ctl.built[tid] = tid < nb ? tid : 0xFFFFFFFFu;
   }
   if (tid == 0) {
     ctl.in_avail = 0;
@@ -2158,7 +2187,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   } else if (wave == 2) {
     feeder(sm, ctl, lane, S, y_end, nb, P.spin);
   } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
-    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0};
+    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
     B.run();
   }
   __syncthreads();

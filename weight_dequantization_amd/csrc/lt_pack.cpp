@@ -292,6 +292,20 @@ lt_status lt_compress_chunks_greedy(const uint8_t *src, const uint64_t *dst_off,
   return compress_chunks<true>(src, dst_off, n_chunks, comp, comp_cap, comp_off, threads, max_dist);
 }
 
+lt_status lt_order_chunks(const uint64_t *dst_off, uint32_t n_chunks, uint32_t *order) {
+  if (n_chunks == 0) return LT_OK;
+  if (!dst_off || !order) return LT_ERR_INVALID_ARG;
+  for (uint32_t i = 0; i < n_chunks; i++)
+    if (dst_off[i + 1] < dst_off[i]) return LT_ERR_INVALID_ARG;
+  // largest decoded size first; equal sizes keep table order (neighbouring
+  // chunks then run side by side, as without an order)
+  for (uint32_t i = 0; i < n_chunks; i++) order[i] = i;
+  std::stable_sort(order, order + n_chunks, [&](uint32_t a, uint32_t b) {
+    return dst_off[a + 1] - dst_off[a] > dst_off[b + 1] - dst_off[b];
+  });
+  return LT_OK;
+}
+
 lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks,
                           uint64_t *seq_off, uint32_t *seq_pos, uint64_t seq_cap, int threads) {
   if (!comp_off || !seq_off) return LT_ERR_INVALID_ARG;
