@@ -87,6 +87,8 @@ def lib():
             "ltref_zr_encode": (u64, [vp, u64, vp, vp, vp]),
             "ltref_zr_decode": (None, [vp, vp, vp, u64, u64, vp, vp]),
             "ltref_crc32_chunks": (None, [vp, vp, u32, vp]),
+            "ltref_xxh3_64": (C.c_uint64, [vp, u64]),
+            "ltref_xxh3_chunks": (None, [vp, vp, u32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -276,6 +278,25 @@ def fused_int4_chunked(t: Table, scales, zp, group: int, out: np.ndarray, thread
                                          t.n, t.total, _p(scales), _p(zp), group, _p(out),
                                          _p(status), threads)
     return int(bad), status[:t.n]
+
+
+# ----------------------------------------------------------------- XXH3-64
+
+def xxh3_64(data) -> int:
+    """XXH3 64-bit hash (seed 0, default secret) of a byte buffer."""
+    a = _c(np.frombuffer(bytes(data), np.uint8) if isinstance(data, (bytes, bytearray)) else data, np.uint8)
+    return int(lib().ltref_xxh3_64(_p(a) if a.size else None, a.size))
+
+
+def xxh3_chunks(comp: np.ndarray, comp_off: np.ndarray) -> np.ndarray:
+    """One XXH3-64 per chunk over its compressed bytes, uint64 [n]."""
+    comp = _c(comp, np.uint8)
+    comp_off = _c(comp_off, np.uint64)
+    n = comp_off.size - 1
+    out = np.zeros(max(n, 1), np.uint64)
+    if n > 0:
+        lib().ltref_xxh3_chunks(_p(comp), _p(comp_off), n, _p(out))
+    return out[:n]
 
 
 # ----------------------------------------------------------------- CRC-32

@@ -587,6 +587,148 @@ void ltref_crc32_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t 
   for (uint32_t i = 0; i < n; i++) crc[i] = ltref_crc32(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
 }
 
+/* ---------------------------------------------------------------- XXH3-64 */
+
+/* XXH3, 64-bit result, seed 0, the default 192-byte secret: the block
+ * checksum named by the roadmap's container format (page "GPU Compression
+ * Pipeline - TDD Roadmap", Phase 6.1 HCT Format V2).  The pages only name
+ * it; the steps below follow the public XXH3 definition, one input-length
+ * class at a time, with arithmetic modulo 2^64 and the 128-bit products
+ * taken whole. */
+static const uint8_t XXH_SECRET[192] = {
+  0xb8, 0xfe, 0x6c, 0x39, 0x23, 0xa4, 0x4b, 0xbe, 0x7c, 0x01, 0x81, 0x2c, 0xf7, 0x21, 0xad, 0x1c,
+  0xde, 0xd4, 0x6d, 0xe9, 0x83, 0x90, 0x97, 0xdb, 0x72, 0x40, 0xa4, 0xa4, 0xb7, 0xb3, 0x67, 0x1f,
+  0xcb, 0x79, 0xe6, 0x4e, 0xcc, 0xc0, 0xe5, 0x78, 0x82, 0x5a, 0xd0, 0x7d, 0xcc, 0xff, 0x72, 0x21,
+  0xb8, 0x08, 0x46, 0x74, 0xf7, 0x43, 0x24, 0x8e, 0xe0, 0x35, 0x90, 0xe6, 0x81, 0x3a, 0x26, 0x4c,
+  0x3c, 0x28, 0x52, 0xbb, 0x91, 0xc3, 0x00, 0xcb, 0x88, 0xd0, 0x65, 0x8b, 0x1b, 0x53, 0x2e, 0xa3,
+  0x71, 0x64, 0x48, 0x97, 0xa2, 0x0d, 0xf9, 0x4e, 0x38, 0x19, 0xef, 0x46, 0xa9, 0xde, 0xac, 0xd8,
+  0xa8, 0xfa, 0x76, 0x3f, 0xe3, 0x9c, 0x34, 0x3f, 0xf9, 0xdc, 0xbb, 0xc7, 0xc7, 0x0b, 0x4f, 0x1d,
+  0x8a, 0x51, 0xe0, 0x4b, 0xcd, 0xb4, 0x59, 0x31, 0xc8, 0x9f, 0x7e, 0xc9, 0xd9, 0x78, 0x73, 0x64,
+  0xea, 0xc5, 0xac, 0x83, 0x34, 0xd3, 0xeb, 0xc3, 0xc5, 0x81, 0xa0, 0xff, 0xfa, 0x13, 0x63, 0xeb,
+  0x17, 0x0d, 0xdd, 0x51, 0xb7, 0xf0, 0xda, 0x49, 0xd3, 0x16, 0x55, 0x26, 0x29, 0xd4, 0x68, 0x9e,
+  0x2b, 0x16, 0xbe, 0x58, 0x7d, 0x47, 0xa1, 0xfc, 0x8f, 0xf8, 0xb8, 0xd1, 0x7a, 0xd0, 0x31, 0xce,
+  0x45, 0xcb, 0x3a, 0x8f, 0x95, 0x16, 0x04, 0x28, 0xaf, 0xd7, 0xfb, 0xca, 0xbb, 0x4b, 0x40, 0x7e,
+};
+static const uint64_t XP32_1 = 0x9E3779B1u, XP32_2 = 0x85EBCA77u, XP32_3 = 0xC2B2AE3Du;
+static const uint64_t XP64_1 = 0x9E3779B185EBCA87ull, XP64_2 = 0xC2B2AE3D27D4EB4Full,
+                      XP64_3 = 0x165667B19E3779F9ull, XP64_4 = 0x85EBCA77C2B2AE63ull,
+                      XP64_5 = 0x27D4EB2F165667C5ull;
+
+static uint64_t x_rd64(const uint8_t *p) {
+  uint64_t v = 0;
+  for (int k = 7; k >= 0; k--) v = (v << 8) | p[k];
+  return v;
+}
+static uint32_t x_rd32(const uint8_t *p) { return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24); }
+static uint64_t x_rotl(uint64_t v, int r) { return (v << r) | (v >> (64 - r)); }
+static uint64_t x_swap64(uint64_t v) {
+  uint64_t r = 0;
+  for (int k = 0; k < 8; k++) r = (r << 8) | ((v >> (8 * k)) & 0xFF);
+  return r;
+}
+/* the 128-bit product of a and b, its two halves XORed together */
+static uint64_t x_fold(uint64_t a, uint64_t b) {
+  const unsigned __int128 m = (unsigned __int128)a * b;
+  return (uint64_t)m ^ (uint64_t)(m >> 64);
+}
+/* final mixes: the one XXH64 ends with, and XXH3's own */
+static uint64_t x_avalanche64(uint64_t h) {
+  h ^= h >> 33;
+  h *= XP64_2;
+  h ^= h >> 29;
+  h *= XP64_3;
+  return h ^ (h >> 32);
+}
+static uint64_t x_avalanche3(uint64_t h) {
+  h ^= h >> 37;
+  h *= 0x165667919E3779F9ull;
+  return h ^ (h >> 32);
+}
+static uint64_t x_mix16(const uint8_t *in, const uint8_t *sec) {
+  return x_fold(x_rd64(in) ^ x_rd64(sec), x_rd64(in + 8) ^ x_rd64(sec + 8));
+}
+
+/* one 64-byte stripe into the eight accumulators */
+static void x_stripe(uint64_t acc[8], const uint8_t *in, const uint8_t *sec) {
+  for (int i = 0; i < 8; i++) {
+    const uint64_t v = x_rd64(in + 8 * i);
+    const uint64_t k = v ^ x_rd64(sec + 8 * i);
+    acc[i ^ 1] += v;
+    acc[i] += (k & 0xFFFFFFFFu) * (k >> 32);
+  }
+}
+static void x_scramble(uint64_t acc[8], const uint8_t *sec) {
+  for (int i = 0; i < 8; i++) {
+    uint64_t a = acc[i];
+    a ^= a >> 47;
+    a ^= x_rd64(sec + 8 * i);
+    acc[i] = a * XP32_1;
+  }
+}
+
+uint64_t ltref_xxh3_64(const uint8_t *in, uint64_t n) {
+  const uint8_t *sec = XXH_SECRET;
+  if (n == 0) return x_avalanche64(x_rd64(sec + 56) ^ x_rd64(sec + 64));
+  if (n <= 3) {
+    const uint32_t c = ((uint32_t)in[0] << 16) | ((uint32_t)in[n >> 1] << 24) | (uint32_t)in[n - 1] | ((uint32_t)n << 8);
+    const uint64_t flip = (uint64_t)(x_rd32(sec) ^ x_rd32(sec + 4));
+    return x_avalanche64((uint64_t)c ^ flip);
+  }
+  if (n <= 8) {
+    const uint64_t flip = x_rd64(sec + 8) ^ x_rd64(sec + 16);
+    const uint64_t v = (uint64_t)x_rd32(in + n - 4) + ((uint64_t)x_rd32(in) << 32);
+    uint64_t h = v ^ flip;
+    h ^= x_rotl(h, 49) ^ x_rotl(h, 24);
+    h *= 0x9FB21C651E98DF25ull;
+    h ^= (h >> 35) + n;
+    h *= 0x9FB21C651E98DF25ull;
+    return h ^ (h >> 28);
+  }
+  if (n <= 16) {
+    const uint64_t lo = x_rd64(in) ^ (x_rd64(sec + 24) ^ x_rd64(sec + 32));
+    const uint64_t hi = x_rd64(in + n - 8) ^ (x_rd64(sec + 40) ^ x_rd64(sec + 48));
+    return x_avalanche3(n + x_swap64(lo) + hi + x_fold(lo, hi));
+  }
+  if (n <= 128) {
+    uint64_t acc = n * XP64_1;
+    /* pairs of 16-byte pieces from both ends, inward */
+    const uint64_t pairs = (n - 1) / 32;   /* 0 .. 3: how many extra pairs */
+    for (uint64_t j = pairs + 1; j-- > 0;) {
+      acc += x_mix16(in + 16 * j, sec + 32 * j);
+      acc += x_mix16(in + n - 16 * (j + 1), sec + 32 * j + 16);
+    }
+    return x_avalanche3(acc);
+  }
+  if (n <= 240) {
+    uint64_t acc = n * XP64_1;
+    for (uint64_t j = 0; j < 8; j++) acc += x_mix16(in + 16 * j, sec + 16 * j);
+    acc = x_avalanche3(acc);
+    for (uint64_t j = 8; j < n / 16; j++) acc += x_mix16(in + 16 * j, sec + 16 * (j - 8) + 3);
+    acc += x_mix16(in + n - 16, sec + 136 - 17);
+    return x_avalanche3(acc);
+  }
+  /* long inputs: blocks of 16 stripes (1024 bytes), each followed by a
+   * scramble; then the last block's whole stripes, the input's last 64
+   * bytes as one more stripe, and the merge of the accumulators */
+  uint64_t acc[8] = {XP32_3, XP64_1, XP64_2, XP64_3, XP64_4, XP32_2, XP64_5, XP32_1};
+  const uint64_t nblocks = (n - 1) / 1024;
+  for (uint64_t b = 0; b < nblocks; b++) {
+    for (uint64_t s = 0; s < 16; s++) x_stripe(acc, in + 1024 * b + 64 * s, sec + 8 * s);
+    x_scramble(acc, sec + 192 - 64);
+  }
+  const uint64_t nstripes = ((n - 1) - 1024 * nblocks) / 64;
+  for (uint64_t s = 0; s < nstripes; s++) x_stripe(acc, in + 1024 * nblocks + 64 * s, sec + 8 * s);
+  x_stripe(acc, in + n - 64, sec + 192 - 64 - 7);
+  uint64_t h = n * XP64_1;
+  for (int i = 0; i < 4; i++) h += x_fold(acc[2 * i] ^ x_rd64(sec + 11 + 16 * i), acc[2 * i + 1] ^ x_rd64(sec + 11 + 16 * i + 8));
+  return x_avalanche3(h);
+}
+
+/* One XXH3-64 per chunk over comp[comp_off[i] .. comp_off[i+1]). */
+void ltref_xxh3_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n, uint64_t *h) {
+  for (uint32_t i = 0; i < n; i++) h[i] = ltref_xxh3_64(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
+}
+
 /* ------------------------------------------------------------ zero runs */
 
 /* Block b covers elements [1024 b, min(1024 (b + 1), n)).  Bit k of bitmap
