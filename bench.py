@@ -179,6 +179,31 @@ def plain_lz4_forms(torch, lt, packed, comp, comp_off, w, scales, zp, dev, out_r
     return res, bad_total
 
 
+def checked_form(torch, lt, comp, comp_off, w, scales, zp, dev, out_ref, scratch, stream, steps):
+    """The headline table with each chunk's XXH3-64 stored: every launch
+    hashes the compressed bytes as the decoder stages them and checks them
+    (no second pass over HBM).  Timed like the headline; the output is
+    compared bit for bit with the headline's and every status must be OK."""
+    n_elem = w.rows * w.cols
+    tb = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev, lt.PACK_WINDOW, index=True, checksum=True)
+    status = torch.full((tb.n_chunks,), -1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(out_ref)
+
+    def fn():
+        lt.fused_lz4_int4(tb, scales, zp, (w.rows, w.cols), w.group, out=out, status=status)
+    fn()
+    torch.cuda.synchronize()
+    lt.check_status(status)
+    bad = int((out.view(torch.int16) != out_ref.view(torch.int16)).sum().item())
+    ms, _ = timed_launches(torch, fn, steps, scratch, stream)
+    lt.check_status(status)
+    alg = tb.comp_bytes + 2 * n_elem
+    kern = float(np.mean(ms))
+    return {"kernel_ms": round(kern, 5), "GBps": round(alg / kern / 1e6, 2),
+            "frac": round(alg / kern / 1e6 / HBM_PEAK_GBS, 4), "checksum_bytes": 8 * tb.n_chunks,
+            "mismatches_vs_headline": bad}, bad
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +325,10 @@ def bench_int4_layer(args) -> int:
         plain, bad_plain = plain_lz4_forms(torch, lt, packed, comp, comp_off, w, scales, zp, dev, out, scratch,
                                            stream, max(5, args.steps // 5))
         result["plain_lz4"] = plain
+        checked, bad_checked = checked_form(torch, lt, comp, comp_off, w, scales, zp, dev, out, scratch, stream,
+                                            max(10, args.steps // 2))
+        result["checksum_in_decode"] = checked
+        bad_plain += bad_checked
     if args.calib_copy:
         src = torch.empty(2 * n_elem, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -615,7 +644,7 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "fill_fp16_GBps": round(2 * n_elem / ms_fill / 1e6, 1),
         "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
         "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),
-        "verify_crc32": verify_measurement(torch, lt, w, packed, dev, timed),
+        "verify_xxh3": verify_measurement(torch, lt, w, packed, dev, timed),
         "activations_4096x14336": activation_measurements(torch, lt, dev, timed),
         "gemv": gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed),
     }
@@ -705,12 +734,13 @@ def activation_measurements(torch, lt, dev, timed):
 
 
 def verify_measurement(torch, lt, w, packed, dev, timed):
-    """lt_verify_chunks (CRC-32 of every chunk's compressed bytes against the
-    stored values) on the same table, as GB/s of compressed bytes."""
+    """lt_verify_chunks (XXH3-64 of every chunk's compressed bytes against the
+    stored values, without decoding) on the same table, as GB/s of
+    compressed bytes."""
     comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
     table = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev)
-    expect = torch.from_numpy(lt.checksum_chunks(comp, comp_off).view(np.int32)).to(dev)
-    got = torch.empty(table.n_chunks, dtype=torch.int32, device=dev)
+    expect = torch.from_numpy(lt.checksum_chunks(comp, comp_off).view(np.int64)).to(dev)
+    got = torch.empty(table.n_chunks, dtype=torch.int64, device=dev)
     status = torch.empty(table.n_chunks, dtype=torch.int32, device=dev)
     ms = timed(lambda: lt.verify_chunks(table, expect, got, status))
     lt.check_status(status)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 12
+#define LT_ABI_VERSION 13
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -66,7 +66,7 @@ enum {
   LT_CHUNK_OVERRUN = 3,       /* a sequence would write past the chunk end */
   LT_CHUNK_SIZE_MISMATCH = 4, /* block decoded to fewer bytes than the chunk */
   LT_CHUNK_BAD_TABLE = 5,     /* the chunk's table entries are inconsistent */
-  LT_CHUNK_CHECKSUM = 6,      /* lt_verify_chunks: stored bytes do not match their CRC-32 */
+  LT_CHUNK_CHECKSUM = 6,      /* the stored bytes do not match their XXH3-64 (see xxh, lt_verify_chunks) */
   LT_CHUNK_STALLED = 7        /* a wait inside the decoder polled past its bound (see spin_limit) */
 };
 
@@ -124,6 +124,17 @@ enum {
  *              chunks differ in size start the largest first
  *              (lt_order_chunks).  Chunk-range and streamed calls decode in
  *              table order and ignore it.
+ *   xxh        DEVICE uint64[n_chunks] or NULL: the expected XXH3-64 (seed 0)
+ *              of each chunk's compressed bytes comp[comp_off[i] ..
+ *              comp_off[i+1]), as lt_checksum_chunks computes it (the block
+ *              checksum of page "GPU Compression Pipeline - TDD Roadmap",
+ *              Phase 6.1).  When given, every decode call hashes each chunk's
+ *              bytes as it stages them for the decoder (no second pass over
+ *              HBM), streams every chunk whole, and reports
+ *              LT_CHUNK_CHECKSUM for a chunk whose hash differs, whatever its
+ *              decode gave; that chunk's output range then holds unspecified
+ *              bytes.  Range and streamed calls check their chunks too (the
+ *              streamed calls copy xxh with the offsets).
  * The index lets a chunk's sequences be parsed side by side instead of one
  * after another (lt_index_chunks builds it from the blocks).  It is checked
  * against the blocks: a listed sequence that does not end where the next
@@ -148,6 +159,7 @@ typedef struct lt_chunk_table {
   const uint32_t *seq_pos;
   uint64_t n_seq;
   const uint32_t *order;
+  const uint64_t *xxh;
 } lt_chunk_table;
 
 /*
@@ -304,16 +316,16 @@ typedef struct lt_zr_tensor {
 lt_status lt_decode_zero_runs(const lt_zr_tensor *z, uint16_t *out, int32_t *block_status, void *stream);
 
 /*
- * lt_verify_chunks -- per-chunk CRC-32 of the compressed bytes on the
- * device, to validate stored blocks before they are decoded (the block
- * checksum of the roadmap's container validation, "GPU Compression
- * Pipeline - TDD Roadmap", Phase 6.1: a flipped stored byte must be
- * reported as a checksum mismatch).  CRC-32 is the IEEE 802.3 / zlib CRC:
- * polynomial 0x04C11DB7 bit-reflected, initial value and final XOR
- * 0xFFFFFFFF; chunk i covers t->comp[comp_off[i] .. comp_off[i+1]).
- *   expect        DEVICE uint32 [n_chunks] stored checksums, or NULL
+ * lt_verify_chunks -- per-chunk XXH3-64 (seed 0, the default secret) of the
+ * compressed bytes on the device, without decoding (the container check of
+ * page "GPU Compression Pipeline - TDD Roadmap", Phase 6.1: a changed stored
+ * byte must be reported as a checksum mismatch); chunk i covers
+ * t->comp[comp_off[i] .. comp_off[i+1]).  Decode calls check the same value
+ * on the fly when the table carries xxh; this call checks a table without
+ * decoding it.
+ *   expect        DEVICE uint64 [n_chunks] stored checksums, or NULL
  *                 (compute only)
- *   got           DEVICE uint32 [n_chunks], receives the computed values, or
+ *   got           DEVICE uint64 [n_chunks], receives the computed values, or
  *                 NULL
  *   chunk_status  DEVICE int32 [n_chunks]: LT_CHUNK_OK, LT_CHUNK_CHECKSUM
  *                 when expect[i] differs, LT_CHUNK_BAD_TABLE for offsets
@@ -321,7 +333,7 @@ lt_status lt_decode_zero_runs(const lt_zr_tensor *z, uint16_t *out, int32_t *blo
  * Only comp, comp_off and comp_bytes of the table are read.  The host
  * packer's lt_checksum_chunks computes the stored values.
  */
-lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint32_t *got, int32_t *chunk_status,
+lt_status lt_verify_chunks(const lt_chunk_table *t, const uint64_t *expect, uint64_t *got, int32_t *chunk_status,
                            void *stream);
 
 /*
@@ -399,10 +411,10 @@ lt_status lt_stream_fused_lz4_int4_static(const lt_chunk_table *host_table, cons
 lt_status lt_encode_zero_runs(const uint16_t *x, uint64_t n, uint32_t *bitmap, uint64_t *val_off, uint16_t *vals,
                               uint64_t vals_cap, int threads);
 
-/* CRC-32 of each chunk's compressed bytes (as lt_verify_chunks computes
- * them on the device), on up to `threads` host threads (0: all).  crc has
- * n_chunks entries. */
-lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint32_t *crc,
+/* XXH3-64 (seed 0, the default secret) of each chunk's compressed bytes, as
+ * lt_verify_chunks and the decode calls compute them on the device, on up
+ * to `threads` host threads (0: all).  xxh has n_chunks entries. */
+lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint64_t *xxh,
                              int threads);
 
 /* The order field of a table (HOST arrays): order (uint32[n_chunks])

@@ -23,8 +23,9 @@ What it computes (every function is the plain definition, written from):
 * zero-run coding of fp16 activations (per 1024-element block a nonzero bitmap,
   then the nonzero values in order): the pages' zero-run encoding of ReLU
   outputs, in the bitmap form the GPU decoder reads.
-* CRC-32 of each chunk's compressed bytes, bit by bit from the polynomial: the
-  per-block checksum of the roadmap's container validation (Phase 6.1).
+* XXH3-64 of each chunk's compressed bytes, from the hash's public
+  definition: the per-block checksum the roadmap's container format names
+  (Phase 6.1).
 """
 from __future__ import annotations
 
@@ -82,11 +83,9 @@ def lib():
             "ltref_fused_int8": (u32, [vp, u64, vp, vp, u32, u64, vp, vp, u64, u64, vp, vp, C.c_int]),
             "ltref_fused_int4_chunked": (u32, [vp, u64, vp, vp, u32, u64, vp, vp, u64, vp, vp, C.c_int]),
             "ltref_seqgen": (u64, [u64, u64, vp, u64, vp, u64, vp]),
-            "ltref_crc32": (u32, [vp, u64]),
             "ltref_dequant_int4_lut": (None, [vp, u64, vp, u64, vp]),
             "ltref_zr_encode": (u64, [vp, u64, vp, vp, vp]),
             "ltref_zr_decode": (None, [vp, vp, vp, u64, u64, vp, vp]),
-            "ltref_crc32_chunks": (None, [vp, vp, u32, vp]),
             "ltref_xxh3_64": (C.c_uint64, [vp, u64]),
             "ltref_xxh3_chunks": (None, [vp, vp, u32, vp]),
         }
@@ -297,25 +296,6 @@ def xxh3_chunks(comp: np.ndarray, comp_off: np.ndarray) -> np.ndarray:
     if n > 0:
         lib().ltref_xxh3_chunks(_p(comp), _p(comp_off), n, _p(out))
     return out[:n]
-
-
-# ----------------------------------------------------------------- CRC-32
-
-def crc32(data) -> int:
-    """CRC-32 (IEEE 802.3 / zlib polynomial) of a byte buffer, bit by bit."""
-    a = _c(np.frombuffer(bytes(data), np.uint8) if isinstance(data, (bytes, bytearray)) else data, np.uint8)
-    return int(lib().ltref_crc32(_p(a), a.size))
-
-
-def crc32_chunks(comp: np.ndarray, comp_off: np.ndarray) -> np.ndarray:
-    """One CRC-32 per chunk over its compressed bytes."""
-    comp = _c(comp, np.uint8)
-    comp_off = _c(comp_off, np.uint64)
-    n = comp_off.size - 1
-    out = np.zeros(max(n, 0), np.uint32)
-    if n > 0:
-        lib().ltref_crc32_chunks(_p(comp), _p(comp_off), n, _p(out))
-    return out
 
 
 # ------------------------------------------------------------- zero runs

@@ -35,11 +35,10 @@
  *     of 1024 elements a bitmap marks the nonzero elements, and the nonzero
  *     values follow in element order; element bits are compared, so -0.0
  *     counts as nonzero and the round trip is exact;
- *   - CRC-32 (the IEEE 802.3 / zlib polynomial, bit-reflected, initial value
- *     and final XOR all ones) of each chunk's compressed bytes, bit by bit
- *     from the polynomial division: the per-block checksum the roadmap's
- *     container validation asks for ("GPU Compression Pipeline - TDD
- *     Roadmap", Phase 6.1), in a form whose definition is the polynomial.
+ *   - XXH3-64 (seed 0, default secret) of each chunk's compressed bytes: the
+ *     per-block checksum the roadmap's container format names ("GPU
+ *     Compression Pipeline - TDD Roadmap", Phase 6.1), written from the
+ *     hash's public definition, one input-length class at a time.
  *
  * Floating point: the product (q - zp) * s has at most 19 significant bits, so
  * it is exact in fp64 (and in fp32); the only rounding is the final one to
@@ -562,29 +561,6 @@ uint64_t ltref_seqgen(uint64_t seed, uint64_t target, uint8_t *stream, uint64_t 
   free(lit);
   *out_len = op;
   return o;
-}
-
-/* ----------------------------------------------------------------- CRC-32 */
-
-/* CRC-32: the message, bits taken least significant first, times x^32, is
- * divided by x^32 + x^26 + x^23 + x^22 + x^16 + x^12 + x^11 + x^10 + x^8 +
- * x^7 + x^5 + x^4 + x^2 + x + 1; the register starts at all ones and the
- * remainder is complemented.  In the reflected register the polynomial's
- * low 32 coefficients read 0xEDB88320, and one step per message bit shifts
- * the register right, subtracting (XOR) the polynomial when the bit shifted
- * out is 1. */
-uint32_t ltref_crc32(const uint8_t *p, uint64_t n) {
-  uint32_t r = 0xFFFFFFFFu;
-  for (uint64_t i = 0; i < n; i++) {
-    r ^= p[i];
-    for (int b = 0; b < 8; b++) r = (r & 1u) ? (r >> 1) ^ 0xEDB88320u : (r >> 1);
-  }
-  return r ^ 0xFFFFFFFFu;
-}
-
-/* One CRC-32 per chunk over comp[comp_off[i] .. comp_off[i+1]). */
-void ltref_crc32_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n, uint32_t *crc) {
-  for (uint32_t i = 0; i < n; i++) crc[i] = ltref_crc32(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
 }
 
 /* ---------------------------------------------------------------- XXH3-64 */

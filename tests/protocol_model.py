@@ -26,8 +26,12 @@ It checks what the protocol must guarantee, at the moment of every access:
   - no interleaving deadlocks (a step bound far above the work);
 and at the end that the decoded chunk equals the expected bytes.
 
+With `checksum` one builder's wave hashes the compressed bytes instead (a
+reader that announces its position like the others) and the feeder streams
+every block to its end.
+
 `fault` plants one protocol mistake in the model (test of the model
-itself): "no_window" (the feeder ignores the readers' bound), "early_need"
+itself): "hasher_silent" (the hasher never announces its position), "no_window" (the feeder ignores the readers' bound), "early_need"
 (a builder releases its tile's input before building it), "no_slot_rule"
 (a builder skips the history-slot reuse wait), "no_write_rule" (a
 builder overwrites a slot without waiting for the old tile's write-out),
@@ -106,8 +110,10 @@ def parse_block(blk):
 class Chunk:
     """One chunk's decode under the protocol, with a seeded schedule."""
 
-    def __init__(self, blk, n_out, index=None, hlog=14, dmax=65535, head=0, seed=0, builders=None, fault=None):
+    def __init__(self, blk, n_out, index=None, hlog=14, dmax=65535, head=0, seed=0, builders=None, fault=None,
+                 checksum=False):
         self.fault = fault
+        self.checksum = checksum
         self.blk = bytes(blk)
         self.N = n_out
         self.hlog = hlog
@@ -120,7 +126,7 @@ class Chunk:
         self.stream = bytes(head) + self.blk          # the 16-byte aligned blocks the feeder reads
         self.index = None if index is None else [head + int(v) for v in index]
         self.direct = self.index is not None and len(self.index) > 0
-        self.nb = (builders if builders is not None else 5) + (1 if self.direct else 0)
+        self.nb = (builders if builders is not None else 5) + (1 if self.direct else 0) - (1 if checksum else 0)
         self.rng = random.Random(seed)
         self.seqs, self.expect = parse_block(self.blk)
         assert len(self.expect) == n_out
@@ -128,7 +134,7 @@ class Chunk:
         self.nseg = (self.y_end + SEG - 1) // SEG
         # shared state (the Ctl counters)
         self.in_avail = 0
-        self.need = [0 if i <= self.nb else FF for i in range(8)]
+        self.need = [0 if (i <= self.nb or (checksum and i == 7)) else FF for i in range(8)]
         self.bk = [0 if i < self.nb else FF for i in range(8)]
         self.next_tile = [i if i < self.nb else FF for i in range(8)]
         self.built_to = [i if i < self.nb else FF for i in range(8)]   # the kernel's built[]
@@ -201,7 +207,7 @@ class Chunk:
                 if landed == self.nseg:
                     break
                 yield
-                if self.nfinished == self.nb and self.need[0] == FF:
+                if not self.checksum and self.nfinished == self.nb and self.need[0] == FF:
                     break
                 used = min(self.need)
                 yield
@@ -569,6 +575,35 @@ class Chunk:
         self.pstate = ST_DONE if final == 0 else ST_FAIL
         yield
 
+    def hasher(self):
+        """With checksums: hashes whole 1 KiB blocks of the compressed bytes in
+        order as they land (two at a time when both have), announcing in
+        need[7] the first byte it still reads; then the tail (the last
+        partial block and the last 64 bytes)."""
+        head, n = self.head, len(self.blk)
+        hblocks = (n - 1) // 1024 if n > 240 else 0
+        tail = min(1024 * hblocks, n - 64) if n > 240 else 0
+        hb = avail = 0
+        while hb < hblocks:
+            while avail < head + 1024 * (hb + 1):
+                avail = self.in_avail
+                yield
+            while hb < hblocks and head + 1024 * (hb + 1) <= avail:
+                k = 2 if hb + 1 < hblocks and head + 1024 * (hb + 2) <= avail else 1
+                self.read_input(head + 1024 * hb, head + 1024 * (hb + k), "hasher")
+                hb += k
+                yield
+            if self.fault != "hasher_silent":
+                self.need[7] = head + (1024 * hb if hb < hblocks else tail)
+            yield
+        while avail < self.y_end:
+            avail = self.in_avail
+            yield
+        self.read_input(head + tail, self.y_end, "hasher tail")
+        self.hashed = True
+        self.need[7] = FF
+        yield
+
     def builder(self, b):
         k = 0
         nrec = cov = 0
@@ -763,6 +798,9 @@ class Chunk:
         if not self.direct:
             roles["recorder"] = self.recorder()
             builders = list(range(self.nb))
+        if self.checksum:   # one builder wave fewer (nb counts it already)
+            roles["hasher"] = self.hasher()
+            self.hashed = False
         for b in builders:
             roles["builder %d" % b] = self.builder(b)
         # uneven speeds: each role gets a random weight

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 12
+    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 13
     assert lt.lib().lt_status_str(1) == b"invalid argument"
     assert lt.lib().lt_status_str(lt.LT_ERR_TOO_LARGE) == b"request exceeds the static workspace"
 
@@ -343,22 +343,29 @@ def test_range_arguments_rejected_without_gpu():
 
 
 def test_checksum_chunks_matches_oracle():
-    """The host packer's per-chunk CRC-32 equals the oracle's (bit by bit from
-    the polynomial), on packer blocks and on arbitrary byte ranges."""
+    """The host packer's per-chunk XXH3-64 equals the oracle's (and the
+    xxhash package's), on packer blocks and on arbitrary byte ranges that
+    cover every length class of the hash."""
     w = synth.int4_weight(64, 4096, 128, 6, chunking="mixed")
     comp, comp_off = lt.compress_chunks(lt.pack_int4(w.codes), w.dst_off)
-    assert np.array_equal(lt.checksum_chunks(comp, comp_off), O.crc32_chunks(comp, comp_off))
+    assert np.array_equal(lt.checksum_chunks(comp, comp_off), O.xxh3_chunks(comp, comp_off))
     rng = np.random.default_rng(3)
-    buf = rng.integers(0, 256, 100000, dtype=np.uint8)
-    cuts = np.sort(rng.integers(0, buf.size, 60)).astype(np.uint64)
-    off = np.concatenate([[0], cuts, cuts[-1:], [buf.size]]).astype(np.uint64)   # includes an empty chunk
-    assert np.array_equal(lt.checksum_chunks(buf, off, threads=3), O.crc32_chunks(buf, off))
+    buf = rng.integers(0, 256, 200000, dtype=np.uint8)
+    lens = [0, 1, 2, 3, 4, 7, 8, 9, 16, 17, 32, 33, 64, 65, 96, 97, 128, 129, 240, 241, 1024, 1025, 1088, 5000]
+    lens += list(rng.integers(0, 3000, 60))
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.uint64)
+    assert off[-1] <= buf.size
+    got = lt.checksum_chunks(buf, off, threads=3)
+    assert np.array_equal(got, O.xxh3_chunks(buf, off))
+    xxhash = pytest.importorskip("xxhash")
+    for i in range(len(lens)):
+        assert int(got[i]) == xxhash.xxh3_64_intdigest(buf[int(off[i]):int(off[i + 1])].tobytes())
     L = lt.lib()
     V = C.c_void_p
     ptr = lambda a: a.ctypes.data_as(V)
-    crc = np.zeros(2, np.uint32)
-    assert L.lt_checksum_chunks(ptr(buf), ptr(np.array([5, 1, 9], np.uint64)), 2, ptr(crc), 1) == lt.LT_ERR_INVALID_ARG
-    assert L.lt_checksum_chunks(ptr(buf), None, 2, ptr(crc), 1) == lt.LT_ERR_INVALID_ARG
+    h = np.zeros(2, np.uint64)
+    assert L.lt_checksum_chunks(ptr(buf), ptr(np.array([5, 1, 9], np.uint64)), 2, ptr(h), 1) == lt.LT_ERR_INVALID_ARG
+    assert L.lt_checksum_chunks(ptr(buf), None, 2, ptr(h), 1) == lt.LT_ERR_INVALID_ARG
 
 
 def test_verify_arguments_rejected_without_gpu():

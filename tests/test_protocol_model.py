@@ -113,3 +113,38 @@ def test_model_catches_planted_mistakes():
     db = O.lz4_compress(d)
     assert _fault_caught("no_split", db, d.tobytes(), None, 16, 65535, 2) == 2
     assert _fault_caught(None, db, d.tobytes(), None, 16, 65535, 2) == 0
+
+
+def test_checksum_hasher():
+    """With checksums the hasher reads every compressed byte once it has
+    landed and before it is reloaded, on indexed and walked layer blocks,
+    activation stress blocks and long generated streams; a hasher that
+    never announces its position is caught."""
+    w = synth.mlp_int4_small(rows=64)
+    packed = lt.pack_int4(w.codes)
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    a = synth.activation(1024, 8192, 1104)
+    acomp, aoff = lt.compress_chunks(a.data, a.dst_off, max_dist=lt.PACK_WINDOW)
+    g, e = O.seqgen(77, 262144)
+    cases = [(comp, comp_off, w.dst_off, packed, [0, 3], 14, lt.PACK_WINDOW),
+             (acomp, aoff, a.dst_off, a.data, a.stress["random"][:1] + a.stress["ab_run"][:1], 14, lt.PACK_WINDOW),
+             (g, np.array([0, g.size], np.uint64), np.array([0, e.size], np.uint64), e, [0], 16, 65535)]
+    for cb, co, do, src, picks, hlog, dmax in cases:
+        for i, blk, expect, idx in _chunks(cb, co, do, src, picks):
+            for seed in (1,):
+                for indexed in (True, False):
+                    c = Chunk(blk, len(expect), index=idx if indexed else None, hlog=hlog, dmax=dmax, seed=seed,
+                              checksum=True)
+                    st, out, _ = c.run()
+                    assert st == 0 and out == expect and c.hashed, (i, seed, indexed)
+    b = comp[int(comp_off[0]):int(comp_off[1])]
+    caught = 0
+    for seed in range(6):
+        c = Chunk(b, int(w.dst_off[1]), index=None, hlog=14, dmax=lt.PACK_WINDOW, seed=seed, checksum=True,
+                  fault="hasher_silent")
+        try:
+            c.run()
+        except ProtocolError:
+            caught += 1
+            break
+    assert caught >= 1

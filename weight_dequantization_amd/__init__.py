@@ -49,7 +49,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblt.so")
 
-ABI_VERSION = 12          # LT_ABI_VERSION of the library this binding speaks to
+ABI_VERSION = 13          # LT_ABI_VERSION of the library this binding speaks to
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE = range(6)
 STATIC_SCRATCH_BYTES = 32 << 20   # LT_STATIC_SCRATCH_BYTES
 (CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
@@ -79,7 +79,7 @@ class _Table(C.Structure):
                 ("total_bytes", C.c_uint64), ("comp_bytes", C.c_uint64),
                 ("max_dist", C.c_uint32), ("spin_limit", C.c_uint32),
                 ("seq_off", C.c_void_p), ("seq_pos", C.c_void_p), ("n_seq", C.c_uint64),
-                ("order", C.c_void_p)]
+                ("order", C.c_void_p), ("xxh", C.c_void_p)]
 
 
 class _ZrTensor(C.Structure):
@@ -183,15 +183,15 @@ def compress_chunks(src: np.ndarray, dst_off: np.ndarray, threads: int = 0, max_
 
 
 def checksum_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0) -> np.ndarray:
-    """CRC-32 (zlib's) of each chunk's compressed bytes, uint32 [n]."""
+    """XXH3-64 (seed 0) of each chunk's compressed bytes, uint64 [n]."""
     comp = np.ascontiguousarray(comp, dtype=np.uint8)
     comp_off = np.ascontiguousarray(comp_off, dtype=np.uint64)
     n = comp_off.size - 1
-    crc = np.zeros(max(n, 1), np.uint32)
-    st = _lib().lt_checksum_chunks(_np_ptr(comp), _np_ptr(comp_off), max(n, 0), _np_ptr(crc), threads)
+    xxh = np.zeros(max(n, 1), np.uint64)
+    st = _lib().lt_checksum_chunks(_np_ptr(comp), _np_ptr(comp_off), max(n, 0), _np_ptr(xxh), threads)
     if st != LT_OK:
         raise LtError(st, "lt_checksum_chunks")
-    return crc[:max(n, 0)]
+    return xxh[:max(n, 0)]
 
 
 def encode_zero_runs(x: np.ndarray, threads: int = 0):
@@ -288,14 +288,17 @@ class ChunkTable:
     host_dst_off: object = None   # numpy uint64 [n+1], kept for chunk-range calls
     spin_limit: int = 0     # polls per decoder wave before a wait gives up (0: the library's default)
     order: object = None    # torch.int32 [n] (read as uint32): launch order, or None: table order
+    xxh: object = None      # torch.int64 [n] (read as uint64): expected XXH3-64 per chunk, or None: unchecked
 
     @classmethod
     def from_host(cls, comp: np.ndarray, comp_off: np.ndarray, dst_off: np.ndarray, device="cuda",
-                  max_dist: int = 0, index: bool = False, pin: bool = False, order: bool = False):
+                  max_dist: int = 0, index: bool = False, pin: bool = False, order: bool = False,
+                  checksum: bool = False):
         """Place a host-built table on `device`; with device="cpu" and
         pin=True the arrays go to pinned host memory, the form the streamed
         entry points read.  index adds the sequence index, order the launch
-        order (order_chunks) when the chunks differ in size."""
+        order (order_chunks) when the chunks differ in size, checksum each
+        chunk's XXH3-64 (checksum_chunks), which every decode then checks."""
         comp_off = np.ascontiguousarray(comp_off, np.uint64)
         dst_off = np.ascontiguousarray(dst_off, np.uint64)
         n = dst_off.size - 1
@@ -313,6 +316,8 @@ class ChunkTable:
             t.set_index(seq_off, seq_pos, device, pin)
         if order and n > 0 and np.unique(sizes).size > 1:   # one size: table order already
             t.order = _place(order_chunks(dst_off).view(np.int32), device, pin)
+        if checksum and n > 0:
+            t.xxh = _place(checksum_chunks(comp, comp_off).view(np.int64), device, pin)
         return t
 
     def set_index(self, seq_off: np.ndarray, seq_pos: np.ndarray, device=None, pin: bool = None):
@@ -328,8 +333,8 @@ class ChunkTable:
         self.seq_pos = _place(seq_pos.view(np.int32), device, pin)
 
     def staging_bytes(self, chunks_per_half: int = 512) -> int:
-        """A staging size for the streamed entry points: the table's offsets
-        and index, then two halves that each hold the compressed bytes of
+        """A staging size for the streamed entry points: the table's offsets,
+        checksums and index, then two halves that each hold the compressed bytes of
         the largest `chunks_per_half` consecutive chunks (the library's
         layout: every piece rounded up to 256 bytes)."""
         up = lambda x: (x + 255) // 256 * 256
@@ -339,6 +344,8 @@ class ChunkTable:
         k = max(1, min(int(chunks_per_half), n))
         co = self.comp_off.cpu().numpy().astype(np.int64)
         meta = 2 * up(8 * (n + 1))
+        if self.xxh is not None:
+            meta += up(8 * n)
         if self.seq_off is not None:
             meta += up(8 * (n + 1)) + up(4 * int(self.seq_off[-1]))
         return meta + 2 * up(int(np.max(co[k:] - co[:-k])) + 16)
@@ -346,18 +353,19 @@ class ChunkTable:
     @classmethod
     def build(cls, src: np.ndarray, dst_off: np.ndarray, device="cuda", threads: int = 0,
               max_dist: int = None, index: bool = True, pin: bool = False, greedy: bool = False,
-              order: bool = True):
+              order: bool = True, checksum: bool = False):
         """Compress `src` chunk by chunk on the host and upload the table.  By
         default matches stay within PACK_WINDOW bytes, which the table
         declares, so the device decoder keeps a short history per chunk, and
         the table carries the sequence index, so each chunk's sequences are
         parsed side by side, and a launch order that starts the largest
         chunks first.  greedy=True packs with the plain greedy parse
-        (compress_chunks)."""
+        (compress_chunks); checksum=True stores each chunk's XXH3-64, which
+        every decode of the table then checks."""
         if max_dist is None:
             max_dist = PACK_WINDOW
         comp, comp_off = compress_chunks(src, dst_off, threads, max_dist, greedy)
-        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin, order)
+        return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin, order, checksum)
 
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
@@ -366,7 +374,8 @@ class ChunkTable:
                       self.seq_off.data_ptr() if self.seq_off is not None else None,
                       self.seq_pos.data_ptr() if self.seq_pos is not None else None,
                       self.n_seq if self.seq_off is not None else 0,
-                      self.order.data_ptr() if self.order is not None else None)
+                      self.order.data_ptr() if self.order is not None else None,
+                      self.xxh.data_ptr() if self.xxh is not None else None)
 
 
 def _check(st, where):
@@ -513,13 +522,14 @@ def decode_zero_runs(z: ZeroRunTensor, out=None, status=None, stream=None):
 # --------------------------------------------------------------- checksums
 
 def verify_chunks(table: ChunkTable, expect=None, got=None, status=None, stream=None):
-    """CRC-32 of each chunk's compressed bytes on the device.  With `expect`
-    (device uint32/int32 [n], as checksum_chunks computes) each chunk's
-    status is CHUNK_OK or CHUNK_CHECKSUM; returns (got, status)."""
+    """XXH3-64 of each chunk's compressed bytes on the device, without
+    decoding.  With `expect` (device int64 [n], the uint64 values
+    checksum_chunks computes) each chunk's status is CHUNK_OK or
+    CHUNK_CHECKSUM; returns (got, status)."""
     torch = _torch()
     dev = table.comp.device
     if got is None:
-        got = torch.empty(max(table.n_chunks, 1), dtype=torch.int32, device=dev)
+        got = torch.empty(max(table.n_chunks, 1), dtype=torch.int64, device=dev)
     if status is None and expect is not None:
         status = torch.empty(max(table.n_chunks, 1), dtype=torch.int32, device=dev)
     t = table.as_c()

@@ -14,7 +14,7 @@
 #include "lt.h"
 #include "lt_device.hpp"
 #include "lt_lz4.hpp"
-#include "lt_crc.hpp"
+#include "lt_verify.hpp"
 #include "lt_zr.hpp"
 
 namespace lt {
@@ -307,6 +307,7 @@ lt::ChunkParams make_params(const lt_chunk_table *t, void *out, int32_t *chunk_s
   P.cols = 0;
   P.spin = t->spin_limit ? t->spin_limit : lt::SPIN_DEFAULT;
   P.order = t->order;
+  P.xxh = t->xxh;
   return P;
 }
 
@@ -321,13 +322,14 @@ lt_status launch_chunks(int mode, const lt_chunk_table *t, void *out, int32_t *c
 constexpr uint64_t kAlign = 256;
 uint64_t up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
-// Staging layout for a host table t: first the whole table's offsets and
-// sequence index (copied once, before the first batch), then two halves
-// that take the compressed bytes of alternate batches.  Every piece starts
+// Staging layout for a host table t: first the whole table's offsets,
+// checksums and sequence index (copied once, before the first batch), then
+// two halves that take the compressed bytes of alternate batches.  Every piece starts
 // on a 256-byte boundary.
 uint64_t meta_bytes(const lt_chunk_table *t) {
   const uint64_t n = t->n_chunks;
   uint64_t b = 2 * up(8 * (n + 1));
+  if (t->xxh) b += up(8 * n);
   if (t->seq_off) b += up(8 * (n + 1)) + up(4 * t->seq_off[n]);
   return b;
 }
@@ -368,8 +370,11 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   const bool one = cs == ds;
   uint64_t *m_coff = (uint64_t *)staging;
   uint64_t *m_doff = (uint64_t *)(staging + up(8 * (n + 1)));
-  uint64_t *m_soff = (uint64_t *)(staging + 2 * up(8 * (n + 1)));
-  uint32_t *m_spos = (uint32_t *)(staging + 3 * up(8 * (n + 1)));
+  uint8_t *m_rest = staging + 2 * up(8 * (n + 1));
+  uint64_t *m_xxh = t->xxh ? (uint64_t *)m_rest : nullptr;
+  if (t->xxh) m_rest += up(8 * n);
+  uint64_t *m_soff = (uint64_t *)m_rest;
+  uint32_t *m_spos = (uint32_t *)(m_rest + up(8 * (n + 1)));
   const uint64_t ns = t->seq_off ? t->seq_off[n] : 0;
   hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, start = nullptr;
   lt_status st = LT_OK;
@@ -387,6 +392,7 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   if (st == LT_OK) {
     bool ok = hipMemcpyAsync(m_coff, t->comp_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess &&
               hipMemcpyAsync(m_doff, t->dst_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess;
+    if (ok && t->xxh) ok = hipMemcpyAsync(m_xxh, t->xxh, 8 * n, hipMemcpyHostToDevice, cs) == hipSuccess;
     if (ok && t->seq_off)
       ok = hipMemcpyAsync(m_soff, t->seq_off, 8 * (n + 1), hipMemcpyHostToDevice, cs) == hipSuccess &&
            (ns == 0 || hipMemcpyAsync(m_spos, t->seq_pos, 4 * ns, hipMemcpyHostToDevice, cs) == hipSuccess);
@@ -412,6 +418,7 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
     // the batch's first byte
     lt::ChunkParams P = make_params(t, out, chunk_status ? chunk_status + c : nullptr, scales, zp, group);
     P.order = nullptr;   // batches are decoded in table order
+    P.xxh = m_xxh ? m_xxh + c : nullptr;
     P.comp = p_comp;
     P.comp_off = m_coff + c;
     P.dst_off = m_doff + c;
@@ -520,6 +527,7 @@ lt_status range_common(int mode, const lt_chunk_table *t, const uint16_t *scales
   if (count == 0) return LT_OK;
   lt::ChunkParams P = make_params(t, (void *)((uintptr_t)out - scale * dst_first), chunk_status, scales, zp, group);
   P.order = nullptr;   // a range is decoded in table order
+  if (t->xxh) P.xxh = t->xxh + first;
   P.comp_off = t->comp_off + first;
   P.dst_off = t->dst_off + first;
   if (t->seq_off) P.seq_off = t->seq_off + first;
@@ -700,13 +708,13 @@ lt_status lt_decode_zero_runs(const lt_zr_tensor *z, uint16_t *out, int32_t *blo
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
 
-lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint32_t *got, int32_t *chunk_status,
+lt_status lt_verify_chunks(const lt_chunk_table *t, const uint64_t *expect, uint64_t *got, int32_t *chunk_status,
                            void *stream) {
   if (!table_ok(t)) return LT_ERR_INVALID_ARG;
   if (!got && !chunk_status) return LT_ERR_INVALID_ARG;   // nothing to report into
   if (expect && !chunk_status) return LT_ERR_INVALID_ARG;
   if (t->n_chunks == 0) return LT_OK;
-  lt::CrcParams P;
+  lt::XxhParams P;
   P.comp = t->comp;
   P.comp_off = t->comp_off;
   P.comp_bytes = t->comp_bytes;
@@ -714,7 +722,8 @@ lt_status lt_verify_chunks(const lt_chunk_table *t, const uint32_t *expect, uint
   P.expect = expect;
   P.got = got;
   P.status = chunk_status;
-  hipLaunchKernelGGL(lt::crc_kernel, dim3(t->n_chunks), dim3(lt::CRC_THREADS), 0, (hipStream_t)stream, P);
+  const uint32_t grid = (t->n_chunks + lt::XXH_WAVES - 1) / lt::XXH_WAVES;
+  hipLaunchKernelGGL(lt::xxh_kernel, dim3(grid), dim3(64 * lt::XXH_WAVES), 0, (hipStream_t)stream, P);
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
 

@@ -106,6 +106,7 @@
 #include <stdint.h>
 
 #include "lt_device.hpp"
+#include "lt_xxh.hpp"
 
 namespace lt {
 
@@ -174,6 +175,7 @@ struct __attribute__((aligned(16))) Ctl {
   uint32_t tile_ctr;          // builders: the next tile nobody has taken
   int32_t status;
   uint32_t stall;             // any wave: a bounded wait gave up (the chunk fails with C_STALL)
+  uint32_t xbad;              // feeder: the block's bytes do not match their checksum
 };
 
 // The history ring holds 2^HLOG decoded bytes: 64 KiB for any LZ4 block
@@ -230,6 +232,7 @@ struct ChunkParams {
   uint64_t cols;
   uint32_t spin;             // polls each wave may make per chunk (>= 1)
   const uint32_t *order;     // workgroup k decodes chunk order[k] (NULL: chunk k)
+  const uint64_t *xxh;       // expected XXH3-64 of each chunk's compressed bytes (NULL: not checked)
 };
 
 // ------------------------------------------------------------ LDS sync
@@ -1285,16 +1288,33 @@ __device__ __forceinline__ uint32_t land_and_bound_k(uint32_t k, const uint32_t 
   }
 }
 
+// 8 input bytes from ring position pos (any alignment) as a little-endian
+// word; every lane's pos has the same alignment
+template <class SM>
+__device__ __forceinline__ uint64_t ring8(const SM &sm, uint32_t pos) {
+  constexpr uint32_t WM = SM::IMASK >> 2;
+  const uint32_t *R = (const uint32_t *)sm.inr;
+  const uint32_t w = pos >> 2, sh = pos & 3;
+  uint32_t x0 = R[w & WM], x1 = R[(w + 1) & WM];
+  if (sh) {
+    const uint32_t x2 = R[(w + 2) & WM];
+    x0 = __builtin_amdgcn_alignbyte(x1, x0, sh);
+    x1 = __builtin_amdgcn_alignbyte(x2, x1, sh);
+  }
+  return ((uint64_t)x1 << 32) | x0;
+}
+
 // Wave 2.  Streams the chunk's 16-byte aligned blocks into the input ring,
 // one 1 KiB segment (one LDS-DMA load per lane) at a time, keeping up to QMAX
 // segments in flight within the ring space that every reader has released.
 // Each landed segment costs one LDS round trip, overlapped with the wait for
 // the segment: the readers' bound is read while the segment is in flight,
 // and the exit check (every reader gone: a failed chunk) is made only when
-// nothing is in flight.
+// nothing is in flight.  With a checksum (`whole`) the block is streamed to
+// its end in any case, for the hasher.
 template <class SM>
 __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb,
-                                       uint32_t spin) {
+                                       uint32_t spin, bool whole) {
   constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
   static_assert(QMAX <= 16, "land_and_bound_k waits for up to 15 loads in flight");
   const uint32_t nblk = (y_end + 15) / 16;
@@ -1314,7 +1334,7 @@ __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const ui
       if (landed == nseg) break;
       // the window is closed and nothing is in flight: nobody reads input
       // once the walk has ended and every builder has left
-      if (lds_get_asm(&ctl.nfinished) == nb && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
+      if (!whole && lds_get_asm(&ctl.nfinished) == nb && lds_get_asm(&ctl.need[0]) == 0xFFFFFFFFu) break;
       const uint32_t used = min8(ctl.need);
       limit = used / SEG + QMAX;
       if (limit > nseg) limit = nseg;
@@ -1332,6 +1352,65 @@ __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const ui
     if (limit > nseg) limit = nseg;
   }
   wait_vm<0>();   // no LDS-DMA write outlives this wave
+}
+
+// The hasher (a table with checksums): XXH3-64 of the chunk's compressed
+// bytes, read from the input ring as the feeder lands them, whole 1 KiB
+// blocks in order (two at a time when both have landed).  It is one more
+// reader of the ring: need[HSLOT] holds the first byte it still reads, so
+// the feeder reloads no slot before it is hashed.  A hash that differs from
+// `want` marks the chunk (ctl.xbad); the hasher gives up only when a wave
+// has stalled or its own polls run out.
+constexpr uint32_t HSLOT = NSLOT - 1;
+template <class SM>
+__device__ __forceinline__ void hasher(SM &sm, Ctl &ctl, uint32_t lane, uint32_t head, uint32_t y_end, uint64_t want,
+                                       uint32_t spin) {
+  constexpr uint32_t IMASK = SM::IMASK;
+  const uint32_t n = y_end - head;   // the chunk's compressed bytes
+  const uint32_t hblocks = n > xxh::SHORT_MAX ? (n - 1) / xxh::BLOCK : 0u;
+  const uint32_t tail = n > xxh::SHORT_MAX ? min(xxh::BLOCK * hblocks, n - 64) : 0u;
+  xxh::Wave H;
+  H.init(lane);
+  uint32_t hb = 0, avail = 0;
+  auto wait_for = [&](uint32_t upto) -> bool {
+    while (avail < upto) {
+      avail = lds_get(&ctl.in_avail);
+      if (avail >= upto) break;
+      if (lds_get(&ctl.stall) || !spin_ok(spin, ctl)) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+  };
+  bool ok = true;
+  while (ok && hb < hblocks) {
+    ok = wait_for(head + xxh::BLOCK * (hb + 1));
+    while (ok && hb < hblocks && head + xxh::BLOCK * (hb + 1) <= avail) {
+      const uint32_t q = head + xxh::BLOCK * hb + 8 * lane;
+      if (hb + 1 < hblocks && head + xxh::BLOCK * (hb + 2) <= avail) {
+        H.block2(ring8(sm, q), ring8(sm, q + 512), ring8(sm, q + xxh::BLOCK), ring8(sm, q + xxh::BLOCK + 512));
+        hb += 2;
+      } else {
+        H.block(ring8(sm, q), ring8(sm, q + 512));
+        hb++;
+      }
+    }
+    lds_set(&ctl.need[HSLOT], head + (hb < hblocks ? xxh::BLOCK * hb : tail), lane);
+  }
+  if (ok) ok = wait_for(y_end);
+  if (ok) {
+    uint64_t h;
+    if (n <= xxh::SHORT_MAX) {
+      h = xxh::short_hash(n, [&](uint32_t k) { return (uint32_t)sm.inr[(head + k) & IMASK]; });
+    } else {
+      const uint32_t ns = ((n - 1) - xxh::BLOCK * hblocks) / 64;   // whole stripes of the last block
+      const uint32_t q = head + xxh::BLOCK * hblocks + 8 * lane;
+      H.partial(ring8(sm, q), ring8(sm, q + 512), lane, ns);
+      H.last(ring8(sm, head + n - 64 + 8 * (lane & 7)), lane);
+      h = H.merge(n);
+    }
+    if (h != want) lds_set(&ctl.xbad, 1u, lane);
+  }
+  lds_set(&ctl.need[HSLOT], 0xFFFFFFFFu, lane);
 }
 
 // ------------------------------------------------------------ write-out
@@ -2144,9 +2223,13 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   // with a sequence index the walker makes the records itself and wave 1
   // becomes one more builder
   const bool direct = P.seq_pos != nullptr && s1 > s0;
-  const uint32_t nb = (uint32_t)NB + (direct ? 1u : 0u);
+  // With checksums one builder wave hashes instead: wave 1 with an index
+  // (six builders become five), wave 7 without (five become four).
+  const bool check = P.xxh != nullptr;
+  const uint32_t nb = (uint32_t)NB + (direct ? 1u : 0u) - (check ? 1u : 0u);
+  const uint32_t hwave = check ? (direct ? 1u : 7u) : 0xFFFFFFFFu;
   if (tid < NSLOT) {
-    ctl.need[tid] = tid <= nb ? 0u : 0xFFFFFFFFu;
+    ctl.need[tid] = (tid <= nb || (check && tid == HSLOT)) ? 0u : 0xFFFFFFFFu;
     ctl.bk[tid] = tid < nb ? 0u : 0xFFFFFFFFu;
     ctl.next_tile[tid] = tid < nb ? tid : 0xFFFFFFFFu;
     ctl.built[tid] = tid < nb ? tid : 0xFFFFFFFFu;
@@ -2162,6 +2245,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     ctl.tile_ctr = nb;
     ctl.status = 0;
     ctl.stall = 0;
+    ctl.xbad = 0;
   }
   __syncthreads();
 
@@ -2185,13 +2269,17 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     if (lane == 0) ctl.status = st;
     lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
   } else if (wave == 2) {
-    feeder(sm, ctl, lane, S, y_end, nb, P.spin);
+    feeder(sm, ctl, lane, S, y_end, nb, P.spin, check);
+  } else if (wave == hwave) {
+    hasher(sm, ctl, lane, head, y_end, P.xxh[i], P.spin);
   } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
     Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
     B.run();
   }
   __syncthreads();
-  if (tid == 0 && P.status) P.status[i] = ctl.stall ? C_STALL : ctl.status;
+  // a stall first, then a checksum mismatch (the stored bytes are wrong,
+  // whatever their decode gave), then the decode's own status
+  if (tid == 0 && P.status) P.status[i] = ctl.stall ? C_STALL : ctl.xbad ? C_CHECKSUM : ctl.status;
 }
 
 }  // namespace lt

@@ -28,6 +28,7 @@
 #include <vector>
 
 #include "lt.h"
+#include "lt_xxh_secret.h"
 
 namespace {
 
@@ -187,32 +188,90 @@ void parallel_chunks(uint32_t n, int threads, F &&fn) {
   for (auto &th : pool) th.join();
 }
 
-// CRC-32 (IEEE 802.3 / zlib polynomial, reflected), eight bytes per step:
-// table k maps a byte to its register contribution when k zero bytes
-// follow it.
-struct CrcTables {
-  uint32_t t[8][256];
-  CrcTables() {
-    for (uint32_t v = 0; v < 256; v++) {
-      uint32_t c = v;
-      for (int b = 0; b < 8; b++) c = (c & 1u) ? (c >> 1) ^ 0xEDB88320u : c >> 1;
-      t[0][v] = c;
-    }
-    for (int k = 1; k < 8; k++)
-      for (uint32_t v = 0; v < 256; v++) t[k][v] = (t[k - 1][v] >> 8) ^ t[0][t[k - 1][v] & 255];
-  }
-};
+// XXH3-64 with seed 0 and the default secret (the hash's public
+// definition): the per-chunk checksum the device verifies.
+constexpr uint64_t kXSec[24] = {LT_XXH_SECRET_WORDS};
+constexpr uint64_t kXP64_1 = 0x9E3779B185EBCA87ull, kXP64_2 = 0xC2B2AE3D27D4EB4Full, kXP64_3 = 0x165667B19E3779F9ull;
 
-uint32_t crc32_bytes(const uint8_t *p, uint64_t n) {
-  static const CrcTables T;
-  uint32_t r = 0xFFFFFFFFu;
-  for (; n >= 8; n -= 8, p += 8) {
-    const uint32_t lo = r ^ rd32(p), hi = rd32(p + 4);
-    r = T.t[7][lo & 255] ^ T.t[6][(lo >> 8) & 255] ^ T.t[5][(lo >> 16) & 255] ^ T.t[4][lo >> 24] ^
-        T.t[3][hi & 255] ^ T.t[2][(hi >> 8) & 255] ^ T.t[1][(hi >> 16) & 255] ^ T.t[0][hi >> 24];
+inline uint64_t ld64(const uint8_t *p) {
+  uint64_t v;
+  memcpy(&v, p, 8);
+  return v;
+}
+inline uint32_t ld32(const uint8_t *p) { return rd32(p); }
+// secret bytes off .. off + 7
+inline uint64_t xsec(uint32_t off) {
+  const uint32_t w = off / 8, sh = (off % 8) * 8;
+  return sh ? (kXSec[w] >> sh) | (kXSec[w + 1] << (64 - sh)) : kXSec[w];
+}
+inline uint64_t xfold(uint64_t a, uint64_t b) {
+  const unsigned __int128 m = (unsigned __int128)a * b;
+  return (uint64_t)m ^ (uint64_t)(m >> 64);
+}
+inline uint64_t xfinish3(uint64_t h) {
+  h ^= h >> 37;
+  h *= 0x165667919E3779F9ull;
+  return h ^ (h >> 32);
+}
+inline uint64_t xfinish64(uint64_t h) {
+  h ^= h >> 33;
+  h *= kXP64_2;
+  h ^= h >> 29;
+  h *= kXP64_3;
+  return h ^ (h >> 32);
+}
+inline uint64_t xmix16(const uint8_t *p, uint32_t s) { return xfold(ld64(p) ^ xsec(s), ld64(p + 8) ^ xsec(s + 8)); }
+
+uint64_t xxh3_bytes(const uint8_t *p, uint64_t n) {
+  if (n == 0) return xfinish64(xsec(56) ^ xsec(64));
+  if (n <= 3) {
+    const uint64_t c = ((uint64_t)p[0] << 16) | ((uint64_t)p[n / 2] << 24) | p[n - 1] | (n << 8);
+    return xfinish64(c ^ (uint64_t)((uint32_t)xsec(0) ^ (uint32_t)xsec(4)));
   }
-  for (; n > 0; n--, p++) r = (r >> 8) ^ T.t[0][(r ^ *p) & 255];
-  return r ^ 0xFFFFFFFFu;
+  if (n <= 8) {
+    uint64_t h = ((uint64_t)ld32(p + n - 4) | ((uint64_t)ld32(p) << 32)) ^ xsec(8) ^ xsec(16);
+    h ^= ((h << 49) | (h >> 15)) ^ ((h << 24) | (h >> 40));
+    h *= 0x9FB21C651E98DF25ull;
+    h ^= (h >> 35) + n;
+    h *= 0x9FB21C651E98DF25ull;
+    return h ^ (h >> 28);
+  }
+  if (n <= 16) {
+    const uint64_t lo = ld64(p) ^ xsec(24) ^ xsec(32), hi = ld64(p + n - 8) ^ xsec(40) ^ xsec(48);
+    return xfinish3(n + __builtin_bswap64(lo) + hi + xfold(lo, hi));
+  }
+  uint64_t acc = n * kXP64_1;
+  if (n <= 128) {
+    for (uint64_t j = 0; 32 * j < n; j++) acc += xmix16(p + 16 * j, 32 * j) + xmix16(p + n - 16 * (j + 1), 32 * j + 16);
+    return xfinish3(acc);
+  }
+  if (n <= 240) {
+    for (uint64_t j = 0; j < 8; j++) acc += xmix16(p + 16 * j, 16 * j);
+    acc = xfinish3(acc);
+    for (uint64_t j = 8; j < n / 16; j++) acc += xmix16(p + 16 * j, 16 * (j - 8) + 3);
+    return xfinish3(acc + xmix16(p + n - 16, 119));
+  }
+  uint64_t a[8] = {0xC2B2AE3Dull, kXP64_1, kXP64_2, kXP64_3, 0x85EBCA77C2B2AE63ull, 0x85EBCA77ull,
+                   0x27D4EB2F165667C5ull, 0x9E3779B1ull};
+  // stripe at q with secret words starting at byte s8
+  auto stripe = [&](const uint8_t *q, uint32_t s8) {
+    for (int i = 0; i < 8; i++) {
+      const uint64_t v = ld64(q + 8 * i), k = v ^ xsec(s8 + 8 * i);
+      a[i ^ 1] += v;
+      a[i] += (k & 0xFFFFFFFFull) * (k >> 32);
+    }
+  };
+  const uint64_t nblocks = (n - 1) / 1024;
+  for (uint64_t b = 0; b < nblocks; b++) {
+    for (uint32_t s = 0; s < 16; s++) stripe(p + 1024 * b + 64 * s, 8 * s);
+    for (int i = 0; i < 8; i++) a[i] = (a[i] ^ (a[i] >> 47) ^ kXSec[16 + i]) * 0x9E3779B1ull;
+  }
+  const uint64_t tail = 1024 * nblocks;
+  for (uint32_t s = 0; s < ((n - 1) - tail) / 64; s++) stripe(p + tail + 64 * s, 8 * s);
+  stripe(p + n - 64, 121);
+  uint64_t h = n * kXP64_1;
+  for (int i = 0; i < 4; i++) h += xfold(a[2 * i] ^ xsec(11 + 16 * i), a[2 * i + 1] ^ xsec(19 + 16 * i));
+  return xfinish3(h);
 }
 
 }  // namespace
@@ -363,15 +422,15 @@ lt_status lt_encode_zero_runs(const uint16_t *x, uint64_t n, uint32_t *bitmap, u
   return LT_OK;
 }
 
-lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint32_t *crc,
+lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks, uint64_t *xxh,
                              int threads) {
-  if (!comp_off || !crc) return LT_ERR_INVALID_ARG;
+  if (!comp_off || !xxh) return LT_ERR_INVALID_ARG;
   if (n_chunks == 0) return LT_OK;
   if (!comp) return LT_ERR_INVALID_ARG;
   for (uint32_t i = 0; i < n_chunks; i++)
     if (comp_off[i + 1] < comp_off[i]) return LT_ERR_INVALID_ARG;
   parallel_chunks(n_chunks, threads, [&](uint32_t i) {
-    crc[i] = crc32_bytes(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
+    xxh[i] = xxh3_bytes(comp + comp_off[i], comp_off[i + 1] - comp_off[i]);
   });
   return LT_OK;
 }
