@@ -644,6 +644,7 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "fill_fp16_GBps": round(2 * n_elem / ms_fill / 1e6, 1),
         "copy_GBps": round(2 * 2 * n_elem / ms_copy / 1e6, 1),
         "streamed_from_host": streamed_measurements(torch, lt, w, packed, scales, zp, dev, out),
+        "streamed_from_file": file_measurements(torch, lt, w, packed, scales, zp, dev, out),
         "verify_xxh3": verify_measurement(torch, lt, w, packed, dev, timed),
         "activations_4096x14336": activation_measurements(torch, lt, dev, timed),
         "gemv": gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed),
@@ -745,6 +746,57 @@ def verify_measurement(torch, lt, w, packed, dev, timed):
     ms = timed(lambda: lt.verify_chunks(table, expect, got, status))
     lt.check_status(status)
     return {"ms": round(ms, 4), "compressed_GBps": round(table.comp_bytes / ms / 1e6, 1)}
+
+
+def file_measurements(torch, lt, w, packed, scales, zp, dev, out, reps=5):
+    """The layer's compressed bytes in a file (just written, so in the
+    host's page cache): read, copy and decode one after another (the whole
+    table as one batch) against the three stages overlapped (batches of
+    64 to 512 chunks), both through the file-streaming entry point with the
+    same reader (8 threads, and 1 for reference).  Host wall clock,
+    synchronized on both sides: every figure includes the reads and PCIe."""
+    import tempfile
+    import time as _t
+    comp, comp_off = lt.compress_chunks(packed, w.dst_off, max_dist=lt.PACK_WINDOW)
+    ht = lt.ChunkTable.from_host(comp, comp_off, w.dst_off, "cpu", lt.PACK_WINDOW, index=True, pin=True)
+    fd, path = tempfile.mkstemp(suffix=".ltcomp")
+    with os.fdopen(fd, "wb") as f:
+        f.write(comp.tobytes())
+    status = torch.full((ht.n_chunks,), -1, dtype=torch.int32, device=dev)
+    shape = (w.rows, w.cols)
+
+    def run(per_half, threads):
+        pinned = torch.empty(ht.pinned_bytes(per_half), dtype=torch.uint8, pin_memory=True)
+        staging = torch.empty(ht.staging_bytes(per_half), dtype=torch.uint8, device=dev)
+
+        def go():
+            lt.stream_file_fused_lz4_int4(path, 0, ht, scales, zp, shape, w.group, out=out, status=status,
+                                          pinned=pinned, staging=staging, read_threads=threads)
+        go()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = _t.perf_counter()
+            go()
+            torch.cuda.synchronize()
+            ts.append((_t.perf_counter() - t0) * 1e3)
+        lt.check_status(status)
+        return float(np.median(ts))
+
+    try:
+        res = {"compressed_bytes": int(comp.size), "file": "page cache (written just before)"}
+        for threads in (8, 1):
+            seq = run(ht.n_chunks, threads)
+            best = None
+            for per_half in (64, 128, 256, 512):
+                ms = run(per_half, threads)
+                res["t%d_streamed_%d_per_half_ms" % (threads, per_half)] = round(ms, 3)
+                best = ms if best is None else min(best, ms)
+            res["t%d_sequential_ms" % threads] = round(seq, 3)
+            res["t%d_speedup_best" % threads] = round(seq / best, 3)
+        return res
+    finally:
+        os.unlink(path)
 
 
 def streamed_measurements(torch, lt, w, packed, scales, zp, dev, out, reps=10, per_half=512):

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 13
+#define LT_ABI_VERSION 14
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -55,7 +55,8 @@ typedef enum lt_status {
   LT_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve */
   LT_ERR_LAUNCH = 3,      /* the HIP runtime refused the launch */
   LT_ERR_DEVICE = 4,      /* no usable gfx950 device for the current context */
-  LT_ERR_TOO_LARGE = 5    /* the request does not fit a fixed-size workspace */
+  LT_ERR_TOO_LARGE = 5,   /* the request does not fit a fixed-size workspace */
+  LT_ERR_IO = 6           /* a read from a file failed or ended early */
 } lt_status;
 
 /* Per-chunk codes written to chunk_status[i] (DEVICE, int32). */
@@ -353,8 +354,9 @@ lt_status lt_verify_chunks(const lt_chunk_table *t, const uint64_t *expect, uint
  * those of lt_decode_lz4 / lt_fused_lz4_int4 on the same table.
  *   staging        DEVICE scratch owned by the caller, 256-byte aligned
  *   staging_bytes  its size: with u(x) = x rounded up to 256, at least
- *                  2*u(8(n+1)) [+ u(8(n+1)) + u(4 n_seq) with an index]
- *                  for the table, plus two halves each holding
+ *                  2*u(8(n+1)) [+ u(8 n) with checksums] [+ u(8(n+1)) +
+ *                  u(4 n_seq) with an index] for the table, plus two
+ *                  halves each holding
  *                  u(largest chunk's compressed bytes + 16);
  *                  LT_ERR_INVALID_ARG otherwise
  *   copy_stream    the stream the host-to-device copies run on (it may
@@ -377,6 +379,46 @@ lt_status lt_stream_fused_lz4_int8(const lt_chunk_table *host_table, const uint1
                                    uint64_t rows, uint64_t cols, uint64_t group, uint16_t *out,
                                    int32_t *chunk_status, uint8_t *staging, uint64_t staging_bytes,
                                    void *copy_stream, void *stream);
+
+/*
+ * The streamed calls with the compressed bytes in a file, the roadmap's
+ * three stages ("GPU Compression Pipeline - TDD Roadmap", Phase 5.1: read
+ * part N+1 while part N is transferred and part N-1 decompressed).  Chunk
+ * i's compressed bytes are the file's bytes at file_offset + comp_off[i]
+ * (the table's comp array is not read and may be NULL); the table's other
+ * arrays are HOST arrays as for lt_stream_decode_lz4.  The calling thread
+ * reads each batch with pread (read_threads threads side by side, pieces
+ * of at least 1 MiB) into half b % 2 of `pinned`, then enqueues its copy
+ * and decode as lt_stream_decode_lz4 does; it reads the next batch while
+ * those run, and reads into a half again only after the copy that last
+ * read it has finished.  Batches are as large as both a staging half and a
+ * pinned half hold.
+ *   fd            a file descriptor open for reading (pread: the file
+ *                 position is not used or moved)
+ *   pinned        HOST pinned memory (hipHostMalloc, torch's pin_memory)
+ *                 owned by the caller, split into two halves of
+ *                 (pinned_bytes / 2) rounded down to 256 bytes, each at
+ *                 least the largest chunk's compressed bytes
+ * Output, statuses and errors are those of the memory-resident streamed
+ * calls, plus LT_ERR_IO when a read fails or the file ends early (the
+ * batches before it stay enqueued).  The call returns once every batch has
+ * been read and its copy and decode enqueued; the copies still read
+ * `pinned`, so it and the staging buffer must stay untouched until the
+ * work on `stream` finishes.
+ */
+lt_status lt_stream_file_decode_lz4(int fd, uint64_t file_offset, const lt_chunk_table *host_table, uint8_t *dst,
+                                    int32_t *chunk_status, uint8_t *pinned, uint64_t pinned_bytes, int read_threads,
+                                    uint8_t *staging, uint64_t staging_bytes, void *copy_stream, void *stream);
+lt_status lt_stream_file_fused_lz4_int4(int fd, uint64_t file_offset, const lt_chunk_table *host_table,
+                                        const uint16_t *scales, const int8_t *zp, uint64_t rows, uint64_t cols,
+                                        uint64_t group, uint16_t *out, int32_t *chunk_status, uint8_t *pinned,
+                                        uint64_t pinned_bytes, int read_threads, uint8_t *staging,
+                                        uint64_t staging_bytes, void *copy_stream, void *stream);
+lt_status lt_stream_file_fused_lz4_int8(int fd, uint64_t file_offset, const lt_chunk_table *host_table,
+                                        const uint16_t *scales, const int8_t *zp, uint64_t rows, uint64_t cols,
+                                        uint64_t group, uint16_t *out, int32_t *chunk_status, uint8_t *pinned,
+                                        uint64_t pinned_bytes, int read_threads, uint8_t *staging,
+                                        uint64_t staging_bytes, void *copy_stream, void *stream);
 
 /*
  * lt_stream_fused_lz4_int4_static -- lt_stream_fused_lz4_int4 for callers

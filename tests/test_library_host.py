@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 13
+    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 14
     assert lt.lib().lt_status_str(1) == b"invalid argument"
     assert lt.lib().lt_status_str(lt.LT_ERR_TOO_LARGE) == b"request exceeds the static workspace"
 
@@ -480,3 +480,29 @@ def test_order_chunks_starts_the_largest_first():
     bad[3] = bad[5]
     with pytest.raises(lt.LtError):
         lt.order_chunks(bad)
+
+
+def test_file_stream_arguments_rejected_without_gpu():
+    """The file-streaming calls refuse a bad descriptor, a missing or too
+    small pinned buffer and a bad table before any device work."""
+    L = lt.lib()
+    V = C.c_void_p
+    ptr = lambda a: a.ctypes.data_as(V)
+    comp = np.zeros(64, np.uint8)
+    coff = np.array([0, 32, 64], np.uint64)
+    doff = np.array([0, 64, 128], np.uint64)
+    h = lt._Table(ptr(comp), ptr(coff), ptr(doff), 2, 4096, 128, 64)
+    fake = V(0x10000)
+    pin = np.zeros(1 << 16, np.uint8)
+    inv = lt.LT_ERR_INVALID_ARG
+    assert L.lt_stream_file_decode_lz4(-1, 0, C.byref(h), fake, None, ptr(pin), pin.size, 1, fake, 1 << 20, None,
+                                       None) == inv
+    assert L.lt_stream_file_decode_lz4(0, 0, C.byref(h), fake, None, None, pin.size, 1, fake, 1 << 20, None,
+                                       None) == inv
+    assert L.lt_stream_file_decode_lz4(0, 0, C.byref(h), fake, None, ptr(pin), 256, 1, fake, 1 << 20, None,
+                                       None) == inv
+    assert L.lt_stream_file_decode_lz4(0, 0, None, fake, None, ptr(pin), pin.size, 1, fake, 1 << 20, None,
+                                       None) == inv
+    assert L.lt_stream_file_fused_lz4_int4(0, 0, C.byref(h), None, None, 16, 16, 16, fake, None, ptr(pin),
+                                           pin.size, 1, fake, 1 << 20, None, None) == inv   # no scales
+    assert L.lt_status_str(lt.LT_ERR_IO).decode() == "a file read failed or ended early"

@@ -49,8 +49,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblt.so")
 
-ABI_VERSION = 13          # LT_ABI_VERSION of the library this binding speaks to
-LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE = range(6)
+ABI_VERSION = 14          # LT_ABI_VERSION of the library this binding speaks to
+LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE, LT_ERR_IO = range(7)
 STATIC_SCRATCH_BYTES = 32 << 20   # LT_STATIC_SCRATCH_BYTES
 (CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
  CHUNK_CHECKSUM, CHUNK_STALLED) = range(8)
@@ -119,6 +119,11 @@ def _lib():
             "lt_checksum_chunks": (i32, [vp, vp, u32, vp, i32]),
             "lt_stream_fused_lz4_int4": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
             "lt_stream_fused_lz4_int8": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp, u64, vp, vp]),
+            "lt_stream_file_decode_lz4": (i32, [C.c_int, u64, tp, vp, vp, vp, u64, C.c_int, vp, u64, vp, vp]),
+            "lt_stream_file_fused_lz4_int4": (i32, [C.c_int, u64, tp, vp, vp, u64, u64, u64, vp, vp, vp, u64,
+                                                    C.c_int, vp, u64, vp, vp]),
+            "lt_stream_file_fused_lz4_int8": (i32, [C.c_int, u64, tp, vp, vp, u64, u64, u64, vp, vp, vp, u64,
+                                                    C.c_int, vp, u64, vp, vp]),
             "lt_stream_fused_lz4_int4_static": (i32, [tp, vp, vp, u64, u64, u64, vp, vp, vp]),
             "lt_lz4_bound": (u64, [u64]),
             "lt_pack_int4": (i32, [vp, u64, vp]),
@@ -331,6 +336,18 @@ class ChunkTable:
             seq_pos = np.zeros(1, np.uint32)
         self.seq_off = _place(seq_off.view(np.int64), device, pin)
         self.seq_pos = _place(seq_pos.view(np.int32), device, pin)
+
+    def pinned_bytes(self, chunks_per_half: int = 512) -> int:
+        """A pinned host buffer size for the file-streaming entry points: two
+        halves that each hold the compressed bytes of the largest
+        `chunks_per_half` consecutive chunks (rounded up to 256 bytes)."""
+        up = lambda x: (x + 255) // 256 * 256
+        n = self.n_chunks
+        if n == 0:
+            return 2 * 256
+        k = max(1, min(int(chunks_per_half), n))
+        co = self.comp_off.cpu().numpy().astype(np.int64)
+        return 2 * up(int(np.max(co[k:] - co[:-k])))
 
     def staging_bytes(self, chunks_per_half: int = 512) -> int:
         """A staging size for the streamed entry points: the table's offsets,
@@ -674,6 +691,71 @@ def stream_fused_lz4_int8(table: ChunkTable, scales, zp, shape, group: int, out=
     """fused_lz4_int8 over a host-resident table, as stream_fused_lz4_int4."""
     return _stream_fused("lt_stream_fused_lz4_int8", table, scales, zp, shape, group, out, status, staging,
                          copy_stream, stream)
+
+
+def _stream_file(name, fd, file_offset, table, mid, out, status, pinned, staging, copy_stream, stream, read_threads):
+    """Run a file-streaming entry point.  fd is a file descriptor or a path
+    (opened and closed here; the reads are done when the call returns)."""
+    torch = _torch()
+    staging, copy_stream, owned = _stream_setup(table, out.device, staging, copy_stream)
+    own_pin = pinned is None
+    if own_pin:
+        pinned = torch.empty(table.pinned_bytes(), dtype=torch.uint8, pin_memory=True)
+    close = isinstance(fd, (str, bytes, os.PathLike))
+    if close:
+        fd = os.open(fd, os.O_RDONLY)
+    try:
+        t = table.as_c()
+        _check(getattr(_lib(), name)(fd, int(file_offset), C.byref(t), *mid, _dptr(out), _dptr(status), _dptr(pinned),
+                                     pinned.numel(), int(read_threads), _dptr(staging), staging.numel(),
+                                     _stream_ptr(copy_stream), _stream_ptr(stream)), name)
+    finally:
+        if close:
+            os.close(fd)
+        _stream_release(staging, owned, copy_stream, stream)
+        if own_pin:   # the copies read the pinned buffer allocated here
+            copy_stream.synchronize()
+    return out
+
+
+def stream_file_decode_lz4(fd, file_offset: int, table: ChunkTable, out=None, status=None, pinned=None,
+                           staging=None, read_threads: int = 8, copy_stream=None, stream=None, device="cuda"):
+    """stream_decode_lz4 with the compressed bytes read from a file (chunk
+    i's at file_offset + comp_off[i]): each batch is read with pread into a
+    pinned half while the batches before it are copied and decoded.  `table`
+    is a host table whose comp array is not read."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(max(table.total_bytes, 1), dtype=torch.uint8, device=device)
+    _stream_file("lt_stream_file_decode_lz4", fd, file_offset, table, (), out, status, pinned, staging,
+                 copy_stream, stream, read_threads)
+    return out[:table.total_bytes] if out.numel() > table.total_bytes else out
+
+
+def _stream_file_fused(name, fd, file_offset, table, scales, zp, shape, group, out, status, pinned, staging,
+                       read_threads, copy_stream, stream):
+    rows, cols = _shape(shape)
+    out = _out_f16(out, rows * cols, scales.device)
+    _stream_file(name, fd, file_offset, table, (_dptr(scales), _dptr(zp), rows, cols, group), out, status, pinned,
+                 staging, copy_stream, stream, read_threads)
+    return out.view(rows, cols)
+
+
+def stream_file_fused_lz4_int4(fd, file_offset: int, table: ChunkTable, scales, zp, shape, group: int, out=None,
+                               status=None, pinned=None, staging=None, read_threads: int = 8, copy_stream=None,
+                               stream=None):
+    """stream_fused_lz4_int4 with the compressed bytes read from a file, as
+    stream_file_decode_lz4."""
+    return _stream_file_fused("lt_stream_file_fused_lz4_int4", fd, file_offset, table, scales, zp, shape, group,
+                              out, status, pinned, staging, read_threads, copy_stream, stream)
+
+
+def stream_file_fused_lz4_int8(fd, file_offset: int, table: ChunkTable, scales, zp, shape, group: int, out=None,
+                               status=None, pinned=None, staging=None, read_threads: int = 8, copy_stream=None,
+                               stream=None):
+    """stream_fused_lz4_int8 with the compressed bytes read from a file."""
+    return _stream_file_fused("lt_stream_file_fused_lz4_int8", fd, file_offset, table, scales, zp, shape, group,
+                              out, status, pinned, staging, read_threads, copy_stream, stream)
 
 
 def stream_fused_lz4_int4_static(table: ChunkTable, scales, zp, shape, group: int, out=None, status=None,

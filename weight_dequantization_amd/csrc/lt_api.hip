@@ -9,7 +9,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <unistd.h>
+
+#include <algorithm>
+#include <atomic>
 #include <mutex>
+#include <thread>
+#include <vector>
 
 #include "lt.h"
 #include "lt_device.hpp"
@@ -340,6 +346,47 @@ uint64_t batch_bytes(const lt_chunk_table *t, uint64_t c, uint64_t e) {
   return up(t->comp_off[e] - t->comp_off[c] + 16);
 }
 
+// Where a streamed batch's compressed bytes come from when they are not in
+// host memory: a file, read with pread into the two halves of a pinned host
+// buffer in turn.  The calling thread reads batch b while the copy and the
+// decode of the batches before it run on the streams; a half is read into
+// again only once the copy that last read it has finished.
+struct FileSource {
+  int fd;
+  uint64_t offset;    // file offset of compressed byte 0
+  uint8_t *pinned;    // pinned host memory, two halves of `half` bytes
+  uint64_t half;
+  int threads;        // reader threads per batch
+};
+
+// Read len bytes at file offset off into dst, in up to `threads` pieces
+// read side by side; false on an error or an early end of file.
+bool read_range(int fd, uint64_t off, uint64_t len, uint8_t *dst, int threads) {
+  auto rd = [&](uint64_t a, uint64_t b) {
+    while (a < b) {
+      const ssize_t r = pread(fd, dst + a, (size_t)std::min<uint64_t>(b - a, 1ull << 30), (off_t)(off + a));
+      if (r <= 0) return false;
+      a += (uint64_t)r;
+    }
+    return true;
+  };
+  constexpr uint64_t kPiece = 1ull << 20;   // no thread reads less
+  const uint64_t pieces = (len + kPiece - 1) / kPiece;
+  const int T = (int)std::min<uint64_t>(std::max(threads, 1), std::max<uint64_t>(pieces, 1));
+  if (T <= 1) return rd(0, len);
+  const uint64_t per = (len + T - 1) / T;
+  std::atomic<bool> ok{true};
+  std::vector<std::thread> pool;
+  for (int k = 1; k < T; k++)
+    pool.emplace_back([&, k] {
+      const uint64_t a = k * per, b = std::min(len, a + per);
+      if (a < b && !rd(a, b)) ok = false;
+    });
+  if (!rd(0, std::min(len, per))) ok = false;
+  for (auto &th : pool) th.join();
+  return ok;
+}
+
 // Copy-and-decode of a table whose arrays are in host memory: batches of
 // chunks go to the two halves of a device staging buffer in turn, the
 // copies on copy_stream and the decode on stream, each half reused once the
@@ -348,7 +395,7 @@ uint64_t batch_bytes(const lt_chunk_table *t, uint64_t c, uint64_t e) {
 // batch cost more than the batch's compressed bytes.
 lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *chunk_status,
                         const uint16_t *scales, const int8_t *zp, uint64_t group, uint8_t *staging,
-                        uint64_t staging_bytes, void *copy_stream, void *stream) {
+                        uint64_t staging_bytes, void *copy_stream, void *stream, const FileSource *fs = nullptr) {
   if (t->n_chunks == 0) return LT_OK;
   if (!staging || ((uintptr_t)staging & (kAlign - 1)) != 0) return LT_ERR_INVALID_ARG;
   // host-side checks of what the batching relies on (the device checks the rest)
@@ -362,12 +409,15 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   const uint64_t mb = meta_bytes(t);
   if (staging_bytes < mb + 2 * kAlign) return LT_ERR_INVALID_ARG;
   const uint64_t half = ((staging_bytes - mb) / 2) & ~(kAlign - 1);
-  for (uint64_t i = 0; i < n; i++)
+  for (uint64_t i = 0; i < n; i++) {
     if (batch_bytes(t, i, i + 1) > half) return LT_ERR_INVALID_ARG;   // a chunk must fit a half
+    if (fs && t->comp_off[i + 1] - t->comp_off[i] > fs->half) return LT_ERR_INVALID_ARG;
+  }
   hipStream_t cs = (hipStream_t)copy_stream, ds = (hipStream_t)stream;
   // on one stream the copies and decodes are ordered by the stream itself,
-  // and no event is needed (nor created)
-  const bool one = cs == ds;
+  // and no event is needed (nor created); a file source needs the copy
+  // events to know when a pinned half is free
+  const bool one = cs == ds && !fs;
   uint64_t *m_coff = (uint64_t *)staging;
   uint64_t *m_doff = (uint64_t *)(staging + up(8 * (n + 1)));
   uint8_t *m_rest = staging + 2 * up(8 * (n + 1));
@@ -402,13 +452,21 @@ lt_status stream_common(int mode, const lt_chunk_table *t, void *out, int32_t *c
   for (uint64_t batch = 0; st == LT_OK && c < n; batch++) {
     // the batch: as many chunks as the half holds
     uint64_t e = c + 1;
-    while (e < n && batch_bytes(t, c, e + 1) <= half) e++;
+    while (e < n && batch_bytes(t, c, e + 1) <= half && (!fs || t->comp_off[e + 1] - t->comp_off[c] <= fs->half)) e++;
     const int h = (int)(batch & 1);
     uint8_t *p_comp = staging + mb + h * half;
     const uint64_t cb = t->comp_off[e] - t->comp_off[c];
     // copies into this half wait for the decode that last read it
     if (!one && batch >= 2 && hipStreamWaitEvent(cs, done[h], 0) != hipSuccess) { st = LT_ERR_DEVICE; break; }
-    if (hipMemcpyAsync(p_comp, t->comp + t->comp_off[c], cb, hipMemcpyHostToDevice, cs) != hipSuccess ||
+    const uint8_t *src = t->comp + t->comp_off[c];
+    if (fs) {
+      // the pinned half was last read by the copy of batch - 2
+      uint8_t *pin = fs->pinned + h * fs->half;
+      if (batch >= 2 && hipEventSynchronize(copied[h]) != hipSuccess) { st = LT_ERR_DEVICE; break; }
+      if (!read_range(fs->fd, fs->offset + t->comp_off[c], cb, pin, fs->threads)) { st = LT_ERR_IO; break; }
+      src = pin;
+    }
+    if (hipMemcpyAsync(p_comp, src, cb, hipMemcpyHostToDevice, cs) != hipSuccess ||
         (!one && (hipEventRecord(copied[h], cs) != hipSuccess || hipStreamWaitEvent(ds, copied[h], 0) != hipSuccess))) {
       st = LT_ERR_DEVICE;
       break;
@@ -755,6 +813,55 @@ lt_status lt_stream_fused_lz4_int8(const lt_chunk_table *host_table, const uint1
                        copy_stream, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The streamed calls with the compressed bytes in a file: the table's comp
+// array is not read (chunk i's bytes are at file_offset + comp_off[i]).
+lt_status file_common(int mode, int fd, uint64_t file_offset, const lt_chunk_table *host_table,
+                      const uint16_t *scales, const int8_t *zp, uint64_t rows, uint64_t cols, uint64_t group,
+                      void *out, int32_t *chunk_status, uint8_t *pinned, uint64_t pinned_bytes, int read_threads,
+                      uint8_t *staging, uint64_t staging_bytes, void *copy_stream, void *stream) {
+  if (!host_table || fd < 0 || !pinned || pinned_bytes < 2 * kAlign) return LT_ERR_INVALID_ARG;
+  lt_chunk_table t = *host_table;
+  t.comp = pinned;   // any host pointer: only checked against NULL
+  const lt_status a = stream_args(mode, &t, scales, rows, cols, group, out);
+  if (a != LT_OK) return a;
+  const FileSource fs{fd, file_offset, pinned, (pinned_bytes / 2) & ~(kAlign - 1), read_threads};
+  return stream_common(mode, &t, out, chunk_status, scales, zp, group, staging, staging_bytes, copy_stream, stream,
+                       &fs);
+}
+
+}  // namespace
+
+extern "C" {
+
+lt_status lt_stream_file_decode_lz4(int fd, uint64_t file_offset, const lt_chunk_table *host_table, uint8_t *dst,
+                                    int32_t *chunk_status, uint8_t *pinned, uint64_t pinned_bytes, int read_threads,
+                                    uint8_t *staging, uint64_t staging_bytes, void *copy_stream, void *stream) {
+  return file_common(lt::MODE_BYTES, fd, file_offset, host_table, nullptr, nullptr, 0, 0, 1, dst, chunk_status, pinned,
+                     pinned_bytes, read_threads, staging, staging_bytes, copy_stream, stream);
+}
+
+lt_status lt_stream_file_fused_lz4_int4(int fd, uint64_t file_offset, const lt_chunk_table *host_table,
+                                        const uint16_t *scales, const int8_t *zp, uint64_t rows, uint64_t cols,
+                                        uint64_t group, uint16_t *out, int32_t *chunk_status, uint8_t *pinned,
+                                        uint64_t pinned_bytes, int read_threads, uint8_t *staging,
+                                        uint64_t staging_bytes, void *copy_stream, void *stream) {
+  return file_common(lt::MODE_INT4, fd, file_offset, host_table, scales, zp, rows, cols, group, out, chunk_status,
+                     pinned, pinned_bytes, read_threads, staging, staging_bytes, copy_stream, stream);
+}
+
+lt_status lt_stream_file_fused_lz4_int8(int fd, uint64_t file_offset, const lt_chunk_table *host_table,
+                                        const uint16_t *scales, const int8_t *zp, uint64_t rows, uint64_t cols,
+                                        uint64_t group, uint16_t *out, int32_t *chunk_status, uint8_t *pinned,
+                                        uint64_t pinned_bytes, int read_threads, uint8_t *staging,
+                                        uint64_t staging_bytes, void *copy_stream, void *stream) {
+  return file_common(lt::MODE_INT8, fd, file_offset, host_table, scales, zp, rows, cols, group, out, chunk_status,
+                     pinned, pinned_bytes, read_threads, staging, staging_bytes, copy_stream, stream);
+}
+
 lt_status lt_stream_fused_lz4_int4_static(const lt_chunk_table *host_table, const uint16_t *scales,
                                           const int8_t *zp, uint64_t rows, uint64_t cols, uint64_t group,
                                           uint16_t *out, int32_t *chunk_status, void *stream) {
@@ -785,6 +892,7 @@ const char *lt_status_str(lt_status s) {
     case LT_ERR_LAUNCH: return "kernel launch failed";
     case LT_ERR_DEVICE: return "no usable device";
     case LT_ERR_TOO_LARGE: return "request exceeds the static workspace";
+    case LT_ERR_IO: return "a file read failed or ended early";
   }
   return "unknown status";
 }
