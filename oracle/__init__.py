@@ -343,6 +343,24 @@ def dequant_int4_lut(packed, lut, group: int, n_elem: int | None = None) -> np.n
 
 # ---------------------------------------------------------- decode + GEMV
 
+def gemm_int4_tiled(t: Table, scales, zp, group: int, rows: int, cols: int, x_f16) -> np.ndarray:
+    """Y = X W^T in fp64 for a table whose decoded bytes hold W's INT4 codes
+    in tiles of 16 rows x 128 columns (16-row blocks in order, each block's
+    column tiles in order, each tile's rows of 64 bytes in turn, low nibble
+    first).  Code (r, c) sits in byte ((r // 16) * (cols // 128) + c // 128)
+    * 1024 + (r % 16) * 64 + (c % 128) // 2, nibble c % 2.  W is the fp16
+    matrix dequant_int4 gives for the codes in row-major order; x fp16 bits
+    [batch, cols]; returns (Y float64 [batch, rows], chunk statuses)."""
+    data, st = decode_table(t)
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    c = np.arange(cols, dtype=np.int64)[None, :]
+    byte = ((r // 16) * (cols // 128) + c // 128) * 1024 + (r % 16) * 64 + (c % 128) // 2
+    codes = (data[byte] >> (4 * (c % 2))) & 15
+    W = f64_from_f16(dequant_int4(pack_int4(codes.astype(np.uint8).ravel()), scales, zp, group)).reshape(rows, cols)
+    X = f64_from_f16(_c(x_f16, np.uint16)).reshape(-1, cols)
+    return X @ W.T, st
+
+
 def gemv_int4(t: Table, scales, zp, group: int, rows: int, cols: int, x_f16) -> np.ndarray:
     """y = W x in fp64, W = fused_int4(t) as an fp16 rows x cols matrix and
     x fp16 bits [cols]; returns (y float64 [rows], chunk statuses)."""
