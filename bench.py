@@ -648,6 +648,7 @@ def extra_measurements(torch, lt, w, packed, scales, zp, dev, reps=20):
         "verify_xxh3": verify_measurement(torch, lt, w, packed, dev, timed),
         "activations_4096x14336": activation_measurements(torch, lt, dev, timed),
         "gemv": gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed),
+        "gemm": gemm_measurement(torch, lt, w, packed, scales, zp, dev, out, timed),
     }
 
 
@@ -706,6 +707,34 @@ def gemv_measurement(torch, lt, w, packed, scales, zp, dev, out, timed):
     res["llama70b_layer_concurrent_ms"] = round(ms_streams, 4)
     res["llama70b_80_layers_ms"] = round(80 * min(ms_layer, ms_streams), 3)
     res["llama70b_layer_compressed_bytes"] = int(sum(tb.comp_bytes for _, tb, *_ in layer))
+    return res
+
+
+def gemm_measurement(torch, lt, w, packed, scales, zp, dev, out, timed):
+    """Y = X W^T on the same layer for batches of 16 and 32: the decode fused
+    with the product on the matrix cores (W's codes in the GEMM tile layout,
+    2048 chunks of 56 tiles; W never written) against lt_fused_lz4_int4
+    writing W (the headline table) followed by torch.mm, and torch.mm alone
+    on the resident fp16 W.  Back to back, without cache clearing."""
+    rows, cols = w.rows, w.cols
+    gt = lt.ChunkTable.build(lt.pack_int4_tiles(w.codes.reshape(rows, cols), rows, cols),
+                             lt.gemm_chunks(rows, cols), dev)
+    rt = lt.ChunkTable.build(packed, w.dst_off, dev)
+    W = out.view(rows, cols)
+    res = {"chunks": gt.n_chunks, "compressed_bytes": gt.comp_bytes}
+    for batch in (16, 32):
+        x = torch.randn(batch, cols, dtype=torch.float16, device=dev)
+        xt = x.t().contiguous()
+        y = torch.empty(batch, rows, dtype=torch.float32, device=dev)
+        ws = torch.empty(lt.gemm_workspace_bytes(gt.n_chunks, batch) // 4, dtype=torch.float32, device=dev)
+        ms_f = timed(lambda: lt.fused_lz4_int4_gemm(gt, scales, zp, (rows, cols), w.group, x, y=y, workspace=ws))
+        ms_2 = timed(lambda: (lt.fused_lz4_int4(rt, scales, zp, (rows, cols), w.group, out=out), torch.mm(W, xt)))
+        ms_mm = timed(lambda: torch.mm(W, xt))
+        y2 = torch.mm(W.float(), xt.float()).t()
+        rel = float((y - y2).abs().max() / y2.abs().max())
+        res["batch%d" % batch] = {"fused_ms": round(ms_f, 4), "decode_then_mm_ms": round(ms_2, 4),
+                                  "mm_alone_ms": round(ms_mm, 4), "speedup": round(ms_2 / ms_f, 3),
+                                  "max_rel_diff_vs_fp32_mm": rel}
     return res
 
 

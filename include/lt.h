@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LT_ABI_VERSION 14
+#define LT_ABI_VERSION 15
 
 typedef enum lt_status {
   LT_OK = 0,
@@ -240,6 +240,35 @@ lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, con
 lt_status lt_fused_lz4_int4_gemv(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,
                                  uint64_t rows, uint64_t cols, uint64_t group, const uint16_t *x, float *y,
                                  int32_t *chunk_status, void *stream);
+
+/*
+ * lt_fused_lz4_int4_gemm -- Y = X W^T with W never stored: the decode feeds
+ * dequantized tiles straight into a product on the matrix cores (the decode
+ * plus GEMM benchmark of page "Openai/691a41cd-... (section 38)"; the
+ * roadmap's decoded tensor used in a matmul, Phase 4.1).  W [rows, cols] is
+ * the fp16 matrix lt_fused_lz4_int4 would write from the same codes, scales
+ * and zero points, but the table's decoded bytes hold its codes in the GEMM
+ * layout: tiles of 16 rows x 128 columns (1 KiB), the 16-row blocks in
+ * order, each block's column tiles in order, each tile's 16 rows of 64
+ * bytes in turn, two codes per byte, low nibble first.  Every chunk holds
+ * whole tiles of one 16-row block (others fail with LT_CHUNK_BAD_TABLE and
+ * leave their rows of Y unspecified).
+ *   x          DEVICE fp16 [batch][cols], 16-byte aligned; batch 16 or 32
+ *   y          DEVICE fp32 [batch][rows], receives Y
+ *   workspace  DEVICE fp32 scratch of at least lt_gemm_workspace_bytes(
+ *              n_chunks, batch) bytes, 16-byte aligned, owned by the caller:
+ *              each chunk's builders leave their partial products there and
+ *              a second kernel sums them per row block in a fixed order, so
+ *              Y is the same bits on every call
+ * rows % 16 == 0, cols % 128 == 0, group a power of two >= 128
+ * (LT_ERR_UNSUPPORTED otherwise); the fp16 products are exact in fp32 and
+ * the sums are fp32.
+ */
+lt_status lt_fused_lz4_int4_gemm(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp, uint64_t rows,
+                                 uint64_t cols, uint64_t group, const uint16_t *x, uint32_t batch, float *y,
+                                 float *workspace, uint64_t workspace_bytes, int32_t *chunk_status, void *stream);
+/* Bytes of workspace lt_fused_lz4_int4_gemm needs for n_chunks and batch. */
+uint64_t lt_gemm_workspace_bytes(uint32_t n_chunks, uint32_t batch);
 
 /*
  * lt_fused_lz4_int8 -- LZ4 decode fused with INT8 dequantization; the

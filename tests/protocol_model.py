@@ -26,6 +26,9 @@ It checks what the protocol must guarantee, at the moment of every access:
   - no interleaving deadlocks (a step bound far above the work);
 and at the end that the decoded chunk equals the expected bytes.
 
+With `static_tiles` builder b takes tiles b, b + nb, b + 2 nb, ... (the
+matrix-product mode) instead of the next tile from the shared counter.
+
 With `checksum` one builder's wave hashes the compressed bytes instead (a
 reader that announces its position like the others) and the feeder streams
 every block to its end.
@@ -111,8 +114,9 @@ class Chunk:
     """One chunk's decode under the protocol, with a seeded schedule."""
 
     def __init__(self, blk, n_out, index=None, hlog=14, dmax=65535, head=0, seed=0, builders=None, fault=None,
-                 checksum=False):
+                 checksum=False, static_tiles=False):
         self.fault = fault
+        self.static_tiles = static_tiles
         self.checksum = checksum
         self.blk = bytes(blk)
         self.N = n_out
@@ -641,8 +645,11 @@ class Chunk:
                 yield
 
         while t < self.ntiles:
-            u = self.tile_ctr
-            self.tile_ctr += 1
+            if self.static_tiles:     # builder b takes tiles b, b + nb, ...
+                u = t + self.nb
+            else:
+                u = self.tile_ctr
+                self.tile_ctr += 1
             yield
             T, Tend = t * TILE, min(t * TILE + TILE, self.N)
             ok = True

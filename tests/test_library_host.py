@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
     L = C.CDLL(lt.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 14
+    assert lt.lib().lt_abi_version() == lt.ABI_VERSION == 15
     assert lt.lib().lt_status_str(1) == b"invalid argument"
     assert lt.lib().lt_status_str(lt.LT_ERR_TOO_LARGE) == b"request exceeds the static workspace"
 
@@ -506,3 +506,26 @@ def test_file_stream_arguments_rejected_without_gpu():
     assert L.lt_stream_file_fused_lz4_int4(0, 0, C.byref(h), None, None, 16, 16, 16, fake, None, ptr(pin),
                                            pin.size, 1, fake, 1 << 20, None, None) == inv   # no scales
     assert L.lt_status_str(lt.LT_ERR_IO).decode() == "a file read failed or ended early"
+
+
+def test_gemm_arguments_rejected_without_gpu():
+    """The fused GEMM refuses shapes off the tile grid, batches other than 16
+    and 32, small groups and a short workspace before any device work."""
+    L = lt.lib()
+    fake = C.c_void_p(0x10000)
+    n = 8
+    t = lt._Table(0x10000, 0x10000, 0x10000, n, 1 << 16, 16 * 256 // 2, 100)
+    ws = lt.gemm_workspace_bytes(n, 16)
+    assert ws == n * 6 * 16 * 16 * 4
+    call = lambda rows, cols, group, batch, wsb, tb=t: L.lt_fused_lz4_int4_gemm(
+        C.byref(tb), fake, None, rows, cols, group, fake, batch, fake, fake, wsb, None, None)
+    assert call(16, 256, 128, 16, ws - 4) == lt.LT_ERR_INVALID_ARG              # workspace too small
+    assert call(16, 256, 128, 8, ws) == lt.LT_ERR_UNSUPPORTED                   # batch
+    assert call(16, 256, 64, 16, ws) == lt.LT_ERR_UNSUPPORTED                   # group under 128
+    t2 = lt._Table(0x10000, 0x10000, 0x10000, n, 1 << 16, 8 * 256 // 2, 100)
+    assert call(8, 256, 128, 16, ws, t2) == lt.LT_ERR_UNSUPPORTED               # rows % 16
+    t3 = lt._Table(0x10000, 0x10000, 0x10000, n, 1 << 16, 16 * 192 // 2, 100)
+    assert call(16, 192, 64, 16, ws, t3) == lt.LT_ERR_UNSUPPORTED               # cols % 128
+    assert call(16, 512, 128, 16, ws) == lt.LT_ERR_INVALID_ARG                  # table size != shape
+    assert L.lt_fused_lz4_int4_gemm(None, fake, None, 16, 256, 128, fake, 16, fake, fake, ws, None,
+                                    None) == lt.LT_ERR_INVALID_ARG

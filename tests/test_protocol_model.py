@@ -148,3 +148,21 @@ def test_checksum_hasher():
             caught += 1
             break
     assert caught >= 1
+
+
+def test_static_tile_assignment():
+    """The matrix-product mode's static tiles (builder b takes b, b + nb, ...)
+    keep every rule and cannot deadlock, on layer blocks in the GEMM layout's
+    chunk size (56 KiB) with both history classes, indexed and walked."""
+    w = synth.mlp_int4_small(rows=64)
+    codes = w.codes.reshape(w.rows, w.cols)
+    data = lt.pack_int4_tiles(codes, w.rows, w.cols)
+    dst_off = lt.gemm_chunks(w.rows, w.cols)
+    for window, hlog in ((lt.PACK_WINDOW, 14), (0, 16)):
+        comp, comp_off = lt.compress_chunks(data, dst_off, max_dist=window)
+        for i, blk, expect, idx in _chunks(comp, comp_off, dst_off, data, [0, 5]):
+            for indexed in (True, False):
+                c = Chunk(blk, len(expect), index=idx if indexed else None, hlog=hlog,
+                          dmax=window or 65535, seed=3, static_tiles=True)
+                st, out, _ = c.run()
+                assert st == 0 and out == expect and all(v == 1 for v in c.built), (i, indexed, hlog)

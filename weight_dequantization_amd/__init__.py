@@ -49,7 +49,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblt.so")
 
-ABI_VERSION = 14          # LT_ABI_VERSION of the library this binding speaks to
+ABI_VERSION = 15          # LT_ABI_VERSION of the library this binding speaks to
 LT_OK, LT_ERR_INVALID_ARG, LT_ERR_UNSUPPORTED, LT_ERR_LAUNCH, LT_ERR_DEVICE, LT_ERR_TOO_LARGE, LT_ERR_IO = range(7)
 STATIC_SCRATCH_BYTES = 32 << 20   # LT_STATIC_SCRATCH_BYTES
 (CHUNK_OK, CHUNK_TRUNCATED, CHUNK_BAD_OFFSET, CHUNK_OVERRUN, CHUNK_SIZE_MISMATCH, CHUNK_BAD_TABLE,
@@ -131,6 +131,8 @@ def _lib():
             "lt_compress_chunks_greedy": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
             "lt_index_chunks": (i32, [vp, vp, u32, vp, vp, u64, i32]),
             "lt_order_chunks": (i32, [vp, u32, vp]),
+            "lt_gemm_workspace_bytes": (u64, [u32, u32]),
+            "lt_fused_lz4_int4_gemm": (i32, [tp, vp, vp, u64, u64, u64, vp, u32, vp, vp, u64, vp, vp]),
             "lt_status_str": (C.c_char_p, [i32]),
             "lt_abi_version": (i32, []),
         }
@@ -478,6 +480,60 @@ def fused_lz4_int4_gemv(table: ChunkTable, scales, zp, shape, group: int, x, y=N
     t = table.as_c()
     _check(_lib().lt_fused_lz4_int4_gemv(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group, _dptr(x),
                                          _dptr(y), _dptr(status), _stream_ptr(stream)), "lt_fused_lz4_int4_gemv")
+    return y
+
+
+def pack_int4_tiles(codes: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """INT4 codes [rows, cols] (values 0..15, row-major) in the GEMM layout:
+    tiles of 16 rows x 128 columns, the 16-row blocks in order and each
+    block's column tiles in order, each tile's 16 rows of 64 bytes in turn,
+    two codes per byte, low nibble first.  rows % 16 == 0, cols % 128 == 0."""
+    if rows % 16 or cols % 128:
+        raise ValueError("the GEMM layout needs rows % 16 == 0 and cols % 128 == 0")
+    c = np.ascontiguousarray(codes, np.uint8).reshape(rows // 16, 16, cols // 128, 128)
+    return pack_int4(np.ascontiguousarray(c.transpose(0, 2, 1, 3)).ravel())
+
+
+def gemm_chunks(rows: int, cols: int, tiles_per_chunk: int = 56) -> np.ndarray:
+    """Chunk boundaries (dst_off) for a GEMM-layout table: each 16-row
+    block's cols / 128 tiles cut into chunks of tiles_per_chunk tiles (the
+    block's last chunk holds the rest), so no chunk spans two blocks."""
+    tpr = cols // 128
+    cuts = list(range(tiles_per_chunk, tpr, tiles_per_chunk)) + [tpr]
+    per = np.array(cuts, np.uint64) * 1024
+    base = np.arange(rows // 16, dtype=np.uint64)[:, None] * np.uint64(tpr * 1024)
+    return np.concatenate([np.zeros(1, np.uint64), (base + per[None, :]).ravel()])
+
+
+def gemm_workspace_bytes(n_chunks: int, batch: int) -> int:
+    return int(_lib().lt_gemm_workspace_bytes(n_chunks, batch))
+
+
+def fused_lz4_int4_gemm(table: ChunkTable, scales, zp, shape, group: int, x, y=None, workspace=None, status=None,
+                        stream=None):
+    """Y = X W^T, with W [rows, cols] the fp16 matrix fused_lz4_int4 would
+    write from the same codes, never stored: the table holds W's codes in
+    the GEMM layout (pack_int4_tiles, chunked by gemm_chunks); x fp16
+    [batch, cols] on the device, batch 16 or 32; returns y fp32 [batch, rows].
+    The partial products go to `workspace` (allocated here when None)."""
+    torch = _torch()
+    rows, cols = _shape(shape)
+    if x.dim() != 2 or int(x.shape[1]) != cols:
+        raise ValueError("x must be [batch, cols]")
+    batch = int(x.shape[0])
+    dev = table.comp.device
+    if y is None:
+        y = torch.empty((batch, rows), dtype=torch.float32, device=dev)
+    own = workspace is None
+    if own:
+        workspace = torch.empty(max(gemm_workspace_bytes(table.n_chunks, batch) // 4, 4), dtype=torch.float32,
+                                device=dev)
+    t = table.as_c()
+    _check(_lib().lt_fused_lz4_int4_gemm(C.byref(t), _dptr(scales), _dptr(zp), rows, cols, group, _dptr(x), batch,
+                                         _dptr(y), _dptr(workspace), workspace.numel() * 4, _dptr(status),
+                                         _stream_ptr(stream)), "lt_fused_lz4_int4_gemm")
+    if own:   # dropped on return while the launch still uses it
+        workspace.record_stream(stream if stream is not None else torch.cuda.current_stream(dev))
     return y
 
 

@@ -280,6 +280,8 @@ lt_status launch_params(int mode, lt::ChunkParams &P, void *stream) {
     case 7: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
     case 8: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMV, 16>), grid, block, 0, s, P); break;
     case 9: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMV, 14>), grid, block, 0, s, P); break;
+    case 10: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMM, 16>), grid, block, 0, s, P); break;
+    case 11: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMM, 14>), grid, block, 0, s, P); break;
     default: return LT_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
@@ -311,6 +313,9 @@ lt::ChunkParams make_params(const lt_chunk_table *t, void *out, int32_t *chunk_s
   P.gemv_x = nullptr;
   P.gemv_y = nullptr;
   P.cols = 0;
+  P.gemm_part = nullptr;
+  P.gemm_nbt = 0;
+  P.gemm_tpr = 1;
   P.spin = t->spin_limit ? t->spin_limit : lt::SPIN_DEFAULT;
   P.order = t->order;
   P.xxh = t->xxh;
@@ -709,6 +714,70 @@ lt_status lt_fused_lz4_int4_gemv(const lt_chunk_table *t, const uint16_t *scales
   P.gemv_y = y;
   P.cols = cols;
   return launch_params(lt::MODE_GEMV, P, stream);
+}
+
+}  // extern "C"
+
+namespace lt {
+
+// The GEMM's second pass: y[b][16 rb + w] = the sum, over the chunks of row
+// block rb in table order and their GEMM_SLOTS slots in order, of the
+// partial products D[w][b].  One workgroup per 16-row block, one thread per
+// (row, vector); the chunks of a block are found by binary search on
+// dst_off (chunks hold whole tiles of one block, in order).
+__global__ void __launch_bounds__(512) gemm_reduce(const float *part, const uint64_t *dst_off, uint32_t n,
+                                                   uint32_t nbt, uint64_t rows, uint64_t cols, float *y) {
+  const uint64_t rb = blockIdx.x, rb_bytes = 8 * cols;   // 16 rows of cols 4-bit codes
+  auto first_at = [&](uint64_t pos) {   // first chunk starting at or after pos
+    uint32_t lo = 0, hi = n;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) / 2;
+      if (dst_off[mid] < pos) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
+  const uint32_t c0 = first_at(rb * rb_bytes), c1 = first_at((rb + 1) * rb_bytes);
+  const uint32_t tid = threadIdx.x, w = tid & 15, b = tid >> 4, bt = b >> 4, bc = b & 15;
+  if (b >= 16 * nbt) return;
+  float sum = 0.0f;
+  for (uint32_t c = c0; c < c1; c++)
+    for (uint32_t slot = 0; slot < GEMM_SLOTS; slot++)
+      sum += part[(((uint64_t)c * GEMM_SLOTS + slot) * nbt + bt) * 256 + w * 16 + bc];
+  y[(uint64_t)b * rows + 16 * rb + w] = sum;
+}
+
+}  // namespace lt
+
+extern "C" {
+
+uint64_t lt_gemm_workspace_bytes(uint32_t n_chunks, uint32_t batch) {
+  return (uint64_t)n_chunks * lt::GEMM_SLOTS * batch * 16 * sizeof(float);
+}
+
+lt_status lt_fused_lz4_int4_gemm(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp, uint64_t rows,
+                                 uint64_t cols, uint64_t group, const uint16_t *x, uint32_t batch, float *y,
+                                 float *workspace, uint64_t workspace_bytes, int32_t *chunk_status, void *stream) {
+  if (!table_ok(t) || !scales || !x || !y || !workspace || !aligned16(x) || ((uintptr_t)y & 3) != 0 ||
+      ((uintptr_t)workspace & 15) != 0)
+    return LT_ERR_INVALID_ARG;
+  if (!shape_ok(rows, cols, group)) return LT_ERR_INVALID_ARG;
+  if (t->total_bytes != rows * cols / 2) return LT_ERR_INVALID_ARG;
+  if (rows % 16 != 0 || cols % 128 != 0 || shift_of(group) >= 64 || group < 128) return LT_ERR_UNSUPPORTED;
+  if (batch != 16 && batch != 32) return LT_ERR_UNSUPPORTED;
+  if (workspace_bytes < lt_gemm_workspace_bytes(t->n_chunks, batch)) return LT_ERR_INVALID_ARG;
+  if (rows / 16 > 0x7FFFFFFFull) return LT_ERR_UNSUPPORTED;
+  lt::ChunkParams P = make_params(t, nullptr, chunk_status, scales, zp, group);
+  P.gemv_x = x;
+  P.cols = cols;
+  P.gemm_part = workspace;
+  P.gemm_nbt = batch / 16;
+  P.gemm_tpr = cols / 128;
+  const lt_status st = launch_params(lt::MODE_GEMM, P, stream);
+  if (st != LT_OK) return st;
+  hipLaunchKernelGGL(lt::gemm_reduce, dim3((uint32_t)(rows / 16)), dim3(16 * batch), 0, (hipStream_t)stream,
+                     workspace, t->dst_off, t->n_chunks, batch / 16, rows, cols, y);
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
 }
 
 lt_status lt_fused_lz4_int4(const lt_chunk_table *t, const uint16_t *scales, const int8_t *zp,

@@ -158,7 +158,13 @@ constexpr uint32_t SPIN_DEFAULT = 1u << 24;
 // leaner scale / zero-point fetch).
 // MODE_GEMV is MODE_INT4G whose whole tiles are dotted with a vector and
 // added to y instead of being written.
-enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2, MODE_INT4G = 3, MODE_GEMV = 4 };
+// MODE_GEMM takes a table whose bytes are INT4 codes in tiles of 16 rows x
+// 128 columns (1 KiB, each row's 64 bytes in turn) and multiplies every
+// tile with the matching 128 columns of a batch of 16 or 32 vectors on the
+// matrix cores; each builder keeps its partial products, and a second
+// kernel sums them per row block in a fixed order.
+enum Mode : int { MODE_BYTES = 0, MODE_INT4 = 1, MODE_INT8 = 2, MODE_INT4G = 3, MODE_GEMV = 4, MODE_GEMM = 5 };
+constexpr uint32_t GEMM_SLOTS = NB + 1;   // partial-product slots per chunk (one per builder)
 
 struct __attribute__((aligned(16))) Ctl {
   uint32_t need[NSLOT];       // first input byte still read: [0] walker, [1 + b] builder b
@@ -231,6 +237,11 @@ struct ChunkParams {
   float *gemv_y;             // fp32 [rows]
   uint64_t cols;
   uint32_t spin;             // polls each wave may make per chunk (>= 1)
+  // MODE_GEMM: partial products [chunk][GEMM_SLOTS][gemm_nbt][16 x 16]
+  // fp32, x fp16 [16 gemm_nbt][cols] in gemv_x, tiles per 16-row block
+  float *gemm_part;
+  uint32_t gemm_nbt;
+  uint64_t gemm_tpr;
   const uint32_t *order;     // workgroup k decodes chunk order[k] (NULL: chunk k)
   const uint64_t *xxh;       // expected XXH3-64 of each chunk's compressed bytes (NULL: not checked)
 };
@@ -1568,6 +1579,76 @@ __device__ __forceinline__ void flush_int4_few(Smem<HLOG> &sm, uint32_t lane, co
   }
 }
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// (MODE_GEMM) the scale and zero point of the tile row lane l multiplies:
+// row l % 16 of the tile's 16-row block, whose 128 columns lie in one group
+__device__ __forceinline__ MetaG gemm_meta(const ChunkParams &P, uint64_t dst0, uint32_t t, uint32_t lane) {
+  const uint64_t tg = (dst0 + (uint64_t)t * TILE) / TILE;   // the tile's index in the table
+  const uint64_t rb = tg / P.gemm_tpr, kc = tg - rb * P.gemm_tpr;
+  const uint64_t g = ((16 * rb + (lane & 15)) * P.cols + 128 * kc) >> P.group_shift;
+  // without zero points, read any valid byte and discard it (no branch)
+  const int8_t *zsrc = P.zp ? P.zp : (const int8_t *)P.scales;
+  MetaG m;
+  m.s = P.scales[g];
+  m.z = (uint32_t)(uint8_t)zsrc[g];
+  return m;
+}
+
+// (MODE_GEMM) one tile times the batch: D[w][b] += sum_k W[w][k] x[b][k]
+// over the tile's 16 rows w and 128 columns k, for batch blocks of 16
+// vectors b.  The matrix cores' 16x16x32 fp16 product takes, in lane l,
+// row l % 16 of A with its columns 8 (l / 16) .. + 7, and column l % 16 of
+// B with those rows; A is the tile (lane l dequantizes the 8 codes of its
+// row at columns 32 j + 8 (l / 16) .. + 7: one dword of the history, the
+// write-out's two-magic arithmetic, so the values are the fused kernel's
+// fp16 outputs), B the transposed batch (lane l loads 8 values of vector
+// l % 16).  The products are exact in fp32, the sums are fp32.
+template <int HLOG>
+__device__ __forceinline__ void gemm_block(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, uint32_t T,
+                                           const uint16_t *xs, uint32_t c2, uint32_t s2, float4_t &acc) {
+  constexpr uint32_t HMASK = (1u << HLOG) - 1;
+  uint4 xv[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) xv[j] = *(const uint4 *)(xs + 32 * j);
+  const uint8_t *src = sm.hist + (T & HMASK) + 64 * (lane & 15) + 4 * (lane >> 4);   // a tile never wraps
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint4 a = deq8_int4_dual(*(const uint32_t *)(src + 16 * j), as_h2(c2), as_h2(s2));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, xv[j]),
+                                                 acc, 0, 0, 0);
+  }
+}
+
+template <int HLOG>
+__device__ __forceinline__ void gemm_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
+                                          uint32_t T, const MetaG &m, float4_t (&acc)[2]) {
+  const uint64_t tg = (dst0 + T) / TILE;
+  const uint64_t kc = tg % P.gemm_tpr;
+  const uint16_t *xs = P.gemv_x + (uint64_t)(lane & 15) * P.cols + 128 * kc + 8 * (lane >> 4);
+  const uint32_t s2 = (m.s & 0xFFFFu) * 0x10001u;
+  const int z = P.zp ? (int)(int8_t)m.z : 0;
+  const uint32_t c2 = f16_bits_int(1024 + z) | (f16_bits_int(64 + z) << 16);
+  // one batch block of 16 vectors at a time (the second re-reads the codes)
+  gemm_block<HLOG>(sm, lane, P, T, xs, c2, s2, acc[0]);
+  if (P.gemm_nbt > 1) gemm_block<HLOG>(sm, lane, P, T, xs + 16 * P.cols, c2, s2, acc[1]);
+}
+
+// (MODE_GEMM) a builder's partial products into its slot of the chunk: lane
+// l holds D[4 (l / 16) + v][l % 16] of each batch block
+__device__ __forceinline__ void gemm_store(const ChunkParams &P, uint32_t chunk, uint32_t slot, uint32_t lane,
+                                           const float4_t (&acc)[2]) {
+  float *part = P.gemm_part + ((uint64_t)chunk * GEMM_SLOTS + slot) * 256 * P.gemm_nbt;
+  const uint32_t r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (uint32_t bt = 0; bt < 2; bt++) {
+    if (bt >= P.gemm_nbt) break;
+#pragma unroll
+    for (int v = 0; v < 4; v++) part[256 * bt + (4 * q + v) * 16 + r] = acc[bt][v];
+  }
+}
+
 template <int MODE, int HLOG>
 __device__ __forceinline__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const ChunkParams &P, uint64_t dst0,
                            uint32_t t, uint32_t N, const Meta4 &m, bool fast) {
@@ -1673,6 +1754,8 @@ struct Builder {
   uint32_t done;       // cached: tiles below this are built
   uint32_t fdone;      // cached: tiles below this are built and written out
   uint32_t need_pub;   // announced in need[1 + b]
+  uint32_t chunk = 0;  // the chunk's index in the table (MODE_GEMM's partial-product slot)
+  uint32_t nbs = 0;    // builders in this chunk
 
   __device__ void refresh() {
     const uint2 r = read_rec(ctl);
@@ -2034,14 +2117,21 @@ struct Builder {
     // load and store in flight, the previous tile's stores included
     Meta4 cur{};
     MetaG cug{};
-    if constexpr (G) {
+    MetaG gm{};
+    float4_t gacc[2] = {};
+    if constexpr (MODE == MODE_GEMM) {
+      if (b < ntiles) gm = gemm_meta(P, dst0, b, lane);
+    } else if constexpr (G) {
       if (b < ntiles) cug = int4g_meta(P, dst0, b, lane31, ng);
     } else {
       if (fast && b < ntiles) cur = int4_meta(P, dst0, b, lane, N, few);
     }
     uint32_t u;
     for (uint32_t t = b; t < ntiles; t = u) {
-      const uint32_t uv = grab_issue();
+      // MODE_GEMM assigns tiles statically (builder b takes b, b + nbs, ...):
+      // each builder's partial products then cover a fixed set of tiles,
+      // summed in a fixed order, so the product is the same bits every call
+      const uint32_t uv = MODE == MODE_GEMM ? 0u : grab_issue();
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
       if (!wait_cov(T, Tend)) break;
@@ -2117,7 +2207,7 @@ struct Builder {
           if (__ballot(mine) != ~0ull) break;
         }
       }
-      u = grab_take(uv);
+      u = MODE == MODE_GEMM ? t + nbs : grab_take(uv);
       // tiles before this one that are read
       uint32_t need_tiles = (src_need + TILE - 1) / TILE;
       uint32_t written = 0;
@@ -2152,25 +2242,32 @@ struct Builder {
       // the tile's history bytes are final: tiles that copy from it may
       // start while it is written out
       lds_set(&ctl.built[b], u, lane);
-      if constexpr (G) {
-        cur.s[0] = cug.s;
-        cur.z[0] = cug.z;
-        cur.g0 = (uint32_t)((2 * (dst0 + T)) >> P.group_shift);
-      }
-      if (few && Tend - T == TILE) {
-        meta_pack_few(cur, P.zp != nullptr);
-        flush_int4_few<MODE, HLOG>(sm, lane, P, dst0, T, cur);
+      if constexpr (MODE == MODE_GEMM) {
+        gemm_tile<HLOG>(sm, lane, P, dst0, T, gm, gacc);
       } else {
-        if (fast) meta_ready(cur, P.zp != nullptr, P, dst0, t, lane, N, few);
-        flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
+        if constexpr (G) {
+          cur.s[0] = cug.s;
+          cur.z[0] = cug.z;
+          cur.g0 = (uint32_t)((2 * (dst0 + T)) >> P.group_shift);
+        }
+        if (few && Tend - T == TILE) {
+          meta_pack_few(cur, P.zp != nullptr);
+          flush_int4_few<MODE, HLOG>(sm, lane, P, dst0, T, cur);
+        } else {
+          if (fast) meta_ready(cur, P.zp != nullptr, P, dst0, t, lane, N, few);
+          flush_tile<MODE, HLOG>(sm, lane, P, dst0, t, N, cur, fast);
+        }
       }
       lds_set(&ctl.next_tile[b], u, lane);
-      if constexpr (G) {
+      if constexpr (MODE == MODE_GEMM) {
+        if (u < ntiles) gm = gemm_meta(P, dst0, u, lane);
+      } else if constexpr (G) {
         if (u < ntiles) cug = int4g_meta(P, dst0, u, lane31, ng);
       } else {
         if (fast && u < ntiles) cur = int4_meta(P, dst0, u, lane, N, few);
       }
     }
+    if constexpr (MODE == MODE_GEMM) gemm_store(P, chunk, b, lane, gacc);
     lds_set(&ctl.need[1 + b], 0xFFFFFFFFu, lane);
     lds_set(&ctl.bk[b], 0xFFFFFFFFu, lane);
     lds_set(&ctl.built[b], 0xFFFFFFFFu, lane);
@@ -2200,6 +2297,8 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
              d0 < P.d_first || d1 > P.d_last || (i == 0 && d0 != P.d_first) ||
              (i == P.n - 1 && d1 != P.d_last) || (d0 & 15) != 0 ||
              (MODE == MODE_GEMV && ((d0 | d1) & (TILE - 1)) != 0) ||
+             (MODE == MODE_GEMM && (((d0 | d1) & (TILE - 1)) != 0 || d1 == d0 ||
+                                    d0 / TILE / P.gemm_tpr != (d1 - 1) / TILE / P.gemm_tpr)) ||
              d1 - d0 > (uint64_t)P.max_chunk || c1 - c0 > (uint64_t)LEN_CAP;
   c0 -= P.comp_base;
   c1 -= P.comp_base;
@@ -2262,6 +2361,10 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
       if (lane == 0) ctl.status = st;
       lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
     }
+    if constexpr (MODE == MODE_GEMM) {   // the slots of builders this chunk does not have
+      const float4_t zero[2] = {};
+      for (uint32_t slot = nb; slot < GEMM_SLOTS; slot++) gemm_store(P, i, slot, lane, zero);
+    }
   } else if (wave == 1 && !direct) {
     Rec<Smem<HLOG>> R{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0};
     R.spin = P.spin;
@@ -2274,6 +2377,8 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     hasher(sm, ctl, lane, head, y_end, P.xxh[i], P.spin);
   } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
     Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
+    B.chunk = i;
+    B.nbs = nb;
     B.run();
   }
   __syncthreads();
