@@ -494,6 +494,21 @@ lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint
  * LT_ERR_INVALID_ARG for a non-monotone dst_off. */
 lt_status lt_order_chunks(const uint64_t *dst_off, uint32_t n_chunks, uint32_t *order);
 
+/*
+ * lt_debug_violations -- only in the LT_DEBUG build (liblt_debug.so): the
+ * number of calls of the decoder's exec-narrowing LDS stores that were not
+ * wave-uniform (HOST *count) and the source line of the first (HOST
+ * *first_line, 0 if none), since the library was loaded or last reset;
+ * reset != 0 clears both afterwards.  Synchronous with the device.  The
+ * release build returns LT_ERR_UNSUPPORTED.
+ */
+lt_status lt_debug_violations(uint32_t *count, uint32_t *first_line, int reset);
+/* lt_debug_selftest -- LT_DEBUG build only: one wave on `stream` makes two
+ * calls that break the uniformity rule on purpose (harmless LDS stores; sink
+ * is DEVICE uint32[1] scratch), so that lt_debug_violations then counts 2.
+ * The release build returns LT_ERR_UNSUPPORTED. */
+lt_status lt_debug_selftest(uint32_t *sink, void *stream);
+
 /* Worst-case size of one LZ4 block holding n bytes. */
 uint64_t lt_lz4_bound(uint64_t n);
 

@@ -529,3 +529,10 @@ def test_gemm_arguments_rejected_without_gpu():
     assert call(16, 512, 128, 16, ws) == lt.LT_ERR_INVALID_ARG                  # table size != shape
     assert L.lt_fused_lz4_int4_gemm(None, fake, None, 16, 256, 128, fake, 16, fake, fake, ws, None,
                                     None) == lt.LT_ERR_INVALID_ARG
+
+
+def test_release_build_has_no_debug_counters():
+    L = lt.lib()
+    n = C.c_uint32(5)
+    assert L.lt_debug_violations(C.byref(n), C.byref(n), 0) == lt.LT_ERR_UNSUPPORTED
+    assert L.lt_debug_selftest(None, None) == lt.LT_ERR_UNSUPPORTED

@@ -25,10 +25,17 @@ HIP_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+DEBUG_LIB = os.path.join(PKG, "liblt_debug.so")
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Build liblt.so and, with debug, liblt_debug.so: the same library with
+    LT_DEBUG, whose decoder checks that every exec-narrowing LDS store is
+    called wave-uniformly (lt_debug_violations)."""
     os.makedirs(BUILD, exist_ok=True)
     pack_o = os.path.join(BUILD, "lt_pack.o")
     api_o = os.path.join(BUILD, "lt_api.o")
+    dbg_o = os.path.join(BUILD, "lt_api_debug.o")
     cmds = [
         ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-I" + os.path.join(ROOT, "include"), "-c",
          os.path.join(CSRC, "lt_pack.cpp"), "-o", pack_o],
@@ -36,6 +43,12 @@ def build(verbose: bool = False) -> str:
         [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", api_o, pack_o, "-pthread",
          "-o", LIB + ".tmp"],
     ]
+    if debug:
+        cmds += [
+            [HIPCC, *HIP_FLAGS, "-DLT_DEBUG", "-c", os.path.join(CSRC, "lt_api.hip"), "-o", dbg_o],
+            [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", dbg_o, pack_o, "-pthread",
+             "-o", DEBUG_LIB + ".tmp"],
+        ]
     for c in cmds:
         if verbose:
             print(" ".join(c), flush=True)
@@ -47,6 +60,8 @@ def build(verbose: bool = False) -> str:
         if verbose and err.strip():
             print(err, file=sys.stderr)
     os.replace(LIB + ".tmp", LIB)
+    if debug:
+        os.replace(DEBUG_LIB + ".tmp", DEBUG_LIB)
     return LIB
 
 

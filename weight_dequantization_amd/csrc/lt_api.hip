@@ -969,3 +969,56 @@ const char *lt_status_str(lt_status s) {
 int lt_abi_version(void) { return LT_ABI_VERSION; }
 
 }  // extern "C"
+
+#ifdef LT_DEBUG
+namespace lt {
+// Two calls that break the uniformity rule on purpose (lane 0 inactive; a
+// value that differs between lanes), each a harmless store to a local LDS
+// word: the debug counter must count both.
+__global__ void debug_selftest_kernel(uint32_t *sink) {
+  __shared__ uint32_t x;
+  const uint32_t lane = threadIdx.x & 63;
+  if (lane >= 32) lds_set(&x, 7u);
+  lds_set(&x, lane);
+  __syncthreads();
+  if (threadIdx.x == 0) sink[0] = x;
+}
+}  // namespace lt
+#endif
+
+extern "C" {
+
+lt_status lt_debug_selftest(uint32_t *sink, void *stream) {
+#ifdef LT_DEBUG
+  if (!sink) return LT_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(lt::debug_selftest_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, sink);
+  return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;
+#else
+  (void)sink;
+  (void)stream;
+  return LT_ERR_UNSUPPORTED;
+#endif
+}
+
+lt_status lt_debug_violations(uint32_t *count, uint32_t *first_line, int reset) {
+#ifdef LT_DEBUG
+  if (!count || !first_line) return LT_ERR_INVALID_ARG;
+  if (hipMemcpyFromSymbol(count, HIP_SYMBOL(lt::g_debug_count), sizeof(uint32_t)) != hipSuccess ||
+      hipMemcpyFromSymbol(first_line, HIP_SYMBOL(lt::g_debug_line), sizeof(uint32_t)) != hipSuccess)
+    return LT_ERR_DEVICE;
+  if (reset) {
+    const uint32_t zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(lt::g_debug_count), &zero, sizeof zero) != hipSuccess ||
+        hipMemcpyToSymbol(HIP_SYMBOL(lt::g_debug_line), &zero, sizeof zero) != hipSuccess)
+      return LT_ERR_DEVICE;
+  }
+  return LT_OK;
+#else
+  (void)count;
+  (void)first_line;
+  (void)reset;
+  return LT_ERR_UNSUPPORTED;
+#endif
+}
+
+}  // extern "C"

@@ -290,7 +290,39 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // loop (a lane-dependent branch inside it would make the compiler treat the
 // loop's values as per-lane).  One wave's LDS operations complete in order,
 // so a store made here is seen after every LDS store the wave made before it.
+// The stores below narrow the exec mask to lane 0 (or to lanes 0 .. n-1)
+// inside their asm block, whatever the caller's mask: they are correct only
+// where the call is wave-uniform, lane 0 active and the address and value
+// the same in every active lane (lds_store_lanes: lanes 0 .. n-1 active).
+// An LT_DEBUG build checks this at every call and counts each violation in
+// a device counter (read with lt_debug_violations), with the first one's
+// source line; release builds check nothing.
+#ifdef LT_DEBUG
+__device__ uint32_t g_debug_count;
+__device__ uint32_t g_debug_line;
+__device__ __forceinline__ void debug_flag(bool bad, uint32_t line) {
+  const uint64_t ex = __builtin_amdgcn_read_exec();
+  const uint32_t me = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  if (__ballot(bad) && me == (uint32_t)__builtin_ctzll(ex)) {
+    atomicAdd(&g_debug_count, 1u);
+    atomicCAS(&g_debug_line, 0u, line);
+  }
+}
+__device__ __forceinline__ void debug_uniform(uint32_t a, uint32_t v, uint32_t line) {
+  const bool lane0 = (__builtin_amdgcn_read_exec() & 1ull) != 0;
+  const bool differs = a != (uint32_t)__builtin_amdgcn_readfirstlane(a) || v != (uint32_t)__builtin_amdgcn_readfirstlane(v);
+  debug_flag(!lane0 || differs, line);
+}
+#define LT_UNIFORM(a, v) debug_uniform((a), (v), __LINE__)
+#define LT_LANES(n) debug_flag((__builtin_amdgcn_read_exec() & ((n) >= 64 ? ~0ull : ((1ull << (n)) - 1))) != \
+                                   ((n) >= 64 ? ~0ull : ((1ull << (n)) - 1)), __LINE__)
+#else
+#define LT_UNIFORM(a, v) ((void)0)
+#define LT_LANES(n) ((void)0)
+#endif
+
 __device__ __forceinline__ void lds_set(uint32_t *p, uint32_t v, uint32_t = 0) {
+  LT_UNIFORM(lds_addr(p), v);
   uint64_t sv;
   asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 1\n\tds_write_b32 %1, %2\n\ts_mov_b64 exec, %0"
                : "=&s"(sv) : "v"(lds_addr(p)), "v"(v) : "memory");
@@ -301,6 +333,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // lanes 0 .. n-1 (n <= 64) each store 16 bytes at their own address; the
 // exec mask is narrowed inside the asm block, as for lds_set
 __device__ __forceinline__ void lds_store_lanes(uint32_t addr, u32x4 v, uint32_t n) {
+  LT_LANES(n);
   uint64_t sv, m;
   asm volatile("s_bfm_b64 %1, %4, 0\n\ts_cmp_eq_u32 %4, 64\n\ts_cselect_b64 %1, -1, %1\n\t"
                "s_mov_b64 %0, exec\n\ts_mov_b64 exec, %1\n\tds_write_b128 %2, %3\n\ts_mov_b64 exec, %0"
@@ -309,6 +342,8 @@ __device__ __forceinline__ void lds_store_lanes(uint32_t addr, u32x4 v, uint32_t
 
 // lane 0 stores a 16-byte entry and then a counter
 __device__ __forceinline__ void lds_set_entry(void *e, u32x4 v, uint32_t *p, uint32_t c) {
+  LT_UNIFORM(lds_addr(e), v.x ^ v.y ^ v.z ^ v.w);
+  LT_UNIFORM(lds_addr(p), c);
   uint64_t sv;
   asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 1\n\tds_write_b128 %1, %2\n\t"
                "ds_write_b32 %3, %4\n\ts_mov_b64 exec, %0"
@@ -318,6 +353,7 @@ __device__ __forceinline__ void lds_set_entry(void *e, u32x4 v, uint32_t *p, uin
 // nrec and cov are written together with one 8-byte store and read with one
 // 8-byte load, so a reader never sees coverage by records it does not count.
 __device__ __forceinline__ void publish_rec(Ctl &c, uint32_t nrec, uint32_t cov, uint32_t = 0) {
+  LT_UNIFORM(nrec, cov);
   uint64_t sv;
   const uint64_t v = ((uint64_t)cov << 32) | nrec;
   asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, 1\n\tds_write_b64 %1, %2\n\ts_mov_b64 exec, %0"
