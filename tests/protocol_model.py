@@ -114,8 +114,10 @@ class Chunk:
     """One chunk's decode under the protocol, with a seeded schedule."""
 
     def __init__(self, blk, n_out, index=None, hlog=14, dmax=65535, head=0, seed=0, builders=None, fault=None,
-                 checksum=False, static_tiles=False):
+                 checksum=False, static_tiles=False, spec=False):
         self.fault = fault
+        self.spec = spec      # the byte-output kernel's speculative build
+        self.nspec = 0        # tiles built that way
         self.static_tiles = static_tiles
         self.checksum = checksum
         self.blk = bytes(blk)
@@ -634,6 +636,20 @@ class Chunk:
                 self.bk[b] = k
                 yield
 
+        def wait_done(tiles, written):
+            nonlocal done, fdone
+            while done < tiles or fdone < written:
+                done = min(self.built_to)
+                yield
+                fdone = min(self.next_tile)
+                yield
+                if done >= tiles and fdone >= written:
+                    break
+                if self.pstate == ST_FAIL:
+                    return False
+                yield
+            return True
+
         def announce(T, r):
             nonlocal need_pub
             o, ys, L = r[0], r[1], r[2]
@@ -705,25 +721,28 @@ class Chunk:
             if seen and m > 16 and 2 * (1 + extra) > m:
                 hard = True
             need_tiles = (src_need + TILE - 1) // TILE
-            written = 0
+            slot_tiles = written = 0
             if t >= self.HTILES and self.fault != "no_slot_rule":
                 if reach < self.HTILES:
-                    need_tiles = max(need_tiles, t - self.HTILES + reach + 1)
+                    slot_tiles = t - self.HTILES + reach + 1
+                    need_tiles = max(need_tiles, slot_tiles)
                 else:
-                    need_tiles = t
+                    hard = hard or extra > 0
+                    need_tiles = slot_tiles = t
                 if self.fault != "no_write_rule":
                     written = t - self.HTILES + 1
-            while done < need_tiles or fdone < written:
-                done = min(self.built_to)
-                yield
-                fdone = min(self.next_tile)
-                yield
-                if done >= need_tiles and fdone >= written:
-                    break
-                if self.pstate == ST_FAIL:
-                    ok = False
-                    break
-                yield
+            # speculative build: while the sources are not all built, wait
+            # for the slot rule alone, build at once, then wait for the
+            # sources and make the copies again in record order
+            spec = False
+            if self.spec and not hard and slot_tiles < need_tiles:
+                if done < need_tiles or fdone < written:
+                    done = min(self.built_to)
+                    yield
+                    fdone = min(self.next_tile)
+                    yield
+                spec = done < need_tiles or fdone < written
+            ok = yield from wait_done(slot_tiles if spec else need_tiles, written)
             if not ok:
                 break
             while avail < in_end:
@@ -747,11 +766,29 @@ class Chunk:
                 if not self.written[old]:
                     raise ProtocolError("%s overwrote tile %d's history before its write-out" % (who, old))
             self.hist_tile[slot] = t
+            if spec:   # literals and known-byte runs final, copies not yet
+                self.nspec += 1
+                for j in js:
+                    o, ys, L, dist, fill, flags = rec(j)
+                    a, e = max(o, T), min(o + L, Tend)
+                    if a < e:
+                        lit = self.read_input(ys + (a - o), ys + (e - o), who + " literals")
+                        for q in range(a, e):
+                            self.hist[q % self.HIST] = lit[q - a]
+                            self.hist_owner[q % self.HIST] = t
+                    for q in range(max(o + L, T), min(start_of(j + 1), Tend)):
+                        self.hist_owner[q % self.HIST] = t
+                        self.hist[q % self.HIST] = fill if fill is not None else self.rng.randrange(256)
+                yield
+                if self.fault != "spec_no_wait":
+                    ok = yield from wait_done(need_tiles, written)
+                    if not ok:
+                        break
             for j in js:
                 o, ys, L, dist, fill, flags = rec(j)
                 re = start_of(j + 1)
                 a, e = max(o, T), min(o + L, Tend)
-                if a < e:
+                if a < e and not spec:
                     lit = self.read_input(ys + (a - o), ys + (e - o), who + " literals")
                     for q in range(a, e):
                         self.hist[q % self.HIST] = lit[q - a]

@@ -7,8 +7,10 @@ class), generator-built streams with far and overlapping matches and chunks
 over 64 KiB, and all-literal and long-run blocks; each with and without the
 sequence index and on several schedules.  Every read must see landed,
 unoverwritten input, live records and final history; no schedule may
-deadlock; the decode must equal the expected bytes.  The model is also
-shown to catch planted protocol mistakes.
+deadlock; the decode must equal the expected bytes.  Every case runs
+again with the byte-output kernel's speculative build (a tile whose sources
+are not built yet is built at once, then its copies are made again after the
+wait).  The model is also shown to catch planted protocol mistakes.
 """
 import numpy as np
 import pytest
@@ -27,14 +29,19 @@ def _chunks(comp, comp_off, dst_off, src, picks):
 
 
 def _run(blk, expect, idx, hlog, dmax, seeds, what):
+    """Returns how many tiles were built speculatively."""
+    nspec = 0
     for seed in seeds:
         for indexed in (True, False):
-            c = Chunk(blk, len(expect), index=idx if indexed else None, hlog=hlog, dmax=dmax, head=seed % 16,
-                      seed=seed)
-            st, out, _ = c.run()
-            assert st == 0, (what, seed, indexed, st)
-            assert out == expect, (what, seed, indexed)
-            assert all(v == 1 for v in c.built), (what, seed, indexed)
+            for spec in (False, True):
+                c = Chunk(blk, len(expect), index=idx if indexed else None, hlog=hlog, dmax=dmax, head=seed % 16,
+                          seed=seed, spec=spec)
+                st, out, _ = c.run()
+                assert st == 0, (what, seed, indexed, spec, st)
+                assert out == expect, (what, seed, indexed, spec)
+                assert all(v == 1 for v in c.built), (what, seed, indexed, spec)
+                nspec += c.nspec
+    return nspec
 
 
 def test_weight_layer_chunks():
@@ -50,11 +57,13 @@ def test_activation_chunks_with_stress_blocks():
     a = synth.activation(1024, 8192, 1104)
     picks = sorted(set(a.stress["random"] + a.stress["all_ab"] + a.stress["ab_run"] + [0, 1, 100]))
     comp, comp_off = lt.compress_chunks(a.data, a.dst_off, max_dist=lt.PACK_WINDOW)
+    nspec = 0
     for i, blk, expect, idx in _chunks(comp, comp_off, a.dst_off, a.data, picks):
-        _run(blk, expect, idx, 14, lt.PACK_WINDOW, (4, 5), "activation chunk %d, packer" % i)
+        nspec += _run(blk, expect, idx, 14, lt.PACK_WINDOW, (4, 5), "activation chunk %d, packer" % i)
     ot = O.compress_table(a.data, a.dst_off)
     for i, blk, expect, idx in _chunks(ot.comp, ot.comp_off, a.dst_off, a.data, picks):
-        _run(blk, expect, idx, 16, 65535, (6, 7), "activation chunk %d, oracle compressor" % i)
+        nspec += _run(blk, expect, idx, 16, 65535, (6, 7), "activation chunk %d, oracle compressor" % i)
+    assert nspec > 0   # the speculative build was taken
 
 
 @pytest.mark.parametrize("target", [5000, 70000, 262144])
@@ -99,6 +108,21 @@ def test_model_catches_planted_mistakes():
     i64 = lt.index_chunks(b64, o64)[1]
     for fault in ("no_window", "early_need"):
         assert _fault_caught(fault, b64, p64.tobytes(), i64, 14, lt.PACK_WINDOW, 4) >= 3, fault
+    # a speculatively built tile whose copies are made again without waiting
+    # for their sources
+    a = synth.activation(1024, 8192, 1104)
+    ab, ao = lt.compress_chunks(a.data, a.dst_off, max_dist=lt.PACK_WINDOW)
+    caught = 0
+    for i, blk, expect, idx in _chunks(ab, ao, a.dst_off, a.data, a.stress["ab_run"][:2] + [0, 1]):
+        for seed in range(3):
+            c = Chunk(blk, len(expect), index=idx, hlog=14, dmax=lt.PACK_WINDOW, seed=seed, spec=True,
+                      fault="spec_no_wait")
+            try:
+                _, out, _ = c.run()
+                caught += out != expect
+            except ProtocolError:
+                caught += 1
+    assert caught >= 1
     # a slot reused while the tile that held it is still being written out
     b256, o256 = lt.compress_chunks(p256, np.array([0, p256.size], np.uint64), max_dist=lt.PACK_WINDOW)
     i256 = lt.index_chunks(b256, o256)[1]

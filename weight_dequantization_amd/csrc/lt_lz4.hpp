@@ -1811,6 +1811,16 @@ struct Builder {
     return true;
   }
 
+  // true if the tiles below `tiles` are built and those below `written`
+  // written out too (one look, no wait)
+  __device__ __forceinline__ bool ready(uint32_t tiles, uint32_t written) {
+    if (done < tiles || fdone < written) {
+      done = min8(ctl.built);
+      fdone = min8(ctl.next_tile);
+    }
+    return done >= tiles && fdone >= written;
+  }
+
   // wait until tiles [0, tiles) are final; false if the chunk failed first
   // Wait until the tiles below `tiles` are built and those below `written`
   // are written out too; false if the chunk failed first.
@@ -2101,20 +2111,52 @@ struct Builder {
     return (acc & keep) | (v & ~keep);
   }
 
-  // Build [T, Tend) from the m records k .. k + m - 1 held in lanes 0 .. m - 1
-  // of rv (lane m holds the end of the last one; rve holds each record's end,
-  // the start of the next), in 1 + extra passes.  Each
-  // lane builds its 16 bytes from the pieces that meet them, in order; the
-  // first piece covers the block's first byte.
-  __device__ __forceinline__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t rve, uint32_t m, uint32_t extra) {
+  // The copies of a tile built before their sources were all final, made
+  // again in record order now that they are: record i's copy is the part of
+  // its match in [T, Tend) that is not a run of a known byte (rv and rve as
+  // for tile_bulk; a tile built this way has no overlapping copy other than
+  // distance-1 runs, and every source lies before the bytes it fills).
+  __device__ __forceinline__ void redo_copies(uint32_t T, uint32_t Tend, uint4 rv, uint32_t rve, uint32_t m) {
+    const uint32_t le = rv.x + rv.z;
+    const uint32_t base = le > T ? le : T;
+    const uint32_t pend = rve < Tend ? rve : Tend;
+    uint64_t cps = __ballot(lane < m && base < pend && !(rv.w & F_FILL));
+    while (cps) {
+      const uint32_t i = (uint32_t)__builtin_ctzll(cps);
+      cps &= cps - 1;
+      const uint32_t a = __builtin_amdgcn_readlane(base, i), n = __builtin_amdgcn_readlane(pend, i) - a;
+      const uint32_t dist = rec_dist(__builtin_amdgcn_readlane(rv.w, i));
+      if (n <= 64) {
+        match_lanes(dist, a, n);
+      } else if (dist == 1) {   // a run of the byte before it
+        fill_exact(a, __builtin_amdgcn_readfirstlane(sm.hist[(a - 1) & HMASK]), n);
+      } else {
+        copy_exact<HMASK>(sm.hist, a - dist, a, n);   // dist >= n: no source among the bytes written
+      }
+    }
+  }
+
+  // the record (of the m in lanes 0 .. m - 1 of rv) under the first byte of
+  // this lane's block of the tile at T
+  __device__ __forceinline__ uint32_t first_rec(uint32_t T, uint4 rv, uint32_t m) const {
     const uint32_t P = T + 16 * lane;
-    const uint32_t bend = P + 16 < Tend ? P + 16 : Tend;
-    // the record under the block's first byte
     uint32_t j0 = 0;
     for (uint32_t i = 1; i < m; i++) {
       const uint32_t xi = __builtin_amdgcn_readlane(rv.x, i);
       j0 = (xi <= P) ? i : j0;
     }
+    return j0;
+  }
+
+  // Build [T, Tend) from the m records k .. k + m - 1 held in lanes 0 .. m - 1
+  // of rv (lane m holds the end of the last one; rve holds each record's end,
+  // the start of the next), in 1 + extra passes.  Each lane builds its 16
+  // bytes from the pieces that meet them, in order, from record j0 (the one
+  // under the block's first byte).
+  __device__ __forceinline__ void tile_bulk(uint32_t T, uint32_t Tend, uint4 rv, uint32_t rve, uint32_t j0,
+                                            uint32_t extra) {
+    const uint32_t P = T + 16 * lane;
+    const uint32_t bend = P + 16 < Tend ? P + 16 : Tend;
     const uint32_t inr_at = lds_addr(sm.inr), hist_at = lds_addr(sm.hist);
     for (uint32_t pass = 0; pass <= extra; pass++) {
       uint32_t pos = P, j = j0;
@@ -2246,6 +2288,7 @@ struct Builder {
       u = MODE == MODE_GEMM ? t + nbs : grab_take(uv);
       // tiles before this one that are read
       uint32_t need_tiles = (src_need + TILE - 1) / TILE;
+      uint32_t slot_tiles = 0;   // the tiles the slot rule alone waits for
       uint32_t written = 0;
       if (t >= HTILES) {
         // This tile overwrites the ring slot of tile t - HTILES, whose
@@ -2262,18 +2305,41 @@ struct Builder {
         if (reach < HTILES) {
           const uint32_t fin = t - HTILES + reach + 1;
           need_tiles = need_tiles > fin ? need_tiles : fin;
+          slot_tiles = fin;
         } else {
           if (extra) hard = true;
           need_tiles = t;
+          slot_tiles = t;
         }
       }
       if (t >= HTILES) written = t - HTILES + 1;
-      if (!wait_done(need_tiles, written)) break;
+      // The tiles after this one wait for it, so while its sources are not
+      // all built it is built at once from whatever the history holds
+      // (literals and runs of a known byte are final then), and after the
+      // wait only its copies are made again, in record order: the wait ends
+      // in a few copies instead of a whole build.  (Only when no source can
+      // share this tile's own slot: slot_tiles < need_tiles then.)  The
+      // record under each lane's first byte is found before the wait too.
+      // Byte output only: on quantised weights, whose matches are short and
+      // rarely chained, the extra code measured slower than the waits it
+      // saves.
+      constexpr bool SPEC = MODE == MODE_BYTES;
+      uint32_t j0 = 0;
+      if constexpr (SPEC) {
+        if (!hard) j0 = first_rec(T, rv, m);
+      }
+      const bool spec = SPEC && !hard && slot_tiles < need_tiles && !ready(need_tiles, written);
+      if (!wait_done(spec ? slot_tiles : need_tiles, written)) break;
       if (hard) {
         if (!tile_exact(T, Tend)) break;
       } else {
         if (!need_input(in_end)) break;
-        tile_bulk(T, Tend, rv, re, m, extra);
+        if constexpr (!SPEC) j0 = first_rec(T, rv, m);
+        tile_bulk(T, Tend, rv, re, j0, spec ? 0u : extra);
+        if (spec) {
+          if (!wait_done(need_tiles, written)) break;
+          redo_copies(T, Tend, rv, re, m);
+        }
       }
       // the tile's history bytes are final: tiles that copy from it may
       // start while it is written out
