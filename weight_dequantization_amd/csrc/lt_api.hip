@@ -262,26 +262,41 @@ uint32_t shift_of(uint64_t g) {
   return (g & (g - 1)) == 0 ? (uint32_t)__builtin_ctzll(g) : 64u;
 }
 
+template <int MODE, bool SPEC>
+void launch_kernel(bool small, hipStream_t s, const lt::ChunkParams &P) {
+  if (small) {
+    hipLaunchKernelGGL((lt::chunk_kernel<MODE, 14, SPEC>), dim3(P.n), dim3(lt::NTHREADS), 0, s, P);
+  } else {
+    hipLaunchKernelGGL((lt::chunk_kernel<MODE, 16, SPEC>), dim3(P.n), dim3(lt::NTHREADS), 0, s, P);
+  }
+}
+
 lt_status launch_params(int mode, lt::ChunkParams &P, void *stream) {
   hipStream_t s = (hipStream_t)stream;
-  dim3 grid(P.n), block(lt::NTHREADS);
   // a declared short window lets each chunk keep a 16 KiB history, so more
   // chunks share a CU
   const bool small = P.dmax <= LT_SMALL_WINDOW;
   if (mode == lt::MODE_INT4 && P.group_shift < 64 && P.group >= 128) mode = lt::MODE_INT4G;
-  switch (mode * 2 + (small ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 16>), grid, block, 0, s, P); break;
-    case 1: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_BYTES, 14>), grid, block, 0, s, P); break;
-    case 2: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 16>), grid, block, 0, s, P); break;
-    case 3: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4, 14>), grid, block, 0, s, P); break;
-    case 4: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 16>), grid, block, 0, s, P); break;
-    case 5: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT8, 14>), grid, block, 0, s, P); break;
-    case 6: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 16>), grid, block, 0, s, P); break;
-    case 7: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_INT4G, 14>), grid, block, 0, s, P); break;
-    case 8: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMV, 16>), grid, block, 0, s, P); break;
-    case 9: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMV, 14>), grid, block, 0, s, P); break;
-    case 10: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMM, 16>), grid, block, 0, s, P); break;
-    case 11: hipLaunchKernelGGL((lt::chunk_kernel<lt::MODE_GEMM, 14>), grid, block, 0, s, P); break;
+  // Speculative tile builds pay where tiles wait on the tiles just before
+  // them: general-purpose LZ4 parses (about 4.5 sequences per KiB on INT4
+  // weights, twice as fast with them) and activations (decode-only always
+  // takes them).  On the host packer's weight blocks (about 2.6 per KiB)
+  // they cost 1-2.5%, so a table whose index counts fewer than 3.5
+  // sequences per KiB goes without; a table without an index takes them.
+  const bool spec = !P.seq_off || P.n_seq * 2048 >= 7 * P.total;
+  switch (mode) {
+    case lt::MODE_BYTES: launch_kernel<lt::MODE_BYTES, true>(small, s, P); break;
+    case lt::MODE_INT4:
+      spec ? launch_kernel<lt::MODE_INT4, true>(small, s, P) : launch_kernel<lt::MODE_INT4, false>(small, s, P);
+      break;
+    case lt::MODE_INT8:
+      spec ? launch_kernel<lt::MODE_INT8, true>(small, s, P) : launch_kernel<lt::MODE_INT8, false>(small, s, P);
+      break;
+    case lt::MODE_INT4G:
+      spec ? launch_kernel<lt::MODE_INT4G, true>(small, s, P) : launch_kernel<lt::MODE_INT4G, false>(small, s, P);
+      break;
+    case lt::MODE_GEMV: launch_kernel<lt::MODE_GEMV, false>(small, s, P); break;
+    case lt::MODE_GEMM: launch_kernel<lt::MODE_GEMM, false>(small, s, P); break;
     default: return LT_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? LT_OK : LT_ERR_LAUNCH;

@@ -1771,8 +1771,9 @@ __device__ __forceinline__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const 
 // ------------------------------------------------------------ builders
 
 // Waves 3 .. 3 + NB - 1.  Builder b starts with tile b and then takes the
-// next untaken tile each time it starts one.
-template <int MODE, int HLOG>
+// next untaken tile each time it starts one.  SPEC: tiles whose sources are
+// not yet built may be built speculatively (see run()).
+template <int MODE, int HLOG, bool SPEC>
 struct Builder {
   static constexpr uint32_t HIST = 1u << HLOG, HMASK = HIST - 1, HTILES = HIST / TILE;
   static constexpr uint32_t IMASK = Smem<HLOG>::IMASK;
@@ -2320,10 +2321,6 @@ struct Builder {
       // in a few copies instead of a whole build.  (Only when no source can
       // share this tile's own slot: slot_tiles < need_tiles then.)  The
       // record under each lane's first byte is found before the wait too.
-      // Byte output only: on quantised weights, whose matches are short and
-      // rarely chained, the extra code measured slower than the waits it
-      // saves.
-      constexpr bool SPEC = MODE == MODE_BYTES;
       uint32_t j0 = 0;
       if constexpr (SPEC) {
         if (!hard) j0 = first_rec(T, rv, m);
@@ -2380,7 +2377,7 @@ struct Builder {
 
 // -------------------------------------------------------------- kernel
 
-template <int MODE, int HLOG>
+template <int MODE, int HLOG, bool SPEC>
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) chunk_kernel(ChunkParams P) {
   __shared__ __attribute__((aligned(16))) Smem<HLOG> sm;
   __shared__ Ctl ctl;
@@ -2478,7 +2475,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
   } else if (wave == hwave) {
     hasher(sm, ctl, lane, head, y_end, P.xxh[i], P.spin);
   } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
-    Builder<MODE, HLOG> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
+    Builder<MODE, HLOG, SPEC> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
     B.chunk = i;
     B.nbs = nb;
     B.run();
