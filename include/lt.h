@@ -164,7 +164,11 @@ typedef struct lt_chunk_table {
 } lt_chunk_table;
 
 /*
- * lt_decode_lz4 -- decode-only mode (zero-heavy activations, or any bytes).
+ * lt_decode_lz4 -- decode-only mode (zero-heavy activations, or any bytes):
+ * the chunk-parallel LZ4 block decompression of page "GPU Compression
+ * Pipeline - TDD Roadmap", Phase 3.1, with nothing fused after it; the
+ * activations it serves are the mostly-zero ReLU outputs that page
+ * "Openai/691a41cd-... (section 38)" lists among the compression targets.
  * dst: DEVICE uint8[t->total_bytes], 16-byte aligned.
  * chunk_status: DEVICE int32[t->n_chunks] or NULL.
  * Decodes every chunk of the table into dst.  One workgroup per chunk.
