@@ -150,7 +150,8 @@ def plain_lz4_forms(torch, lt, packed, comp, comp_off, w, scales, zp, dev, out_r
     forms = (
         ("packer_blocks_no_index", lambda: lt.ChunkTable.from_host(comp, comp_off, w.dst_off, dev, lt.PACK_WINDOW)),
         ("greedy_64k_window_no_index", lambda: lt.ChunkTable.from_host(gcomp, gcomp_off, w.dst_off, dev, 0)),
-        ("greedy_64k_window_indexed", lambda: lt.ChunkTable.from_host(gcomp, gcomp_off, w.dst_off, dev, 0, index=True)),
+        ("greedy_64k_window_indexed", lambda: lt.ChunkTable.from_host(gcomp, gcomp_off, w.dst_off, dev, 0, index=True,
+                                                                      order=True)),
     )
     n_seq = {False: int(lt.index_chunks(comp, comp_off)[1].size),
              True: int(lt.index_chunks(gcomp, gcomp_off)[1].size)}
@@ -310,7 +311,7 @@ def bench_int4_layer(args) -> int:
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
-            "kernel": "lt::chunk_kernel<3, 14, false>", "avg_launch_ms": round(avg_kern_ms, 5),
+            "kernel": "lt::chunk_kernel<3, 14, false, false>", "avg_launch_ms": round(avg_kern_ms, 5),
             "min_launch_ms": round(float(np.min(kern_ms)), 5),
             "bytes_per_launch": alg_bytes,
         },
@@ -426,7 +427,7 @@ def bench_int8(args) -> int:
                                           n_elem, n_elem)},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "lt::chunk_kernel<2, 14, false>", "avg_launch_ms": round(kf, 5), "bytes_per_launch": alg},
+                     "kernel": "lt::chunk_kernel<2, 14, false, false>", "avg_launch_ms": round(kf, 5), "bytes_per_launch": alg},
         "two_pass": {"decode_ms": round(kd, 5), "dequant_ms": round(kq, 5), "total_ms": round(kd + kq, 5),
                      "GBps": round(alg / (kd + kq) / 1e6, 2), "fused_speedup": round((kd + kq) / kf, 3),
                      "mismatches_vs_fused": bad_two},
@@ -577,7 +578,7 @@ def bench_stack(args) -> int:
                    "compressed_bytes_resident": int(sum(layer_comp)), "fp16_bytes_per_layer": 2 * n_elem_layer},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "lt::chunk_kernel<3, 14, false>", "bytes_per_launch": None},
+                     "kernel": "lt::chunk_kernel<3, 14, false, false>", "bytes_per_launch": None},
         "layer_concurrent": conc,
         "layer_sequential": seq,
     }

@@ -123,7 +123,9 @@ enum {
  *              not listed is neither decoded nor given a status.  A launch
  *              lasts at least as long as its slowest chunk, so tables whose
  *              chunks differ in size start the largest first
- *              (lt_order_chunks).  Chunk-range and streamed calls decode in
+ *              (lt_order_chunks), and sequence-dense tables also the chunks
+ *              with the most sequences (lt_order_chunks_by_sequences).
+ *              Chunk-range and streamed calls decode in
  *              table order and ignore it.
  *   xxh        DEVICE uint64[n_chunks] or NULL: the expected XXH3-64 (seed 0)
  *              of each chunk's compressed bytes comp[comp_off[i] ..
@@ -497,6 +499,16 @@ lt_status lt_checksum_chunks(const uint8_t *comp, const uint64_t *comp_off, uint
  * (dst_off[i+1] - dst_off[i]); chunks of one size keep table order.
  * LT_ERR_INVALID_ARG for a non-monotone dst_off. */
 lt_status lt_order_chunks(const uint64_t *dst_off, uint32_t n_chunks, uint32_t *order);
+
+/* The order field of a sequence-dense table (HOST arrays): like
+ * lt_order_chunks, and chunks of one size by decreasing sequence count
+ * (seq_off[i+1] - seq_off[i], the table's sequence index offsets); equal
+ * counts keep table order.  A chunk with many short sequences lives longer
+ * than one of the same size with few, and a launch lasts as long as its
+ * slowest chunk, so those start first.  LT_ERR_INVALID_ARG for a NULL
+ * array or a non-monotone dst_off or seq_off. */
+lt_status lt_order_chunks_by_sequences(const uint64_t *dst_off, const uint64_t *seq_off, uint32_t n_chunks,
+                                       uint32_t *order);
 
 /*
  * lt_debug_violations -- only in the LT_DEBUG build (liblt_debug.so): the

@@ -482,6 +482,32 @@ def test_order_chunks_starts_the_largest_first():
         lt.order_chunks(bad)
 
 
+def test_order_chunks_by_sequences():
+    """On a sequence-dense table the launch order is by decreasing decoded
+    size, then by decreasing sequence count, equal counts in table order."""
+    rng = np.random.default_rng(9)
+    n = 700
+    sizes = rng.choice([16384, 65536], n)
+    seqs = rng.integers(0, 40, n)
+    seqs[::7] = 17                                   # ties keep table order
+    dst_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.uint64)
+    seq_off = np.concatenate([[0], np.cumsum(seqs)]).astype(np.uint64)
+    order = lt.order_chunks(dst_off, seq_off)
+    assert sorted(order.tolist()) == list(range(n))
+    assert order.tolist() == sorted(range(n), key=lambda i: (-int(sizes[i]), -int(seqs[i]), i))
+    one = np.arange(0, 5 * 65536, 65536, dtype=np.uint64)
+    assert lt.order_chunks(one, np.array([0, 3, 3, 10, 11], np.uint64)).tolist() == [2, 0, 3, 1]
+    L = lt.lib()
+    out = np.zeros(4, np.uint32)
+    assert L.lt_order_chunks_by_sequences(one.ctypes.data_as(C.c_void_p), None, 4,
+                                          out.ctypes.data_as(C.c_void_p)) == lt.LT_ERR_INVALID_ARG
+    bad = np.array([0, 3, 2, 10, 11], np.uint64)        # seq_off not monotone
+    with pytest.raises(lt.LtError):
+        lt.order_chunks(one, bad)
+    with pytest.raises(ValueError):
+        lt.order_chunks(one, seq_off[:3])
+
+
 def test_file_stream_arguments_rejected_without_gpu():
     """The file-streaming calls refuse a bad descriptor, a missing or too
     small pinned buffer and a bad table before any device work."""

@@ -131,6 +131,7 @@ def _lib():
             "lt_compress_chunks_greedy": (i32, [vp, vp, u32, vp, u64, vp, i32, u32]),
             "lt_index_chunks": (i32, [vp, vp, u32, vp, vp, u64, i32]),
             "lt_order_chunks": (i32, [vp, u32, vp]),
+            "lt_order_chunks_by_sequences": (i32, [vp, vp, u32, vp]),
             "lt_gemm_workspace_bytes": (u64, [u32, u32]),
             "lt_fused_lz4_int4_gemm": (i32, [tp, vp, vp, u64, u64, u64, vp, u32, vp, vp, u64, vp, vp]),
             "lt_status_str": (C.c_char_p, [i32]),
@@ -239,13 +240,20 @@ def index_chunks(comp: np.ndarray, comp_off: np.ndarray, threads: int = 0):
     return seq_off, seq_pos[:int(seq_off[-1])]
 
 
-def order_chunks(dst_off: np.ndarray) -> np.ndarray:
+def order_chunks(dst_off: np.ndarray, seq_off: np.ndarray = None) -> np.ndarray:
     """A table's launch order (uint32 [n]): chunks by decreasing decoded
-    size, chunks of one size in table order."""
+    size, chunks of one size in table order, or with the sequence index's
+    offsets by decreasing sequence count."""
     dst_off = np.ascontiguousarray(dst_off, np.uint64)
     n = dst_off.size - 1
     order = np.zeros(max(n, 1), np.uint32)
-    st = _lib().lt_order_chunks(_np_ptr(dst_off), max(n, 0), _np_ptr(order))
+    if seq_off is None:
+        st = _lib().lt_order_chunks(_np_ptr(dst_off), max(n, 0), _np_ptr(order))
+    else:
+        seq_off = np.ascontiguousarray(seq_off, np.uint64)
+        if seq_off.size != dst_off.size:
+            raise ValueError("seq_off must have one entry per chunk plus one")
+        st = _lib().lt_order_chunks_by_sequences(_np_ptr(dst_off), _np_ptr(seq_off), max(n, 0), _np_ptr(order))
     if st != LT_OK:
         raise LtError(st, "lt_order_chunks")
     return order[:n]
@@ -304,8 +312,11 @@ class ChunkTable:
         """Place a host-built table on `device`; with device="cpu" and
         pin=True the arrays go to pinned host memory, the form the streamed
         entry points read.  index adds the sequence index, order the launch
-        order (order_chunks) when the chunks differ in size, checksum each
-        chunk's XXH3-64 (checksum_chunks), which every decode then checks."""
+        order (order_chunks) when the chunks differ in size or the index
+        shows a sequence-dense table (3.5 or more sequences per KiB, the
+        tables the decoder builds speculatively: then chunks of one size go
+        by sequence count), checksum each chunk's XXH3-64 (checksum_chunks),
+        which every decode then checks."""
         comp_off = np.ascontiguousarray(comp_off, np.uint64)
         dst_off = np.ascontiguousarray(dst_off, np.uint64)
         n = dst_off.size - 1
@@ -318,10 +329,14 @@ class ChunkTable:
                 n, max(1, int(sizes.max())) if n > 0 else 0, int(dst_off[-1]) if n >= 0 else 0,
                 int(comp_off[-1]) if comp_off.size else 0, max_dist)
         t.host_dst_off = dst_off.copy()
+        seq_off = None
         if index and n > 0:
             seq_off, seq_pos = index_chunks(comp, comp_off)
             t.set_index(seq_off, seq_pos, device, pin)
-        if order and n > 0 and np.unique(sizes).size > 1:   # one size: table order already
+        dense = seq_off is not None and int(seq_off[-1]) * 2048 >= 7 * int(dst_off[-1])
+        if order and n > 0 and dense:
+            t.order = _place(order_chunks(dst_off, seq_off).view(np.int32), device, pin)
+        elif order and n > 0 and np.unique(sizes).size > 1:   # one size: table order already
             t.order = _place(order_chunks(dst_off).view(np.int32), device, pin)
         if checksum and n > 0:
             t.xxh = _place(checksum_chunks(comp, comp_off).view(np.int64), device, pin)
@@ -378,7 +393,8 @@ class ChunkTable:
         declares, so the device decoder keeps a short history per chunk, and
         the table carries the sequence index, so each chunk's sequences are
         parsed side by side, and a launch order that starts the largest
-        chunks first.  greedy=True packs with the plain greedy parse
+        chunks first (on sequence-dense tables, then those with the most
+        sequences).  greedy=True packs with the plain greedy parse
         (compress_chunks); checksum=True stores each chunk's XXH3-64, which
         every decode of the table then checks."""
         if max_dist is None:

@@ -262,13 +262,20 @@ uint32_t shift_of(uint64_t g) {
   return (g & (g - 1)) == 0 ? (uint32_t)__builtin_ctzll(g) : 64u;
 }
 
-template <int MODE, bool SPEC>
+template <int MODE, bool SPEC, bool LPF = false>
 void launch_kernel(bool small, hipStream_t s, const lt::ChunkParams &P) {
   if (small) {
-    hipLaunchKernelGGL((lt::chunk_kernel<MODE, 14, SPEC>), dim3(P.n), dim3(lt::NTHREADS), 0, s, P);
+    hipLaunchKernelGGL((lt::chunk_kernel<MODE, 14, SPEC, LPF>), dim3(P.n), dim3(lt::NTHREADS), 0, s, P);
   } else {
-    hipLaunchKernelGGL((lt::chunk_kernel<MODE, 16, SPEC>), dim3(P.n), dim3(lt::NTHREADS), 0, s, P);
+    hipLaunchKernelGGL((lt::chunk_kernel<MODE, 16, SPEC, LPF>), dim3(P.n), dim3(lt::NTHREADS), 0, s, P);
   }
+}
+
+// the kernel for a table that takes the speculative build: with progress
+// priority too when its index shows it sequence-dense (lt::prio_by_progress)
+template <int MODE>
+void launch_spec(bool dense, bool small, hipStream_t s, const lt::ChunkParams &P) {
+  dense ? launch_kernel<MODE, true, true>(small, s, P) : launch_kernel<MODE, true, false>(small, s, P);
 }
 
 lt_status launch_params(int mode, lt::ChunkParams &P, void *stream) {
@@ -283,17 +290,22 @@ lt_status launch_params(int mode, lt::ChunkParams &P, void *stream) {
   // takes them).  On the host packer's weight blocks (about 2.6 per KiB)
   // they cost 1-2.5%, so a table whose index counts fewer than 3.5
   // sequences per KiB goes without; a table without an index takes them.
-  const bool spec = !P.seq_off || P.n_seq * 2048 >= 7 * P.total;
+  // The sequence-dense tables (index present, 3.5 or more per KiB) also take
+  // progress priority; without an index the density is unknown and the
+  // weight tables the packer writes are not dense, so those keep the
+  // default (oldest waves first).
+  const bool dense = P.seq_off && P.n_seq * 2048 >= 7 * P.total;
+  const bool spec = !P.seq_off || dense;
   switch (mode) {
-    case lt::MODE_BYTES: launch_kernel<lt::MODE_BYTES, true>(small, s, P); break;
+    case lt::MODE_BYTES: launch_spec<lt::MODE_BYTES>(dense, small, s, P); break;
     case lt::MODE_INT4:
-      spec ? launch_kernel<lt::MODE_INT4, true>(small, s, P) : launch_kernel<lt::MODE_INT4, false>(small, s, P);
+      spec ? launch_spec<lt::MODE_INT4>(dense, small, s, P) : launch_kernel<lt::MODE_INT4, false>(small, s, P);
       break;
     case lt::MODE_INT8:
-      spec ? launch_kernel<lt::MODE_INT8, true>(small, s, P) : launch_kernel<lt::MODE_INT8, false>(small, s, P);
+      spec ? launch_spec<lt::MODE_INT8>(dense, small, s, P) : launch_kernel<lt::MODE_INT8, false>(small, s, P);
       break;
     case lt::MODE_INT4G:
-      spec ? launch_kernel<lt::MODE_INT4G, true>(small, s, P) : launch_kernel<lt::MODE_INT4G, false>(small, s, P);
+      spec ? launch_spec<lt::MODE_INT4G>(dense, small, s, P) : launch_kernel<lt::MODE_INT4G, false>(small, s, P);
       break;
     case lt::MODE_GEMV: launch_kernel<lt::MODE_GEMV, false>(small, s, P); break;
     case lt::MODE_GEMM: launch_kernel<lt::MODE_GEMM, false>(small, s, P); break;

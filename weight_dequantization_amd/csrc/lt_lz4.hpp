@@ -370,6 +370,23 @@ __device__ __forceinline__ uint2 read_rec(Ctl &c) {
 // a value every lane holds, stated so the compiler keeps it in a scalar register
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Issue priority from a chunk's progress (done of total, wave-uniform): 3 in
+// its first quarter down to 0 in its last.  Every wave of a chunk of a
+// sequence-dense table (the kernels with LPF) calls it as it advances, so the
+// chunks resident on a CU move forward together instead of oldest first.
+// Such chunks vary widely in how long they live, and the launch ends with
+// the slowest: decode-only on ReLU activations is 8% faster with it, greedy
+// LZ4 blocks of a weight layer 2%; on the packer's weight tables the same
+// was 9% slower (13% without the index), as oldest-first frees each CU's
+// slots early, which the second round of chunks needs.
+__device__ __forceinline__ void prio_by_progress(uint32_t done, uint32_t total) {
+  const uint32_t d4 = 4u * __builtin_amdgcn_readfirstlane(done), t = __builtin_amdgcn_readfirstlane(total);
+  if (d4 < t) __builtin_amdgcn_s_setprio(3);
+  else if (d4 < 2 * t) __builtin_amdgcn_s_setprio(2);
+  else if (d4 < 3 * t) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // A load from device memory through a global (not flat) address: a flat
 // load also counts in the LDS wait counter, so every LDS wait after it would
 // wait for the memory round trip too.
@@ -666,7 +683,8 @@ struct Rec {
 // the walker announces a literal run before it waits for the bytes after it,
 // so the builders can release the ring.  Only the chain wait can end with the
 // recorder gone (a failed chunk): then the walk stops.
-template <class SM>
+// LPF: the issue priority follows the walk's progress (prio_by_progress)
+template <class SM, bool LPF = false>
 struct Walker {
   static constexpr uint32_t INR = SM::INR, IMASK = SM::IMASK, CHAIN = SM::CHAIN;
   SM &sm;
@@ -1195,6 +1213,7 @@ struct Walker {
     }
     ij += took;
     y = uni(__builtin_amdgcn_readlane(pn, took - 1));
+    if constexpr (LPF) prio_by_progress(y, y_end);
     if (y - pub >= SEG) {
       pub = y;
       lds_set(&ctl.need[0], pub);
@@ -1238,6 +1257,7 @@ struct Walker {
   }
 
   __device__ __forceinline__ void run() {
+    if constexpr (LPF) prio_by_progress(0, 1);
     if (icnt) {
       run_indexed();
     } else {
@@ -1245,6 +1265,7 @@ struct Walker {
         y = uni(y);
         if (fast_step()) {
           if (stop) break;
+          if constexpr (LPF) prio_by_progress(y, y_end);
           continue;
         }
         have_tw = 0;
@@ -1369,7 +1390,7 @@ __device__ __forceinline__ uint64_t ring8(const SM &sm, uint32_t pos) {
 // and the exit check (every reader gone: a failed chunk) is made only when
 // nothing is in flight.  With a checksum (`whole`) the block is streamed to
 // its end in any case, for the hasher.
-template <class SM>
+template <class SM, bool LPF>
 __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const uint8_t *S, uint32_t y_end, uint32_t nb,
                                        uint32_t spin, bool whole) {
   constexpr uint32_t IMASK = SM::IMASK, QMAX = SM::QMAX;
@@ -1378,6 +1399,7 @@ __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const ui
   const uint32_t nseg = (y_end + SEG - 1) / SEG;
   uint32_t issued = 0, landed = 0;
   uint32_t limit = QMAX < nseg ? QMAX : nseg;   // every reader starts at input byte 0
+  if constexpr (LPF) prio_by_progress(0, 1);
   for (;;) {
     while (issued < limit && issued - landed < QMAX) {
       uint32_t blk = issued * (SEG / 16) + lane;
@@ -1405,6 +1427,7 @@ __device__ __forceinline__ void feeder(SM &sm, Ctl &ctl, uint32_t lane, const ui
     const uint32_t k = issued - landed - 1;
     landed++;
     const uint32_t used = land_and_bound_k(k, ctl.need, &ctl.in_avail, landed * SEG);
+    if constexpr (LPF) prio_by_progress(landed, nseg);
     limit = used / SEG + QMAX;
     if (limit > nseg) limit = nseg;
   }
@@ -1783,7 +1806,7 @@ __device__ __forceinline__ void flush_tile(Smem<HLOG> &sm, uint32_t lane, const 
 // Waves 3 .. 3 + NB - 1.  Builder b starts with tile b and then takes the
 // next untaken tile each time it starts one.  SPEC: tiles whose sources are
 // not yet built may be built speculatively (see run()).
-template <int MODE, int HLOG, bool SPEC>
+template <int MODE, int HLOG, bool SPEC, bool LPF>
 struct Builder {
   static constexpr uint32_t HIST = 1u << HLOG, HMASK = HIST - 1, HTILES = HIST / TILE;
   static constexpr uint32_t IMASK = Smem<HLOG>::IMASK;
@@ -2220,6 +2243,7 @@ struct Builder {
       // MODE_GEMM assigns tiles statically (builder b takes b, b + nbs, ...):
       // each builder's partial products then cover a fixed set of tiles,
       // summed in a fixed order, so the product is the same bits every call
+      if constexpr (LPF) prio_by_progress(t, ntiles);
       const uint32_t uv = MODE == MODE_GEMM ? 0u : grab_issue();
       const uint32_t T = t * TILE;
       const uint32_t Tend = T + TILE < N ? T + TILE : N;
@@ -2387,7 +2411,7 @@ struct Builder {
 
 // -------------------------------------------------------------- kernel
 
-template <int MODE, int HLOG, bool SPEC>
+template <int MODE, int HLOG, bool SPEC, bool LPF>
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) chunk_kernel(ChunkParams P) {
   __shared__ __attribute__((aligned(16))) Smem<HLOG> sm;
   __shared__ Ctl ctl;
@@ -2461,9 +2485,10 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     // INT8 tiles write half the fp16 bytes of INT4 tiles per decoded byte,
     // so their builders have slack and the walk sets the pace: the walker
     // then issues ahead of them (11% faster on an 8192 x 8192 matrix; with
-    // INT4 or bytes output the same priority measured 1-3% slower)
-    if constexpr (MODE == MODE_INT8) __builtin_amdgcn_s_setprio(1);
-    Walker<Smem<HLOG>> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
+    // INT4 or bytes output the same priority measured 1-3% slower).
+    // Sequence-dense tables take prio_by_progress instead.
+    if constexpr (MODE == MODE_INT8 && !LPF) __builtin_amdgcn_s_setprio(1);
+    Walker<Smem<HLOG>, LPF> W{sm, ctl, lane, head, y_end, N, 0, 0xFFFFFF00u, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0,
                          direct ? P.seq_pos + s0 : nullptr, direct ? (uint32_t)(s1 - s0) : 0u, 0, head, 0, 0, 0,
                          Rec<Smem<HLOG>>{sm, P.dmax, ctl, lane, N, 0, 0, 0, 0, 0, 0}, direct ? 1u : 0u, -1};
     W.spin = P.spin;
@@ -2486,11 +2511,11 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(8
     if (lane == 0) ctl.status = st;
     lds_set(&ctl.pstate, st == C_OK ? ST_DONE : ST_FAIL, lane);
   } else if (wave == 2) {
-    feeder(sm, ctl, lane, S, y_end, nb, P.spin, check);
+    feeder<Smem<HLOG>, LPF>(sm, ctl, lane, S, y_end, nb, P.spin, check);
   } else if (wave == hwave) {
     hasher(sm, ctl, lane, head, y_end, P.xxh[i], P.spin);
   } else {   // waves 3 .. 7 are builders 0 .. 4; with an index wave 1 is builder 5
-    Builder<MODE, HLOG, SPEC> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
+    Builder<MODE, HLOG, SPEC, LPF> B{sm, ctl, P, d0, lane, wave == 1 ? (uint32_t)NB : wave - 3, N, 0, 0, 0, 0, 0, 0, 0};
     B.chunk = i;
     B.nbs = nb;
     B.run();

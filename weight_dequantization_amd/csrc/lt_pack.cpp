@@ -365,6 +365,24 @@ lt_status lt_order_chunks(const uint64_t *dst_off, uint32_t n_chunks, uint32_t *
   return LT_OK;
 }
 
+lt_status lt_order_chunks_by_sequences(const uint64_t *dst_off, const uint64_t *seq_off, uint32_t n_chunks,
+                                       uint32_t *order) {
+  if (n_chunks == 0) return LT_OK;
+  if (!dst_off || !seq_off || !order) return LT_ERR_INVALID_ARG;
+  for (uint32_t i = 0; i < n_chunks; i++)
+    if (dst_off[i + 1] < dst_off[i] || seq_off[i + 1] < seq_off[i]) return LT_ERR_INVALID_ARG;
+  // largest decoded size first, then the most sequences: on sequence-dense
+  // tables a chunk's life grows with its sequences, and a launch ends with
+  // its slowest chunk
+  for (uint32_t i = 0; i < n_chunks; i++) order[i] = i;
+  std::stable_sort(order, order + n_chunks, [&](uint32_t a, uint32_t b) {
+    const uint64_t sa = dst_off[a + 1] - dst_off[a], sb = dst_off[b + 1] - dst_off[b];
+    if (sa != sb) return sa > sb;
+    return seq_off[a + 1] - seq_off[a] > seq_off[b + 1] - seq_off[b];
+  });
+  return LT_OK;
+}
+
 lt_status lt_index_chunks(const uint8_t *comp, const uint64_t *comp_off, uint32_t n_chunks,
                           uint64_t *seq_off, uint32_t *seq_pos, uint64_t seq_cap, int threads) {
   if (!comp_off || !seq_off) return LT_ERR_INVALID_ARG;
