@@ -459,16 +459,19 @@ def bench_int8(args) -> int:
 def bench_stack(args) -> int:
     """The 80-layer Llama-70B-shaped INT4 stack (q, k, v, o, gate, up, down
     per layer; group 128; 16/64/256 KiB chunks drawn per chunk), resident on
-    the device in the default table form and expanded layer by layer into
-    seven reused fp16 buffers: one lt_fused_lz4_int4 launch per tensor, 560
+    the device in the default table form and expanded layer by layer.  The
+    headline decodes each layer with one lt_fused_lz4_int4 launch over a
+    table of its seven projections end to end (ChunkTable.build_concat: the
+    same compressed chunks, one launch order over the layer) into one fp16
+    buffer; beside it, one launch per tensor into seven reused buffers, 560
     per pass.  Two distinct layers are generated (the seeds of layers 0 and
     79) and copied on the device into 80 separate allocations (even layers
     from layer 0, odd from layer 79); 80 layers of host generation would
-    take far longer than a benchmark may run.  Each layer's seven launches
-    are bracketed by HIP events, timed twice: one after another on one
-    stream, and spread over four streams (the projections are independent);
-    no cache clearing is needed, as each layer reads and writes about
-    2 GB."""
+    take far longer than a benchmark may run.  Each layer's launches are
+    bracketed by HIP events; the per-tensor launches are timed one after
+    another on one stream, and spread over four streams (the projections are
+    independent).  No cache clearing is needed, as each layer reads and
+    writes about 2 GB."""
     import torch
 
     import synth
@@ -476,8 +479,9 @@ def bench_stack(args) -> int:
 
     dev = torch.device("cuda:0")
     names = [n for n, _, _ in synth.LLAMA70B_LAYER]
-    base, host = {}, {}
+    base, host, cat_base = {}, {}, {}
     for src in (0, 79):
+        packs, dsts, scs, zps = [], [], [], []
         for t in range(len(names)):
             w = synth.llama70b_tensor(src, t)
             packed = lt.pack_int4(w.codes)
@@ -486,23 +490,39 @@ def bench_stack(args) -> int:
             base[(src, t)] = (tb, torch.from_numpy(w.scales.view(np.int16)).to(dev), torch.from_numpy(w.zp).to(dev))
             if src == 0 and t == 6:
                 host["down"] = (w, comp, comp_off)
-            del packed
+            packs.append(packed)
+            dsts.append(w.dst_off)
+            scs.append(w.scales)
+            zps.append(w.zp)
             print("stack: layer %d %s packed and resident" % (src, names[t]), file=sys.stderr, flush=True)
-    layers = []
+        # the same layer as one table over its seven projections, end to end
+        ct, _ = lt.ChunkTable.build_concat(packs, dsts, dev)
+        cat_base[src] = (ct, torch.from_numpy(np.concatenate(scs).view(np.int16)).to(dev),
+                         torch.from_numpy(np.concatenate(zps)).to(dev))
+        del packs
+        print("stack: layer %d as one table resident" % src, file=sys.stderr, flush=True)
+    def clone(tb):
+        return lt.ChunkTable(tb.comp.clone(), tb.comp_off.clone(), tb.dst_off.clone(), tb.n_chunks,
+                             tb.max_chunk_bytes, tb.total_bytes, tb.comp_bytes, tb.max_dist,
+                             tb.seq_off.clone(), tb.seq_pos.clone(), tb.n_seq, order=tb.order.clone())
+
+    layers, cat_layers = [], []
     for layer in range(synth.N_LAYERS_70B):
         src = 0 if layer % 2 == 0 else 79
         tensors = []
         for t in range(len(names)):
             tb, sc, zp = base[(src, t)]
-            c = lt.ChunkTable(tb.comp.clone(), tb.comp_off.clone(), tb.dst_off.clone(), tb.n_chunks,
-                              tb.max_chunk_bytes, tb.total_bytes, tb.comp_bytes, tb.max_dist,
-                              tb.seq_off.clone(), tb.seq_pos.clone(), tb.n_seq, order=tb.order.clone())
-            tensors.append((c, sc.clone(), zp.clone()))
+            tensors.append((clone(tb), sc.clone(), zp.clone()))
         layers.append(tensors)
+        ct, sc, zp = cat_base[src]
+        cat_layers.append((clone(ct), sc.clone(), zp.clone()))
     shapes = [(r, c) for _, r, c in synth.LLAMA70B_LAYER]
     outs = [torch.empty(r * c, dtype=torch.float16, device=dev) for r, c in shapes]
     nmax = max(tb.n_chunks for L in layers for tb, _, _ in L)
     statuses = [torch.full((nmax,), -1, dtype=torch.int32, device=dev) for _ in shapes]
+    n_elem_layer = sum(r * c for r, c in shapes)
+    out_cat = torch.empty(n_elem_layer, dtype=torch.float16, device=dev)
+    st_cat = torch.full((max(ct.n_chunks for ct, _, _ in cat_layers),), -1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     side = [torch.cuda.Stream(device=dev) for _ in range(3)]   # default priority
 
@@ -521,30 +541,39 @@ def bench_stack(args) -> int:
         for s_ in side:
             stream.wait_stream(s_)
 
+    def run_layer_table(C):
+        # the whole layer from one table: one launch, the seven projections
+        # back to back in out_cat
+        ct, sc, zp = C
+        lt.fused_lz4_int4(ct, sc, zp, (1, n_elem_layer), 128, out=out_cat, status=st_cat)
+
     def check():
         for t, (tb, _, _) in enumerate(layers[-1]):
             lt.check_status(statuses[t][:tb.n_chunks])
+        lt.check_status(st_cat[:cat_layers[-1][0].n_chunks])
 
     print("stack: 80 layers resident, warming up", file=sys.stderr, flush=True)
     for _ in range(max(1, args.warmup)):
         for L in layers:
             run_layer(L)
+        for C in cat_layers:
+            run_layer_table(C)
     torch.cuda.synchronize()
     check()
     passes = max(1, min(args.steps, 5))
     layer_comp = [sum(tb.comp_bytes for tb, _, _ in L) for L in layers]
-    n_elem_layer = sum(r * c for r, c in shapes)
     alg_layer = np.array([cb + 2 * n_elem_layer for cb in layer_comp], np.float64)
 
-    def time_form(run):
-        for L in layers[:2]:
+    def time_form(run, items=None):
+        items = layers if items is None else items
+        for L in items[:2]:
             run(L)
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in items]
               for _ in range(passes)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for p in range(passes):
-            for L, (a, b) in zip(layers, ev[p]):
+            for L, (a, b) in zip(items, ev[p]):
                 a.record(stream)
                 run(L)
                 b.record(stream)
@@ -563,24 +592,35 @@ def bench_stack(args) -> int:
 
     ms_seq, seq = time_form(run_layer)
     ms_conc, conc = time_form(run_layer_concurrent)
+    ms_one, one = time_form(run_layer_table, cat_layers)
+    # the one-table form decodes the same compressed chunks (laid end to end)
+    assert sum(ct.comp_bytes for ct, _, _ in cat_layers) == sum(layer_comp)
+    torch.cuda.synchronize()
+    bad_forms = 0
+    for t, o in enumerate(outs):   # the last layer, both forms: the same fp16 bytes
+        e0 = sum(r * c for r, c in shapes[:t])
+        bad_forms += int((out_cat[e0:e0 + o.numel()].view(torch.int16) != o.view(torch.int16)).sum().item())
     alg_pass = float(alg_layer.sum())
-    value = alg_pass / ms_conc / 1e6
+    value = alg_pass / ms_one / 1e6
     result = {
         "metric": "fused LZ4+INT4->fp16 GB/s over the 80-layer stack (compressed in + fp16 out), 1 GPU",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": passes, "warmup": max(1, args.warmup),
-        "ms_per_step": round(ms_conc, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_one, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic (seeded; two generated layers copied to 80 device allocations)",
         "config": {"workload": "80 Llama-70B-shaped INT4 layers (q, k, v, o 8192x8192 / 8192x1024; gate, up, "
                                "down 8192x28672), group 128, 16/64/256 KiB LZ4 chunks (host packer, declared "
-                               "window 4096 B, sequence index, largest chunks launched first), 560 fused "
-                               "launches per pass; a step is one pass, each layer's seven launches spread "
-                               "over four streams",
+                               "window 4096 B, sequence index, largest chunks launched first); a step is one "
+                               "pass over the 80 layers, each layer decoded by one fused launch over a table of "
+                               "its seven projections end to end (80 launches per pass)",
                    "compressed_bytes_resident": int(sum(layer_comp)), "fp16_bytes_per_layer": 2 * n_elem_layer},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "lt::chunk_kernel<3, 14, false, false>", "bytes_per_launch": None},
+                     "kernel": "lt::chunk_kernel<3, 14, false, false>",
+                     "avg_launch_ms": one["layer_ms_mean"], "bytes_per_launch": int(alg_layer.mean())},
+        "layer_one_table": one,
         "layer_concurrent": conc,
         "layer_sequential": seq,
+        "mismatches_between_forms": bad_forms,
     }
     bad_cpu = 0
     if not args.no_cpu:
@@ -607,8 +647,9 @@ def bench_stack(args) -> int:
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
-    if bad_cpu:
-        print("GPU output differs from the oracle in %d elements" % bad_cpu, file=sys.stderr)
+    if bad_cpu or bad_forms:
+        print("GPU output differs: %d elements from the oracle, %d between the layer forms" % (bad_cpu, bad_forms),
+              file=sys.stderr)
         return 1
     return 0
 

@@ -1,4 +1,5 @@
-"""GPU parity over the 80-layer Llama-70B-shaped INT4 stack (80 layers).
+"""GPU parity over the 80-layer Llama-70B-shaped INT4 stack (80 layers), and
+one layer decoded from a single table over its seven projections.
 
 Every one of the 80 layers x 7 projections (q, k, v, o, gate, up, down; INT4,
 group 128, LZ4 chunks of 16/64/256 KiB drawn per chunk) is resident on the
@@ -131,3 +132,39 @@ def test_llama70b_layer_in_the_default_table_form():
         assert tb.max_dist == lt.PACK_WINDOW and tb.seq_off is not None
         _full_check(w, tb, torch.from_numpy(w.scales.view(np.int16)).to(DEV), torch.from_numpy(w.zp).to(DEV),
                     "layer 5 tensor %s, default table" % synth.LLAMA70B_LAYER[t][0])
+
+
+def test_llama70b_layer_as_one_table():
+    """One whole layer (layer 3's seeds) as a single table over its seven
+    projections end to end (ChunkTable.build_concat, the benchmark's
+    one-launch-per-layer form): one fused launch, every element checked
+    against the oracle, and each projection's slice against its own
+    launch."""
+    ws = [synth.llama70b_tensor(3, t) for t in range(len(synth.LLAMA70B_LAYER))]
+    packs = [lt.pack_int4(w.codes) for w in ws]
+    table, starts = lt.ChunkTable.build_concat(packs, [w.dst_off for w in ws], DEV)
+    assert table.order is not None and table.seq_off is not None
+    assert starts.tolist() == np.cumsum([0] + [p.size for p in packs[:-1]]).tolist()
+    n = sum(w.rows * w.cols for w in ws)
+    sc = torch.from_numpy(np.concatenate([w.scales for w in ws]).view(np.int16)).to(DEV)
+    zp = torch.from_numpy(np.concatenate([w.zp for w in ws])).to(DEV)
+    st = torch.full((table.n_chunks,), -1, dtype=torch.int32, device=DEV)
+    out = lt.fused_lz4_int4(table, sc, zp, (1, n), 128, status=st)
+    torch.cuda.synchronize()
+    s = st.cpu().numpy()
+    assert np.all(s == 0), np.unique(s)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    ref = O.dequant_int4(O.pack_int4(np.concatenate([w.codes for w in ws])),
+                         np.concatenate([w.scales for w in ws]), np.concatenate([w.zp for w in ws]), 128)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "layer as one table: %d differ, first %d" % (bad.size, bad[0])
+    del ref
+    e0 = 0
+    for t, (w, p) in enumerate(zip(ws, packs)):
+        tb = lt.ChunkTable.build(p, w.dst_off, DEV)
+        one = lt.fused_lz4_int4(tb, torch.from_numpy(w.scales.view(np.int16)).to(DEV),
+                                torch.from_numpy(w.zp).to(DEV), (w.rows, w.cols), 128)
+        torch.cuda.synchronize()
+        sl = got[e0:e0 + w.rows * w.cols]
+        assert np.array_equal(one.view(torch.int16).cpu().numpy().view(np.uint16).ravel(), sl), t
+        e0 += w.rows * w.cols

@@ -562,3 +562,39 @@ def test_release_build_has_no_debug_counters():
     n = C.c_uint32(5)
     assert L.lt_debug_violations(C.byref(n), C.byref(n), 0) == lt.LT_ERR_UNSUPPORTED
     assert L.lt_debug_selftest(None, None) == lt.LT_ERR_UNSUPPORTED
+
+
+def test_build_concat_lays_tables_end_to_end():
+    """A table over several tensors is their tables end to end: the same
+    compressed chunks, offsets shifted, and the oracle decodes it to the
+    tensors' bytes back to back."""
+    import oracle as O
+    rng = np.random.default_rng(12)
+    srcs, dst_offs = [], []
+    for n, chunk in ((70000, 16384), (4096, 4096), (200003, 65536)):
+        src = rng.integers(0, 4, n, dtype=np.uint8) * 17
+        srcs.append(src)
+        dst_offs.append(np.append(np.arange(0, n, chunk, dtype=np.uint64), np.uint64(n)))
+    table, starts = lt.ChunkTable.build_concat(srcs, dst_offs, device="cpu", order=False)
+    assert starts.tolist() == [0, 70000, 74096]
+    assert table.n_chunks == sum(d.size - 1 for d in dst_offs)
+    assert table.total_bytes == sum(s.size for s in srcs)
+    comp = table.comp.numpy()[:table.comp_bytes]
+    comp_off = table.comp_off.numpy().view(np.uint64)
+    dst_off = table.dst_off.numpy().view(np.uint64)
+    k = 0
+    for src, d, st in zip(srcs, dst_offs, starts):
+        one, one_off = lt.compress_chunks(src, d, max_dist=lt.PACK_WINDOW)
+        for j in range(d.size - 1):
+            assert dst_off[k + j] == d[j] + st
+            a = comp[comp_off[k + j]:comp_off[k + j + 1]]
+            assert np.array_equal(a, one[one_off[j]:one_off[j + 1]])
+        k += d.size - 1
+    t = O.Table(comp, comp_off, dst_off)
+    got, st = O.decode_table(t, 4)
+    assert not np.any(st)
+    assert np.array_equal(got[:table.total_bytes], np.concatenate(srcs))
+    with pytest.raises(ValueError):
+        lt.ChunkTable.build_concat(srcs, dst_offs[:2], device="cpu")
+    with pytest.raises(ValueError):
+        lt.ChunkTable.build_concat([srcs[0]], [dst_offs[1]], device="cpu")

@@ -402,6 +402,30 @@ class ChunkTable:
         comp, comp_off = compress_chunks(src, dst_off, threads, max_dist, greedy)
         return cls.from_host(comp, comp_off, dst_off, device, max_dist, index, pin, order, checksum)
 
+    @classmethod
+    def build_concat(cls, srcs, dst_offs, device="cuda", **kw):
+        """One table over several tensors decoded back to back, such as the
+        projections of one model layer: tensor i's chunks follow tensor
+        i - 1's (chunk boundaries as in dst_offs[i]), and its decoded bytes
+        start at starts[i].  Chunks are independent, so this is the tensors'
+        tables laid end to end; one launch over it decodes them all, and the
+        launch order (largest chunks first) spans the whole set.  The
+        tensors' scales and zero points go end to end likewise, so each
+        tensor's groups must end where it ends.  Keyword arguments as for
+        build.  Returns (table, starts)."""
+        srcs = [np.ascontiguousarray(s, np.uint8).ravel() for s in srcs]
+        if len(srcs) == 0 or len(srcs) != len(dst_offs):
+            raise ValueError("one dst_off per tensor, at least one tensor")
+        starts = np.cumsum([0] + [s.size for s in srcs]).astype(np.uint64)
+        parts = []
+        for i, (s, d) in enumerate(zip(srcs, dst_offs)):
+            d = np.ascontiguousarray(d, np.uint64)
+            if d.size < 2 or d[0] != 0 or d[-1] != s.size or np.any(np.diff(d.astype(np.int64)) <= 0):
+                raise ValueError("dst_offs[%d] must rise from 0 to the tensor's size" % i)
+            parts.append(d[(0 if i == 0 else 1):] + starts[i])
+        table = cls.build(np.concatenate(srcs), np.concatenate(parts), device, **kw)
+        return table, starts[:-1]
+
     def as_c(self) -> _Table:
         return _Table(self.comp.data_ptr(), self.comp_off.data_ptr(), self.dst_off.data_ptr(),
                       self.n_chunks, self.max_chunk_bytes, self.total_bytes, self.comp_bytes,
