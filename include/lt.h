@@ -89,7 +89,11 @@ enum {
  * decoded bytes [dst_off[i], dst_off[i+1]) and is stored as one raw LZ4 block
  * (no frame, no size prefix, no dictionary) at comp[comp_off[i] ..
  * comp_off[i+1]).  The blocks are independent: a match never reaches before
- * its own chunk's start.
+ * its own chunk's start.  So one table may also cover several tensors laid
+ * end to end (say the projections of one model layer, with their scales and
+ * zero points end to end too, each tensor's groups ending where it ends):
+ * one call then decodes all of them, and the chunks of every tensor share
+ * one launch.
  *   comp       DEVICE uint8[comp_bytes]
  *   comp_off   DEVICE uint64[n_chunks + 1], non-decreasing, comp_off[n] <= comp_bytes
  *   dst_off    DEVICE uint64[n_chunks + 1], dst_off[0] = 0, non-decreasing,
