@@ -675,3 +675,48 @@ def test_bounded_waits_fail_their_chunk_and_exit(form):
         for i in np.nonzero(s == lt.CHUNK_OK)[0]:
             lo, hi = per * int(d[i]), per * int(d[i + 1])
             assert np.array_equal(got[lo:hi], expect[lo:hi]), (what, i)
+
+
+# ------------------------------------------------ every table class, fused
+
+def test_every_table_class_through_the_fused_kernels():
+    """The fused calls pick a kernel per table: history class (declared 4 KiB
+    window, or any distance), speculative build and progress priority
+    (sequence-dense indexed tables, 3.5 or more sequences per KiB; tables
+    without an index take the speculative build alone), and for INT4 the
+    128-code group path or the general one.  Each combination, from the
+    packer's parse and the greedy one, against the oracle (groups of 128,
+    64 and 448 codes: the last two take the general path, 64 is dense even
+    from the packer, 448 sparse); dense tables carry the
+    most-sequences-first launch order."""
+    seen = set()
+    for group, seed in ((128, 4401), (64, 4402), (448, 4404)):
+        w = synth.int4_weight(96, 28672, group, seed)
+        packed = lt.pack_int4(w.codes)
+        for greedy in (False, True):
+            for md in (lt.PACK_WINDOW, 0):
+                for index in (True, False):
+                    tb = lt.ChunkTable.build(packed, w.dst_off, DEV, max_dist=md, greedy=greedy, index=index)
+                    dense = index and tb.n_seq * 2048 >= 7 * tb.total_bytes
+                    assert (tb.order is not None) == dense
+                    seen.add((group, md, dense, index))
+                    _fused4(tb, w, "g%d %s window %d %s" % (group, "greedy" if greedy else "packer", md,
+                                                          "indexed" if index else "walked"))
+    # both history classes met dense and sparse indexed tables, on both INT4 paths
+    assert {(g == 128, md, d) for g, md, d, i in seen if i} == {(p, md, d) for p in (False, True)
+                                                               for md in (lt.PACK_WINDOW, 0) for d in (False, True)}
+    rng = np.random.default_rng(4403)
+    rows, cols = 64, 8192
+    q = rng.integers(-100, 100, rows * cols).astype(np.int8)
+    q[rng.random(q.size) < 0.7] = 0                  # short runs of zeros: a dense table
+    scales = synth.fp16_bits(rng.uniform(1e-3, 1e-2, rows))
+    dst_off = synth.uniform_chunks(q.size)
+    for md in (lt.PACK_WINDOW, 0):
+        for greedy in (False, True):
+            tb = lt.ChunkTable.build(q.view(np.uint8), dst_off, DEV, max_dist=md, greedy=greedy)
+            st = status_tensor(tb.n_chunks)
+            out = lt.fused_lz4_int8(tb, t_u16(scales), None, (rows, cols), cols, status=st)
+            assert np.all(statuses(st, tb.n_chunks) == 0)
+            assert_same(host_u16(out), O.dequant_int8(q, scales, None, cols),
+                        "int8 window %d %s, %.1f sequences per KiB" % (md, "greedy" if greedy else "packer",
+                                                                       tb.n_seq * 1024 / tb.total_bytes))
