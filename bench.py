@@ -796,12 +796,17 @@ def activation_measurements(torch, lt, dev, timed):
     table = lt.ChunkTable.build(a.data, a.dst_off, dev)
     ob = out.view(torch.uint8)
     ms_lz = timed(lambda: lt.decode_lz4(table, out=ob))
+    idx_bytes = 8 * (table.n_chunks + 1) + 4 * table.n_seq
     return {
         "fp16_bytes": int(a.data.size),
         "zero_runs": {"coded_bytes": int(zr_in), "ms": round(ms_zr, 4),
                       "GBps": round((zr_in + a.data.size) / ms_zr / 1e6, 1)},
         "lz4_decode_only": {"coded_bytes": int(table.comp_bytes), "ms": round(ms_lz, 4),
-                            "GBps": round((table.comp_bytes + a.data.size) / ms_lz / 1e6, 1)},
+                            "GBps": round((table.comp_bytes + a.data.size) / ms_lz / 1e6, 1),
+                            # the sequence index and offsets the decoder reads, counted in
+                            "sequence_index_bytes": idx_bytes,
+                            "fp16_over_footprint": round(a.data.size / (table.comp_bytes + idx_bytes +
+                                                                        16 * (table.n_chunks + 1)), 3)},
     }
 
 
